@@ -1,0 +1,193 @@
+"""Workload recipes: shapes, seeds and value distributions of the synthetic inputs.
+
+A recipe says *what* the decode step is run on (the model's configuration fields
+and where every input tensor's bits come from); it says nothing about how the
+step is computed. Model fields follow the OLMo-3-32B configuration listed on the
+architecture pages (hidden 5,120; 40 query / 8 KV heads of 128; SwiGLU 27,648;
+64 layers laid out as three sliding-window layers then one full-attention layer;
+window 4,096; RoPE theta 500,000 with YaRN x8 from 8,192 on the full layers;
+RMSNorm eps 1e-6; vocabulary 100,278).
+
+Tensor ids are (model_id << 48) | (layer << 16) | kind; the global tensors use
+layer 0xFFFF.
+"""
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+import synth as S
+
+SWA, FULL = 0, 1
+
+# tensor kinds
+K_QKV, K_O, K_GATE, K_UP, K_DOWN = 1, 4, 7, 10, 13  # +0 codes, +1 scales, +2 zeros
+K_GQ, K_GK, K_GPA, K_GPF, K_KC, K_VC = 16, 17, 18, 19, 20, 21
+K_XIN, K_EMB, K_LM, K_GFIN, K_TOK = 32, 33, 34, 35, 36
+GLOBAL_LAYER = 0xFFFF
+
+
+@dataclass
+class Model:
+    d: int
+    hq: int
+    hkv: int
+    hd: int
+    dff: int
+    n_layers: int
+    layer_types: List[int]
+    window: int = 4096
+    group: int = 128
+    theta: float = 500000.0
+    yarn_factor: float = 8.0          # applied on FULL layers only
+    yarn_orig_max: int = 8192
+    yarn_beta_fast: float = 32.0
+    yarn_beta_slow: float = 1.0
+    eps: float = 1e-6
+    vocab: int = 100278
+    model_id: int = 0
+
+    @property
+    def n_qkv(self):
+        return (self.hq + 2 * self.hkv) * self.hd
+
+    def linears(self):
+        """(name, tensor kind, N rows, K columns) of every W4 linear in one layer."""
+        return [("qkv", K_QKV, self.n_qkv, self.d),
+                ("o", K_O, self.d, self.hq * self.hd),
+                ("gate", K_GATE, self.dff, self.d),
+                ("up", K_UP, self.dff, self.d),
+                ("down", K_DOWN, self.d, self.dff)]
+
+
+def olmo3_32b(model_id=3, n_layers=64):
+    types = [FULL if (l % 4) == 3 else SWA for l in range(n_layers)]
+    return Model(d=5120, hq=40, hkv=8, hd=128, dff=27648, n_layers=n_layers, layer_types=types,
+                 model_id=model_id)
+
+
+def tiny(model_id=0):
+    return Model(d=640, hq=5, hkv=1, hd=128, dff=1728, n_layers=1, layer_types=[SWA],
+                 window=64, model_id=model_id)
+
+
+@dataclass
+class Workload:
+    name: str
+    model: Model
+    seed: int
+    n_cached: int              # KV positions 0..n_cached-1 pre-filled; new token at pos = n_cached
+    t_max: int                 # KV slots allocated per layer
+    layer_types: Optional[List[int]] = None
+    use_tokens: bool = False   # config 3/4: embedding input; else x ~ N(0,1)
+    final_head: bool = False   # final norm + lm_head + argmax
+    prompt_len: int = 0        # prefill only
+    extra: dict = field(default_factory=dict)
+
+
+def config(i):
+    """The five workload configurations (0: tiny layer, 1: SWA layer at 4,096 keys,
+    2: full layer at 16,385 keys with YaRN, 3: 64-layer step at 16K, 4: prefill)."""
+    if i == 0:
+        return Workload("tiny-swa-layer", tiny(0), seed=0, n_cached=256, t_max=257)
+    if i == 1:
+        m = olmo3_32b(model_id=1, n_layers=1)
+        m.layer_types = [SWA]
+        return Workload("olmo3-32b-swa-layer-4k", m, seed=0, n_cached=4096, t_max=4097)
+    if i == 2:
+        m = olmo3_32b(model_id=2, n_layers=1)
+        m.layer_types = [FULL]
+        return Workload("olmo3-32b-full-layer-16k-yarn", m, seed=0, n_cached=16384, t_max=16385)
+    if i == 3:
+        return Workload("olmo3-32b-w4-decode-16k", olmo3_32b(3), seed=0, n_cached=16384,
+                        t_max=16385, use_tokens=True, final_head=True)
+    if i == 4:
+        return Workload("olmo3-32b-w4-prefill-1200", olmo3_32b(3), seed=0, n_cached=0,
+                        t_max=1200, use_tokens=True, final_head=True, prompt_len=1200)
+    raise ValueError(i)
+
+
+def tid(model, layer, kind):
+    return (model.model_id << 48) | (layer << 16) | kind
+
+
+def key(wl_or_model, seed, layer, kind):
+    m = wl_or_model.model if isinstance(wl_or_model, Workload) else wl_or_model
+    return S.key(seed, tid(m, layer, kind))
+
+
+# ---- per-layer inputs --------------------------------------------------------
+
+def w4_linear(model, seed, layer, kind, N, K):
+    """Packed codes [N][K/8] u32, f16 scale bits [N][G] u16, packed zeros [N][ceil(G/8)] u32.
+    Codes and zeros ~ U{0..15}; scales ~ U(0.002, 0.02) rounded to f16."""
+    G = -(-K // model.group)
+    codes = S.codes(S.key(seed, tid(model, layer, kind)), N * K // 8).reshape(N, K // 8)
+    scales = S.uniform_f16(S.key(seed, tid(model, layer, kind + 1)), N * G, 0.002, 0.02).reshape(N, G)
+    zeros = S.zeros(S.key(seed, tid(model, layer, kind + 2)), N, G)
+    return codes, scales, zeros
+
+
+def gains(model, seed, layer):
+    """RMSNorm gains ~ N(1, 0.02): q-norm [hq*hd], k-norm [hkv*hd], post-attention [d],
+    post-feedforward [d]."""
+    def g(kind, n):
+        return S.normal_f32(S.key(seed, tid(model, layer, kind)), n, 1.0, 0.02)
+    return {"g_q": g(K_GQ, model.hq * model.hd), "g_k": g(K_GK, model.hkv * model.hd),
+            "g_pa": g(K_GPA, model.d), "g_pf": g(K_GPF, model.d)}
+
+
+def layer_tensors(model, seed, layer):
+    out = {}
+    for name, kind, N, K in model.linears():
+        out[name] = w4_linear(model, seed, layer, kind, N, K)
+    out.update(gains(model, seed, layer))
+    return out
+
+
+def kv_cache_into(model, seed, layer, n_cached, t_max, kdst, vdst):
+    """K and V caches [hkv][t_max][hd] f32; slots 0..n_cached-1 ~ N(0,1). Slots at or
+    past n_cached are left as the caller's buffer holds them."""
+    for kind, dst in ((K_KC, kdst), (K_VC, vdst)):
+        if n_cached > 0:
+            S.normal_f32_3d_into(S.key(seed, tid(model, layer, kind)), model.hkv, n_cached, model.hd,
+                                 t_max * model.hd, model.hd, 0.0, 1.0, dst)
+
+
+def kv_cache(model, seed, layer, n_cached, t_max):
+    Kc = np.zeros((model.hkv, t_max, model.hd), np.float32)
+    Vc = np.zeros((model.hkv, t_max, model.hd), np.float32)
+    kv_cache_into(model, seed, layer, n_cached, t_max, Kc, Vc)
+    return Kc, Vc
+
+
+# ---- global inputs -----------------------------------------------------------
+
+def x_in(model, seed):
+    return S.normal_f32(S.key(seed, tid(model, GLOBAL_LAYER, K_XIN)), model.d, 0.0, 1.0)
+
+
+def final_gain(model, seed):
+    return S.normal_f32(S.key(seed, tid(model, GLOBAL_LAYER, K_GFIN)), model.d, 1.0, 0.02)
+
+
+def prompt_tokens(model, seed, n, stream=0):
+    return S.tokens(S.key(seed, tid(model, GLOBAL_LAYER, K_TOK) + (stream << 8)), n, model.vocab)
+
+
+def embedding_rows(model, seed, r0, nr):
+    """bf16 bits of embedding rows [r0, r0+nr) ~ N(0, 0.02)."""
+    return S.normal_bf16_rows(S.key(seed, tid(model, GLOBAL_LAYER, K_EMB)), r0, nr, model.d, 0.0, 0.02)
+
+
+def lm_head_rows(model, seed, r0, nr):
+    """bf16 bits of lm_head rows [r0, r0+nr) ~ N(0, 0.02)."""
+    return S.normal_bf16_rows(S.key(seed, tid(model, GLOBAL_LAYER, K_LM)), r0, nr, model.d, 0.0, 0.02)
+
+
+def emb_key(model, seed):
+    return S.key(seed, tid(model, GLOBAL_LAYER, K_EMB))
+
+
+def lm_key(model, seed):
+    return S.key(seed, tid(model, GLOBAL_LAYER, K_LM))
