@@ -53,8 +53,8 @@ double orc_bf16_to_f64(uint16_t h) {
 
 /* ---- 4-bit codes ---------------------------------------------------------- */
 
-/* Code of column j in a packed row: word j/8, nibble j%8 at bits 4(j%8)..+3
- * ("col j -> u32 word j/8, little-endian nibble", model card, Quantization recipe). */
+/* Code of column j in a packed row: word j/8, nibble j%8 at bits 4(j%8)..+3, the
+ * lowest nibble holding the lowest column (model card, Quantization recipe). */
 static inline int nib(const uint32_t* row, int64_t j) {
     return (int)((row[j / 8] >> (4 * (j % 8))) & 15u);
 }
@@ -72,8 +72,8 @@ static inline double scale_at(const uint16_t* sc, int64_t G, int64_t n, int64_t 
 
 /* Zero point of (row n, group g). Zeros are packed 8 per word along the group
  * axis with the same nibble order as the codes (our reading; the pages' format is
- * symmetric). A NULL table means the symmetric form of the pages, stored nibble =
- * q + 8, i.e. a zero point of 8 for every group. */
+ * symmetric). A NULL table means the symmetric form of the model card, where the
+ * stored nibble is the signed value plus 8, i.e. a zero point of 8 for every group. */
 static inline int zero_at(const uint32_t* zw, int64_t G, int64_t n, int64_t g) {
     if (!zw) return 8;
     return nib(zw + n * ((G + 7) / 8), g);
@@ -156,7 +156,7 @@ void orc_rmsnorm_residual(const float* x, const float* g, const float* resid, in
  * over pair indices between the correction-range bounds
  *   b(beta) = D * ln(L / (2 pi beta)) / (2 ln theta),
  * rounded outward (low = floor b(beta_fast), high = ceil b(beta_slow)) -- our
- * reading of the model card's "YaRN correction range" fix:
+ * reading of the correction-range fix the model card lists for YaRN:
  *   ramp_i = clamp((i - low) / (high - low), 0, 1)
  *   inv'_i = inv_i * (1 - ramp_i) + (inv_i / s) * ramp_i.                        */
 void orc_rope_inv_freq(int D, double theta, double yarn_factor, double orig_max, double beta_fast,
@@ -189,7 +189,8 @@ double orc_yarn_attention_factor(double yarn_factor) {
 /* Rotate H heads of D dims in place at position pos: pair (i, i + D/2) turns by
  * phi = pos * inv_i (angle and sine/cosine in double) and is scaled by mscale:
  *   x_i' = m (x_i cos phi - x_{i+D/2} sin phi),  x_{i+D/2}' = m (x_{i+D/2} cos phi + x_i sin phi).
- * Rotate-half pairing (i, i + D/2) is our reading of "rotary on the full head". */
+ * Rotate-half pairing (i, i + D/2) is our reading of the field table's statement that
+ * the rotation covers the whole head. */
 void orc_rope(float* x, int H, int D, int64_t pos, const double* inv, double mscale) {
     int P = D / 2;
     for (int h = 0; h < H; h++) {

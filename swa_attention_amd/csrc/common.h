@@ -1,0 +1,180 @@
+// Shared device and host helpers of libatlas (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstdarg>
+#include <cstdio>
+
+#include "../../include/atlas.h"
+
+namespace atlas {
+
+// ---- host-side error reporting ---------------------------------------------------
+
+void set_error(const char* fmt, ...);
+int fail(int status, const char* fmt, ...);
+
+#define ATLAS_CHECK_ARG(cond, ...)                                              \
+    do {                                                                        \
+        if (!(cond)) return ::atlas::fail(ATLAS_ERR_INVALID_ARG, __VA_ARGS__);  \
+    } while (0)
+#define ATLAS_CHECK_SHAPE(cond, ...)                                                 \
+    do {                                                                             \
+        if (!(cond)) return ::atlas::fail(ATLAS_ERR_UNSUPPORTED_SHAPE, __VA_ARGS__); \
+    } while (0)
+#define ATLAS_LAUNCH_CHECK(what)                                                            \
+    do {                                                                                    \
+        hipError_t e_ = hipGetLastError();                                                  \
+        if (e_ != hipSuccess)                                                               \
+            return ::atlas::fail(ATLAS_ERR_HIP, "%s: %s", what, hipGetErrorString(e_));     \
+    } while (0)
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---- wave-level reductions (64 lanes) ------------------------------------------------
+// DPP steps inside each row of 16 lanes (quad xor 1, quad xor 2, half-row mirror,
+// row mirror: every lane ends with its row's total), then two lane-xor exchanges
+// across rows.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f<0x141>(v);  // row_half_mirror
+    v += dpp_f<0x140>(v);  // row_mirror
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    v = fmaxf(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+
+__device__ __forceinline__ float quad_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    return v;
+}
+
+__device__ __forceinline__ float quad_max(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    return v;
+}
+
+__device__ __forceinline__ int quad_sum_i(int v) {
+    v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+    v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+    return v;
+}
+
+// Block-wide sum; every thread gets the result. `red` holds >= 16 floats of LDS.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+    v = wave_sum(v);
+    __syncthreads();
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    float t = 0.f;
+    for (int i = 0; i < nw; i++) t += red[i];
+    return t;
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float scale_to_f32(uint16_t b, int scale_dtype) {
+    return scale_dtype ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+}
+
+// ---- activation encoding for the integer-dot W4 GEMV ----------------------------------
+//
+// A GEMV input x[K] is encoded once per vector, per chunk of 32 consecutive elements
+// (one 16-byte word quad of packed codes):
+//   e_c = exponent with max|x| < 2^e_c over the chunk, q_c = 2^(e_c - 22),
+//   i_k = rint(x_k / q_c), |i_k| <= 2^22 (a 24-bit block floating-point mantissa),
+//   i_k = sum_{p<6} 16^p d_{k,p} with balanced digits d in [-8, 7],
+//   plane word (c, w, p) = the eight digits d_{k,p} of k = 32c + 8w .. 32c + 8w + 7
+//   packed as signed nibbles in the same order as the weight codes.
+// With weight codes c_k (4-bit, in the packing order of the weights) and s = 8 the
+// nibble bias removed by xor 0x88888888:
+//   sum_k (c_k - z) x_k = q_c * ( sum_p 16^p dot8(c - 8, d_p) - (z - 8) * sum_k i_k )
+// for a chunk inside one quantisation group. The digit dot products are exact in
+// int32; the result differs from the f32 value of x only by the rounding of x to
+// 2^-22 of its chunk maximum.
+
+constexpr int XQ_PLANES = 6;
+constexpr int XQ_CHUNK = 32;              // elements per chunk
+constexpr int XQ_WORDS_PER_CHUNK = 24;    // 4 words x 6 planes
+
+struct XQ {                 // views into an encoded vector
+    uint32_t* planes;       // [C][4][6]
+    float* qs;              // [C]
+    int* isum;              // [C]
+};
+
+__host__ __device__ inline size_t xq_bytes(int K) {
+    size_t C = (size_t)K / XQ_CHUNK;
+    return C * (XQ_WORDS_PER_CHUNK * 4 + 8);
+}
+__host__ __device__ inline XQ xq_view(void* base, int K) {
+    size_t C = (size_t)K / XQ_CHUNK;
+    XQ v;
+    v.planes = (uint32_t*)base;
+    v.qs = (float*)((char*)base + C * XQ_WORDS_PER_CHUNK * 4);
+    v.isum = (int*)((char*)base + C * (XQ_WORDS_PER_CHUNK * 4 + 4));
+    return v;
+}
+
+// Encode word `w` (8 elements x8[0..7]) of chunk `c`; the 4 threads of a chunk must
+// be lanes 4j..4j+3 of one wave (quad) and call this together.
+__device__ __forceinline__ void xq_encode_word(const float x8[8], XQ out, int c, int w) {
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(x8[i]));
+    m = quad_max(m);
+    int e = (m > 0.f) ? __builtin_amdgcn_frexp_expf(m) : 0;   // m < 2^e
+    int pl[XQ_PLANES] = {0, 0, 0, 0, 0, 0};
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        int v = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(x8[i], 22 - e));
+        s += v;
+#pragma unroll
+        for (int p = 0; p < XQ_PLANES; p++) {
+            int d = ((v + 8) & 15) - 8;
+            pl[p] |= (d & 15) << (4 * i);
+            v = (v - d) >> 4;
+        }
+    }
+    s = quad_sum_i(s);
+    uint32_t* dst = out.planes + (size_t)c * XQ_WORDS_PER_CHUNK + w * XQ_PLANES;
+#pragma unroll
+    for (int p = 0; p < XQ_PLANES; p++) dst[p] = (uint32_t)pl[p];
+    if (w == 0) {
+        out.qs[c] = __builtin_amdgcn_ldexpf(1.0f, e - 22);
+        out.isum[c] = s;
+    }
+}
+
+}  // namespace atlas

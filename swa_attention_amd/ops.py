@@ -1,0 +1,203 @@
+"""Thin Python wrappers over the C ABI with the entry points' names.
+
+Tensors are torch CUDA (HIP) tensors; PyTorch provides device memory and the
+stream, every computation runs in libatlas.so. Each wrapper validates dtype and
+contiguity, marshals pointers and raises AtlasError on a non-zero status.
+"""
+import ctypes
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import torch
+
+from . import _lib as L
+
+F32, U16, I32 = torch.float32, torch.int16, torch.int32
+
+
+def _dev(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+# ---- W4 linear --------------------------------------------------------------------------------
+
+@dataclass
+class W4:
+    """A packed W4 linear held in device memory: qweight int32 [N][K/8], scales int16
+    (f16 or bf16 bits) [N][G], zeros int32 [N][ceil(G/8)] or None."""
+    qweight: torch.Tensor
+    scales: torch.Tensor
+    zeros: Optional[torch.Tensor]
+    N: int
+    K: int
+    group: int = 128
+    scale_dtype: int = 0
+
+    def c(self):
+        return L.atlas_w4(self.qweight.data_ptr(), self.scales.data_ptr(),
+                          self.zeros.data_ptr() if self.zeros is not None else None,
+                          self.N, self.K, self.group, self.scale_dtype)
+
+
+def atlas_w4_gemv_workspace_bytes(w: W4):
+    return L.lib().atlas_w4_gemv_workspace_bytes(ctypes.byref(w.c()))
+
+
+def atlas_w4_gemv(w: W4, x, y=None, ws=None, stream=None):
+    _dev(x, F32, "x")
+    if y is None:
+        y = torch.empty(w.N, dtype=F32, device=x.device)
+    _dev(y, F32, "y")
+    need = atlas_w4_gemv_workspace_bytes(w)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    L.call("atlas_w4_gemv", ctypes.byref(w.c()), L.ptr(x), L.ptr(y), L.ptr(ws), ws.numel(), L.stream_ptr(stream))
+    return y
+
+
+def atlas_w4_dequant(w: W4, out=None, stream=None):
+    if out is None:
+        out = torch.empty((w.N, w.K), dtype=F32, device=w.qweight.device)
+    _dev(out, F32, "out")
+    L.call("atlas_w4_dequant", ctypes.byref(w.c()), L.ptr(out), L.stream_ptr(stream))
+    return out
+
+
+# ---- norms, rotary, attention -------------------------------------------------------------------
+
+def atlas_rmsnorm_residual(x, g, resid=None, out=None, eps=1e-6, stream=None):
+    _dev(x, F32, "x"), _dev(g, F32, "g"), _dev(resid, F32, "resid")
+    if out is None:
+        out = torch.empty_like(x)
+    L.call("atlas_rmsnorm_residual", L.ptr(x), L.ptr(g), L.ptr(resid), L.ptr(out), x.numel(), eps,
+           L.stream_ptr(stream))
+    return out
+
+
+def rope_params(theta=500000.0, yarn_factor=1.0, orig_max_pos=8192, beta_fast=32.0, beta_slow=1.0,
+                attention_factor=0.0):
+    return L.atlas_rope(theta, yarn_factor, float(orig_max_pos), beta_fast, beta_slow, attention_factor)
+
+
+def atlas_qk_norm_rope(q, k, gq, gk, Hq, Hkv, D, d_pos, rope, eps=1e-6, stream=None):
+    for t, n in ((q, "q"), (k, "k"), (gq, "gq"), (gk, "gk")):
+        _dev(t, F32, n)
+    _dev(d_pos, I32, "d_pos")
+    L.call("atlas_qk_norm_rope", L.ptr(q), L.ptr(k), L.ptr(gq), L.ptr(gk), Hq, Hkv, D, L.ptr(d_pos),
+           ctypes.byref(rope), eps, L.stream_ptr(stream))
+    return q, k
+
+
+def atlas_gqa_decode_workspace_bytes(Hq, Hkv, D, T_max):
+    return L.lib().atlas_gqa_decode_workspace_bytes(Hq, Hkv, D, T_max)
+
+
+def atlas_gqa_decode(q, k_cache, v_cache, Hq, Hkv, D, T_max, d_pos, window, scale=None, out=None, ws=None,
+                     stream=None):
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, F32, n)
+    _dev(d_pos, I32, "d_pos")
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty(Hq * D, dtype=F32, device=q.device)
+    need = atlas_gqa_decode_workspace_bytes(Hq, Hkv, D, T_max)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    L.call("atlas_gqa_decode", L.ptr(q), L.ptr(k_cache), L.ptr(v_cache), Hq, Hkv, D, T_max, L.ptr(d_pos), window,
+           scale, L.ptr(out), L.ptr(ws), ws.numel(), L.stream_ptr(stream))
+    return out
+
+
+# ---- model --------------------------------------------------------------------------------------
+
+@dataclass
+class Layer:
+    qkv: W4
+    o: W4
+    gate: W4
+    up: W4
+    down: W4
+    g_q: torch.Tensor
+    g_k: torch.Tensor
+    g_pa: torch.Tensor
+    g_pf: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    type: int
+
+    def c(self):
+        return L.atlas_layer(self.qkv.c(), self.o.c(), self.gate.c(), self.up.c(), self.down.c(),
+                             self.g_q.data_ptr(), self.g_k.data_ptr(), self.g_pa.data_ptr(), self.g_pf.data_ptr(),
+                             self.k_cache.data_ptr(), self.v_cache.data_ptr(), self.type)
+
+
+@dataclass
+class Model:
+    d: int
+    hq: int
+    hkv: int
+    hd: int
+    dff: int
+    window: int
+    vocab: int
+    eps: float
+    t_max: int
+    rope_swa: object
+    rope_full: object
+    layers: List[Layer] = field(default_factory=list)
+    embedding: Optional[torch.Tensor] = None
+    g_final: Optional[torch.Tensor] = None
+    lm_head: Optional[torch.Tensor] = None
+    _c: object = None
+    _arr: object = None
+
+    def c(self):
+        """The atlas_model struct (rebuilt when the layer list changes)."""
+        arr = (L.atlas_layer * len(self.layers))(*[l.c() for l in self.layers])
+        self._arr = arr
+        self._c = L.atlas_model(self.d, self.hq, self.hkv, self.hd, self.dff, len(self.layers), self.window,
+                                self.vocab, self.eps, self.t_max, self.rope_swa, self.rope_full,
+                                ctypes.cast(arr, ctypes.POINTER(L.atlas_layer)),
+                                None if self.embedding is None else self.embedding.data_ptr(),
+                                None if self.g_final is None else self.g_final.data_ptr(),
+                                None if self.lm_head is None else self.lm_head.data_ptr())
+        return self._c
+
+
+def atlas_decode_workspace_bytes(m: Model):
+    return L.lib().atlas_decode_workspace_bytes(ctypes.byref(m.c()))
+
+
+def atlas_decode_step(m: Model, d_pos, d_token=None, hidden_in=None, hidden_out=None, logits=None, argmax=None,
+                      ws=None, stream=None, cm=None):
+    """One decode step. ``cm``: a prebuilt atlas_model struct (m.c()) to skip rebuilding."""
+    cm = cm if cm is not None else m.c()
+    L.call("atlas_decode_step", ctypes.byref(cm), L.ptr(d_token), L.ptr(hidden_in), L.ptr(d_pos),
+           L.ptr(hidden_out), L.ptr(logits), L.ptr(argmax), L.ptr(ws), 0 if ws is None else ws.numel(),
+           L.stream_ptr(stream))
+
+
+def atlas_device_status(ws, stream=None):
+    out = ctypes.c_int32(-1)
+    L.call("atlas_device_status", L.ptr(ws), L.stream_ptr(stream), ctypes.byref(out))
+    return out.value
+
+
+def atlas_prefill_workspace_bytes(m: Model, n_tokens):
+    return L.lib().atlas_prefill_workspace_bytes(ctypes.byref(m.c()), n_tokens)
+
+
+def atlas_prefill(m: Model, d_tokens, start_pos=0, logits=None, argmax=None, ws=None, stream=None, cm=None):
+    cm = cm if cm is not None else m.c()
+    _dev(d_tokens, I32, "tokens")
+    L.call("atlas_prefill", ctypes.byref(cm), L.ptr(d_tokens), d_tokens.numel(), start_pos, L.ptr(logits),
+           L.ptr(argmax), L.ptr(ws), 0 if ws is None else ws.numel(), L.stream_ptr(stream))

@@ -1,0 +1,144 @@
+"""Decode-step and prefill parity of the HIP path against the CPU oracle (GPU).
+
+Bar: normwise ||gpu - oracle||_inf / ||oracle||_inf <= 1e-3 on f32 hidden states and
+logits, identical greedy argmax, bit-identical KV slot placement (the new key and
+value land in slot pos and nowhere else)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle import runner as R
+from synth import workloads as W
+from synth.device import build_model
+from swa_attention_amd import ops
+from gpu_util import TOL, announce, device, normwise
+
+pytestmark = pytest.mark.gpu
+
+
+def _ws(dm, dev):
+    return torch.empty(ops.atlas_decode_workspace_bytes(dm), dtype=torch.uint8, device=dev)
+
+
+def _run_layer_case(wl, dev):
+    m = wl.model
+    dm = build_model(wl, dev, head=False)
+    x = torch.from_numpy(W.x_in(m, wl.seed)).to(dev)
+    out = torch.empty(m.d, dtype=torch.float32, device=dev)
+    pos = torch.tensor([wl.n_cached], dtype=torch.int32, device=dev)
+    ws = _ws(dm, dev)
+    k_before = dm.layers[0].k_cache.clone()
+    ops.atlas_decode_step(dm, pos, hidden_in=x, hidden_out=out, ws=ws)
+    torch.cuda.synchronize()
+    assert ops.atlas_device_status(ws) == 0
+    tr = {}
+    y, Kc, Vc = R.run_layer(wl, 0, trace=tr)
+    p = wl.n_cached
+    gk = dm.layers[0].k_cache.cpu().numpy()
+    gv = dm.layers[0].v_cache.cpu().numpy()
+    # only slot p changed, and it holds the rotated k / raw v
+    kb = k_before.cpu().numpy()
+    changed = np.nonzero(np.any(gk != kb, axis=(0, 2)))[0]
+    assert list(changed) == [p]
+    assert normwise(gk[:, p], Kc[:, p]) < 1e-5
+    assert normwise(gv[:, p], Vc[:, p]) < 1e-5
+    return normwise(out.cpu().numpy(), y)
+
+
+def test_decode_step_tiny_layer():
+    dev = device()
+    announce("decode tiny layer (d 640, 5/1 heads, window 64, 256 cached)")
+    err = _run_layer_case(W.config(0), dev)
+    assert err < TOL, err
+
+
+def test_decode_step_swa_layer_full_size():
+    dev = device()
+    announce("decode OLMo-3-32B SWA layer, 4,096 cached")
+    err = _run_layer_case(W.config(1), dev)
+    print("normwise", err)
+    assert err < TOL, err
+
+
+def test_decode_step_full_layer_yarn_full_size():
+    dev = device()
+    announce("decode OLMo-3-32B full layer with YaRN, 16,384 cached")
+    err = _run_layer_case(W.config(2), dev)
+    print("normwise", err)
+    assert err < TOL, err
+
+
+def _tiny_stack(n_layers=4, vocab=1000, n_cached=80, t_max=128, window=64, model_id=7):
+    m = W.tiny(model_id)
+    m.n_layers = n_layers
+    m.layer_types = [W.FULL if l % 4 == 3 else W.SWA for l in range(n_layers)]
+    m.vocab = vocab
+    m.window = window
+    return W.Workload("tiny-stack", m, seed=0, n_cached=n_cached, t_max=t_max, use_tokens=True, final_head=True)
+
+
+def test_decode_step_tiny_stack_with_head():
+    dev = device()
+    wl = _tiny_stack()
+    announce("decode tiny 4-layer stack + lm_head + argmax")
+    dm = build_model(wl, dev)
+    tok = R.decode_token(wl)
+    d_tok = torch.tensor([tok], dtype=torch.int32, device=dev)
+    pos = torch.tensor([wl.n_cached], dtype=torch.int32, device=dev)
+    logits = torch.empty(wl.model.vocab, dtype=torch.float32, device=dev)
+    am = torch.empty(1, dtype=torch.int32, device=dev)
+    hid = torch.empty(wl.model.d, dtype=torch.float32, device=dev)
+    ws = _ws(dm, dev)
+    ops.atlas_decode_step(dm, pos, d_token=d_tok, hidden_out=hid, logits=logits, argmax=am, ws=ws)
+    ref = R.run_decode(wl)
+    assert normwise(hid.cpu().numpy(), ref["y"]) < TOL
+    assert normwise(logits.cpu().numpy(), ref["logits"]) < TOL
+    assert int(am.item()) == ref["argmax"]
+
+
+def test_bad_position_sets_status_and_leaves_cache():
+    dev = device()
+    wl = _tiny_stack(n_layers=1)
+    dm = build_model(wl, dev)
+    pos = torch.tensor([wl.t_max], dtype=torch.int32, device=dev)     # one past the end
+    x = torch.zeros(wl.model.d, dtype=torch.float32, device=dev)
+    ws = _ws(dm, dev)
+    before = dm.layers[0].k_cache.clone()
+    ops.atlas_decode_step(dm, pos, hidden_in=x, ws=ws)
+    assert ops.atlas_device_status(ws) == 1
+    assert torch.equal(before, dm.layers[0].k_cache)
+    pos.fill_(5)
+    ops.atlas_decode_step(dm, pos, hidden_in=x, ws=ws)
+    assert ops.atlas_device_status(ws) == 0
+
+
+def test_prefill_equals_teacher_forced_decode_and_oracle():
+    dev = device()
+    wl = _tiny_stack(n_cached=0, t_max=64)
+    announce("prefill tiny 4-layer stack, 12 tokens")
+    toks = W.prompt_tokens(wl.model, wl.seed, 12, stream=1)
+    dm = build_model(wl, dev)
+    d_toks = torch.from_numpy(toks).to(dev)
+    logits = torch.empty(wl.model.vocab, dtype=torch.float32, device=dev)
+    am = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(ops.atlas_prefill_workspace_bytes(dm, len(toks)), dtype=torch.uint8, device=dev)
+    ops.atlas_prefill(dm, d_toks, 0, logits, am, ws)
+    ref = R.run_prefill(wl, toks)
+    n = len(toks)
+    for l in range(wl.model.n_layers):
+        assert normwise(dm.layers[l].k_cache[:, :n].cpu().numpy(), ref["K"][l][:, :n]) < TOL
+        assert normwise(dm.layers[l].v_cache[:, :n].cpu().numpy(), ref["V"][l][:, :n]) < TOL
+        assert torch.count_nonzero(dm.layers[l].k_cache[:, n:]).item() == 0
+    assert normwise(logits.cpu().numpy(), ref["logits"]) < TOL
+    assert int(am.item()) == ref["argmax"]
+    # teacher-forced GPU decode on a fresh copy of the model
+    dm2 = build_model(wl, dev)
+    ws2 = _ws(dm2, dev)
+    lg2 = torch.empty_like(logits)
+    for t in range(n):
+        ops.atlas_decode_step(dm2, torch.tensor([t], dtype=torch.int32, device=dev),
+                              d_token=d_toks[t:t + 1], logits=lg2 if t == n - 1 else None, ws=ws2)
+    assert normwise(logits.cpu().numpy(), lg2.cpu().numpy()) < TOL
+    for l in range(wl.model.n_layers):
+        assert normwise(dm.layers[l].k_cache.cpu().numpy(), dm2.layers[l].k_cache.cpu().numpy()) < TOL
