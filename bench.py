@@ -1,0 +1,176 @@
+"""Decode throughput of the W4 OLMo-3-32B-shaped step on one MI355X.
+
+Workload (default): the full 64-layer random-init stack ([SWA x3, full] x16, d 5,120,
+40/8 heads of 128, SwiGLU 27,648, W4 group-128 weights with f16 scales and uint4
+zeros), f32 KV cache pre-filled to 16,384 positions in every layer, batch 1, one new
+token at position 16,384 (SWA layers read the last 4,096 keys, full layers all
+16,385), final RMSNorm, bf16 lm_head 100,278 x 5,120 and greedy argmax. Each step
+feeds back the previous step's argmax token. Inputs are seeded synthetic values
+resident in HBM before timing starts.
+
+Prints one JSON line: tokens/s, ms/step, achieved algorithmic HBM GB/s of the step,
+the roofline of the dominant kernel (the gate/up W4 GEMV) measured with HIP events
+on the launch stream, and the CPU oracle's throughput on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, budget_s):
+    """Oracle (CPU, double accumulation, OpenMP) on whole [SWA,SWA,SWA,full] blocks of
+    the same workload until ~budget_s of compute, plus the lm_head; extrapolated to
+    the 64-layer token. Input generation is not timed."""
+    import numpy as np
+    import oracle as O
+    from oracle import runner as R
+    from synth import workloads as W
+    m = wl.model
+    x = O.embed(W.embedding_rows(m, wl.seed, R.decode_token(wl), 1)[0])
+    t_layers, n_done = 0.0, 0
+    while n_done < m.n_layers and t_layers < budget_s:
+        for l in range(n_done, n_done + 4):
+            T, Kc, Vc = R.layer_inputs(wl, l)
+            t0 = time.perf_counter()
+            x = O.layer_step(m, m.layer_types[l], T, x, Kc, Vc, wl.n_cached)
+            t_layers += time.perf_counter() - t0
+            del T, Kc, Vc
+        n_done += 4
+    lm = W.lm_head_rows(m, wl.seed, 0, m.vocab)
+    g = W.final_gain(m, wl.seed)
+    t0 = time.perf_counter()
+    O.final_logits(x, g, lm, m.eps)
+    t_head = time.perf_counter() - t0
+    per_token = t_layers * m.n_layers / n_done + t_head
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    threads = min(threads, len(os.sched_getaffinity(0)))
+    sample = (f"{n_done} of {m.n_layers} layers ({n_done // 4} [SWA,SWA,SWA,full] blocks at 16,384 cached) "
+              f"+ final norm + bf16 lm_head, timed {t_layers + t_head:.1f} s, extrapolated x{m.n_layers / n_done:g} "
+              f"over layers")
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": threads, "kind": "oracle", "sample": sample,
+            "s_per_token": per_token}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload config (3 = 64-layer 16K decode)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle compute in the CPU leg")
+    ap.add_argument("--profile-steps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "How the step would shard over several GPUs is described in DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synth import workloads as W
+    from synth.device import build_model
+    from swa_attention_amd import accounting as A
+    from swa_attention_amd import ops
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    wl = W.config(args.config)
+    m = wl.model
+    log(f"workload {wl.name}: building the device model ({m.n_layers} layers)")
+    t0 = time.time()
+    dm = build_model(wl, dev, progress=lambda l: (l % 8 == 7) and log(f"  layer {l + 1}/{m.n_layers} resident"))
+    torch.cuda.synchronize()
+    log(f"model resident in {time.time() - t0:.1f} s, {torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
+
+    from oracle import runner as R   # only for the seeded first token id (no oracle arithmetic)
+    tok = torch.tensor([R.decode_token(wl)], dtype=torch.int32, device=dev)
+    pos = torch.tensor([wl.n_cached], dtype=torch.int32, device=dev)
+    head = wl.final_head
+    logits = torch.empty(m.vocab, dtype=torch.float32, device=dev) if head else None
+    am = tok if head else None      # each step feeds back its argmax
+    hidden = torch.empty(m.d, dtype=torch.float32, device=dev)
+    x_in = None if wl.use_tokens else torch.from_numpy(W.x_in(m, wl.seed)).to(dev)
+    ws = torch.empty(ops.atlas_decode_workspace_bytes(dm), dtype=torch.uint8, device=dev)
+    cm = dm.c()
+
+    def step():
+        ops.atlas_decode_step(dm, pos, d_token=tok if wl.use_tokens else None, hidden_in=x_in,
+                              hidden_out=None if head else hidden, logits=logits, argmax=am, ws=ws, cm=cm)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = dt * 1e3 / args.steps
+    assert ops.atlas_device_status(ws) == 0
+
+    # per-launch timing pass (HIP events on the launch stream)
+    ops.atlas_profile_start(4096 * max(1, args.profile_steps))
+    for _ in range(args.profile_steps):
+        step()
+    prof = ops.atlas_profile_stop()
+    log("per-launch timing: " + ", ".join(f"{k} {v[0]}x {v[1] / v[0] * 1e3:.1f}us" for k, v in
+                                          sorted(prof.items(), key=lambda kv: -kv[1][1])))
+
+    sb = A.decode_step_bytes(m, wl.n_cached, head=head)
+    gbps = sb.total / (ms * 1e-3) / 1e9
+    dom = "w4_gemv_gate_up"
+    roof = None
+    if dom in prof:
+        cnt, tot = prof[dom]
+        avg_s = tot / cnt * 1e-3
+        # one launch streams the gate and the up matrix ([dff][d] each)
+        per_launch = 2 * A.w4_bytes(m.dff, m.d, m.group)
+        ach = per_launch / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None,
+                "kernel": f"gate_up_kernel (2 x {m.dff}x{m.d} W4 + SwiGLU)", "bytes_per_launch": per_launch,
+                "avg_launch_us": round(avg_s * 1e6, 2), "launches": cnt}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline (bounded sample)")
+        cpu = cpu_baseline(wl, args.cpu_budget)
+
+    out = {
+        "metric": "decode tokens/s at batch 1, 32B W4, 16K ctx + achieved HBM GB/s vs peak",
+        "value": round(1e3 / ms, 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": m.n_layers, "context": wl.n_cached, "batch": 1,
+                   "weights": "int4 group-128, f16 scales, uint4 zeros", "kv": "f32", "lm_head": "bf16"},
+        "achieved_GBps": round(gbps, 1),
+        "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+        "bytes_per_step": sb.total,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -192,6 +192,22 @@ ATLAS_API size_t atlas_prefill_workspace_bytes(const atlas_model* m, int32_t n_t
 ATLAS_API int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int32_t n_tokens, int32_t start_pos,
                   float* d_last_logits, int32_t* d_argmax, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- launch timing (measurement aid) -------------------------------------------------
+ * Between atlas_profile_start(capacity) and atlas_profile_stop(), every kernel launch
+ * of the library is preceded by a hipEvent on its stream (at most `capacity`
+ * launches). atlas_profile_stop synchronises, then reports per launch label the
+ * number of launches and the summed time from each launch's event to the next event
+ * on the stream (the kernel's execution plus any gap before the next launch). Not
+ * thread-safe; meant for a single stream. */
+typedef struct atlas_profile_entry {
+    char name[48];
+    int32_t count;
+    double total_ms;
+} atlas_profile_entry;
+
+ATLAS_API int atlas_profile_start(int32_t capacity);
+ATLAS_API int atlas_profile_stop(atlas_profile_entry* out, int32_t max_entries, int32_t* n_entries);
+
 #ifdef __cplusplus
 }
 #endif

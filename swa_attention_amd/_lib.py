@@ -37,6 +37,10 @@ class atlas_model(ctypes.Structure):
                 ("lm_head", c_void_p)]
 
 
+class atlas_profile_entry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("count", c_int32), ("total_ms", c_double)]
+
+
 P = ctypes.POINTER
 _SIGS = {
     "atlas_version": (ctypes.c_char_p, []),
@@ -58,6 +62,8 @@ _SIGS = {
     "atlas_prefill_workspace_bytes": (c_size_t, [P(atlas_model), c_int32]),
     "atlas_prefill": (ctypes.c_int, [P(atlas_model), c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                      c_size_t, c_void_p]),
+    "atlas_profile_start": (ctypes.c_int, [c_int32]),
+    "atlas_profile_stop": (ctypes.c_int, [P(atlas_profile_entry), c_int32, P(c_int32)]),
 }
 
 _lib = None

@@ -15,6 +15,7 @@ namespace atlas {
 
 void set_error(const char* fmt, ...);
 int fail(int status, const char* fmt, ...);
+void prof_mark(const char* label, hipStream_t st);   // no-op unless profiling
 
 #define ATLAS_CHECK_ARG(cond, ...)                                              \
     do {                                                                        \

@@ -1,12 +1,14 @@
 // Internal interface of the decode step.
 #pragma once
-#include "common.h"
+#include "decode_kernels.h"
 
 namespace atlas {
 
-constexpr int LM_BLOCKS = 1024;   // lm_head workgroups (argmax partials)
-
 int validate_model(const atlas_model* m);
 size_t decode_ws_bytes(const atlas_model* m);
+int run_decode_layers(const atlas_model* m, const XSource& first, const int32_t* d_pos, void* ws, hipStream_t st,
+                      XSource* last_out);
+int run_head(const atlas_model* m, const XSource& last, void* ws, float* hidden_out, float* logits_out,
+             int32_t* argmax_out, hipStream_t st);
 
 }  // namespace atlas

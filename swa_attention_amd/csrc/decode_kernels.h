@@ -1,0 +1,114 @@
+// Fused kernels of the decode step (internal interface).
+#pragma once
+#include "gemv_core.h"
+
+namespace atlas {
+
+constexpr int GEMV_THREADS = 512;   // 8 waves per GEMV block
+constexpr int ATTN_THREADS = 256;   // 4 waves = 16 key streams per attention block
+constexpr int ATTN_PART_F = 130;    // m, l, acc[128] per (query head, split)
+
+// How a QKV block obtains the layer input x.
+enum XMode { X_FROM_EMBED = 0, X_FROM_HIDDEN = 1, X_FROM_RESIDUAL = 2 };
+
+struct XSource {
+    int mode;
+    const int32_t* d_token;     // X_FROM_EMBED
+    const uint16_t* emb;        //   bf16 [vocab][d]
+    int vocab;
+    const float* hidden;        // X_FROM_HIDDEN: f32 [d]
+    const float* m_part;        // X_FROM_RESIDUAL: x = h + g * m / rms(m), m = sum of S partials
+    int S;
+    const float* h;
+    const float* g;
+    float eps;
+};
+
+struct QkvArgs {
+    W4View W;
+    XSource src;
+    int d, group, CW, tiles_per_block;
+    float* qkv;          // [N] out
+    float* x_out;        // [d] out (block 0): the layer input, kept for the residual
+    int* status;         // reset to OK by block 0 (or set on a bad token id)
+};
+
+struct AttnFusedArgs {
+    const float* qkv;          // raw projection: q [Hq*D], k [Hkv*D], v [Hkv*D]
+    const float *g_q, *g_k;
+    float* k_cache;
+    float* v_cache;
+    int64_t T_max;
+    const int32_t* d_pos;
+    int Hq, Hkv, window, S;
+    float scale, eps;
+    double inv[64];            // rotary inverse frequencies (D = 128)
+    double mscale;
+    float* part;               // [Hq][S][130]
+    int* status;
+    int fused;                 // 1: q/k/v from qkv with norm + rotary + KV append; 0: q final, cache ready
+    const float* q_final;      // fused == 0
+};
+
+struct MergeArgs {
+    const float* part;
+    int S, Hq;
+    float* o;     // may be null
+    XQ xq;        // planes may be null
+};
+
+struct GemvPlanesArgs {    // encoded input already in global memory
+    W4View W;
+    XQ xq;
+    int group, CW, tiles_per_block;
+    float* y;              // [S][N] (blockIdx.y = range)
+};
+
+struct GateUpArgs {
+    W4View Wg, Wu;
+    const float *a, *x, *g;     // h = x + g * a / rms(a)
+    float eps;
+    int d, group, CW, tiles_per_block;
+    float* h_out;               // block 0
+    float* z;                   // [dff]
+};
+
+struct DownArgs {
+    W4View W;
+    const float* z;             // f32 [K]
+    int group, CW, tiles_per_block;
+    float* m_part;              // [S][N]
+};
+
+struct HeadArgs {
+    const uint16_t* lm;         // bf16 [V][d]
+    int V, d, rows_per_block;
+    XSource src;                // X_FROM_RESIDUAL: last layer's output
+    const float* g_final;
+    float eps;
+    float* hidden_out;          // may be null (block 0)
+    float* logits;
+    float* bmax;
+    int* bidx;
+};
+
+struct GemvShape {
+    int CPL, RB, CW, S, tiles_per_block, blocks;
+};
+// Reduction ranges, tile shape and grid of a W4 GEMV. max_cpl bounds the register
+// footprint (the gate/up kernel holds two matrices' tiles and uses 3).
+GemvShape gemv_shape(int N, int K, bool split_k, int target_blocks, int max_cpl = 5);
+
+int launch_qkv(const QkvArgs& a, const GemvShape& s, hipStream_t st);
+int launch_attn_fused(const AttnFusedArgs& a, int G, hipStream_t st);
+int launch_merge(const MergeArgs& a, hipStream_t st);
+int launch_gemv_planes(const GemvPlanesArgs& a, const GemvShape& s, hipStream_t st, const char* label);
+int launch_gate_up(const GateUpArgs& a, const GemvShape& s, hipStream_t st);
+int launch_down(const DownArgs& a, const GemvShape& s, hipStream_t st);
+int launch_head(const HeadArgs& a, int blocks, hipStream_t st);
+int launch_final_hidden(const XSource& src, int d, float* out, hipStream_t st);
+int launch_argmax_final(const float* bmax, const int* bidx, int nb, int32_t* out, hipStream_t st);
+
+int attn_splits(int64_t maxkeys, int Hkv);
+
+}  // namespace atlas

@@ -1,0 +1,931 @@
+// Fused kernels of the decode step. One decoder layer is six launches:
+//   qkv      W_qkv x, where x = h + RMSNorm_pf(m) of the previous layer is rebuilt
+//            and encoded by every block in its prologue (m summed from the down
+//            projection's split-K partials);
+//   attn     per (KV head, key split): full-projection QK RMSNorm, RoPE (+YaRN
+//            factor), new key/value written to slot pos, then an online-softmax pass
+//            over the split's keys for the Hq/Hkv query heads sharing the KV head;
+//   merge    rescales the split partials into o and encodes it;
+//   o        W_o o;
+//   gate/up  h = x + RMSNorm_pa(a) rebuilt per block, then both SwiGLU projections
+//            of the same rows and z = silu(gate) * up;
+//   down     split-K W_down z; every block encodes its own range of z.
+// Sources: "ATLAS-OLMo-3-32B-Think-v4" (Architecture deep-dive; Quantization
+// recipe), "OLMo 3 32B" knowledge-base page (reordered post-norm; QK RMSNorm before
+// the dot product), "Olmo-3-1125-32B" (eps, SwiGLU, YaRN on full layers only).
+// No kernel uses atomics or waits on another block: every dependency is a launch
+// boundary, and normalisation statistics are recomputed where they are needed.
+// Prologue loads are issued all at once (one memory latency, not one per element)
+// and weight loads of the first tile are in flight while the prologue runs.
+#include <algorithm>
+
+#include "decode_kernels.h"
+
+namespace atlas {
+
+// ---- shared prologue --------------------------------------------------------------------
+
+constexpr int MAX_DOWN_SPLITS = 4;
+
+__device__ __forceinline__ float4 f4_zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+
+// s_x[0..d) <- the layer input described by src (block-wide; ends with a barrier).
+// NV4 >= d / (4 * blockDim.x).
+template <int NV4>
+__device__ void build_x(const XSource& src, int d, float* s_x, float* red) {
+    const int n4 = d >> 2, bd = blockDim.x;
+    float4* sx4 = reinterpret_cast<float4*>(s_x);
+    if (src.mode == X_FROM_EMBED) {
+        int tok = *src.d_token;
+        if (tok < 0 || tok >= src.vocab) tok = 0;
+        const uint2* row = reinterpret_cast<const uint2*>(src.emb + (size_t)tok * d);
+        uint2 v[NV4];
+#pragma unroll
+        for (int j = 0; j < NV4; j++) {
+            const int i = threadIdx.x + j * bd;
+            v[j] = row[i < n4 ? i : 0];
+        }
+#pragma unroll
+        for (int j = 0; j < NV4; j++) {
+            const int i = threadIdx.x + j * bd;
+            if (i < n4)
+                sx4[i] = make_float4(bf16_bits_to_f32(v[j].x & 0xFFFFu), bf16_bits_to_f32(v[j].x >> 16),
+                                     bf16_bits_to_f32(v[j].y & 0xFFFFu), bf16_bits_to_f32(v[j].y >> 16));
+        }
+    } else if (src.mode == X_FROM_HIDDEN) {
+        const float4* h4 = reinterpret_cast<const float4*>(src.hidden);
+        float4 v[NV4];
+#pragma unroll
+        for (int j = 0; j < NV4; j++) {
+            const int i = threadIdx.x + j * bd;
+            v[j] = h4[i < n4 ? i : 0];
+        }
+#pragma unroll
+        for (int j = 0; j < NV4; j++) {
+            const int i = threadIdx.x + j * bd;
+            if (i < n4) sx4[i] = v[j];
+        }
+    } else {
+        const float4* p4 = reinterpret_cast<const float4*>(src.m_part);
+        const float4* h4 = reinterpret_cast<const float4*>(src.h);
+        const float4* g4 = reinterpret_cast<const float4*>(src.g);
+        float4 m[NV4], hh[NV4], gg[NV4], pv[MAX_DOWN_SPLITS][NV4];
+#pragma unroll
+        for (int j = 0; j < NV4; j++) {
+            const int i = threadIdx.x + j * bd, ic = i < n4 ? i : 0;
+            hh[j] = h4[ic];
+            gg[j] = g4[ic];
+#pragma unroll
+            for (int s = 0; s < MAX_DOWN_SPLITS; s++) pv[s][j] = p4[(size_t)min(s, src.S - 1) * n4 + ic];
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < NV4; j++) {
+            const int i = threadIdx.x + j * bd;
+            float4 v = pv[0][j];
+#pragma unroll
+            for (int s = 1; s < MAX_DOWN_SPLITS; s++) {
+                if (s < src.S) {
+                    v.x += pv[s][j].x;
+                    v.y += pv[s][j].y;
+                    v.z += pv[s][j].z;
+                    v.w += pv[s][j].w;
+                }
+            }
+            if (i >= n4) v = f4_zero();
+            m[j] = v;
+            ss = fmaf(v.x, v.x, ss);
+            ss = fmaf(v.y, v.y, ss);
+            ss = fmaf(v.z, v.z, ss);
+            ss = fmaf(v.w, v.w, ss);
+        }
+        ss = block_sum(ss, red);
+        const float r = 1.0f / sqrtf(ss / (float)d + src.eps);
+#pragma unroll
+        for (int j = 0; j < NV4; j++) {
+            const int i = threadIdx.x + j * bd;
+            if (i < n4)
+                sx4[i] = make_float4(hh[j].x + gg[j].x * (m[j].x * r), hh[j].y + gg[j].y * (m[j].y * r),
+                                     hh[j].z + gg[j].z * (m[j].z * r), hh[j].w + gg[j].w * (m[j].w * r));
+        }
+    }
+    __syncthreads();
+}
+
+template <int RB>
+__device__ __forceinline__ void write_rows(const float acc[RB], int row0, int N, float* out, int lane) {
+#pragma unroll
+    for (int r = 0; r < RB; r++) {
+        const float s = wave_sum(acc[r]);
+        if (lane == 0 && row0 + r < N) out[row0 + r] = s;
+    }
+}
+
+// Stream tiles t, t+NW, ... < t_end of one matrix; A holds tile t already loaded.
+// The next tile's loads are issued (and pinned by a scheduling barrier) before the
+// current tile is reduced.
+template <int CPL, int RB>
+__device__ __forceinline__ void stream_rows(const W4View& W, const LaneMap<CPL, RB>& m, const LanePlanes<CPL>& P,
+                                            TileRegs<CPL>& A, int t, int t_end, int NW, float* out, int lane) {
+    TileRegs<CPL> B;
+    for (; t < t_end; t += 2 * NW) {
+        const int t2 = t + NW;
+        if (t2 < t_end) load_tile(B, W, m, t2 * RB);
+        __builtin_amdgcn_sched_barrier(0);
+        float acc[RB];
+        tile_dot(A, P, m, W.scale_dtype, acc);
+        write_rows<RB>(acc, t * RB, W.N, out, lane);
+        if (t2 >= t_end) break;
+        if (t2 + NW < t_end) load_tile(A, W, m, (t2 + NW) * RB);
+        __builtin_amdgcn_sched_barrier(0);
+        tile_dot(B, P, m, W.scale_dtype, acc);
+        write_rows<RB>(acc, t2 * RB, W.N, out, lane);
+    }
+}
+
+// LDS carve for the GEMV kernels: [s_x: dx floats][planes CW*24][qs CW][isum CW]
+struct GemvLds {
+    float* s_x;
+    uint32_t* s_pl;
+    float* s_qs;
+    int* s_is;
+    __device__ GemvLds(uint32_t* smem, int dx, int CW) {
+        s_x = reinterpret_cast<float*>(smem);
+        s_pl = smem + dx;
+        s_qs = reinterpret_cast<float*>(s_pl + CW * XQ_WORDS_PER_CHUNK);
+        s_is = reinterpret_cast<int*>(s_qs + CW);
+    }
+};
+
+constexpr int GEMV_NV4 = 8192 / 4 / GEMV_THREADS;   // float4 per thread for d <= 8192
+
+// ---- qkv projection ----------------------------------------------------------------------
+
+template <int CPL, int RB>
+__global__ __launch_bounds__(GEMV_THREADS) void qkv_kernel(QkvArgs a) {
+    extern __shared__ uint32_t smem[];
+    __shared__ float red[16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, NW = blockDim.x >> 6;
+    GemvLds L(smem, a.d, a.CW);
+    LaneMap<CPL, RB> m;
+    m.init(lane, 0, a.CW, a.group);
+    const int T = (a.W.N + RB - 1) / RB;
+    const int t_begin = blockIdx.x * a.tiles_per_block, t_end = min(T, t_begin + a.tiles_per_block);
+    int t = t_begin + wave;
+    TileRegs<CPL> A;
+    if (t < t_end) load_tile(A, a.W, m, t * RB);   // in flight during the prologue
+
+    if (a.status && blockIdx.x == 0 && threadIdx.x == 0) {
+        int ok = 1;
+        if (a.src.mode == X_FROM_EMBED) {
+            const int tok = *a.src.d_token;
+            ok = tok >= 0 && tok < a.src.vocab;
+        }
+        *a.status = ok ? ATLAS_OK : ATLAS_ERR_INVALID_ARG;
+    }
+    build_x<GEMV_NV4>(a.src, a.d, L.s_x, red);
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < a.d; i += blockDim.x) a.x_out[i] = L.s_x[i];
+    encode_lds(L.s_x, a.d, L.s_pl, L.s_qs, L.s_is);
+    __syncthreads();
+    LanePlanes<CPL> P;
+    P.load(m, L.s_pl, L.s_qs, L.s_is, 0);
+    stream_rows<CPL, RB>(a.W, m, P, A, t, t_end, NW, a.qkv, lane);
+}
+
+// ---- generic GEMV over an input already encoded in global memory ----------------------------
+
+template <int CPL, int RB>
+__global__ __launch_bounds__(GEMV_THREADS) void gemv_planes_kernel(GemvPlanesArgs a) {
+    extern __shared__ uint32_t smem[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, NW = blockDim.x >> 6;
+    const int kr = blockIdx.y, C0 = kr * a.CW;
+    GemvLds L(smem, 0, a.CW);
+    LaneMap<CPL, RB> m;
+    m.init(lane, C0, a.CW, a.group);
+    const int T = (a.W.N + RB - 1) / RB;
+    const int t_begin = blockIdx.x * a.tiles_per_block, t_end = min(T, t_begin + a.tiles_per_block);
+    int t = t_begin + wave;
+    TileRegs<CPL> A;
+    if (t < t_end) load_tile(A, a.W, m, t * RB);
+    stage_planes(a.xq, C0, a.CW, L.s_pl, L.s_qs, L.s_is);
+    __syncthreads();
+    LanePlanes<CPL> P;
+    P.load(m, L.s_pl, L.s_qs, L.s_is, C0);
+    stream_rows<CPL, RB>(a.W, m, P, A, t, t_end, NW, a.y + (size_t)kr * a.W.N, lane);
+}
+
+// ---- gate/up projections + SwiGLU ---------------------------------------------------------
+
+template <int CPL, int RB>
+__device__ __forceinline__ void swiglu_rows(const float ag[RB], const float au[RB], int row0, int N, float* z,
+                                            int lane) {
+#pragma unroll
+    for (int rr = 0; rr < RB; rr++) {
+        const float sg = wave_sum(ag[rr]);
+        const float su = wave_sum(au[rr]);
+        if (lane == 0 && row0 + rr < N) z[row0 + rr] = sg / (1.0f + __expf(-sg)) * su;
+    }
+}
+
+template <int CPL, int RB>
+__global__ __launch_bounds__(GEMV_THREADS) void gate_up_kernel(GateUpArgs a) {
+    extern __shared__ uint32_t smem[];
+    __shared__ float red[16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, NW = blockDim.x >> 6;
+    GemvLds L(smem, a.d, a.CW);
+    LaneMap<CPL, RB> m;
+    m.init(lane, 0, a.CW, a.group);
+    const int T = (a.Wg.N + RB - 1) / RB;
+    const int t_begin = blockIdx.x * a.tiles_per_block, t_end = min(T, t_begin + a.tiles_per_block);
+    int t = t_begin + wave;
+    TileRegs<CPL> G0, U0, G1, U1;
+    if (t < t_end) {
+        load_tile(G0, a.Wg, m, t * RB);
+        load_tile(U0, a.Wu, m, t * RB);
+    }
+    // h = x + g * a / rms(a)
+    {
+        const int n4 = a.d >> 2, bd = blockDim.x;
+        const float4* a4 = reinterpret_cast<const float4*>(a.a);
+        const float4* x4 = reinterpret_cast<const float4*>(a.x);
+        const float4* g4 = reinterpret_cast<const float4*>(a.g);
+        float4 va[GEMV_NV4], vx[GEMV_NV4], vg[GEMV_NV4];
+#pragma unroll
+        for (int j = 0; j < GEMV_NV4; j++) {
+            const int i = threadIdx.x + j * bd, ic = i < n4 ? i : 0;
+            va[j] = a4[ic];
+            vx[j] = x4[ic];
+            vg[j] = g4[ic];
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < GEMV_NV4; j++) {
+            if (threadIdx.x + j * bd < n4) {
+                ss = fmaf(va[j].x, va[j].x, ss);
+                ss = fmaf(va[j].y, va[j].y, ss);
+                ss = fmaf(va[j].z, va[j].z, ss);
+                ss = fmaf(va[j].w, va[j].w, ss);
+            }
+        }
+        ss = block_sum(ss, red);
+        const float r = 1.0f / sqrtf(ss / (float)a.d + a.eps);
+        float4* sx4 = reinterpret_cast<float4*>(L.s_x);
+        float4* h4 = reinterpret_cast<float4*>(a.h_out);
+#pragma unroll
+        for (int j = 0; j < GEMV_NV4; j++) {
+            const int i = threadIdx.x + j * bd;
+            if (i < n4) {
+                const float4 h = make_float4(vx[j].x + vg[j].x * (va[j].x * r), vx[j].y + vg[j].y * (va[j].y * r),
+                                             vx[j].z + vg[j].z * (va[j].z * r), vx[j].w + vg[j].w * (va[j].w * r));
+                sx4[i] = h;
+                if (blockIdx.x == 0) h4[i] = h;
+            }
+        }
+        __syncthreads();
+    }
+    encode_lds(L.s_x, a.d, L.s_pl, L.s_qs, L.s_is);
+    __syncthreads();
+    LanePlanes<CPL> P;
+    P.load(m, L.s_pl, L.s_qs, L.s_is, 0);
+    for (; t < t_end; t += 2 * NW) {
+        const int t2 = t + NW;
+        if (t2 < t_end) {
+            load_tile(G1, a.Wg, m, t2 * RB);
+            load_tile(U1, a.Wu, m, t2 * RB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        float ag[RB], au[RB];
+        tile_dot(G0, P, m, a.Wg.scale_dtype, ag);
+        tile_dot(U0, P, m, a.Wu.scale_dtype, au);
+        swiglu_rows<CPL, RB>(ag, au, t * RB, a.Wg.N, a.z, lane);
+        if (t2 >= t_end) break;
+        if (t2 + NW < t_end) {
+            load_tile(G0, a.Wg, m, (t2 + NW) * RB);
+            load_tile(U0, a.Wu, m, (t2 + NW) * RB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        tile_dot(G1, P, m, a.Wg.scale_dtype, ag);
+        tile_dot(U1, P, m, a.Wu.scale_dtype, au);
+        swiglu_rows<CPL, RB>(ag, au, t2 * RB, a.Wg.N, a.z, lane);
+    }
+}
+
+// ---- down projection (split-K) --------------------------------------------------------------
+
+constexpr int DOWN_MAX_ROUNDS = 3;   // CW <= 3 * GEMV_THREADS / 4 chunks
+
+template <int CPL, int RB>
+__global__ __launch_bounds__(GEMV_THREADS) void down_kernel(DownArgs a) {
+    extern __shared__ uint32_t smem[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, NW = blockDim.x >> 6;
+    const int kr = blockIdx.y, C0 = kr * a.CW;
+    GemvLds L(smem, 0, a.CW);
+    LaneMap<CPL, RB> m;
+    m.init(lane, C0, a.CW, a.group);
+    const int T = (a.W.N + RB - 1) / RB;
+    const int t_begin = blockIdx.x * a.tiles_per_block, t_end = min(T, t_begin + a.tiles_per_block);
+    int t = t_begin + wave;
+    TileRegs<CPL> A;
+    if (t < t_end) load_tile(A, a.W, m, t * RB);
+    {   // encode z[C0*32 .. (C0+CW)*32) straight into LDS
+        XQ o;
+        o.planes = L.s_pl;
+        o.qs = L.s_qs;
+        o.isum = L.s_is;
+        const int nwords = a.CW * 4;
+        const float4* zb = reinterpret_cast<const float4*>(a.z + (size_t)C0 * XQ_CHUNK);
+        float4 u[DOWN_MAX_ROUNDS], v[DOWN_MAX_ROUNDS];
+#pragma unroll
+        for (int r = 0; r < DOWN_MAX_ROUNDS; r++) {
+            const int w = threadIdx.x + r * blockDim.x, wc = w < nwords ? w : 0;
+            u[r] = zb[2 * wc];
+            v[r] = zb[2 * wc + 1];
+        }
+#pragma unroll
+        for (int r = 0; r < DOWN_MAX_ROUNDS; r++) {
+            const int w = threadIdx.x + r * blockDim.x;
+            if (w < nwords) {   // whole quads in or out
+                const float x8[8] = {u[r].x, u[r].y, u[r].z, u[r].w, v[r].x, v[r].y, v[r].z, v[r].w};
+                xq_encode_word(x8, o, w >> 2, w & 3);
+            }
+        }
+    }
+    __syncthreads();
+    LanePlanes<CPL> P;
+    P.load(m, L.s_pl, L.s_qs, L.s_is, C0);
+    stream_rows<CPL, RB>(a.W, m, P, A, t, t_end, NW, a.m_part + (size_t)kr * a.W.N, lane);
+}
+
+// ---- attention ---------------------------------------------------------------------------------
+//
+// grid (S, Hkv), 256 threads. 16 lanes hold one key (8 dims each); the four 16-lane
+// groups of each wave are independent key streams with their own online softmax,
+// combined at the end. Queries stay in registers.
+
+template <int G>
+__global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(AttnFusedArgs a) {
+    constexpr int D = 128;
+    __shared__ float s_q[G][D];
+    __shared__ float s_kn[D], s_vn[D];
+    __shared__ float s_cos[64], s_sin[64];
+    __shared__ float red[16];
+    __shared__ float s_wm[4][G], s_wl[4][G];
+    __shared__ float s_wacc[4][G][D];
+    const int s = blockIdx.x, kv = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane & 15, grp = lane >> 4;
+    const int nq = a.Hq * D, nk = a.Hkv * D;
+    const int pos = *a.d_pos;
+    const bool pos_ok = pos >= 0 && pos < a.T_max;
+    float* part0 = a.part + (size_t)(kv * G) * a.S * ATTN_PART_F;
+    if (!pos_ok) {
+        for (int t = threadIdx.x; t < G * (2 + D); t += blockDim.x) {
+            const int h = t / (2 + D), e = t % (2 + D);
+            part0[((size_t)h * a.S + s) * ATTN_PART_F + e] = e == 0 ? -INFINITY : 0.f;
+        }
+        if (a.status && s == 0 && kv == 0 && threadIdx.x == 0) *a.status = ATLAS_ERR_INVALID_ARG;
+        return;
+    }
+    int lo = a.window > 0 ? pos - a.window + 1 : 0;
+    if (lo < 0) lo = 0;
+    const int nkeys = pos - lo + 1;
+    const int Lk = (nkeys + a.S - 1) / a.S;
+    const int k0 = lo + s * Lk;
+    int cnt = min(Lk, lo + nkeys - k0);
+    if (cnt < 0) cnt = 0;
+    const int stream = wave * 4 + grp;
+    const float* Kh = a.k_cache + (size_t)kv * a.T_max * D;
+    const float* Vh = a.v_cache + (size_t)kv * a.T_max * D;
+    // K/V of key i of this split (clamped into the split)
+    auto load_kv = [&](int i, float4& ka, float4& kb, float4& va, float4& vb) {
+        const int j = k0 + min(i, cnt - 1);
+        const float4* kp = reinterpret_cast<const float4*>(Kh + (size_t)j * D + 8 * sub);
+        const float4* vp = reinterpret_cast<const float4*>(Vh + (size_t)j * D + 8 * sub);
+        ka = kp[0];
+        kb = kp[1];
+        va = vp[0];
+        vb = vp[1];
+    };
+    float4 nka, nkb, nva, nvb;
+    if (stream < cnt) load_kv(stream, nka, nkb, nva, nvb);   // in flight during the prologue
+
+    if (a.fused) {
+        // sums of squares of the whole q and k projections (all loads issued first)
+        const int n4 = (nq + nk) >> 2, nq4 = nq >> 2;
+        const float4* qkv4 = reinterpret_cast<const float4*>(a.qkv);
+        float ssq = 0.f, ssk = 0.f;
+        for (int base = 0; base < n4; base += 8 * ATTN_THREADS) {
+            float4 v[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const int i = base + threadIdx.x + j * ATTN_THREADS;
+                v[j] = qkv4[i < n4 ? i : 0];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const int i = base + threadIdx.x + j * ATTN_THREADS;
+                const float e = v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+                if (i < nq4) ssq += e;
+                else if (i < n4) ssk += e;
+            }
+        }
+        // this block's q heads and k head (loads issued before the reductions)
+        float xq0[2], xq1[2], gq0[2], gq1[2];
+#pragma unroll
+        for (int r = 0; r < 2; r++) {
+            const int t = threadIdx.x + r * ATTN_THREADS;
+            const int tt = t < (G + 1) * 64 ? t : 0;
+            const int hh = tt >> 6, i = tt & 63;
+            const bool isk = hh == G;
+            const int base = isk ? nq + kv * D : (kv * G + hh) * D;
+            const float* g = isk ? a.g_k + kv * D : a.g_q + (kv * G + hh) * D;
+            xq0[r] = a.qkv[base + i];
+            xq1[r] = a.qkv[base + i + 64];
+            gq0[r] = g[i];
+            gq1[r] = g[i + 64];
+        }
+        const float vnew = a.qkv[nq + nk + kv * D + (threadIdx.x & (D - 1))];
+        ssq = block_sum(ssq, red);
+        ssk = block_sum(ssk, red);
+        const float rq = 1.0f / sqrtf(ssq / (float)nq + a.eps);
+        const float rk = 1.0f / sqrtf(ssk / (float)nk + a.eps);
+        if (threadIdx.x < 64) {
+            double sn, cs;
+            sincos((double)pos * a.inv[threadIdx.x], &sn, &cs);
+            s_cos[threadIdx.x] = (float)(cs * a.mscale);
+            s_sin[threadIdx.x] = (float)(sn * a.mscale);
+        }
+        if (threadIdx.x < D) s_vn[threadIdx.x] = vnew;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 2; r++) {
+            const int t = threadIdx.x + r * ATTN_THREADS;
+            if (t < (G + 1) * 64) {
+                const int hh = t >> 6, i = t & 63;
+                const bool isk = hh == G;
+                const float rr = isk ? rk : rq;
+                const float x0 = gq0[r] * (xq0[r] * rr), x1 = gq1[r] * (xq1[r] * rr);
+                const float c = s_cos[i], sn = s_sin[i];
+                const float y0 = x0 * c - x1 * sn, y1 = x1 * c + x0 * sn;
+                if (isk) {
+                    s_kn[i] = y0;
+                    s_kn[i + 64] = y1;
+                } else {
+                    s_q[hh][i] = y0;
+                    s_q[hh][i + 64] = y1;
+                }
+            }
+        }
+        __syncthreads();
+        if (pos >= k0 && pos < k0 + cnt && threadIdx.x < D) {   // the split that holds the new token
+            const size_t off = ((size_t)kv * a.T_max + pos) * D + threadIdx.x;
+            a.k_cache[off] = s_kn[threadIdx.x];
+            a.v_cache[off] = s_vn[threadIdx.x];
+        }
+    } else {
+        for (int t = threadIdx.x; t < G * D; t += blockDim.x) s_q[t / D][t % D] = a.q_final[(size_t)kv * G * D + t];
+        __syncthreads();
+    }
+
+    float q[G][8];
+#pragma unroll
+    for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) q[h][i] = s_q[h][8 * sub + i];
+    float mh[G], lh[G], acc[G][8];
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        mh[h] = -INFINITY;
+        lh[h] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) acc[h][i] = 0.f;
+    }
+    // keys stream, stream+16, ...; the next key's K/V are loaded before the current
+    // one is used. The new token's key and value come from LDS (the cache write above
+    // may still be in flight).
+    for (int i = stream; i < cnt; i += 16) {
+        const int j = k0 + i;
+        float kx[8] = {nka.x, nka.y, nka.z, nka.w, nkb.x, nkb.y, nkb.z, nkb.w};
+        float vx[8] = {nva.x, nva.y, nva.z, nva.w, nvb.x, nvb.y, nvb.z, nvb.w};
+        if (i + 16 < cnt) load_kv(i + 16, nka, nkb, nva, nvb);
+        if (a.fused && j == pos) {
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                kx[e] = s_kn[8 * sub + e];
+                vx[e] = s_vn[8 * sub + e];
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            float dsum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) dsum = fmaf(q[h][e], kx[e], dsum);
+            const float sc = row16_sum(dsum) * a.scale;
+            const float mn = fmaxf(mh[h], sc);
+            const float c = __expf(mh[h] - mn);
+            const float p = __expf(sc - mn);
+            lh[h] = fmaf(lh[h], c, p);
+#pragma unroll
+            for (int e = 0; e < 8; e++) acc[h][e] = fmaf(acc[h][e], c, p * vx[e]);
+            mh[h] = mn;
+        }
+    }
+    // combine the four streams of the wave (lanes l, l^16, l^32, l^48)
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        float M = fmaxf(mh[h], __shfl_xor(mh[h], 16, 64));
+        M = fmaxf(M, __shfl_xor(M, 32, 64));
+        const float w = (M == -INFINITY) ? 0.f : __expf(mh[h] - M);
+        float l = lh[h] * w;
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            float v = acc[h][e] * w;
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            acc[h][e] = v;
+        }
+        if (lane == 0) {
+            s_wm[wave][h] = M;
+            s_wl[wave][h] = l;
+        }
+        if (grp == 0)
+#pragma unroll
+            for (int e = 0; e < 8; e++) s_wacc[wave][h][8 * sub + e] = acc[h][e];
+    }
+    __syncthreads();
+    // combine the four waves and write the split partial
+    for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
+        const int h = t / D, dd = t % D;
+        float M = fmaxf(fmaxf(s_wm[0][h], s_wm[1][h]), fmaxf(s_wm[2][h], s_wm[3][h]));
+        float l = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+            const float e = (s_wm[w][h] == -INFINITY) ? 0.f : __expf(s_wm[w][h] - M);
+            l = fmaf(s_wl[w][h], e, l);
+            o = fmaf(s_wacc[w][h][dd], e, o);
+        }
+        float* dst = part0 + ((size_t)h * a.S + s) * ATTN_PART_F;
+        dst[2 + dd] = o;
+        if (dd == 0) {
+            dst[0] = M;
+            dst[1] = l;
+        }
+    }
+}
+
+// ---- merge of the key splits -----------------------------------------------------------------
+// grid Hq, 128 threads: o = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s.
+constexpr int MERGE_MAX_S = 1024;
+__global__ __launch_bounds__(128) void merge_kernel(MergeArgs a) {
+    __shared__ float s_w[MERGE_MAX_S];
+    __shared__ float s_wl[MERGE_MAX_S];
+    __shared__ float s_o[128];
+    __shared__ float s_M;
+    const int h = blockIdx.x, d = threadIdx.x;
+    const float* p = a.part + (size_t)h * a.S * ATTN_PART_F;
+    for (int s0 = 0; s0 < a.S; s0 += 8 * 128) {
+        float mloc[8], lloc[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int s = s0 + d + j * 128, sc = s < a.S ? s : 0;
+            mloc[j] = p[(size_t)sc * ATTN_PART_F];
+            lloc[j] = p[(size_t)sc * ATTN_PART_F + 1];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int s = s0 + d + j * 128;
+            if (s < a.S) {
+                s_w[s] = mloc[j];
+                s_wl[s] = lloc[j];
+            }
+        }
+    }
+    __syncthreads();
+    if (d < 64) {
+        float M = -INFINITY;
+        for (int s = d; s < a.S; s += 64) M = fmaxf(M, s_w[s]);
+        M = wave_max(M);
+        if (d == 0) s_M = M;
+    }
+    __syncthreads();
+    const float M = s_M;
+    for (int s = d; s < a.S; s += 128) {
+        const float m = s_w[s];
+        const float w = (m == -INFINITY || M == -INFINITY) ? 0.f : __expf(m - M);
+        s_w[s] = w;
+        s_wl[s] = w * s_wl[s];
+    }
+    __syncthreads();
+    float L = 0.f, o = 0.f;
+    for (int s0 = 0; s0 < a.S; s0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            const int s = min(s0 + j, a.S - 1);
+            v[j] = p[(size_t)s * ATTN_PART_F + 2 + d];
+        }
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            if (s0 + j < a.S) {
+                o = fmaf(s_w[s0 + j], v[j], o);
+                L += s_wl[s0 + j];
+            }
+        }
+    }
+    const float r = L > 0.f ? o / L : 0.f;
+    if (a.o) a.o[(size_t)h * 128 + d] = r;
+    if (a.xq.planes) {
+        s_o[d] = r;
+        __syncthreads();
+        if (d < 16) {
+            float x8[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) x8[i] = s_o[8 * d + i];
+            xq_encode_word(x8, a.xq, h * 4 + (d >> 2), d & 3);
+        }
+    }
+}
+
+// ---- final norm, bf16 lm_head and argmax partials ------------------------------------------------
+//
+// 512 threads; every block rebuilds the last layer's output and its final RMSNorm
+// (d <= 8192), then each wave streams whole rows: lane l reads 16-byte words
+// l, l+64, ... of the row (KW per lane); two rows are in flight per wave.
+
+constexpr int HEAD_THREADS = 512;
+template <int KW>
+__global__ __launch_bounds__(HEAD_THREADS) void head_kernel(HeadArgs a) {
+    __shared__ float s_x[8192];
+    __shared__ float red[16];
+    __shared__ float s_v[HEAD_THREADS / 64];
+    __shared__ int s_i[HEAD_THREADS / 64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, NW = HEAD_THREADS / 64;
+    const int nw = a.d / 8;
+    const int r0 = blockIdx.x * a.rows_per_block, r1 = min(a.V, r0 + a.rows_per_block);
+    auto load_row = [&](int row, uint4 (&w)[KW]) {
+        const uint4* W = reinterpret_cast<const uint4*>(a.lm + (size_t)min(row, a.V - 1) * a.d);
+#pragma unroll
+        for (int j = 0; j < KW; j++) {
+            const int wd = lane + 64 * j;
+            w[j] = W[wd < nw ? wd : 0];
+        }
+    };
+    uint4 wa[KW], wb[KW];
+    int row = r0 + wave;
+    if (row < r1) load_row(row, wa);
+    build_x<8192 / 4 / HEAD_THREADS>(a.src, a.d, s_x, red);
+    if (a.hidden_out && blockIdx.x == 0)
+        for (int i = threadIdx.x; i < a.d; i += blockDim.x) a.hidden_out[i] = s_x[i];
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < a.d; i += blockDim.x) ss = fmaf(s_x[i], s_x[i], ss);
+    ss = block_sum(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)a.d + a.eps);
+    for (int i = threadIdx.x; i < a.d; i += blockDim.x) s_x[i] = a.g_final[i] * (s_x[i] * r);
+    __syncthreads();
+    float xr[KW][8];
+#pragma unroll
+    for (int j = 0; j < KW; j++) {
+        const int wd = lane + 64 * j;
+#pragma unroll
+        for (int i = 0; i < 8; i++) xr[j][i] = wd < nw ? s_x[8 * wd + i] : 0.f;
+    }
+    float best = -INFINITY;
+    int besti = 0x7FFFFFFF;
+    auto dot_row = [&](const uint4 (&w)[KW]) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < KW; j++) {
+            const uint32_t ww[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                acc = fmaf(__uint_as_float(ww[q] << 16), xr[j][2 * q], acc);
+                acc = fmaf(__uint_as_float(ww[q] & 0xFFFF0000u), xr[j][2 * q + 1], acc);
+            }
+        }
+        return wave_sum(acc);
+    };
+    for (; row < r1; row += 2 * NW) {
+        const int row2 = row + NW;
+        if (row2 < r1) load_row(row2, wb);
+        __builtin_amdgcn_sched_barrier(0);
+        float v = dot_row(wa);
+        if (lane == 0) a.logits[row] = v;
+        if (v > best) {   // rows increase within a wave: the first maximum stays
+            best = v;
+            besti = row;
+        }
+        if (row2 >= r1) break;
+        if (row2 + NW < r1) load_row(row2 + NW, wa);
+        __builtin_amdgcn_sched_barrier(0);
+        v = dot_row(wb);
+        if (lane == 0) a.logits[row2] = v;
+        if (v > best) {
+            best = v;
+            besti = row2;
+        }
+    }
+    if (lane == 0) {
+        s_v[wave] = best;
+        s_i[wave] = besti;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = s_v[0];
+        int bi = s_i[0];
+        for (int w = 1; w < NW; w++)
+            if (s_v[w] > b || (s_v[w] == b && s_i[w] < bi)) {
+                b = s_v[w];
+                bi = s_i[w];
+            }
+        a.bmax[blockIdx.x] = b;
+        a.bidx[blockIdx.x] = bi;
+    }
+}
+
+__global__ __launch_bounds__(1024) void final_hidden_kernel(XSource src, int d, float* out) {
+    __shared__ float s_x[8192];
+    __shared__ float red[16];
+    build_x<8192 / 4 / 1024>(src, d, s_x, red);
+    for (int i = threadIdx.x; i < d; i += blockDim.x) out[i] = s_x[i];
+}
+
+__global__ __launch_bounds__(1024) void argmax_final2_kernel(const float* bmax, const int* bidx, int nb, int32_t* out) {
+    __shared__ float s_v[1024];
+    __shared__ int s_i[1024];
+    float b = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int i = threadIdx.x; i < nb; i += blockDim.x)
+        if (bmax[i] > b || (bmax[i] == b && bidx[i] < bi)) {
+            b = bmax[i];
+            bi = bidx[i];
+        }
+    s_v[threadIdx.x] = b;
+    s_i[threadIdx.x] = bi;
+    __syncthreads();
+    for (int off = 512; off > 0; off >>= 1) {
+        if (threadIdx.x < off) {
+            const float v = s_v[threadIdx.x + off];
+            const int vi = s_i[threadIdx.x + off];
+            if (v > s_v[threadIdx.x] || (v == s_v[threadIdx.x] && vi < s_i[threadIdx.x])) {
+                s_v[threadIdx.x] = v;
+                s_i[threadIdx.x] = vi;
+            }
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *out = s_i[0] == 0x7FFFFFFF ? 0 : s_i[0];
+}
+
+// ---- host-side planning and launch ---------------------------------------------------------------
+
+GemvShape gemv_shape(int N, int K, bool split_k, int target_blocks, int max_cpl) {
+    GemvShape g{};
+    const int C = K / XQ_CHUNK;
+    int best_s = -1, best_rb = 1, best_cpl = 0;
+    double best_u = -1;
+    for (int s = 1; s <= (split_k ? std::min(C, MAX_DOWN_SPLITS) : 1); s++) {
+        if (C % s) continue;
+        const int cw = C / s;
+        if (cw * 4 > DOWN_MAX_ROUNDS * GEMV_THREADS) continue;
+        for (int rb = 2; rb >= 1; rb--) {
+            if (rb == 2 && (2 * cw) % 64) continue;
+            const int cpl = (rb * cw + 63) / 64;
+            if (cpl > max_cpl) continue;
+            const double u = (double)(rb * cw) / (64.0 * cpl);
+            if (u > best_u + 1e-9) {
+                best_u = u;
+                best_s = s;
+                best_rb = rb;
+                best_cpl = cpl;
+            }
+        }
+        if (best_s > 0) break;   // fewest ranges first
+    }
+    if (best_s < 0) return g;   // CPL stays 0: unsupported
+    g.S = best_s;
+    g.CW = C / best_s;
+    g.RB = best_rb;
+    g.CPL = best_cpl;
+    const int T = (N + g.RB - 1) / g.RB;
+    int bx = std::max(1, target_blocks / g.S);
+    bx = std::min(bx, T);
+    g.tiles_per_block = (T + bx - 1) / bx;
+    g.blocks = (T + g.tiles_per_block - 1) / g.tiles_per_block;
+    return g;
+}
+
+#define GEMV_CASE(KERNEL, C_, R_, grid, lds, st, args)                                         \
+    if (s.CPL == C_ && s.RB == R_) {                                                            \
+        hipLaunchKernelGGL((KERNEL<C_, R_>), grid, dim3(GEMV_THREADS), lds, st, args);          \
+        ATLAS_LAUNCH_CHECK(#KERNEL);                                                            \
+        return ATLAS_OK;                                                                        \
+    }
+#define GEMV_DISPATCH5(KERNEL, grid, lds, st, args)                                             \
+    GEMV_CASE(KERNEL, 1, 1, grid, lds, st, args) GEMV_CASE(KERNEL, 2, 1, grid, lds, st, args)   \
+    GEMV_CASE(KERNEL, 3, 1, grid, lds, st, args) GEMV_CASE(KERNEL, 4, 1, grid, lds, st, args)   \
+    GEMV_CASE(KERNEL, 5, 1, grid, lds, st, args) GEMV_CASE(KERNEL, 1, 2, grid, lds, st, args)   \
+    GEMV_CASE(KERNEL, 2, 2, grid, lds, st, args) GEMV_CASE(KERNEL, 3, 2, grid, lds, st, args)   \
+    GEMV_CASE(KERNEL, 4, 2, grid, lds, st, args) GEMV_CASE(KERNEL, 5, 2, grid, lds, st, args)   \
+    return fail(ATLAS_ERR_UNSUPPORTED_SHAPE, #KERNEL ": no instance for CPL=%d RB=%d", s.CPL, s.RB);
+#define GEMV_DISPATCH3(KERNEL, grid, lds, st, args)                                             \
+    GEMV_CASE(KERNEL, 1, 1, grid, lds, st, args) GEMV_CASE(KERNEL, 2, 1, grid, lds, st, args)   \
+    GEMV_CASE(KERNEL, 3, 1, grid, lds, st, args) GEMV_CASE(KERNEL, 1, 2, grid, lds, st, args)   \
+    GEMV_CASE(KERNEL, 2, 2, grid, lds, st, args) GEMV_CASE(KERNEL, 3, 2, grid, lds, st, args)   \
+    return fail(ATLAS_ERR_UNSUPPORTED_SHAPE, #KERNEL ": no instance for CPL=%d RB=%d", s.CPL, s.RB);
+
+int launch_qkv(const QkvArgs& a0, const GemvShape& s, hipStream_t st) {
+    QkvArgs a = a0;
+    a.CW = s.CW;
+    a.tiles_per_block = s.tiles_per_block;
+    const size_t lds = (size_t)a.d * 4 + planes_lds_bytes(s.CW);
+    prof_mark("w4_gemv_qkv", st);
+    GEMV_DISPATCH5(qkv_kernel, dim3(s.blocks), lds, st, a);
+}
+
+int launch_gemv_planes(const GemvPlanesArgs& a0, const GemvShape& s, hipStream_t st, const char* label) {
+    GemvPlanesArgs a = a0;
+    a.CW = s.CW;
+    a.tiles_per_block = s.tiles_per_block;
+    prof_mark(label, st);
+    GEMV_DISPATCH5(gemv_planes_kernel, dim3(s.blocks, s.S), planes_lds_bytes(s.CW), st, a);
+}
+
+int launch_gate_up(const GateUpArgs& a0, const GemvShape& s, hipStream_t st) {
+    GateUpArgs a = a0;
+    a.CW = s.CW;
+    a.tiles_per_block = s.tiles_per_block;
+    const size_t lds = (size_t)a.d * 4 + planes_lds_bytes(s.CW);
+    prof_mark("w4_gemv_gate_up", st);
+    GEMV_DISPATCH3(gate_up_kernel, dim3(s.blocks), lds, st, a);
+}
+
+int launch_down(const DownArgs& a0, const GemvShape& s, hipStream_t st) {
+    DownArgs a = a0;
+    a.CW = s.CW;
+    a.tiles_per_block = s.tiles_per_block;
+    prof_mark("w4_gemv_down", st);
+    GEMV_DISPATCH5(down_kernel, dim3(s.blocks, s.S), planes_lds_bytes(s.CW), st, a);
+}
+
+int attn_splits(int64_t maxkeys, int Hkv) {
+    int64_t S = (maxkeys + 127) / 128;
+    const int64_t cap = std::max(1, (512 + Hkv - 1) / Hkv);
+    if (S > cap) S = cap;
+    if (S < 1) S = 1;
+    return (int)S;
+}
+
+int launch_attn_fused(const AttnFusedArgs& a, int G, hipStream_t st) {
+    dim3 grid(a.S, a.Hkv);
+    prof_mark(a.window > 0 ? "attn_window" : "attn_full", st);
+    switch (G) {
+#define C(G_)                                                                           \
+    case G_:                                                                            \
+        hipLaunchKernelGGL((attn_kernel<G_>), grid, dim3(ATTN_THREADS), 0, st, a);      \
+        break;
+        C(1) C(2) C(3) C(4) C(5) C(6) C(7) C(8)
+#undef C
+        default: return fail(ATLAS_ERR_UNSUPPORTED_SHAPE, "Hq/Hkv=%d > 8", G);
+    }
+    ATLAS_LAUNCH_CHECK("attn_kernel");
+    return ATLAS_OK;
+}
+
+int launch_merge(const MergeArgs& a, hipStream_t st) {
+    if (a.S > MERGE_MAX_S) return fail(ATLAS_ERR_UNSUPPORTED_SHAPE, "too many key splits (%d)", a.S);
+    prof_mark("attn_merge", st);
+    hipLaunchKernelGGL(merge_kernel, dim3(a.Hq), dim3(128), 0, st, a);
+    ATLAS_LAUNCH_CHECK("merge_kernel");
+    return ATLAS_OK;
+}
+
+int launch_head(const HeadArgs& a, int blocks, hipStream_t st) {
+    const int kw = (a.d / 8 + 63) / 64;
+    prof_mark("lm_head_bf16", st);
+    if (kw <= 2) hipLaunchKernelGGL((head_kernel<2>), dim3(blocks), dim3(HEAD_THREADS), 0, st, a);
+    else if (kw <= 4) hipLaunchKernelGGL((head_kernel<4>), dim3(blocks), dim3(HEAD_THREADS), 0, st, a);
+    else if (kw <= 10) hipLaunchKernelGGL((head_kernel<10>), dim3(blocks), dim3(HEAD_THREADS), 0, st, a);
+    else if (kw <= 16) hipLaunchKernelGGL((head_kernel<16>), dim3(blocks), dim3(HEAD_THREADS), 0, st, a);
+    else return fail(ATLAS_ERR_UNSUPPORTED_SHAPE, "d=%d too large for the lm_head kernel", a.d);
+    ATLAS_LAUNCH_CHECK("head_kernel");
+    return ATLAS_OK;
+}
+
+int launch_final_hidden(const XSource& src, int d, float* out, hipStream_t st) {
+    prof_mark("final_hidden", st);
+    hipLaunchKernelGGL(final_hidden_kernel, dim3(1), dim3(1024), 0, st, src, d, out);
+    ATLAS_LAUNCH_CHECK("final_hidden_kernel");
+    return ATLAS_OK;
+}
+
+int launch_argmax_final(const float* bmax, const int* bidx, int nb, int32_t* out, hipStream_t st) {
+    prof_mark("argmax", st);
+    hipLaunchKernelGGL(argmax_final2_kernel, dim3(1), dim3(1024), 0, st, bmax, bidx, nb, out);
+    ATLAS_LAUNCH_CHECK("argmax_final_kernel");
+    return ATLAS_OK;
+}
+
+}  // namespace atlas

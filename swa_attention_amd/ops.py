@@ -201,3 +201,17 @@ def atlas_prefill(m: Model, d_tokens, start_pos=0, logits=None, argmax=None, ws=
     _dev(d_tokens, I32, "tokens")
     L.call("atlas_prefill", ctypes.byref(cm), L.ptr(d_tokens), d_tokens.numel(), start_pos, L.ptr(logits),
            L.ptr(argmax), L.ptr(ws), 0 if ws is None else ws.numel(), L.stream_ptr(stream))
+
+
+# ---- launch timing -------------------------------------------------------------------------------
+
+def atlas_profile_start(capacity=100000):
+    L.call("atlas_profile_start", capacity)
+
+
+def atlas_profile_stop(max_entries=64):
+    """{label: (launch count, total ms)} of the launches since atlas_profile_start."""
+    arr = (L.atlas_profile_entry * max_entries)()
+    n = ctypes.c_int32(0)
+    L.call("atlas_profile_stop", arr, max_entries, ctypes.byref(n))
+    return {arr[i].name.decode(): (arr[i].count, arr[i].total_ms) for i in range(n.value)}
