@@ -121,25 +121,47 @@ __device__ __forceinline__ void write_rows(const float acc[RB], int row0, int N,
     }
 }
 
-// Stream tiles t, t+NW, ... < t_end of one matrix; A holds tile t already loaded.
-// The next tile's loads are issued (and pinned by a scheduling barrier) before the
-// current tile is reduced.
-template <int CPL, int RB>
+// Streaming pipeline of NS register stages. A wave owns tiles t0, t0+NW, ... (nt of
+// them). Before the prologue it loads its first NS-1 tiles into R[0..NS-2]; each
+// step then issues the load of the tile NS-1 positions ahead (pinned by a
+// scheduling barrier) and reduces the oldest one, so NS-1 tiles per wave are always
+// in flight. The main loop runs whole groups of NS tiles with unconditional loads
+// (indices clamped to the wave's last tile, so the compiler's wait counting stays
+// exact); the remainder needs no further loads.
+__device__ __forceinline__ int wave_tiles(int t0, int t_end, int NW) {
+    return t0 < t_end ? (t_end - t0 + NW - 1) / NW : 0;
+}
+
+template <int CPL, int RB, int NS>
+__device__ __forceinline__ void prefetch_tiles(TileRegs<CPL> (&R)[NS], const W4View& W, const LaneMap<CPL, RB>& m,
+                                               int t0, int nt, int NW) {
+    if (nt <= 0) return;
+#pragma unroll
+    for (int k = 0; k < NS - 1; k++) load_tile(R[k], W, m, (t0 + min(k, nt - 1) * NW) * RB);
+}
+
+template <int CPL, int RB, int NS>
 __device__ __forceinline__ void stream_rows(const W4View& W, const LaneMap<CPL, RB>& m, const LanePlanes<CPL>& P,
-                                            TileRegs<CPL>& A, int t, int t_end, int NW, float* out, int lane) {
-    TileRegs<CPL> B;
-    for (; t < t_end; t += 2 * NW) {
-        const int t2 = t + NW;
-        if (t2 < t_end) load_tile(B, W, m, t2 * RB);
-        __builtin_amdgcn_sched_barrier(0);
-        float acc[RB];
-        tile_dot(A, P, m, W.scale_dtype, acc);
-        write_rows<RB>(acc, t * RB, W.N, out, lane);
-        if (t2 >= t_end) break;
-        if (t2 + NW < t_end) load_tile(A, W, m, (t2 + NW) * RB);
-        __builtin_amdgcn_sched_barrier(0);
-        tile_dot(B, P, m, W.scale_dtype, acc);
-        write_rows<RB>(acc, t2 * RB, W.N, out, lane);
+                                            TileRegs<CPL> (&R)[NS], int t0, int nt, int NW, float* out,
+                                            int lane) {
+    int i = 0;
+    for (; i + NS <= nt; i += NS) {
+#pragma unroll
+        for (int k = 0; k < NS; k++) {
+            load_tile(R[(k + NS - 1) % NS], W, m, (t0 + min(i + k + NS - 1, nt - 1) * NW) * RB);
+            __builtin_amdgcn_sched_barrier(0);
+            float acc[RB];
+            tile_dot(R[k], P, m, W, acc);
+            write_rows<RB>(acc, (t0 + (i + k) * NW) * RB, W.N, out, lane);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < NS - 1; k++) {   // nt - i < NS tiles left, already loaded in R[0..]
+        if (i + k < nt) {
+            float acc[RB];
+            tile_dot(R[k], P, m, W, acc);
+            write_rows<RB>(acc, (t0 + (i + k) * NW) * RB, W.N, out, lane);
+        }
     }
 }
 
@@ -158,6 +180,10 @@ struct GemvLds {
 };
 
 constexpr int GEMV_NV4 = 8192 / 4 / GEMV_THREADS;   // float4 per thread for d <= 8192
+// register stages of the single-matrix kernels (CPL >= 4 tiles are larger: one stage less)
+template <int CPL>
+constexpr int gemv_stages() { return CPL >= 4 ? 3 : 4; }
+constexpr int GU_STAGES = 3;                          // gate/up: 2 tile pairs in flight per wave
 
 // ---- qkv projection ----------------------------------------------------------------------
 
@@ -171,9 +197,9 @@ __global__ __launch_bounds__(GEMV_THREADS) void qkv_kernel(QkvArgs a) {
     m.init(lane, 0, a.CW, a.group);
     const int T = (a.W.N + RB - 1) / RB;
     const int t_begin = blockIdx.x * a.tiles_per_block, t_end = min(T, t_begin + a.tiles_per_block);
-    int t = t_begin + wave;
-    TileRegs<CPL> A;
-    if (t < t_end) load_tile(A, a.W, m, t * RB);   // in flight during the prologue
+    const int t = t_begin + wave, nt = wave_tiles(t, t_end, NW);
+    TileRegs<CPL> R[gemv_stages<CPL>()];
+    prefetch_tiles<CPL, RB, gemv_stages<CPL>()>(R, a.W, m, t, nt, NW);   // in flight during the prologue
 
     if (a.status && blockIdx.x == 0 && threadIdx.x == 0) {
         int ok = 1;
@@ -190,7 +216,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void qkv_kernel(QkvArgs a) {
     __syncthreads();
     LanePlanes<CPL> P;
     P.load(m, L.s_pl, L.s_qs, L.s_is, 0);
-    stream_rows<CPL, RB>(a.W, m, P, A, t, t_end, NW, a.qkv, lane);
+    stream_rows<CPL, RB, gemv_stages<CPL>()>(a.W, m, P, R, t, nt, NW, a.qkv, lane);
 }
 
 // ---- generic GEMV over an input already encoded in global memory ----------------------------
@@ -205,14 +231,14 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_planes_kernel(GemvPlanesArg
     m.init(lane, C0, a.CW, a.group);
     const int T = (a.W.N + RB - 1) / RB;
     const int t_begin = blockIdx.x * a.tiles_per_block, t_end = min(T, t_begin + a.tiles_per_block);
-    int t = t_begin + wave;
-    TileRegs<CPL> A;
-    if (t < t_end) load_tile(A, a.W, m, t * RB);
+    const int t = t_begin + wave, nt = wave_tiles(t, t_end, NW);
+    TileRegs<CPL> R[gemv_stages<CPL>()];
+    prefetch_tiles<CPL, RB, gemv_stages<CPL>()>(R, a.W, m, t, nt, NW);
     stage_planes(a.xq, C0, a.CW, L.s_pl, L.s_qs, L.s_is);
     __syncthreads();
     LanePlanes<CPL> P;
     P.load(m, L.s_pl, L.s_qs, L.s_is, C0);
-    stream_rows<CPL, RB>(a.W, m, P, A, t, t_end, NW, a.y + (size_t)kr * a.W.N, lane);
+    stream_rows<CPL, RB, gemv_stages<CPL>()>(a.W, m, P, R, t, nt, NW, a.y + (size_t)kr * a.W.N, lane);
 }
 
 // ---- gate/up projections + SwiGLU ---------------------------------------------------------
@@ -238,12 +264,10 @@ __global__ __launch_bounds__(GEMV_THREADS) void gate_up_kernel(GateUpArgs a) {
     m.init(lane, 0, a.CW, a.group);
     const int T = (a.Wg.N + RB - 1) / RB;
     const int t_begin = blockIdx.x * a.tiles_per_block, t_end = min(T, t_begin + a.tiles_per_block);
-    int t = t_begin + wave;
-    TileRegs<CPL> G0, U0, G1, U1;
-    if (t < t_end) {
-        load_tile(G0, a.Wg, m, t * RB);
-        load_tile(U0, a.Wu, m, t * RB);
-    }
+    const int t = t_begin + wave, nt = wave_tiles(t, t_end, NW);
+    TileRegs<CPL> RG[GU_STAGES], RU[GU_STAGES];
+    prefetch_tiles<CPL, RB, GU_STAGES>(RG, a.Wg, m, t, nt, NW);
+    prefetch_tiles<CPL, RB, GU_STAGES>(RU, a.Wu, m, t, nt, NW);
     // h = x + g * a / rms(a)
     {
         const int n4 = a.d >> 2, bd = blockDim.x;
@@ -288,26 +312,29 @@ __global__ __launch_bounds__(GEMV_THREADS) void gate_up_kernel(GateUpArgs a) {
     __syncthreads();
     LanePlanes<CPL> P;
     P.load(m, L.s_pl, L.s_qs, L.s_is, 0);
-    for (; t < t_end; t += 2 * NW) {
-        const int t2 = t + NW;
-        if (t2 < t_end) {
-            load_tile(G1, a.Wg, m, t2 * RB);
-            load_tile(U1, a.Wu, m, t2 * RB);
+    // same pipeline as stream_rows, over both matrices
+    int i = 0;
+    for (; i + GU_STAGES <= nt; i += GU_STAGES) {
+#pragma unroll
+        for (int k = 0; k < GU_STAGES; k++) {
+            const int rl = (t + min(i + k + GU_STAGES - 1, nt - 1) * NW) * RB;
+            load_tile(RG[(k + GU_STAGES - 1) % GU_STAGES], a.Wg, m, rl);
+            load_tile(RU[(k + GU_STAGES - 1) % GU_STAGES], a.Wu, m, rl);
+            __builtin_amdgcn_sched_barrier(0);
+            float ag[RB], au[RB];
+            tile_dot(RG[k], P, m, a.Wg, ag);
+            tile_dot(RU[k], P, m, a.Wu, au);
+            swiglu_rows<CPL, RB>(ag, au, (t + (i + k) * NW) * RB, a.Wg.N, a.z, lane);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        float ag[RB], au[RB];
-        tile_dot(G0, P, m, a.Wg.scale_dtype, ag);
-        tile_dot(U0, P, m, a.Wu.scale_dtype, au);
-        swiglu_rows<CPL, RB>(ag, au, t * RB, a.Wg.N, a.z, lane);
-        if (t2 >= t_end) break;
-        if (t2 + NW < t_end) {
-            load_tile(G0, a.Wg, m, (t2 + NW) * RB);
-            load_tile(U0, a.Wu, m, (t2 + NW) * RB);
+    }
+#pragma unroll
+    for (int k = 0; k < GU_STAGES - 1; k++) {
+        if (i + k < nt) {
+            float ag[RB], au[RB];
+            tile_dot(RG[k], P, m, a.Wg, ag);
+            tile_dot(RU[k], P, m, a.Wu, au);
+            swiglu_rows<CPL, RB>(ag, au, (t + (i + k) * NW) * RB, a.Wg.N, a.z, lane);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        tile_dot(G1, P, m, a.Wg.scale_dtype, ag);
-        tile_dot(U1, P, m, a.Wu.scale_dtype, au);
-        swiglu_rows<CPL, RB>(ag, au, t2 * RB, a.Wg.N, a.z, lane);
     }
 }
 
@@ -325,9 +352,9 @@ __global__ __launch_bounds__(GEMV_THREADS) void down_kernel(DownArgs a) {
     m.init(lane, C0, a.CW, a.group);
     const int T = (a.W.N + RB - 1) / RB;
     const int t_begin = blockIdx.x * a.tiles_per_block, t_end = min(T, t_begin + a.tiles_per_block);
-    int t = t_begin + wave;
-    TileRegs<CPL> A;
-    if (t < t_end) load_tile(A, a.W, m, t * RB);
+    const int t = t_begin + wave, nt = wave_tiles(t, t_end, NW);
+    TileRegs<CPL> R[gemv_stages<CPL>()];
+    prefetch_tiles<CPL, RB, gemv_stages<CPL>()>(R, a.W, m, t, nt, NW);
     {   // encode z[C0*32 .. (C0+CW)*32) straight into LDS
         XQ o;
         o.planes = L.s_pl;
@@ -354,7 +381,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void down_kernel(DownArgs a) {
     __syncthreads();
     LanePlanes<CPL> P;
     P.load(m, L.s_pl, L.s_qs, L.s_is, C0);
-    stream_rows<CPL, RB>(a.W, m, P, A, t, t_end, NW, a.m_part + (size_t)kr * a.W.N, lane);
+    stream_rows<CPL, RB, gemv_stages<CPL>()>(a.W, m, P, R, t, nt, NW, a.m_part + (size_t)kr * a.W.N, lane);
 }
 
 // ---- attention ---------------------------------------------------------------------------------
@@ -362,6 +389,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void down_kernel(DownArgs a) {
 // grid (S, Hkv), 256 threads. 16 lanes hold one key (8 dims each); the four 16-lane
 // groups of each wave are independent key streams with their own online softmax,
 // combined at the end. Queries stay in registers.
+
+constexpr int ATTN_KV_STAGES = 4;   // keys in flight per 16-lane stream: 3
 
 template <int G>
 __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(AttnFusedArgs a) {
@@ -407,8 +436,12 @@ __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(AttnFusedArgs a) {
         va = vp[0];
         vb = vp[1];
     };
-    float4 nka, nkb, nva, nvb;
-    if (stream < cnt) load_kv(stream, nka, nkb, nva, nvb);   // in flight during the prologue
+    // ring of ATTN_KV_STAGES keys per stream; the first ATTN_KV_STAGES-1 are in flight
+    // during the prologue
+    float4 rk[ATTN_KV_STAGES][2], rv[ATTN_KV_STAGES][2];
+#pragma unroll
+    for (int k = 0; k < ATTN_KV_STAGES - 1; k++)
+        if (stream + 16 * k < cnt) load_kv(stream + 16 * k, rk[k][0], rk[k][1], rv[k][0], rv[k][1]);
 
     if (a.fused) {
         // sums of squares of the whole q and k projections (all loads issued first)
@@ -504,31 +537,42 @@ __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(AttnFusedArgs a) {
     // keys stream, stream+16, ...; the next key's K/V are loaded before the current
     // one is used. The new token's key and value come from LDS (the cache write above
     // may still be in flight).
-    for (int i = stream; i < cnt; i += 16) {
-        const int j = k0 + i;
-        float kx[8] = {nka.x, nka.y, nka.z, nka.w, nkb.x, nkb.y, nkb.z, nkb.w};
-        float vx[8] = {nva.x, nva.y, nva.z, nva.w, nvb.x, nvb.y, nvb.z, nvb.w};
-        if (i + 16 < cnt) load_kv(i + 16, nka, nkb, nva, nvb);
-        if (a.fused && j == pos) {
+    for (int i0 = stream; i0 < cnt; i0 += 16 * ATTN_KV_STAGES) {
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                kx[e] = s_kn[8 * sub + e];
-                vx[e] = s_vn[8 * sub + e];
+        for (int k = 0; k < ATTN_KV_STAGES; k++) {
+            const int i = i0 + 16 * k;
+            if (i >= cnt) break;
+            const int il = i + 16 * (ATTN_KV_STAGES - 1);
+            if (il < cnt) {
+                const int slot = (k + ATTN_KV_STAGES - 1) % ATTN_KV_STAGES;
+                load_kv(il, rk[slot][0], rk[slot][1], rv[slot][0], rv[slot][1]);
             }
-        }
+            const int j = k0 + i;
+            float kx[8] = {rk[k][0].x, rk[k][0].y, rk[k][0].z, rk[k][0].w,
+                           rk[k][1].x, rk[k][1].y, rk[k][1].z, rk[k][1].w};
+            float vx[8] = {rv[k][0].x, rv[k][0].y, rv[k][0].z, rv[k][0].w,
+                           rv[k][1].x, rv[k][1].y, rv[k][1].z, rv[k][1].w};
+            if (a.fused && j == pos) {
 #pragma unroll
-        for (int h = 0; h < G; h++) {
-            float dsum = 0.f;
+                for (int e = 0; e < 8; e++) {
+                    kx[e] = s_kn[8 * sub + e];
+                    vx[e] = s_vn[8 * sub + e];
+                }
+            }
 #pragma unroll
-            for (int e = 0; e < 8; e++) dsum = fmaf(q[h][e], kx[e], dsum);
-            const float sc = row16_sum(dsum) * a.scale;
-            const float mn = fmaxf(mh[h], sc);
-            const float c = __expf(mh[h] - mn);
-            const float p = __expf(sc - mn);
-            lh[h] = fmaf(lh[h], c, p);
+            for (int h = 0; h < G; h++) {
+                float dsum = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; e++) acc[h][e] = fmaf(acc[h][e], c, p * vx[e]);
-            mh[h] = mn;
+                for (int e = 0; e < 8; e++) dsum = fmaf(q[h][e], kx[e], dsum);
+                const float sc = row16_sum(dsum) * a.scale;
+                const float mn = fmaxf(mh[h], sc);
+                const float c = __expf(mh[h] - mn);
+                const float p = __expf(sc - mn);
+                lh[h] = fmaf(lh[h], c, p);
+#pragma unroll
+                for (int e = 0; e < 8; e++) acc[h][e] = fmaf(acc[h][e], c, p * vx[e]);
+                mh[h] = mn;
+            }
         }
     }
     // combine the four streams of the wave (lanes l, l^16, l^32, l^48)
@@ -586,6 +630,15 @@ __global__ __launch_bounds__(128) void merge_kernel(MergeArgs a) {
     __shared__ float s_M;
     const int h = blockIdx.x, d = threadIdx.x;
     const float* p = a.part + (size_t)h * a.S * ATTN_PART_F;
+    // up to MERGE_REG_S split accumulators are loaded at once, in flight while the
+    // maxima are reduced
+    constexpr int MERGE_REG_S = 64;
+    const bool in_regs = a.S <= MERGE_REG_S;
+    float accv[MERGE_REG_S];
+    if (in_regs) {
+#pragma unroll
+        for (int j = 0; j < MERGE_REG_S; j++) accv[j] = p[(size_t)min(j, a.S - 1) * ATTN_PART_F + 2 + d];
+    }
     for (int s0 = 0; s0 < a.S; s0 += 8 * 128) {
         float mloc[8], lloc[8];
 #pragma unroll
@@ -620,7 +673,16 @@ __global__ __launch_bounds__(128) void merge_kernel(MergeArgs a) {
     }
     __syncthreads();
     float L = 0.f, o = 0.f;
-    for (int s0 = 0; s0 < a.S; s0 += 16) {
+    if (in_regs) {
+#pragma unroll
+        for (int j = 0; j < MERGE_REG_S; j++) {
+            if (j < a.S) {
+                o = fmaf(s_w[j], accv[j], o);
+                L += s_wl[j];
+            }
+        }
+    }
+    for (int s0 = 0; s0 < (in_regs ? 0 : a.S); s0 += 16) {
         float v[16];
 #pragma unroll
         for (int j = 0; j < 16; j++) {
@@ -871,7 +933,7 @@ int launch_down(const DownArgs& a0, const GemvShape& s, hipStream_t st) {
 }
 
 int attn_splits(int64_t maxkeys, int Hkv) {
-    int64_t S = (maxkeys + 127) / 128;
+    int64_t S = (maxkeys + 63) / 64;
     const int64_t cap = std::max(1, (512 + Hkv - 1) / Hkv);
     if (S > cap) S = cap;
     if (S < 1) S = 1;

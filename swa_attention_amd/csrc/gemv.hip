@@ -50,7 +50,7 @@ __global__ void w4_dequant_kernel(W4View a, int group, float* __restrict__ out) 
         for (int e = 0; e < 8; e++) {
             const int k = wi * 8 + e;
             const int g = k / group;
-            const int z = a.zeros ? (int)((a.zeros[n * GW + (g >> 3)] >> ((g & 7) * 4)) & 15u) : 8;
+            const int z = a.zsym ? 8 : (int)((a.zeros[n * GW + (g >> 3)] >> ((g & 7) * 4)) & 15u);
             const int c = (int)((word >> (4 * e)) & 15u);
             out[n * a.K + k] = (float)(c - z) * scale_to_f32(a.scales[n * G + g], a.scale_dtype);
         }

@@ -18,20 +18,27 @@ namespace atlas {
 struct W4View {
     const uint32_t* qweight;
     const uint16_t* scales;
-    const uint32_t* zeros;   // null: zero point 8
+    const uint32_t* zeros;   // never null: without a zero table it aliases qweight
+    int zsym;                // 1: no zero table, zero point 8 for every group
+    int zstride;             // words per row of the zero table (0 when aliased)
     int N, K, G, GW, KW, scale_dtype;
 };
 
+// Without a zero table the zero-word loads read word g/8 < K/8 of qweight's first
+// row (always in bounds) and the result is replaced by the symmetric zero point, so
+// tile loads carry no branch.
 __host__ __device__ inline W4View w4_view(const uint32_t* q, const uint16_t* s, const uint32_t* z, int N, int K,
                                           int group, int sd) {
     W4View v;
     v.qweight = q;
     v.scales = s;
-    v.zeros = z;
+    v.zsym = z == nullptr;
+    v.zeros = z ? z : q;
     v.N = N;
     v.K = K;
     v.G = (K + group - 1) / group;
     v.GW = (v.G + 7) / 8;
+    v.zstride = z ? v.GW : 0;
     v.KW = K / 8;
     v.scale_dtype = sd;
     return v;
@@ -100,14 +107,14 @@ __device__ __forceinline__ void load_tile(TileRegs<CPL>& T, const W4View& W, con
         const size_t rr = (size_t)min(row0 + m.rt[j], W.N - 1);
         T.w[j] = reinterpret_cast<const uint4*>(W.qweight + rr * W.KW)[m.ch[j]];
         T.sb[j] = W.scales[rr * W.G + m.gi[j]];
-        T.zw[j] = W.zeros ? W.zeros[rr * W.GW + (m.gi[j] >> 3)] : 0x88888888u;
+        T.zw[j] = W.zeros[rr * W.zstride + (m.gi[j] >> 3)];   // raw: used only in tile_dot
     }
 }
 
 // Per-lane partial sums of the RB rows of a tile.
 template <int CPL, int RB>
 __device__ __forceinline__ void tile_dot(const TileRegs<CPL>& T, const LanePlanes<CPL>& P, const LaneMap<CPL, RB>& m,
-                                         int scale_dtype, float acc[RB]) {
+                                         const W4View& W, float acc[RB]) {
 #pragma unroll
     for (int r = 0; r < RB; r++) acc[r] = 0.f;
 #pragma unroll
@@ -124,9 +131,9 @@ __device__ __forceinline__ void tile_dot(const TileRegs<CPL>& T, const LanePlane
         const int E0 = D[0] + (D[1] << 4) + (D[2] << 8);
         const int E1 = D[3] + (D[4] << 4) + (D[5] << 8);
         const float f = fmaf(4096.f, (float)E1, (float)E0);
-        const int z = (T.zw[j] >> ((m.gi[j] & 7) * 4)) & 15;
+        const int z = W.zsym ? 8 : (int)((T.zw[j] >> ((m.gi[j] & 7) * 4)) & 15u);
         const float tt = fmaf((float)(8 - z), P.icf[j], f);
-        const float c = scale_to_f32(T.sb[j], scale_dtype) * P.qs[j] * tt;
+        const float c = scale_to_f32(T.sb[j], W.scale_dtype) * P.qs[j] * tt;
         if (RB == 1) {
             acc[0] += c;
         } else {
