@@ -22,10 +22,30 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode64_16k_hbm_traffic.md")
+KERNEL_SOURCES = ["swa_attention_amd/csrc/gemv_core.h", "swa_attention_amd/csrc/decode_kernels.hip",
+                  "swa_attention_amd/csrc/decode_kernels.h", "swa_attention_amd/csrc/common.h"]
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate/up kernel from the committed PMC summary
+    (FETCH_SIZE and WRITE_SIZE, calibrated against a plain copy), or None when the
+    kernel sources have changed since the counters were taken."""
+    import hashlib
+    try:
+        line = [l for l in open(TRAFFIC_PROFILE) if l.startswith("traffic-json: ")][0]
+    except (OSError, IndexError):
+        return None
+    rec = json.loads(line[len("traffic-json: "):])
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return rec["bytes_per_launch"] if h.hexdigest()[:16] == rec["source_sha256_16"] else None
 
 
 def cpu_baseline(wl, budget_s):
@@ -71,6 +91,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle compute in the CPU leg")
     ap.add_argument("--profile-steps", type=int, default=3)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB (3 times); its HBM counters "
+                         "calibrate the FETCH_SIZE/WRITE_SIZE readings of the decode kernels")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
@@ -120,7 +143,7 @@ def main():
     ms = dt * 1e3 / args.steps
     assert ops.atlas_device_status(ws) == 0
 
-    # per-launch timing pass (HIP events on the launch stream)
+    # per-launch timing pass: each dispatch stamps a start and a stop hipEvent on its stream
     ops.atlas_profile_start(4096 * max(1, args.profile_steps))
     for _ in range(args.profile_steps):
         step()
@@ -139,9 +162,19 @@ def main():
         per_launch = 2 * A.w4_bytes(m.dff, m.d, m.group)
         ach = per_launch / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None,
+                "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(),
                 "kernel": f"gate_up_kernel (2 x {m.dff}x{m.d} W4 + SwiGLU)", "bytes_per_launch": per_launch,
                 "avg_launch_us": round(avg_s * 1e6, 2), "launches": cnt}
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 18   # f32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: 3 x {args.copy_probe_mib} MiB device copies")
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -194,11 +194,12 @@ ATLAS_API int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int32
 
 /* ---- launch timing (measurement aid) -------------------------------------------------
  * Between atlas_profile_start(capacity) and atlas_profile_stop(), every kernel launch
- * of the library is preceded by a hipEvent on its stream (at most `capacity`
- * launches). atlas_profile_stop synchronises, then reports per launch label the
- * number of launches and the summed time from each launch's event to the next event
- * on the stream (the kernel's execution plus any gap before the next launch). Not
- * thread-safe; meant for a single stream. */
+ * of the library (at most `capacity` launches) carries a start and a stop hipEvent
+ * that its dispatch stamps when the kernel begins and ends (hipExtLaunchKernel).
+ * atlas_profile_stop synchronises the stream of the last launch, then reports per
+ * launch label the number of launches and their summed execution time. Returns
+ * ATLAS_ERR_INVALID_ARG if not started or if more than `capacity` launches were made.
+ * Not thread-safe; meant for a single stream. */
 typedef struct atlas_profile_entry {
     char name[48];
     int32_t count;

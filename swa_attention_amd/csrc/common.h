@@ -1,6 +1,7 @@
 // Shared device and host helpers of libatlas (gfx950, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -16,6 +17,15 @@ namespace atlas {
 void set_error(const char* fmt, ...);
 int fail(int status, const char* fmt, ...);
 void prof_mark(const char* label, hipStream_t st);   // no-op unless profiling
+// Start/stop events for the launch announced by the last prof_mark (null when not
+// profiling). The dispatch itself stamps them, so they bracket the kernel's execution.
+void prof_take(hipEvent_t* start, hipEvent_t* stop);
+#define ATLAS_KLAUNCH(kern, grid, block, shmem, st, ...)                                   \
+    do {                                                                                   \
+        hipEvent_t e0_, e1_;                                                               \
+        prof_take(&e0_, &e1_);                                                             \
+        hipExtLaunchKernelGGL(kern, grid, block, shmem, st, e0_, e1_, 0u, __VA_ARGS__);    \
+    } while (0)
 
 #define ATLAS_CHECK_ARG(cond, ...)                                              \
     do {                                                                        \

@@ -881,7 +881,7 @@ GemvShape gemv_shape(int N, int K, bool split_k, int target_blocks, int max_cpl)
 
 #define GEMV_CASE(KERNEL, C_, R_, grid, lds, st, args)                                         \
     if (s.CPL == C_ && s.RB == R_) {                                                            \
-        hipLaunchKernelGGL((KERNEL<C_, R_>), grid, dim3(GEMV_THREADS), lds, st, args);          \
+        ATLAS_KLAUNCH((KERNEL<C_, R_>), grid, dim3(GEMV_THREADS), lds, st, args);          \
         ATLAS_LAUNCH_CHECK(#KERNEL);                                                            \
         return ATLAS_OK;                                                                        \
     }
@@ -946,7 +946,7 @@ int launch_attn_fused(const AttnFusedArgs& a, int G, hipStream_t st) {
     switch (G) {
 #define C(G_)                                                                           \
     case G_:                                                                            \
-        hipLaunchKernelGGL((attn_kernel<G_>), grid, dim3(ATTN_THREADS), 0, st, a);      \
+        ATLAS_KLAUNCH((attn_kernel<G_>), grid, dim3(ATTN_THREADS), 0, st, a);      \
         break;
         C(1) C(2) C(3) C(4) C(5) C(6) C(7) C(8)
 #undef C
@@ -959,7 +959,7 @@ int launch_attn_fused(const AttnFusedArgs& a, int G, hipStream_t st) {
 int launch_merge(const MergeArgs& a, hipStream_t st) {
     if (a.S > MERGE_MAX_S) return fail(ATLAS_ERR_UNSUPPORTED_SHAPE, "too many key splits (%d)", a.S);
     prof_mark("attn_merge", st);
-    hipLaunchKernelGGL(merge_kernel, dim3(a.Hq), dim3(128), 0, st, a);
+    ATLAS_KLAUNCH(merge_kernel, dim3(a.Hq), dim3(128), 0, st, a);
     ATLAS_LAUNCH_CHECK("merge_kernel");
     return ATLAS_OK;
 }
@@ -967,10 +967,10 @@ int launch_merge(const MergeArgs& a, hipStream_t st) {
 int launch_head(const HeadArgs& a, int blocks, hipStream_t st) {
     const int kw = (a.d / 8 + 63) / 64;
     prof_mark("lm_head_bf16", st);
-    if (kw <= 2) hipLaunchKernelGGL((head_kernel<2>), dim3(blocks), dim3(HEAD_THREADS), 0, st, a);
-    else if (kw <= 4) hipLaunchKernelGGL((head_kernel<4>), dim3(blocks), dim3(HEAD_THREADS), 0, st, a);
-    else if (kw <= 10) hipLaunchKernelGGL((head_kernel<10>), dim3(blocks), dim3(HEAD_THREADS), 0, st, a);
-    else if (kw <= 16) hipLaunchKernelGGL((head_kernel<16>), dim3(blocks), dim3(HEAD_THREADS), 0, st, a);
+    if (kw <= 2) ATLAS_KLAUNCH((head_kernel<2>), dim3(blocks), dim3(HEAD_THREADS), 0, st, a);
+    else if (kw <= 4) ATLAS_KLAUNCH((head_kernel<4>), dim3(blocks), dim3(HEAD_THREADS), 0, st, a);
+    else if (kw <= 10) ATLAS_KLAUNCH((head_kernel<10>), dim3(blocks), dim3(HEAD_THREADS), 0, st, a);
+    else if (kw <= 16) ATLAS_KLAUNCH((head_kernel<16>), dim3(blocks), dim3(HEAD_THREADS), 0, st, a);
     else return fail(ATLAS_ERR_UNSUPPORTED_SHAPE, "d=%d too large for the lm_head kernel", a.d);
     ATLAS_LAUNCH_CHECK("head_kernel");
     return ATLAS_OK;
@@ -978,14 +978,14 @@ int launch_head(const HeadArgs& a, int blocks, hipStream_t st) {
 
 int launch_final_hidden(const XSource& src, int d, float* out, hipStream_t st) {
     prof_mark("final_hidden", st);
-    hipLaunchKernelGGL(final_hidden_kernel, dim3(1), dim3(1024), 0, st, src, d, out);
+    ATLAS_KLAUNCH(final_hidden_kernel, dim3(1), dim3(1024), 0, st, src, d, out);
     ATLAS_LAUNCH_CHECK("final_hidden_kernel");
     return ATLAS_OK;
 }
 
 int launch_argmax_final(const float* bmax, const int* bidx, int nb, int32_t* out, hipStream_t st) {
     prof_mark("argmax", st);
-    hipLaunchKernelGGL(argmax_final2_kernel, dim3(1), dim3(1024), 0, st, bmax, bidx, nb, out);
+    ATLAS_KLAUNCH(argmax_final2_kernel, dim3(1), dim3(1024), 0, st, bmax, bidx, nb, out);
     ATLAS_LAUNCH_CHECK("argmax_final_kernel");
     return ATLAS_OK;
 }

@@ -77,14 +77,14 @@ int validate_w4(const atlas_w4* W) {
 int launch_xq_encode(const float* x, int K, XQ out, hipStream_t st) {
     const int nwords = K / 8;
     prof_mark("xq_encode", st);
-    hipLaunchKernelGGL(xq_encode_kernel, dim3((nwords + 255) / 256), dim3(256), 0, st, x, K, out);
+    ATLAS_KLAUNCH(xq_encode_kernel, dim3((nwords + 255) / 256), dim3(256), 0, st, x, K, out);
     ATLAS_LAUNCH_CHECK("xq_encode_kernel");
     return ATLAS_OK;
 }
 
 int launch_sum_partials(const float* part, int S, int N, float* y, hipStream_t st) {
     prof_mark("sum_partials", st);
-    hipLaunchKernelGGL(sum_partials_kernel, dim3((N + 255) / 256), dim3(256), 0, st, part, S, N, y);
+    ATLAS_KLAUNCH(sum_partials_kernel, dim3((N + 255) / 256), dim3(256), 0, st, part, S, N, y);
     ATLAS_LAUNCH_CHECK("sum_partials_kernel");
     return ATLAS_OK;
 }
@@ -136,7 +136,7 @@ extern "C" int atlas_w4_dequant(const atlas_w4* W, float* out, void* stream) {
     ATLAS_CHECK_ARG(out != nullptr, "null out");
     const W4View a = w4_view(W->qweight, W->scales, W->zeros, W->N, W->K, W->group, W->scale_dtype);
     prof_mark("w4_dequant", (hipStream_t)stream);
-    hipLaunchKernelGGL(w4_dequant_kernel, dim3(1024), dim3(256), 0, (hipStream_t)stream, a, W->group, out);
+    ATLAS_KLAUNCH(w4_dequant_kernel, dim3(1024), dim3(256), 0, (hipStream_t)stream, a, W->group, out);
     ATLAS_LAUNCH_CHECK("w4_dequant_kernel");
     return ATLAS_OK;
 }

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_residual_kernel(const float* __r
 int launch_rmsnorm_residual(const float* xpart, int S, const float* g, const float* resid, float* out, int n,
                             float eps, XQ xq, hipStream_t st) {
     prof_mark("rmsnorm_residual", st);
-    hipLaunchKernelGGL(rmsnorm_residual_kernel, dim3(1), dim3(1024), (size_t)n * 4, st, xpart, S, g, resid,
+    ATLAS_KLAUNCH(rmsnorm_residual_kernel, dim3(1), dim3(1024), (size_t)n * 4, st, xpart, S, g, resid,
                        out, n, eps, xq);
     ATLAS_LAUNCH_CHECK("rmsnorm_residual_kernel");
     return ATLAS_OK;
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(1024) void qk_norm_rope_kernel(QkArgs a) {
 int launch_qk_norm_rope(const QkArgs& a, hipStream_t st) {
     const size_t sh = (size_t)(a.Hq + a.Hkv) * a.D * 4;
     prof_mark("qk_norm_rope", st);
-    hipLaunchKernelGGL(qk_norm_rope_kernel, dim3(1), dim3(1024), sh, st, a);
+    ATLAS_KLAUNCH(qk_norm_rope_kernel, dim3(1), dim3(1024), sh, st, a);
     ATLAS_LAUNCH_CHECK("qk_norm_rope_kernel");
     return ATLAS_OK;
 }

@@ -43,7 +43,7 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
     const size_t dws = decode_ws_bytes(m);
     int32_t* pos = (int32_t*)((char*)ws + dws);
     prof_mark("positions", st);
-    hipLaunchKernelGGL(positions_kernel, dim3((n_tokens + 255) / 256), dim3(256), 0, st, pos, n_tokens, start_pos);
+    ATLAS_KLAUNCH(positions_kernel, dim3((n_tokens + 255) / 256), dim3(256), 0, st, pos, n_tokens, start_pos);
     ATLAS_LAUNCH_CHECK("positions_kernel");
     for (int t = 0; t < n_tokens; t++) {
         const bool last = t == n_tokens - 1;
