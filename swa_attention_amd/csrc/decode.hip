@@ -27,7 +27,7 @@ struct Carver {
 
 struct DecodeWs {
     int* status;
-    float *x, *h, *qkv, *attn_part, *a, *z, *m_part, *logits, *bmax;
+    float *x, *h, *qkv, *ssq, *attn_part, *a, *z, *m_part, *logits, *bmax;
     int* bidx;
     XQ xq_o;
     size_t bytes;
@@ -62,6 +62,7 @@ static DecodeWs carve(const atlas_model* m, const DecodePlan& p, void* base) {
     w.x = (float*)c.take((size_t)m->d * 4);
     w.h = (float*)c.take((size_t)m->d * 4);
     w.qkv = (float*)c.take((size_t)nqkv * 4);
+    w.ssq = (float*)c.take((size_t)p.qkv.blocks * 2 * 4);
     w.attn_part = (float*)c.take((size_t)m->hq * p.S_max * ATTN_PART_F * 4);
     w.xq_o = xq_view(c.take(xq_bytes(nq)), nq);
     w.a = (float*)c.take((size_t)m->d * 4);
@@ -90,6 +91,7 @@ int validate_model(const atlas_model* m) {
     const DecodePlan p = make_plan(m);
     ATLAS_CHECK_SHAPE(p.qkv.CPL && p.o.CPL && p.gu.CPL && p.down.CPL, "projection shapes unsupported");
     ATLAS_CHECK_SHAPE(p.S_max <= 1024, "too many key splits");
+    ATLAS_CHECK_SHAPE(p.qkv.blocks <= ATTN_SSQ_MAX_BLOCKS, "qkv projection needs too many blocks");
     for (int l = 0; l < m->n_layers; l++) {
         const atlas_layer& L = m->layers[l];
         struct { const atlas_w4* w; int N, K; const char* name; } ws[5] = {
@@ -145,6 +147,9 @@ int run_decode_layers(const atlas_model* m, const XSource& first, const int32_t*
         qa.qkv = w.qkv;
         qa.x_out = w.x;
         qa.status = l == 0 ? w.status : nullptr;
+        qa.ssq_part = w.ssq;
+        qa.nq = m->hq * m->hd;
+        qa.nk = m->hkv * m->hd;
         if ((rc = launch_qkv(qa, p.qkv, st))) return rc;
         // 2. QK-norm, rotary, KV append and split attention
         AttnFusedArgs aa{};
@@ -167,6 +172,8 @@ int run_decode_layers(const atlas_model* m, const XSource& first, const int32_t*
         aa.part = w.attn_part;
         aa.status = w.status;
         aa.fused = 1;
+        aa.ssq_part = w.ssq;
+        aa.n_ssq = p.qkv.blocks;
         if ((rc = launch_attn_fused(aa, m->hq / m->hkv, st))) return rc;
         // 3. merge the key splits into o (encoded for the o projection)
         MergeArgs ma{};

@@ -7,6 +7,7 @@ namespace atlas {
 constexpr int GEMV_THREADS = 512;   // 8 waves per GEMV block
 constexpr int ATTN_THREADS = 256;   // 4 waves = 16 key streams per attention block
 constexpr int ATTN_PART_F = 130;    // m, l, acc[128] per (query head, split)
+constexpr int ATTN_SSQ_MAX_BLOCKS = 512;   // qkv blocks whose sums of squares attention reads
 
 // How a QKV block obtains the layer input x.
 enum XMode { X_FROM_EMBED = 0, X_FROM_HIDDEN = 1, X_FROM_RESIDUAL = 2 };
@@ -31,6 +32,8 @@ struct QkvArgs {
     float* qkv;          // [N] out
     float* x_out;        // [d] out (block 0): the layer input, kept for the residual
     int* status;         // reset to OK by block 0 (or set on a bad token id)
+    float* ssq_part;     // [blocks][2] out (may be null): per-block sums of squares of the
+    int nq, nk;          //   q rows [0, nq) and the k rows [nq, nq + nk)
 };
 
 struct AttnFusedArgs {
@@ -48,6 +51,8 @@ struct AttnFusedArgs {
     int* status;
     int fused;                 // 1: q/k/v from qkv with norm + rotary + KV append; 0: q final, cache ready
     const float* q_final;      // fused == 0
+    const float* ssq_part;     // fused: [n_ssq][2] sums of squares of q and k (qkv kernel)
+    int n_ssq;
 };
 
 struct MergeArgs {

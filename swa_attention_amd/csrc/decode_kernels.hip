@@ -29,67 +29,86 @@ constexpr int MAX_DOWN_SPLITS = 4;
 
 __device__ __forceinline__ float4 f4_zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
 
-// s_x[0..d) <- the layer input described by src (block-wide; ends with a barrier).
-// NV4 >= d / (4 * blockDim.x).
+// The layer input described by src, in two halves: x_issue() issues every load into
+// registers, x_finish() combines them into s_x[0..d) (block-wide; ends with a
+// barrier). Kernels call x_issue() before their first weight load: loads complete in
+// issue order, so inputs loaded after the weight prefetch would wait for it.
+// NV4 >= d / (4 * blockDim.x). Indices past d are clamped to 0 (loads stay
+// unconditional, which keeps the compiler's wait counting exact).
 template <int NV4>
-__device__ void build_x(const XSource& src, int d, float* s_x, float* red) {
+struct XRegs {
+    float4 h[NV4], g[NV4];                  // EMBED: raw bf16 pairs in h[].x, h[].y
+    float4 p[MAX_DOWN_SPLITS][NV4];
+};
+
+template <int NV4, bool RESID_ONLY = false>
+__device__ __forceinline__ void x_issue(const XSource& src, int d, XRegs<NV4>& R) {
     const int n4 = d >> 2, bd = blockDim.x;
-    float4* sx4 = reinterpret_cast<float4*>(s_x);
-    if (src.mode == X_FROM_EMBED) {
+    if (!RESID_ONLY && src.mode == X_FROM_EMBED) {
         int tok = *src.d_token;
         if (tok < 0 || tok >= src.vocab) tok = 0;
         const uint2* row = reinterpret_cast<const uint2*>(src.emb + (size_t)tok * d);
-        uint2 v[NV4];
 #pragma unroll
         for (int j = 0; j < NV4; j++) {
             const int i = threadIdx.x + j * bd;
-            v[j] = row[i < n4 ? i : 0];
+            const uint2 v = row[i < n4 ? i : 0];
+            R.h[j] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), 0.f, 0.f);
         }
-#pragma unroll
-        for (int j = 0; j < NV4; j++) {
-            const int i = threadIdx.x + j * bd;
-            if (i < n4)
-                sx4[i] = make_float4(bf16_bits_to_f32(v[j].x & 0xFFFFu), bf16_bits_to_f32(v[j].x >> 16),
-                                     bf16_bits_to_f32(v[j].y & 0xFFFFu), bf16_bits_to_f32(v[j].y >> 16));
-        }
-    } else if (src.mode == X_FROM_HIDDEN) {
+    } else if (!RESID_ONLY && src.mode == X_FROM_HIDDEN) {
         const float4* h4 = reinterpret_cast<const float4*>(src.hidden);
-        float4 v[NV4];
 #pragma unroll
         for (int j = 0; j < NV4; j++) {
             const int i = threadIdx.x + j * bd;
-            v[j] = h4[i < n4 ? i : 0];
-        }
-#pragma unroll
-        for (int j = 0; j < NV4; j++) {
-            const int i = threadIdx.x + j * bd;
-            if (i < n4) sx4[i] = v[j];
+            R.h[j] = h4[i < n4 ? i : 0];
         }
     } else {
         const float4* p4 = reinterpret_cast<const float4*>(src.m_part);
         const float4* h4 = reinterpret_cast<const float4*>(src.h);
         const float4* g4 = reinterpret_cast<const float4*>(src.g);
-        float4 m[NV4], hh[NV4], gg[NV4], pv[MAX_DOWN_SPLITS][NV4];
 #pragma unroll
         for (int j = 0; j < NV4; j++) {
             const int i = threadIdx.x + j * bd, ic = i < n4 ? i : 0;
-            hh[j] = h4[ic];
-            gg[j] = g4[ic];
+            R.h[j] = h4[ic];
+            R.g[j] = g4[ic];
 #pragma unroll
-            for (int s = 0; s < MAX_DOWN_SPLITS; s++) pv[s][j] = p4[(size_t)min(s, src.S - 1) * n4 + ic];
+            for (int s = 0; s < MAX_DOWN_SPLITS; s++) R.p[s][j] = p4[(size_t)min(s, src.S - 1) * n4 + ic];
         }
+    }
+}
+
+template <int NV4, bool RESID_ONLY = false>
+__device__ void x_finish(const XSource& src, int d, const XRegs<NV4>& R, float* s_x, float* red) {
+    const int n4 = d >> 2, bd = blockDim.x;
+    float4* sx4 = reinterpret_cast<float4*>(s_x);
+    if (!RESID_ONLY && src.mode == X_FROM_EMBED) {
+#pragma unroll
+        for (int j = 0; j < NV4; j++) {
+            const int i = threadIdx.x + j * bd;
+            const uint32_t lo = __float_as_uint(R.h[j].x), hi = __float_as_uint(R.h[j].y);
+            if (i < n4)
+                sx4[i] = make_float4(bf16_bits_to_f32(lo & 0xFFFFu), bf16_bits_to_f32(lo >> 16),
+                                     bf16_bits_to_f32(hi & 0xFFFFu), bf16_bits_to_f32(hi >> 16));
+        }
+    } else if (!RESID_ONLY && src.mode == X_FROM_HIDDEN) {
+#pragma unroll
+        for (int j = 0; j < NV4; j++) {
+            const int i = threadIdx.x + j * bd;
+            if (i < n4) sx4[i] = R.h[j];
+        }
+    } else {
+        float4 m[NV4];
         float ss = 0.f;
 #pragma unroll
         for (int j = 0; j < NV4; j++) {
             const int i = threadIdx.x + j * bd;
-            float4 v = pv[0][j];
+            float4 v = R.p[0][j];
 #pragma unroll
             for (int s = 1; s < MAX_DOWN_SPLITS; s++) {
                 if (s < src.S) {
-                    v.x += pv[s][j].x;
-                    v.y += pv[s][j].y;
-                    v.z += pv[s][j].z;
-                    v.w += pv[s][j].w;
+                    v.x += R.p[s][j].x;
+                    v.y += R.p[s][j].y;
+                    v.z += R.p[s][j].z;
+                    v.w += R.p[s][j].w;
                 }
             }
             if (i >= n4) v = f4_zero();
@@ -105,11 +124,18 @@ __device__ void build_x(const XSource& src, int d, float* s_x, float* red) {
         for (int j = 0; j < NV4; j++) {
             const int i = threadIdx.x + j * bd;
             if (i < n4)
-                sx4[i] = make_float4(hh[j].x + gg[j].x * (m[j].x * r), hh[j].y + gg[j].y * (m[j].y * r),
-                                     hh[j].z + gg[j].z * (m[j].z * r), hh[j].w + gg[j].w * (m[j].w * r));
+                sx4[i] = make_float4(R.h[j].x + R.g[j].x * (m[j].x * r), R.h[j].y + R.g[j].y * (m[j].y * r),
+                                     R.h[j].z + R.g[j].z * (m[j].z * r), R.h[j].w + R.g[j].w * (m[j].w * r));
         }
     }
     __syncthreads();
+}
+
+template <int NV4>
+__device__ void build_x(const XSource& src, int d, float* s_x, float* red) {
+    XRegs<NV4> R;
+    x_issue<NV4>(src, d, R);
+    x_finish<NV4>(src, d, R, s_x, red);
 }
 
 template <int RB>
@@ -135,15 +161,15 @@ __device__ __forceinline__ int wave_tiles(int t0, int t_end, int NW) {
 template <int CPL, int RB, int NS>
 __device__ __forceinline__ void prefetch_tiles(TileRegs<CPL> (&R)[NS], const W4View& W, const LaneMap<CPL, RB>& m,
                                                int t0, int nt, int NW) {
-    if (nt <= 0) return;
+    // unconditional (a wave without tiles loads row 0): a branch here would make the
+    // compiler wait for these loads wherever it waits for anything issued before them
 #pragma unroll
-    for (int k = 0; k < NS - 1; k++) load_tile(R[k], W, m, (t0 + min(k, nt - 1) * NW) * RB);
+    for (int k = 0; k < NS - 1; k++) load_tile(R[k], W, m, max(0, (t0 + min(k, nt - 1) * NW) * RB));
 }
 
-template <int CPL, int RB, int NS>
-__device__ __forceinline__ void stream_rows(const W4View& W, const LaneMap<CPL, RB>& m, const LanePlanes<CPL>& P,
-                                            TileRegs<CPL> (&R)[NS], int t0, int nt, int NW, float* out,
-                                            int lane) {
+template <int CPL, int RB, int NS, class Epi>
+__device__ __forceinline__ void stream_rows_epi(const W4View& W, const LaneMap<CPL, RB>& m, const LanePlanes<CPL>& P,
+                                                TileRegs<CPL> (&R)[NS], int t0, int nt, int NW, Epi epi) {
     int i = 0;
     for (; i + NS <= nt; i += NS) {
 #pragma unroll
@@ -152,7 +178,7 @@ __device__ __forceinline__ void stream_rows(const W4View& W, const LaneMap<CPL, 
             __builtin_amdgcn_sched_barrier(0);
             float acc[RB];
             tile_dot(R[k], P, m, W, acc);
-            write_rows<RB>(acc, (t0 + (i + k) * NW) * RB, W.N, out, lane);
+            epi(acc, (t0 + (i + k) * NW) * RB);
         }
     }
 #pragma unroll
@@ -160,9 +186,17 @@ __device__ __forceinline__ void stream_rows(const W4View& W, const LaneMap<CPL, 
         if (i + k < nt) {
             float acc[RB];
             tile_dot(R[k], P, m, W, acc);
-            write_rows<RB>(acc, (t0 + (i + k) * NW) * RB, W.N, out, lane);
+            epi(acc, (t0 + (i + k) * NW) * RB);
         }
     }
+}
+
+template <int CPL, int RB, int NS>
+__device__ __forceinline__ void stream_rows(const W4View& W, const LaneMap<CPL, RB>& m, const LanePlanes<CPL>& P,
+                                            TileRegs<CPL> (&R)[NS], int t0, int nt, int NW, float* out,
+                                            int lane) {
+    stream_rows_epi<CPL, RB, NS>(W, m, P, R, t0, nt, NW,
+                                 [&](const float (&acc)[RB], int row0) { write_rows<RB>(acc, row0, W.N, out, lane); });
 }
 
 // LDS carve for the GEMV kernels: [s_x: dx floats][planes CW*24][qs CW][isum CW]
@@ -187,10 +221,11 @@ constexpr int GU_STAGES = 3;                          // gate/up: 2 tile pairs i
 
 // ---- qkv projection ----------------------------------------------------------------------
 
-template <int CPL, int RB>
-__global__ __launch_bounds__(GEMV_THREADS) void qkv_kernel(QkvArgs a) {
+template <int CPL, int RB, bool RESID>
+__device__ __forceinline__ void qkv_body(const QkvArgs& a) {
     extern __shared__ uint32_t smem[];
     __shared__ float red[16];
+    __shared__ float s_ss[2][GEMV_THREADS / 64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, NW = blockDim.x >> 6;
     GemvLds L(smem, a.d, a.CW);
     LaneMap<CPL, RB> m;
@@ -198,6 +233,9 @@ __global__ __launch_bounds__(GEMV_THREADS) void qkv_kernel(QkvArgs a) {
     const int T = (a.W.N + RB - 1) / RB;
     const int t_begin = blockIdx.x * a.tiles_per_block, t_end = min(T, t_begin + a.tiles_per_block);
     const int t = t_begin + wave, nt = wave_tiles(t, t_end, NW);
+    XRegs<GEMV_NV4> XR;
+    x_issue<GEMV_NV4, RESID>(a.src, a.d, XR);
+    __builtin_amdgcn_sched_barrier(0);
     TileRegs<CPL> R[gemv_stages<CPL>()];
     prefetch_tiles<CPL, RB, gemv_stages<CPL>()>(R, a.W, m, t, nt, NW);   // in flight during the prologue
 
@@ -209,14 +247,49 @@ __global__ __launch_bounds__(GEMV_THREADS) void qkv_kernel(QkvArgs a) {
         }
         *a.status = ok ? ATLAS_OK : ATLAS_ERR_INVALID_ARG;
     }
-    build_x<GEMV_NV4>(a.src, a.d, L.s_x, red);
+    x_finish<GEMV_NV4, RESID>(a.src, a.d, XR, L.s_x, red);
     if (blockIdx.x == 0)
         for (int i = threadIdx.x; i < a.d; i += blockDim.x) a.x_out[i] = L.s_x[i];
     encode_lds(L.s_x, a.d, L.s_pl, L.s_qs, L.s_is);
     __syncthreads();
     LanePlanes<CPL> P;
     P.load(m, L.s_pl, L.s_qs, L.s_is, 0);
-    stream_rows<CPL, RB, gemv_stages<CPL>()>(a.W, m, P, R, t, nt, NW, a.qkv, lane);
+    // rows are written as they finish; lane 0 also sums the squares of its q rows and
+    // of its k rows (the statistics of the full-projection QK RMSNorm)
+    float ssq = 0.f, ssk = 0.f;
+    stream_rows_epi<CPL, RB, gemv_stages<CPL>()>(a.W, m, P, R, t, nt, NW, [&](const float (&acc)[RB], int row0) {
+#pragma unroll
+        for (int r = 0; r < RB; r++) {
+            const float v = wave_sum(acc[r]);
+            const int row = row0 + r;
+            if (lane == 0 && row < a.W.N) a.qkv[row] = v;
+            const float sq = v * v;
+            ssq += row < a.nq ? sq : 0.f;
+            ssk += (row >= a.nq && row < a.nq + a.nk) ? sq : 0.f;
+        }
+    });
+    if (a.ssq_part) {
+        if (lane == 0) {
+            s_ss[0][wave] = ssq;
+            s_ss[1][wave] = ssk;
+        }
+        __syncthreads();
+        if (threadIdx.x < 2) {
+            float v = 0.f;
+            for (int w = 0; w < NW; w++) v += s_ss[threadIdx.x][w];
+            a.ssq_part[2 * blockIdx.x + threadIdx.x] = v;
+        }
+    }
+}
+
+// layer 0 (input from the embedding or a hidden vector) and every later layer
+template <int CPL, int RB>
+__global__ __launch_bounds__(GEMV_THREADS) void qkv_kernel(QkvArgs a) {
+    qkv_body<CPL, RB, false>(a);
+}
+template <int CPL, int RB>
+__global__ __launch_bounds__(GEMV_THREADS) void qkv_resid_kernel(QkvArgs a) {
+    qkv_body<CPL, RB, true>(a);
 }
 
 // ---- generic GEMV over an input already encoded in global memory ----------------------------
@@ -232,9 +305,12 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_planes_kernel(GemvPlanesArg
     const int T = (a.W.N + RB - 1) / RB;
     const int t_begin = blockIdx.x * a.tiles_per_block, t_end = min(T, t_begin + a.tiles_per_block);
     const int t = t_begin + wave, nt = wave_tiles(t, t_end, NW);
+    PlaneStage PS;
+    planes_issue<GEMV_THREADS>(a.xq, C0, a.CW, PS);
+    __builtin_amdgcn_sched_barrier(0);
     TileRegs<CPL> R[gemv_stages<CPL>()];
     prefetch_tiles<CPL, RB, gemv_stages<CPL>()>(R, a.W, m, t, nt, NW);
-    stage_planes(a.xq, C0, a.CW, L.s_pl, L.s_qs, L.s_is);
+    planes_commit<GEMV_THREADS>(PS, a.CW, L.s_pl, L.s_qs, L.s_is);
     __syncthreads();
     LanePlanes<CPL> P;
     P.load(m, L.s_pl, L.s_qs, L.s_is, C0);
@@ -265,16 +341,13 @@ __global__ __launch_bounds__(GEMV_THREADS) void gate_up_kernel(GateUpArgs a) {
     const int T = (a.Wg.N + RB - 1) / RB;
     const int t_begin = blockIdx.x * a.tiles_per_block, t_end = min(T, t_begin + a.tiles_per_block);
     const int t = t_begin + wave, nt = wave_tiles(t, t_end, NW);
-    TileRegs<CPL> RG[GU_STAGES], RU[GU_STAGES];
-    prefetch_tiles<CPL, RB, GU_STAGES>(RG, a.Wg, m, t, nt, NW);
-    prefetch_tiles<CPL, RB, GU_STAGES>(RU, a.Wu, m, t, nt, NW);
-    // h = x + g * a / rms(a)
+    // h = x + g * a / rms(a): inputs loaded first, then the weight prefetch
+    const int n4 = a.d >> 2, bd = blockDim.x;
+    float4 va[GEMV_NV4], vx[GEMV_NV4], vg[GEMV_NV4];
     {
-        const int n4 = a.d >> 2, bd = blockDim.x;
         const float4* a4 = reinterpret_cast<const float4*>(a.a);
         const float4* x4 = reinterpret_cast<const float4*>(a.x);
         const float4* g4 = reinterpret_cast<const float4*>(a.g);
-        float4 va[GEMV_NV4], vx[GEMV_NV4], vg[GEMV_NV4];
 #pragma unroll
         for (int j = 0; j < GEMV_NV4; j++) {
             const int i = threadIdx.x + j * bd, ic = i < n4 ? i : 0;
@@ -282,6 +355,12 @@ __global__ __launch_bounds__(GEMV_THREADS) void gate_up_kernel(GateUpArgs a) {
             vx[j] = x4[ic];
             vg[j] = g4[ic];
         }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    TileRegs<CPL> RG[GU_STAGES], RU[GU_STAGES];
+    prefetch_tiles<CPL, RB, GU_STAGES>(RG, a.Wg, m, t, nt, NW);
+    prefetch_tiles<CPL, RB, GU_STAGES>(RU, a.Wu, m, t, nt, NW);
+    {
         float ss = 0.f;
 #pragma unroll
         for (int j = 0; j < GEMV_NV4; j++) {
@@ -341,6 +420,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void gate_up_kernel(GateUpArgs a) {
 // ---- down projection (split-K) --------------------------------------------------------------
 
 constexpr int DOWN_MAX_ROUNDS = 3;   // CW <= 3 * GEMV_THREADS / 4 chunks
+static_assert(DOWN_MAX_ROUNDS * GEMV_THREADS / 4 * XQ_WORDS_PER_CHUNK <= PLANE_REGS * 4 * GEMV_THREADS,
+              "an encoded range must fit the register staging of planes_issue");
 
 template <int CPL, int RB>
 __global__ __launch_bounds__(GEMV_THREADS) void down_kernel(DownArgs a) {
@@ -353,22 +434,26 @@ __global__ __launch_bounds__(GEMV_THREADS) void down_kernel(DownArgs a) {
     const int T = (a.W.N + RB - 1) / RB;
     const int t_begin = blockIdx.x * a.tiles_per_block, t_end = min(T, t_begin + a.tiles_per_block);
     const int t = t_begin + wave, nt = wave_tiles(t, t_end, NW);
-    TileRegs<CPL> R[gemv_stages<CPL>()];
-    prefetch_tiles<CPL, RB, gemv_stages<CPL>()>(R, a.W, m, t, nt, NW);
-    {   // encode z[C0*32 .. (C0+CW)*32) straight into LDS
-        XQ o;
-        o.planes = L.s_pl;
-        o.qs = L.s_qs;
-        o.isum = L.s_is;
-        const int nwords = a.CW * 4;
+    // this block's range of z, loaded before the weight prefetch and encoded into LDS
+    const int nwords = a.CW * 4;
+    float4 u[DOWN_MAX_ROUNDS], v[DOWN_MAX_ROUNDS];
+    {
         const float4* zb = reinterpret_cast<const float4*>(a.z + (size_t)C0 * XQ_CHUNK);
-        float4 u[DOWN_MAX_ROUNDS], v[DOWN_MAX_ROUNDS];
 #pragma unroll
         for (int r = 0; r < DOWN_MAX_ROUNDS; r++) {
             const int w = threadIdx.x + r * blockDim.x, wc = w < nwords ? w : 0;
             u[r] = zb[2 * wc];
             v[r] = zb[2 * wc + 1];
         }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    TileRegs<CPL> R[gemv_stages<CPL>()];
+    prefetch_tiles<CPL, RB, gemv_stages<CPL>()>(R, a.W, m, t, nt, NW);
+    {
+        XQ o;
+        o.planes = L.s_pl;
+        o.qs = L.s_qs;
+        o.isum = L.s_is;
 #pragma unroll
         for (int r = 0; r < DOWN_MAX_ROUNDS; r++) {
             const int w = threadIdx.x + r * blockDim.x;
@@ -390,10 +475,14 @@ __global__ __launch_bounds__(GEMV_THREADS) void down_kernel(DownArgs a) {
 // groups of each wave are independent key streams with their own online softmax,
 // combined at the end. Queries stay in registers.
 
-constexpr int ATTN_KV_STAGES = 4;   // keys in flight per 16-lane stream: 3
+constexpr int ATTN_KV_STAGES = 5;   // keys in flight per 16-lane stream: 4
+constexpr int ATTN_SSQ_REGS = ATTN_SSQ_MAX_BLOCKS / ATTN_THREADS;   // sums-of-squares partials per thread
+constexpr int ATTN_QF_REGS = 8 * 128 / ATTN_THREADS;                 // query values per thread (G <= 8)
 
-template <int G>
-__global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(AttnFusedArgs a) {
+// FUSED: q/k/v come raw from the qkv projection (norm, rotary and KV append here);
+// otherwise q is final and the cache already holds the new key.
+template <int G, bool FUSED>
+__global__ __launch_bounds__(ATTN_THREADS, G <= 5 ? 2 : 1) void attn_kernel(AttnFusedArgs a) {
     constexpr int D = 128;
     __shared__ float s_q[G][D];
     __shared__ float s_kn[D], s_vn[D];
@@ -428,7 +517,7 @@ __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(AttnFusedArgs a) {
     const float* Vh = a.v_cache + (size_t)kv * a.T_max * D;
     // K/V of key i of this split (clamped into the split)
     auto load_kv = [&](int i, float4& ka, float4& kb, float4& va, float4& vb) {
-        const int j = k0 + min(i, cnt - 1);
+        const int j = cnt > 0 ? k0 + min(i, cnt - 1) : lo;
         const float4* kp = reinterpret_cast<const float4*>(Kh + (size_t)j * D + 8 * sub);
         const float4* vp = reinterpret_cast<const float4*>(Vh + (size_t)j * D + 8 * sub);
         ka = kp[0];
@@ -436,35 +525,24 @@ __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(AttnFusedArgs a) {
         va = vp[0];
         vb = vp[1];
     };
-    // ring of ATTN_KV_STAGES keys per stream; the first ATTN_KV_STAGES-1 are in flight
-    // during the prologue
-    float4 rk[ATTN_KV_STAGES][2], rv[ATTN_KV_STAGES][2];
+    // Prologue inputs first (loads complete in issue order): the qkv kernel's per-block
+    // sums of squares, this block's q heads and k/v head, and their gains.
+    float ps_q[ATTN_SSQ_REGS], ps_k[ATTN_SSQ_REGS];
+    float xq0[2], xq1[2], gq0[2], gq1[2], vnew = 0.f;
+    float qf[ATTN_QF_REGS];
+    const double inv_i = a.inv[threadIdx.x & 63];   // kernel-argument array: a memory load
+    if (!FUSED) {
 #pragma unroll
-    for (int k = 0; k < ATTN_KV_STAGES - 1; k++)
-        if (stream + 16 * k < cnt) load_kv(stream + 16 * k, rk[k][0], rk[k][1], rv[k][0], rv[k][1]);
-
-    if (a.fused) {
-        // sums of squares of the whole q and k projections (all loads issued first)
-        const int n4 = (nq + nk) >> 2, nq4 = nq >> 2;
-        const float4* qkv4 = reinterpret_cast<const float4*>(a.qkv);
-        float ssq = 0.f, ssk = 0.f;
-        for (int base = 0; base < n4; base += 8 * ATTN_THREADS) {
-            float4 v[8];
+        for (int r = 0; r < ATTN_QF_REGS; r++)
+            qf[r] = a.q_final[(size_t)kv * G * D + min((int)threadIdx.x + r * ATTN_THREADS, G * D - 1)];
+    } else {
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const int i = base + threadIdx.x + j * ATTN_THREADS;
-                v[j] = qkv4[i < n4 ? i : 0];
-            }
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const int i = base + threadIdx.x + j * ATTN_THREADS;
-                const float e = v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
-                if (i < nq4) ssq += e;
-                else if (i < n4) ssk += e;
-            }
+        for (int j = 0; j < ATTN_SSQ_REGS; j++) {
+            const int b = threadIdx.x + j * ATTN_THREADS, bc = b < a.n_ssq ? b : 0;
+            const float2 v = reinterpret_cast<const float2*>(a.ssq_part)[bc];
+            ps_q[j] = v.x;
+            ps_k[j] = v.y;
         }
-        // this block's q heads and k head (loads issued before the reductions)
-        float xq0[2], xq1[2], gq0[2], gq1[2];
 #pragma unroll
         for (int r = 0; r < 2; r++) {
             const int t = threadIdx.x + r * ATTN_THREADS;
@@ -478,16 +556,41 @@ __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(AttnFusedArgs a) {
             gq0[r] = g[i];
             gq1[r] = g[i + 64];
         }
-        const float vnew = a.qkv[nq + nk + kv * D + (threadIdx.x & (D - 1))];
+        vnew = a.qkv[nq + nk + kv * D + (threadIdx.x & (D - 1))];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ring of ATTN_KV_STAGES keys per stream; the first ATTN_KV_STAGES-1 are in flight
+    // during the prologue
+    float4 rk[ATTN_KV_STAGES][2], rv[ATTN_KV_STAGES][2];
+#pragma unroll
+    for (int k = 0; k < ATTN_KV_STAGES - 1; k++) load_kv(stream + 16 * k, rk[k][0], rk[k][1], rv[k][0], rv[k][1]);
+    // (keys past the stream's last one are clamped loads of valid rows, never consumed)
+
+    if (FUSED) {
+        // pin the partial sums here, after the key/value prefetch: otherwise the
+        // compiler may add them up right after their loads and wait for them there
+#pragma unroll
+        for (int j = 0; j < ATTN_SSQ_REGS; j++) asm volatile("" : "+v"(ps_q[j]), "+v"(ps_k[j]));
+        float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+        for (int j = 0; j < ATTN_SSQ_REGS; j++) {
+            if (threadIdx.x + j * ATTN_THREADS < a.n_ssq) {
+                ssq += ps_q[j];
+                ssk += ps_k[j];
+            }
+        }
         ssq = block_sum(ssq, red);
         ssk = block_sum(ssk, red);
         const float rq = 1.0f / sqrtf(ssq / (float)nq + a.eps);
         const float rk = 1.0f / sqrtf(ssk / (float)nk + a.eps);
         if (threadIdx.x < 64) {
-            double sn, cs;
-            sincos((double)pos * a.inv[threadIdx.x], &sn, &cs);
-            s_cos[threadIdx.x] = (float)(cs * a.mscale);
-            s_sin[threadIdx.x] = (float)(sn * a.mscale);
+            // angle pos * inv in f64, reduced to [-pi, pi] in f64, then sine/cosine in f32
+            const double ang = (double)pos * inv_i;
+            const double rr = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+            float sn, cs;
+            sincosf((float)rr, &sn, &cs);
+            s_cos[threadIdx.x] = cs * (float)a.mscale;
+            s_sin[threadIdx.x] = sn * (float)a.mscale;
         }
         if (threadIdx.x < D) s_vn[threadIdx.x] = vnew;
         __syncthreads();
@@ -517,7 +620,11 @@ __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(AttnFusedArgs a) {
             a.v_cache[off] = s_vn[threadIdx.x];
         }
     } else {
-        for (int t = threadIdx.x; t < G * D; t += blockDim.x) s_q[t / D][t % D] = a.q_final[(size_t)kv * G * D + t];
+#pragma unroll
+        for (int r = 0; r < ATTN_QF_REGS; r++) {
+            const int t = threadIdx.x + r * ATTN_THREADS;
+            if (t < G * D) s_q[t / D][t % D] = qf[r];
+        }
         __syncthreads();
     }
 
@@ -534,47 +641,55 @@ __global__ __launch_bounds__(ATTN_THREADS) void attn_kernel(AttnFusedArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; i++) acc[h][i] = 0.f;
     }
-    // keys stream, stream+16, ...; the next key's K/V are loaded before the current
-    // one is used. The new token's key and value come from LDS (the cache write above
-    // may still be in flight).
-    for (int i0 = stream; i0 < cnt; i0 += 16 * ATTN_KV_STAGES) {
+    // This stream's keys are stream, stream+16, ... (< cnt): nks of them. The ring holds
+    // ATTN_KV_STAGES keys; each step loads the key ATTN_KV_STAGES-1 ahead and consumes
+    // the oldest. Whole groups of ATTN_KV_STAGES keys run with unconditional (clamped)
+    // loads so that the compiler's wait counting stays exact; the remainder is already
+    // loaded. The new token's key and value come from LDS (the cache write above may
+    // still be in flight).
+    constexpr int NS = ATTN_KV_STAGES;
+    const int nks = cnt > stream ? (cnt - stream + 15) / 16 : 0;
+    auto consume = [&](int slot, int idx) {
+        const int j = k0 + stream + 16 * idx;
+        float kx[8] = {rk[slot][0].x, rk[slot][0].y, rk[slot][0].z, rk[slot][0].w,
+                       rk[slot][1].x, rk[slot][1].y, rk[slot][1].z, rk[slot][1].w};
+        float vx[8] = {rv[slot][0].x, rv[slot][0].y, rv[slot][0].z, rv[slot][0].w,
+                       rv[slot][1].x, rv[slot][1].y, rv[slot][1].z, rv[slot][1].w};
+        if (FUSED && j == pos) {
 #pragma unroll
-        for (int k = 0; k < ATTN_KV_STAGES; k++) {
-            const int i = i0 + 16 * k;
-            if (i >= cnt) break;
-            const int il = i + 16 * (ATTN_KV_STAGES - 1);
-            if (il < cnt) {
-                const int slot = (k + ATTN_KV_STAGES - 1) % ATTN_KV_STAGES;
-                load_kv(il, rk[slot][0], rk[slot][1], rv[slot][0], rv[slot][1]);
-            }
-            const int j = k0 + i;
-            float kx[8] = {rk[k][0].x, rk[k][0].y, rk[k][0].z, rk[k][0].w,
-                           rk[k][1].x, rk[k][1].y, rk[k][1].z, rk[k][1].w};
-            float vx[8] = {rv[k][0].x, rv[k][0].y, rv[k][0].z, rv[k][0].w,
-                           rv[k][1].x, rv[k][1].y, rv[k][1].z, rv[k][1].w};
-            if (a.fused && j == pos) {
-#pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    kx[e] = s_kn[8 * sub + e];
-                    vx[e] = s_vn[8 * sub + e];
-                }
-            }
-#pragma unroll
-            for (int h = 0; h < G; h++) {
-                float dsum = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; e++) dsum = fmaf(q[h][e], kx[e], dsum);
-                const float sc = row16_sum(dsum) * a.scale;
-                const float mn = fmaxf(mh[h], sc);
-                const float c = __expf(mh[h] - mn);
-                const float p = __expf(sc - mn);
-                lh[h] = fmaf(lh[h], c, p);
-#pragma unroll
-                for (int e = 0; e < 8; e++) acc[h][e] = fmaf(acc[h][e], c, p * vx[e]);
-                mh[h] = mn;
+            for (int e = 0; e < 8; e++) {
+                kx[e] = s_kn[8 * sub + e];
+                vx[e] = s_vn[8 * sub + e];
             }
         }
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            float dsum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) dsum = fmaf(q[h][e], kx[e], dsum);
+            const float sc = row16_sum(dsum) * a.scale;
+            const float mn = fmaxf(mh[h], sc);
+            const float c = __expf(mh[h] - mn);
+            const float p = __expf(sc - mn);
+            lh[h] = fmaf(lh[h], c, p);
+#pragma unroll
+            for (int e = 0; e < 8; e++) acc[h][e] = fmaf(acc[h][e], c, p * vx[e]);
+            mh[h] = mn;
+        }
+    };
+    int ik = 0;
+    for (; ik + NS <= nks; ik += NS) {
+#pragma unroll
+        for (int k = 0; k < NS; k++) {
+            const int slot = (k + NS - 1) % NS;
+            load_kv(stream + 16 * min(ik + k + NS - 1, nks - 1), rk[slot][0], rk[slot][1], rv[slot][0], rv[slot][1]);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(k, ik + k);
+        }
     }
+#pragma unroll
+    for (int k = 0; k < NS - 1; k++)
+        if (ik + k < nks) consume(k, ik + k);
     // combine the four streams of the wave (lanes l, l^16, l^32, l^48)
 #pragma unroll
     for (int h = 0; h < G; h++) {
@@ -735,10 +850,13 @@ __global__ __launch_bounds__(HEAD_THREADS) void head_kernel(HeadArgs a) {
             w[j] = W[wd < nw ? wd : 0];
         }
     };
+    XRegs<8192 / 4 / HEAD_THREADS> XR;
+    x_issue<8192 / 4 / HEAD_THREADS, true>(a.src, a.d, XR);
+    __builtin_amdgcn_sched_barrier(0);
     uint4 wa[KW], wb[KW];
     int row = r0 + wave;
-    if (row < r1) load_row(row, wa);
-    build_x<8192 / 4 / HEAD_THREADS>(a.src, a.d, s_x, red);
+    load_row(row, wa);   // unconditional (clamped), see prefetch_tiles
+    x_finish<8192 / 4 / HEAD_THREADS, true>(a.src, a.d, XR, s_x, red);
     if (a.hidden_out && blockIdx.x == 0)
         for (int i = threadIdx.x; i < a.d; i += blockDim.x) a.hidden_out[i] = s_x[i];
     float ss = 0.f;
@@ -904,6 +1022,9 @@ int launch_qkv(const QkvArgs& a0, const GemvShape& s, hipStream_t st) {
     a.tiles_per_block = s.tiles_per_block;
     const size_t lds = (size_t)a.d * 4 + planes_lds_bytes(s.CW);
     prof_mark("w4_gemv_qkv", st);
+    if (a.src.mode == X_FROM_RESIDUAL) {
+        GEMV_DISPATCH5(qkv_resid_kernel, dim3(s.blocks), lds, st, a);
+    }
     GEMV_DISPATCH5(qkv_kernel, dim3(s.blocks), lds, st, a);
 }
 
@@ -946,7 +1067,8 @@ int launch_attn_fused(const AttnFusedArgs& a, int G, hipStream_t st) {
     switch (G) {
 #define C(G_)                                                                           \
     case G_:                                                                            \
-        ATLAS_KLAUNCH((attn_kernel<G_>), grid, dim3(ATTN_THREADS), 0, st, a);      \
+        if (a.fused) ATLAS_KLAUNCH((attn_kernel<G_, true>), grid, dim3(ATTN_THREADS), 0, st, a);    \
+        else ATLAS_KLAUNCH((attn_kernel<G_, false>), grid, dim3(ATTN_THREADS), 0, st, a);           \
         break;
         C(1) C(2) C(3) C(4) C(5) C(6) C(7) C(8)
 #undef C

@@ -143,16 +143,48 @@ __device__ __forceinline__ void tile_dot(const TileRegs<CPL>& T, const LanePlane
     }
 }
 
-// Copy an encoded range (chunks [C0, C0+CW)) from global memory into LDS.
-__device__ __forceinline__ void stage_planes(const XQ& xq, int C0, int CW, uint32_t* s_pl, float* s_qs, int* s_is) {
+// Copy of an encoded range (chunks [C0, C0+CW)) from global memory into LDS, staged
+// through registers: planes_issue() issues every load (callers do so before their
+// weight prefetch, since loads complete in issue order), planes_commit() stores them.
+// Needs blockDim.x == NT, CW * 6 <= PLANE_REGS * NT and CW <= NT.
+constexpr int PLANE_REGS = 5;
+struct PlaneStage {
+    uint4 v[PLANE_REGS];
+    float qs;
+    int is;
+};
+
+template <int NT>
+__device__ __forceinline__ void planes_issue(const XQ& xq, int C0, int CW, PlaneStage& S) {
     const uint4* src = reinterpret_cast<const uint4*>(xq.planes + (size_t)C0 * XQ_WORDS_PER_CHUNK);
+    const int n = CW * XQ_WORDS_PER_CHUNK / 4;
+#pragma unroll
+    for (int j = 0; j < PLANE_REGS; j++) {
+        const int i = (int)threadIdx.x + j * NT;
+        S.v[j] = src[i < n ? i : 0];
+    }
+    const int c = (int)threadIdx.x < CW ? (int)threadIdx.x : 0;
+    S.qs = xq.qs[C0 + c];
+    S.is = xq.isum[C0 + c];
+}
+
+template <int NT>
+__device__ __forceinline__ void planes_commit(const PlaneStage& S, int CW, uint32_t* s_pl, float* s_qs, int* s_is) {
+    const int n = CW * XQ_WORDS_PER_CHUNK / 4;
     uint4* dst = reinterpret_cast<uint4*>(s_pl);
-    for (int i = threadIdx.x; i < CW * XQ_WORDS_PER_CHUNK / 4; i += blockDim.x) dst[i] = src[i];
-    for (int i = threadIdx.x; i < CW; i += blockDim.x) {
-        s_qs[i] = xq.qs[C0 + i];
-        s_is[i] = xq.isum[C0 + i];
+    const uint4 v0 = S.v[0], v1 = S.v[1], v2 = S.v[2], v3 = S.v[3], v4 = S.v[4];
+    const int i = (int)threadIdx.x;
+    if (i < n) dst[i] = v0;
+    if (i + NT < n) dst[i + NT] = v1;
+    if (i + 2 * NT < n) dst[i + 2 * NT] = v2;
+    if (i + 3 * NT < n) dst[i + 3 * NT] = v3;
+    if (i + 4 * NT < n) dst[i + 4 * NT] = v4;
+    if (i < CW) {
+        s_qs[i] = S.qs;
+        s_is[i] = S.is;
     }
 }
+static_assert(PLANE_REGS == 5, "planes_commit stores five registers");
 
 // Encode `n` floats held in LDS (n % 32 == 0) into LDS planes; all threads of the
 // block call it (quads of lanes form a chunk).
