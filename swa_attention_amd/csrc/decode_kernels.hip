@@ -518,12 +518,15 @@ __global__ __launch_bounds__(ATTN_THREADS, G <= 5 ? 2 : 1) void attn_kernel(Attn
     // K/V of key i of this split (clamped into the split)
     auto load_kv = [&](int i, float4& ka, float4& kb, float4& va, float4& vb) {
         const int j = cnt > 0 ? k0 + min(i, cnt - 1) : lo;
-        const float4* kp = reinterpret_cast<const float4*>(Kh + (size_t)j * D + 8 * sub);
-        const float4* vp = reinterpret_cast<const float4*>(Vh + (size_t)j * D + 8 * sub);
-        ka = kp[0];
-        kb = kp[1];
-        va = vp[0];
-        vb = vp[1];
+        typedef float f32x4_t __attribute__((ext_vector_type(4)));
+        const f32x4_t* kp = reinterpret_cast<const f32x4_t*>(Kh + (size_t)j * D + 8 * sub);
+        const f32x4_t* vp = reinterpret_cast<const f32x4_t*>(Vh + (size_t)j * D + 8 * sub);
+        const f32x4_t k0v = __builtin_nontemporal_load(kp), k1v = __builtin_nontemporal_load(kp + 1);
+        const f32x4_t v0v = __builtin_nontemporal_load(vp), v1v = __builtin_nontemporal_load(vp + 1);
+        ka = make_float4(k0v.x, k0v.y, k0v.z, k0v.w);
+        kb = make_float4(k1v.x, k1v.y, k1v.z, k1v.w);
+        va = make_float4(v0v.x, v0v.y, v0v.z, v0v.w);
+        vb = make_float4(v1v.x, v1v.y, v1v.z, v1v.w);
     };
     // Prologue inputs first (loads complete in issue order): the qkv kernel's per-block
     // sums of squares, this block's q heads and k/v head, and their gains.
@@ -843,11 +846,12 @@ __global__ __launch_bounds__(HEAD_THREADS) void head_kernel(HeadArgs a) {
     const int nw = a.d / 8;
     const int r0 = blockIdx.x * a.rows_per_block, r1 = min(a.V, r0 + a.rows_per_block);
     auto load_row = [&](int row, uint4 (&w)[KW]) {
-        const uint4* W = reinterpret_cast<const uint4*>(a.lm + (size_t)min(row, a.V - 1) * a.d);
+        const u32x4_t* W = reinterpret_cast<const u32x4_t*>(a.lm + (size_t)min(row, a.V - 1) * a.d);
 #pragma unroll
         for (int j = 0; j < KW; j++) {
             const int wd = lane + 64 * j;
-            w[j] = W[wd < nw ? wd : 0];
+            const u32x4_t v = __builtin_nontemporal_load(W + (wd < nw ? wd : 0));
+            w[j] = make_uint4(v.x, v.y, v.z, v.w);
         }
     };
     XRegs<8192 / 4 / HEAD_THREADS> XR;

@@ -99,15 +99,19 @@ struct TileRegs {
 };
 
 // Branch-free: rows past N are clamped (their sums are never stored) and invalid lane
-// items read chunk C0 (their contribution is zeroed through qs = 0).
+// items read chunk C0 (their contribution is zeroed through qs = 0). Weights are read
+// once per step, so they are loaded non-temporally (streaming cache policy) and do not
+// push the activations and partial sums out of L2.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 template <int CPL, int RB>
 __device__ __forceinline__ void load_tile(TileRegs<CPL>& T, const W4View& W, const LaneMap<CPL, RB>& m, int row0) {
 #pragma unroll
     for (int j = 0; j < CPL; j++) {
         const size_t rr = (size_t)min(row0 + m.rt[j], W.N - 1);
-        T.w[j] = reinterpret_cast<const uint4*>(W.qweight + rr * W.KW)[m.ch[j]];
-        T.sb[j] = W.scales[rr * W.G + m.gi[j]];
-        T.zw[j] = W.zeros[rr * W.zstride + (m.gi[j] >> 3)];   // raw: used only in tile_dot
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(W.qweight + rr * W.KW) + m.ch[j]);
+        T.w[j] = make_uint4(v.x, v.y, v.z, v.w);
+        T.sb[j] = __builtin_nontemporal_load(W.scales + rr * W.G + m.gi[j]);
+        T.zw[j] = __builtin_nontemporal_load(W.zeros + rr * W.zstride + (m.gi[j] >> 3));   // raw: used in tile_dot
     }
 }
 
