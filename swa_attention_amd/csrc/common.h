@@ -62,21 +62,36 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-    v = row16_sum(v);
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
+// Butterflies across rows with gfx950's lane-swap instructions. With both operands
+// equal to v, v_permlane16_swap returns (v of the even row of the lane's row pair,
+// v of the odd row) at the lane's position, and v_permlane32_swap the same for the
+// two halves of the wave; combining the two results gives every lane the reduction
+// over itself and lane ^ 16 (lane ^ 32), in the same order for both lanes.
+__device__ __forceinline__ float xor16_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+__device__ __forceinline__ float xor32_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return xor32_sum(xor16_sum(row16_sum(v))); }
 
 __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dpp_f<0xB1>(v));
     v = fmaxf(v, dpp_f<0x4E>(v));
     v = fmaxf(v, dpp_f<0x141>(v));
     v = fmaxf(v, dpp_f<0x140>(v));
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    v = fmaxf(v, __shfl_xor(v, 32, 64));
-    return v;
+    return xor32_max(xor16_max(v));
 }
 
 __device__ __forceinline__ float quad_sum(float v) {
@@ -165,23 +180,24 @@ __device__ __forceinline__ void xq_encode_word(const float x8[8], XQ out, int c,
     for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(x8[i]));
     m = quad_max(m);
     int e = (m > 0.f) ? __builtin_amdgcn_frexp_expf(m) : 0;   // m < 2^e
-    int pl[XQ_PLANES] = {0, 0, 0, 0, 0, 0};
+    // |v| <= 2^22, so b = v + 0x888888 lies in [0, 16^6): its nibbles n_p are the
+    // balanced digits of v plus 8 (v = sum_p (n_p - 8) 16^p), and the 4-bit pattern of
+    // the digit n_p - 8 is n_p ^ 8 (applied to whole plane words at the end)
+    uint32_t pl[XQ_PLANES] = {0u, 0u, 0u, 0u, 0u, 0u};
     int s = 0;
+    const int sh = 22 - e;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        int v = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(x8[i], 22 - e));
+        const int v = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(x8[i], sh));
         s += v;
+        const uint32_t b = (uint32_t)(v + 0x888888);
 #pragma unroll
-        for (int p = 0; p < XQ_PLANES; p++) {
-            int d = ((v + 8) & 15) - 8;
-            pl[p] |= (d & 15) << (4 * i);
-            v = (v - d) >> 4;
-        }
+        for (int p = 0; p < XQ_PLANES; p++) pl[p] |= ((b >> (4 * p)) & 15u) << (4 * i);
     }
     s = quad_sum_i(s);
     uint32_t* dst = out.planes + (size_t)c * XQ_WORDS_PER_CHUNK + w * XQ_PLANES;
 #pragma unroll
-    for (int p = 0; p < XQ_PLANES; p++) dst[p] = (uint32_t)pl[p];
+    for (int p = 0; p < XQ_PLANES; p++) dst[p] = pl[p] ^ 0x88888888u;
     if (w == 0) {
         out.qs[c] = __builtin_amdgcn_ldexpf(1.0f, e - 22);
         out.isum[c] = s;

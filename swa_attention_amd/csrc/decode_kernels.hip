@@ -494,42 +494,13 @@ __global__ __launch_bounds__(ATTN_THREADS, G <= 5 ? 2 : 1) void attn_kernel(Attn
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane & 15, grp = lane >> 4;
     const int nq = a.Hq * D, nk = a.Hkv * D;
-    const int pos = *a.d_pos;
-    const bool pos_ok = pos >= 0 && pos < a.T_max;
+    // the position through a vector load (a scalar load would be waited for together
+    // with the kernel arguments, before anything else is issued)
+    const int pos_v = a.d_pos[__builtin_amdgcn_mbcnt_lo(0u, 0u)];
     float* part0 = a.part + (size_t)(kv * G) * a.S * ATTN_PART_F;
-    if (!pos_ok) {
-        for (int t = threadIdx.x; t < G * (2 + D); t += blockDim.x) {
-            const int h = t / (2 + D), e = t % (2 + D);
-            part0[((size_t)h * a.S + s) * ATTN_PART_F + e] = e == 0 ? -INFINITY : 0.f;
-        }
-        if (a.status && s == 0 && kv == 0 && threadIdx.x == 0) *a.status = ATLAS_ERR_INVALID_ARG;
-        return;
-    }
-    int lo = a.window > 0 ? pos - a.window + 1 : 0;
-    if (lo < 0) lo = 0;
-    const int nkeys = pos - lo + 1;
-    const int Lk = (nkeys + a.S - 1) / a.S;
-    const int k0 = lo + s * Lk;
-    int cnt = min(Lk, lo + nkeys - k0);
-    if (cnt < 0) cnt = 0;
-    const int stream = wave * 4 + grp;
-    const float* Kh = a.k_cache + (size_t)kv * a.T_max * D;
-    const float* Vh = a.v_cache + (size_t)kv * a.T_max * D;
-    // K/V of key i of this split (clamped into the split)
-    auto load_kv = [&](int i, float4& ka, float4& kb, float4& va, float4& vb) {
-        const int j = cnt > 0 ? k0 + min(i, cnt - 1) : lo;
-        typedef float f32x4_t __attribute__((ext_vector_type(4)));
-        const f32x4_t* kp = reinterpret_cast<const f32x4_t*>(Kh + (size_t)j * D + 8 * sub);
-        const f32x4_t* vp = reinterpret_cast<const f32x4_t*>(Vh + (size_t)j * D + 8 * sub);
-        const f32x4_t k0v = __builtin_nontemporal_load(kp), k1v = __builtin_nontemporal_load(kp + 1);
-        const f32x4_t v0v = __builtin_nontemporal_load(vp), v1v = __builtin_nontemporal_load(vp + 1);
-        ka = make_float4(k0v.x, k0v.y, k0v.z, k0v.w);
-        kb = make_float4(k1v.x, k1v.y, k1v.z, k1v.w);
-        va = make_float4(v0v.x, v0v.y, v0v.z, v0v.w);
-        vb = make_float4(v1v.x, v1v.y, v1v.z, v1v.w);
-    };
     // Prologue inputs first (loads complete in issue order): the qkv kernel's per-block
-    // sums of squares, this block's q heads and k/v head, and their gains.
+    // sums of squares, this block's q heads and k/v head, and their gains. None depends
+    // on the position, whose load is still in flight.
     float ps_q[ATTN_SSQ_REGS], ps_k[ATTN_SSQ_REGS];
     float xq0[2], xq1[2], gq0[2], gq1[2], vnew = 0.f;
     float qf[ATTN_QF_REGS];
@@ -562,6 +533,39 @@ __global__ __launch_bounds__(ATTN_THREADS, G <= 5 ? 2 : 1) void attn_kernel(Attn
         vnew = a.qkv[nq + nk + kv * D + (threadIdx.x & (D - 1))];
     }
     __builtin_amdgcn_sched_barrier(0);
+    const int pos = __builtin_amdgcn_readfirstlane(pos_v);
+    const bool pos_ok = pos >= 0 && pos < a.T_max;
+    if (!pos_ok) {
+        for (int t = threadIdx.x; t < G * (2 + D); t += blockDim.x) {
+            const int h = t / (2 + D), e = t % (2 + D);
+            part0[((size_t)h * a.S + s) * ATTN_PART_F + e] = e == 0 ? -INFINITY : 0.f;
+        }
+        if (a.status && s == 0 && kv == 0 && threadIdx.x == 0) *a.status = ATLAS_ERR_INVALID_ARG;
+        return;
+    }
+    int lo = a.window > 0 ? pos - a.window + 1 : 0;
+    if (lo < 0) lo = 0;
+    const int nkeys = pos - lo + 1;
+    const int Lk = (nkeys + a.S - 1) / a.S;
+    const int k0 = lo + s * Lk;
+    int cnt = min(Lk, lo + nkeys - k0);
+    if (cnt < 0) cnt = 0;
+    const int stream = wave * 4 + grp;
+    const float* Kh = a.k_cache + (size_t)kv * a.T_max * D;
+    const float* Vh = a.v_cache + (size_t)kv * a.T_max * D;
+    // K/V of key i of this split (clamped into the split)
+    auto load_kv = [&](int i, float4& ka, float4& kb, float4& va, float4& vb) {
+        const int j = cnt > 0 ? k0 + min(i, cnt - 1) : lo;
+        typedef float f32x4_t __attribute__((ext_vector_type(4)));
+        const f32x4_t* kp = reinterpret_cast<const f32x4_t*>(Kh + (size_t)j * D + 8 * sub);
+        const f32x4_t* vp = reinterpret_cast<const f32x4_t*>(Vh + (size_t)j * D + 8 * sub);
+        const f32x4_t k0v = __builtin_nontemporal_load(kp), k1v = __builtin_nontemporal_load(kp + 1);
+        const f32x4_t v0v = __builtin_nontemporal_load(vp), v1v = __builtin_nontemporal_load(vp + 1);
+        ka = make_float4(k0v.x, k0v.y, k0v.z, k0v.w);
+        kb = make_float4(k1v.x, k1v.y, k1v.z, k1v.w);
+        va = make_float4(v0v.x, v0v.y, v0v.z, v0v.w);
+        vb = make_float4(v1v.x, v1v.y, v1v.z, v1v.w);
+    };
     // ring of ATTN_KV_STAGES keys per stream; the first ATTN_KV_STAGES-1 are in flight
     // during the prologue
     float4 rk[ATTN_KV_STAGES][2], rv[ATTN_KV_STAGES][2];
