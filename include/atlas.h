@@ -127,6 +127,18 @@ ATLAS_API int atlas_w4_gemv(const atlas_w4* W, const float* x, float* y, void* w
  * (code - zero) * scale). For checking the unpacking. */
 ATLAS_API int atlas_w4_dequant(const atlas_w4* W, float* out, void* stream);
 
+/* ---- W4 GEMM (the prefill projections) -------------------------------------------
+ * C[m][n] = sum_k W[n][k] A[m][k] for M rows of f32 activations A [M][K] (row-major,
+ * device) and an atlas_w4 W; C: f32 [M][N] (device). Runs on the matrix cores: A is
+ * held as two bf16 planes (hi + lo, 16 significant bits), W is dequantised to exact
+ * bf16 integers (code - zero) per quantisation group and each group's f32 sum is
+ * scaled and accumulated; result within about 1e-5 relative of the f64 definition.
+ * Needs group == 32 or a multiple of 64 (else ATLAS_ERR_UNSUPPORTED_SHAPE).
+ * ws: atlas_w4_gemm_workspace_bytes(W, M) bytes (the bf16 planes of A). */
+ATLAS_API size_t atlas_w4_gemm_workspace_bytes(const atlas_w4* W, int32_t M);
+ATLAS_API int atlas_w4_gemm(const atlas_w4* W, const float* A, int32_t M, float* C, void* ws, size_t ws_bytes,
+                            void* stream);
+
 /* ---- RMSNorm + residual -----------------------------------------------------------
  * out = resid + g * x / sqrt(mean(x^2) + eps) over n elements; with resid == NULL,
  * out = g * x / sqrt(mean(x^2) + eps) ([kb] reordered post-norm: the norm sits on
@@ -185,9 +197,13 @@ ATLAS_API int atlas_device_status(const void* ws, void* stream, int32_t* status_
  * returns the last token's logits (f32 [vocab], may be NULL) and greedy argmax
  * (int32, may be NULL). By definition it equals n_tokens teacher-forced decode
  * steps ([card] Limitations: prefill currently runs token by token through the
- * decode path); here the projections run as dequantise-into-LDS MFMA GEMMs over
- * all tokens and attention is causal within each layer's window.
- * ws: atlas_prefill_workspace_bytes(m, n_tokens) bytes. */
+ * decode path, with a batched GEMM prefill as the planned fix); here the projections
+ * run as W4 GEMMs on the matrix cores over all tokens (see atlas_w4_gemm), QK norm,
+ * rotary and the KV write per token, and causal attention within each layer's
+ * window on f32 matrix cores. Linear layers need group 32 or a multiple of 64.
+ * ws: atlas_prefill_workspace_bytes(m, n_tokens) bytes; its first word is the status
+ * word of atlas_device_status (ATLAS_ERR_INVALID_ARG when a token id is out of range;
+ * such ids read embedding row 0). */
 ATLAS_API size_t atlas_prefill_workspace_bytes(const atlas_model* m, int32_t n_tokens);
 ATLAS_API int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int32_t n_tokens, int32_t start_pos,
                   float* d_last_logits, int32_t* d_argmax, void* ws, size_t ws_bytes, void* stream);

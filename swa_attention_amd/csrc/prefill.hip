@@ -1,22 +1,84 @@
 // Prefill: process a prompt through every layer, writing its KV slots, and return the
-// last token's logits and greedy argmax.
+// last token's logits and greedy argmax; plus the standalone W4 GEMM entry point.
 //
-// Source: "ATLAS-OLMo-3-32B-Think-v4", Limitations & roadmap -- prefill defined as the
-// prompt run token by token through the decode path (our parity definition).
-// This entry point currently runs exactly that definition: one decode step per
-// prompt token, positions start_pos + t read from device memory.
+// Source: "ATLAS-OLMo-3-32B-Think-v4", Limitations & roadmap -- prefill is defined as
+// the prompt run token by token through the decode path (the parity definition here),
+// and its planned replacement is a batched, tiled GEMM prefill, which this is: per
+// layer one W4 GEMM each for qkv, o, gate+up (SwiGLU fused) and down over all n
+// positions, with QK norm/rotary/KV write, causal attention and the residual norms
+// as per-position kernels (prefill_kernels.hip).
+#include <cmath>
+
 #include "decode.h"
+#include "gemv.h"
+#include "norm_rope.h"
+#include "prefill_kernels.h"
 
 namespace atlas {
 
-__global__ void positions_kernel(int32_t* pos, int n, int start) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) pos[i] = start + i;
+namespace {
+
+struct PrefillWs {
+    void* dec;       // decode workspace (status word, head partials)
+    float *X, *QKV, *A;
+    uint16_t *p1h, *p1l, *p2h, *p2l;
+    int ld1;
+    size_t bytes;
+};
+
+PrefillWs carve_prefill(const atlas_model* m, int n, void* base) {
+    PrefillWs w{};
+    char* b = (char*)base;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        void* p = b ? b + off : nullptr;
+        off += align_up(bytes, 256);
+        return p;
+    };
+    const int nq = m->hq * m->hd, nqkv = (m->hq + 2 * m->hkv) * m->hd;
+    w.ld1 = std::max(m->d, nq);
+    w.dec = take(decode_ws_bytes(m));
+    w.X = (float*)take((size_t)n * m->d * 4);
+    w.QKV = (float*)take((size_t)n * nqkv * 4);
+    w.A = (float*)take((size_t)n * m->d * 4);
+    w.p1h = (uint16_t*)take((size_t)n * w.ld1 * 2);
+    w.p1l = (uint16_t*)take((size_t)n * w.ld1 * 2);
+    w.p2h = (uint16_t*)take((size_t)n * m->dff * 2);
+    w.p2l = (uint16_t*)take((size_t)n * m->dff * 2);
+    w.bytes = off;
+    return w;
 }
 
-static size_t prefill_ws(const atlas_model* m, int n) {
-    return decode_ws_bytes(m) + align_up((size_t)n * 4, 256);
+W4View view(const atlas_w4& w) { return w4_view(w.qweight, w.scales, w.zeros, w.N, w.K, w.group, w.scale_dtype); }
+
+int validate_prefill_model(const atlas_model* m) {
+    for (int l = 0; l < m->n_layers; l++) {
+        const atlas_layer& L = m->layers[l];
+        const atlas_w4* ws[5] = {&L.qkv, &L.o, &L.gate, &L.up, &L.down};
+        for (const atlas_w4* w : ws)
+            ATLAS_CHECK_SHAPE(gemm_supported(w->group), "prefill needs group 32 or a multiple of 64 (layer %d: %d)", l,
+                              w->group);
+        ATLAS_CHECK_SHAPE(L.gate.group == L.up.group && L.gate.scale_dtype == L.up.scale_dtype,
+                          "gate and up must share group and scale type");
+    }
+    return ATLAS_OK;
 }
+
+GemmArgs gemm(const uint16_t* hi, const uint16_t* lo, int lda, const atlas_w4& w, int M) {
+    GemmArgs g{};
+    g.a_hi = hi;
+    g.a_lo = lo;
+    g.lda = lda;
+    g.W0 = view(w);
+    g.W1 = g.W0;
+    g.M = M;
+    g.N = w.N;
+    g.K = w.K;
+    g.group = w.group;
+    return g;
+}
+
+}  // namespace
 
 }  // namespace atlas
 
@@ -24,32 +86,129 @@ using namespace atlas;
 
 extern "C" size_t atlas_prefill_workspace_bytes(const atlas_model* m, int32_t n_tokens) {
     if (validate_model(m) != ATLAS_OK || n_tokens < 1) return 0;
-    return prefill_ws(m, n_tokens);
+    return carve_prefill(m, n_tokens, nullptr).bytes;
 }
 
 extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int32_t n_tokens, int32_t start_pos,
                              float* d_last_logits, int32_t* d_argmax, void* ws, size_t ws_bytes, void* stream) {
     int rc = validate_model(m);
     if (rc) return rc;
+    if ((rc = validate_prefill_model(m))) return rc;
     ATLAS_CHECK_ARG(d_tokens && ws, "null pointer");
     ATLAS_CHECK_ARG(n_tokens >= 1, "n_tokens must be >= 1");
     ATLAS_CHECK_ARG(start_pos >= 0 && (int64_t)start_pos + n_tokens <= m->t_max,
                     "positions %d..%d exceed T_max=%lld", start_pos, start_pos + n_tokens - 1,
                     (long long)m->t_max);
     ATLAS_CHECK_ARG(m->embedding, "prefill needs an embedding table");
-    const size_t need = prefill_ws(m, n_tokens);
-    if (ws_bytes < need) return fail(ATLAS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu", ws_bytes, need);
+    const bool head = d_last_logits || d_argmax;
+    ATLAS_CHECK_ARG(!head || (m->lm_head && m->g_final && m->vocab >= 1), "lm_head/g_final/vocab missing");
+    const PrefillWs w = carve_prefill(m, n_tokens, ws);
+    if (ws_bytes < w.bytes) return fail(ATLAS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu", ws_bytes, w.bytes);
     hipStream_t st = (hipStream_t)stream;
-    const size_t dws = decode_ws_bytes(m);
-    int32_t* pos = (int32_t*)((char*)ws + dws);
-    prof_mark("positions", st);
-    ATLAS_KLAUNCH(positions_kernel, dim3((n_tokens + 255) / 256), dim3(256), 0, st, pos, n_tokens, start_pos);
-    ATLAS_LAUNCH_CHECK("positions_kernel");
-    for (int t = 0; t < n_tokens; t++) {
-        const bool last = t == n_tokens - 1;
-        rc = atlas_decode_step(m, d_tokens + t, nullptr, pos + t, nullptr, last ? d_last_logits : nullptr,
-                               last ? d_argmax : nullptr, ws, dws, stream);
-        if (rc) return rc;
+    const int n = n_tokens, d = m->d, nq = m->hq * m->hd, nqkv = (m->hq + 2 * m->hkv) * m->hd;
+    RopeTable rt_swa, rt_full;
+    rope_table(&m->rope_swa, m->hd, &rt_swa);
+    rope_table(&m->rope_full, m->hd, &rt_full);
+
+    if ((rc = launch_pf_embed(d_tokens, n, m->embedding, m->vocab, d, w.X, w.p1h, w.p1l, w.ld1, (int*)w.dec, st)))
+        return rc;
+    for (int l = 0; l < m->n_layers; l++) {
+        const atlas_layer& L = m->layers[l];
+        const bool last = l == m->n_layers - 1;
+        // qkv projection of all positions
+        GemmArgs qa = gemm(w.p1h, w.p1l, w.ld1, L.qkv, n);
+        qa.C = w.QKV;
+        qa.ldc = nqkv;
+        if ((rc = launch_w4_gemm(qa, 0, st, "pf_gemm_qkv"))) return rc;
+        // QK norm, rotary, KV slots start_pos .. start_pos + n - 1
+        PfRopeArgs ra{};
+        ra.qkv = w.QKV;
+        ra.ld = nqkv;
+        ra.n = n;
+        ra.start_pos = start_pos;
+        ra.Hq = m->hq;
+        ra.Hkv = m->hkv;
+        ra.g_q = L.g_q;
+        ra.g_k = L.g_k;
+        ra.eps = m->eps;
+        const RopeTable& rt = L.type == 1 ? rt_full : rt_swa;
+        for (int i = 0; i < 64; i++) ra.inv[i] = rt.inv[i];
+        ra.mscale = rt.mscale;
+        ra.k_cache = L.k_cache;
+        ra.v_cache = L.v_cache;
+        ra.T_max = m->t_max;
+        if ((rc = launch_pf_rope(ra, st))) return rc;
+        // causal attention; output planes for the o projection
+        PfAttnArgs aa{};
+        aa.qkv = w.QKV;
+        aa.ld_qkv = nqkv;
+        aa.k_cache = L.k_cache;
+        aa.v_cache = L.v_cache;
+        aa.T_max = m->t_max;
+        aa.n = n;
+        aa.start_pos = start_pos;
+        aa.Hq = m->hq;
+        aa.Hkv = m->hkv;
+        aa.window = L.type == 1 ? 0 : m->window;
+        aa.scale = 1.0f / std::sqrt((float)m->hd);
+        aa.o_hi = w.p1h;
+        aa.o_lo = w.p1l;
+        aa.ldo = w.ld1;
+        if ((rc = launch_pf_attn(aa, st))) return rc;
+        // o projection, h = x + RMSNorm_pa(a)
+        GemmArgs oa = gemm(w.p1h, w.p1l, w.ld1, L.o, n);
+        oa.C = w.A;
+        oa.ldc = d;
+        if ((rc = launch_w4_gemm(oa, 0, st, "pf_gemm_o"))) return rc;
+        if ((rc = launch_pf_residual(w.X, w.A, L.g_pa, n, d, m->eps, w.p1h, w.p1l, w.ld1, st))) return rc;
+        // gate/up with SwiGLU, then down
+        GemmArgs ga = gemm(w.p1h, w.p1l, w.ld1, L.gate, n);
+        ga.W1 = view(L.up);
+        ga.z_hi = w.p2h;
+        ga.z_lo = w.p2l;
+        ga.ldz = m->dff;
+        if ((rc = launch_w4_gemm(ga, 1, st, "pf_gemm_gate_up"))) return rc;
+        GemmArgs da = gemm(w.p2h, w.p2l, m->dff, L.down, n);
+        da.C = w.A;
+        da.ldc = d;
+        if ((rc = launch_w4_gemm(da, 0, st, "pf_gemm_down"))) return rc;
+        // y = h + RMSNorm_pf(m): the last layer leaves it to the head (last position only)
+        if (!last || !head)
+            if ((rc = launch_pf_residual(w.X, w.A, L.g_pf, n, d, m->eps, w.p1h, w.p1l, w.ld1, st))) return rc;
     }
-    return ATLAS_OK;
+    if (!head) return ATLAS_OK;
+    XSource lastx{};
+    lastx.mode = X_FROM_RESIDUAL;
+    lastx.m_part = w.A + (size_t)(n - 1) * d;
+    lastx.S = 1;
+    lastx.h = w.X + (size_t)(n - 1) * d;
+    lastx.g = m->layers[m->n_layers - 1].g_pf;
+    lastx.eps = m->eps;
+    return run_head(m, lastx, w.dec, nullptr, d_last_logits, d_argmax, st);
+}
+
+// ---- standalone W4 GEMM ---------------------------------------------------------------------
+
+extern "C" size_t atlas_w4_gemm_workspace_bytes(const atlas_w4* W, int32_t M) {
+    if (validate_w4(W) != ATLAS_OK || M < 1) return 0;
+    return 2 * align_up((size_t)M * W->K * 2, 256);
+}
+
+extern "C" int atlas_w4_gemm(const atlas_w4* W, const float* A, int32_t M, float* C, void* ws, size_t ws_bytes,
+                             void* stream) {
+    int rc = validate_w4(W);
+    if (rc) return rc;
+    ATLAS_CHECK_ARG(A && C && ws, "null pointer");
+    ATLAS_CHECK_ARG(M >= 1, "M must be >= 1");
+    ATLAS_CHECK_SHAPE(gemm_supported(W->group), "W4 GEMM needs group 32 or a multiple of 64 (got %d)", W->group);
+    const size_t plane = align_up((size_t)M * W->K * 2, 256);
+    if (ws_bytes < 2 * plane) return fail(ATLAS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu", ws_bytes, 2 * plane);
+    hipStream_t st = (hipStream_t)stream;
+    uint16_t* hi = (uint16_t*)ws;
+    uint16_t* lo = (uint16_t*)((char*)ws + plane);
+    if ((rc = launch_pf_split(A, M, W->K, W->K, hi, lo, W->K, st))) return rc;
+    GemmArgs g = gemm(hi, lo, W->K, *W, M);
+    g.C = C;
+    g.ldc = W->N;
+    return launch_w4_gemm(g, 0, st, "w4_gemm");
 }

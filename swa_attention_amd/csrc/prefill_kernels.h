@@ -1,0 +1,58 @@
+// Kernels of the matrix-core prefill (prefill_kernels.hip).
+#pragma once
+#include "decode_kernels.h"
+
+namespace atlas {
+
+// C = A W^T for a W4 matrix W [N][K] and activations A [M][K] given as two bf16 planes
+// (A = hi + lo, see pf_split): mode 0 writes C f32 [M][ldc]; mode 1 takes a second
+// matrix W1 of the same shape and writes z = silu(A W^T) * (A W1^T) as bf16 planes.
+struct GemmArgs {
+    const uint16_t* a_hi;
+    const uint16_t* a_lo;
+    int lda;
+    W4View W0, W1;
+    int M, N, K, group;
+    float* C;
+    int ldc;
+    uint16_t* z_hi;
+    uint16_t* z_lo;
+    int ldz;
+};
+
+struct PfAttnArgs {
+    const float* qkv;          // [n][ld_qkv]: q rows already normalised and rotated
+    int ld_qkv;
+    const float* k_cache;      // [Hkv][T_max][128]
+    const float* v_cache;
+    int64_t T_max;
+    int n, start_pos, Hq, Hkv, window;
+    float scale;
+    uint16_t* o_hi;            // [n][ldo] bf16 planes of the attention output (Hq*128 used)
+    uint16_t* o_lo;
+    int ldo;
+};
+
+struct PfRopeArgs {
+    float* qkv;                // [n][ld]: q and k normalised/rotated in place
+    int ld, n, start_pos, Hq, Hkv;
+    const float *g_q, *g_k;
+    float eps;
+    double inv[64];
+    double mscale;
+    float* k_cache;
+    float* v_cache;
+    int64_t T_max;
+};
+
+int gemm_supported(int group);
+int launch_w4_gemm(const GemmArgs& a, int mode, hipStream_t st, const char* label);
+int launch_pf_embed(const int32_t* tokens, int n, const uint16_t* emb, int vocab, int d, float* X, uint16_t* p_hi,
+                    uint16_t* p_lo, int ldp, int* status, hipStream_t st);
+int launch_pf_rope(const PfRopeArgs& a, hipStream_t st);
+int launch_pf_attn(const PfAttnArgs& a, hipStream_t st);
+int launch_pf_split(const float* X, int M, int K, int ldx, uint16_t* p_hi, uint16_t* p_lo, int ldp, hipStream_t st);
+int launch_pf_residual(float* X, const float* A, const float* g, int n, int d, float eps, uint16_t* p_hi,
+                       uint16_t* p_lo, int ldp, hipStream_t st);
+
+}  // namespace atlas

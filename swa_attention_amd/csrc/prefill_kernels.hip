@@ -1,0 +1,513 @@
+// Prefill of a whole prompt on the matrix cores.
+//
+// Source: "ATLAS-OLMo-3-32B-Think-v4" -- Limitations & roadmap (prefill defined as the
+// prompt run through the decode path token by token; the planned fix is a batched,
+// tiled GEMM prefill) and the layer definition of the decode path (Architecture
+// deep-dive; Quantization recipe). Every position t of the prompt computes exactly
+// what the decode step computes at pos = start_pos + t; here the n positions of a
+// layer are processed together:
+//   - the four W4 projections are GEMMs on MFMA (v_mfma_f32_16x16x32_bf16): each
+//     block dequantises one quantisation group of a 128-row weight tile into LDS as
+//     exact small integers (code - zero) in bf16, multiplies it with the activations
+//     held as two bf16 planes (x = hi + lo carries 16 significant bits, so the
+//     products match f32 inputs to about 2^-17), accumulates the group in f32 and
+//     adds it to the output scaled by the group's scale;
+//   - QK RMSNorm, rotary embedding and the KV write run one block per position;
+//   - causal (windowed) GQA attention runs per (16 positions, KV head) with the
+//     query heads of the group in separate waves, on f32 MFMA (16x16x4);
+//   - the post-attention and post-MLP residual norms run one block per position.
+#include "prefill_kernels.h"
+
+namespace atlas {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (x - hi is exact in f32)
+__device__ __forceinline__ void pf_split(float x, uint32_t& hi, uint32_t& lo) {
+    hi = f32_to_bf16_rne(x);
+    lo = f32_to_bf16_rne(x - __uint_as_float(hi << 16));
+}
+
+// Store 4 consecutive values of a row as bf16 planes.
+__device__ __forceinline__ void store_split4(const float4 v, uint16_t* hi, uint16_t* lo) {
+    uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+    pf_split(v.x, h0, l0);
+    pf_split(v.y, h1, l1);
+    pf_split(v.z, h2, l2);
+    pf_split(v.w, h3, l3);
+    *reinterpret_cast<uint2*>(hi) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+    *reinterpret_cast<uint2*>(lo) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+}
+
+// ---- W4 GEMM ------------------------------------------------------------------------------
+//
+// Block tile 64 (rows of A) x 128 (rows of W; mode 1: 64 of W0 and the same 64 of W1),
+// four waves of 32 x 64, k tiles of 64 through LDS. The products of one quantisation
+// group are accumulated on their own and added to the output times the group's
+// scale (per row of W) when the group ends; groups are multiples of 32 columns, so
+// every MFMA k-step of 32 lies in one group. The next k tile's A planes and codes are
+// loaded into registers while the current one is multiplied. Tiles are numbered so
+// that consecutive tile numbers land on one XCD (blocks are dealt to the 8 XCDs
+// round robin) with the row tiles of A fastest: the tiles sharing a weight tile run
+// together on one XCD's L2.
+
+constexpr int GM_BM = 64, GM_BN = 128, GM_BK = 64, GM_THREADS = 256;
+
+template <int MODE>
+__global__ __launch_bounds__(GM_THREADS) void w4_gemm_kernel(GemmArgs a) {
+    constexpr int LDK = GM_BK + 8;                   // padded LDS row (bf16)
+    constexpr int A_PER = GM_BM * GM_BK / 8 / GM_THREADS;   // uint4 per thread and plane: 2
+    static_assert(GM_BN * GM_BK / 32 == GM_THREADS, "one uint4 of codes per thread");
+    __shared__ __align__(16) uint16_t sAh[GM_BM * LDK];
+    __shared__ __align__(16) uint16_t sAl[GM_BM * LDK];
+    __shared__ __align__(16) uint16_t sB[GM_BN * LDK];
+    __shared__ float sS[2][GM_BN];
+
+    const int MT = (a.M + GM_BM - 1) / GM_BM;
+    const int NW_ = MODE ? GM_BN / 2 : GM_BN;   // output columns per tile
+    const int NT = (a.N + NW_ - 1) / NW_;
+    const int T = MT * NT, per = (T + 7) / 8;
+    const int L = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (L >= T) return;
+    const int m0 = (L % MT) * GM_BM, n0 = (L / MT) * NW_;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    const int l16 = lane & 15, l4 = lane >> 4;
+    const int KT = (a.K + GM_BK - 1) / GM_BK;
+
+    // weight-tile row r -> matrix (second one for r >= 64 in mode 1) and row (clamped to N - 1)
+    auto second = [&](int r) { return MODE && r >= GM_BN / 2; };
+    auto wrow = [&](int r) { return min(n0 + (second(r) ? r - GM_BN / 2 : r), a.N - 1); };
+    // tile-local W row of N fragment nf of this wave
+    auto bcol = [&](int nf) { return MODE ? (nf < 2 ? wn * 32 + 16 * nf : 64 + wn * 32 + 16 * (nf - 2)) : wn * 64 + 16 * nf; };
+
+    // this thread's uint4 of codes: W row br, 32 columns from bc
+    const int br = tid / (GM_BK / 32), bc = 32 * (tid % (GM_BK / 32));
+    const int brow = wrow(br);
+    const uint32_t* b_q = second(br) ? a.W1.qweight : a.W0.qweight;   // both matrices share N, K, group
+    const uint32_t* b_z = second(br) ? a.W1.zeros : a.W0.zeros;
+    const int b_zstride = second(br) ? a.W1.zstride : a.W0.zstride;
+    const int b_zsym = second(br) ? a.W1.zsym : a.W0.zsym;
+    const int KW = a.W0.KW, GG = a.W0.G;
+    // the two scale slots of a k tile (group 32: one per k-step; otherwise slot 0)
+    const int srow = tid & (GM_BN - 1), sslot = tid / GM_BN;
+    const uint16_t* s_p = (second(srow) ? a.W1.scales : a.W0.scales) + (size_t)wrow(srow) * GG;
+    const int s_dtype = second(srow) ? a.W1.scale_dtype : a.W0.scale_dtype;
+
+    uint4 rAh0, rAh1, rAl0, rAl1, rB;
+    uint32_t rZ;
+    uint16_t rS;
+    static_assert(A_PER == 2, "two uint4 per thread and plane");
+    // A row / column of this thread's two uint4 per plane
+    const int ar0 = tid / (GM_BK / 8), ac0 = 8 * (tid % (GM_BK / 8));
+    const int ar1 = (tid + GM_THREADS) / (GM_BK / 8), ac1 = 8 * ((tid + GM_THREADS) % (GM_BK / 8));
+    const size_t arow0 = (size_t)min(m0 + ar0, a.M - 1) * a.lda, arow1 = (size_t)min(m0 + ar1, a.M - 1) * a.lda;
+#define LOAD_TILE_K(kt_)                                                                                     \
+    do {                                                                                                     \
+        const int kb_ = (kt_) * GM_BK;                                                                       \
+        const size_t o0_ = arow0 + min(kb_ + ac0, a.K - 8), o1_ = arow1 + min(kb_ + ac1, a.K - 8);           \
+        rAh0 = *reinterpret_cast<const uint4*>(a.a_hi + o0_);                                                \
+        rAl0 = *reinterpret_cast<const uint4*>(a.a_lo + o0_);                                                \
+        rAh1 = *reinterpret_cast<const uint4*>(a.a_hi + o1_);                                                \
+        rAl1 = *reinterpret_cast<const uint4*>(a.a_lo + o1_);                                                \
+        const int kc_ = min(kb_ + bc, a.K - 32);                                                             \
+        const u32x4_t v_ = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(b_q + (size_t)brow * KW + kc_ / 8)); \
+        rB = make_uint4(v_.x, v_.y, v_.z, v_.w);                                                             \
+        rZ = b_z[(size_t)brow * b_zstride + ((kc_ / a.group) >> 3)];                                         \
+        rS = s_p[min((kb_ + 32 * sslot) / a.group, GG - 1)];                                                 \
+    } while (0)
+
+    f32x4_t acc[2][4], accg[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            accg[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+
+    LOAD_TILE_K(0);
+    for (int kt = 0; kt < KT; kt++) {
+        const int kb = kt * GM_BK, kn = min(GM_BK, a.K - kb);
+        __syncthreads();   // the previous tile's fragments have been read
+        *reinterpret_cast<uint4*>(&sAh[ar0 * LDK + ac0]) = rAh0;
+        *reinterpret_cast<uint4*>(&sAl[ar0 * LDK + ac0]) = rAl0;
+        *reinterpret_cast<uint4*>(&sAh[ar1 * LDK + ac1]) = rAh1;
+        *reinterpret_cast<uint4*>(&sAl[ar1 * LDK + ac1]) = rAl1;
+        {
+            const int kc = min(kb + bc, a.K - 32);
+            const int z = b_zsym ? 8 : (int)((rZ >> (((kc / a.group) & 7) * 4)) & 15u);
+            const uint32_t w4[4] = {rB.x, rB.y, rB.z, rB.w};
+            uint32_t o[16];
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    // (code - zero) is an integer in [-15, 15]: exact in bf16
+                    const float v0 = (float)((int)((w4[q] >> (4 * e)) & 15u) - z);
+                    const float v1 = (float)((int)((w4[q] >> (4 * e + 4)) & 15u) - z);
+                    o[q * 4 + e / 2] = (__float_as_uint(v0) >> 16) | (__float_as_uint(v1) & 0xFFFF0000u);
+                }
+            uint4* dst = reinterpret_cast<uint4*>(&sB[br * LDK + bc]);
+#pragma unroll
+            for (int q = 0; q < 4; q++) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+        }
+        sS[sslot][srow] = scale_to_f32(rS, s_dtype);
+        __syncthreads();
+        if (kt + 1 < KT) LOAD_TILE_K(kt + 1);   // in flight during the products below
+
+        for (int ks = 0; ks < kn / 32; ks++) {
+            const int k = ks * 32 + 8 * l4;
+            bf16x8_t ah[2], al[2], b[4];
+#pragma unroll
+            for (int mf = 0; mf < 2; mf++) {
+                const int row = wm * 32 + mf * 16 + l16;
+                ah[mf] = *reinterpret_cast<const bf16x8_t*>(&sAh[row * LDK + k]);
+                al[mf] = *reinterpret_cast<const bf16x8_t*>(&sAl[row * LDK + k]);
+            }
+#pragma unroll
+            for (int nf = 0; nf < 4; nf++) b[nf] = *reinterpret_cast<const bf16x8_t*>(&sB[(bcol(nf) + l16) * LDK + k]);
+#pragma unroll
+            for (int mf = 0; mf < 2; mf++)
+#pragma unroll
+                for (int nf = 0; nf < 4; nf++) {
+                    const f32x4_t c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mf], b[nf], accg[mf][nf], 0, 0, 0);
+                    accg[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[mf], b[nf], c, 0, 0, 0);
+                }
+            const int kabs = kb + 32 * ks + 32;
+            if (kabs % a.group == 0 || kabs >= a.K) {   // group ends: scale and add
+                const int slot = a.group == 32 ? ks : 0;
+#pragma unroll
+                for (int nf = 0; nf < 4; nf++) {
+                    const float s = sS[slot][bcol(nf) + l16];
+#pragma unroll
+                    for (int mf = 0; mf < 2; mf++) {
+#pragma unroll
+                        for (int r = 0; r < 4; r++) acc[mf][nf][r] = fmaf(s, accg[mf][nf][r], acc[mf][nf][r]);
+                        accg[mf][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    }
+                }
+            }
+        }
+    }
+
+    // epilogue: D[row 4*l4 + r][col l16] of each fragment
+#pragma unroll
+    for (int mf = 0; mf < 2; mf++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int row = m0 + wm * 32 + mf * 16 + 4 * l4 + r;
+            if (row >= a.M) continue;
+            if (MODE == 0) {
+#pragma unroll
+                for (int nf = 0; nf < 4; nf++) {
+                    const int col = n0 + bcol(nf) + l16;
+                    if (col < a.N) a.C[(size_t)row * a.ldc + col] = acc[mf][nf][r];
+                }
+            } else {
+#pragma unroll
+                for (int f = 0; f < 2; f++) {
+                    const int col = n0 + wn * 32 + 16 * f + l16;
+                    if (col < a.N) {
+                        const float gt = acc[mf][f][r], up = acc[mf][f + 2][r];
+                        uint32_t hi, lo;
+                        pf_split(gt / (1.0f + __expf(-gt)) * up, hi, lo);
+                        a.z_hi[(size_t)row * a.ldz + col] = (uint16_t)hi;
+                        a.z_lo[(size_t)row * a.ldz + col] = (uint16_t)lo;
+                    }
+                }
+            }
+        }
+#undef LOAD_TILE_K
+}
+
+// ---- per-position kernels ----------------------------------------------------------------
+
+// X[t] = f32(embedding[tokens[t]]) and its bf16 planes. Block 0 also validates every
+// token id (invalid ids read row 0 and set the status word).
+__global__ __launch_bounds__(256) void pf_embed_kernel(const int32_t* tokens, int n, const uint16_t* emb, int vocab,
+                                                      int d, float* X, uint16_t* p_hi, uint16_t* p_lo, int ldp,
+                                                      int* status) {
+    const int t = blockIdx.x;
+    if (t == 0 && status) {
+        __shared__ int s_bad;
+        if (threadIdx.x == 0) s_bad = 0;
+        __syncthreads();
+        for (int i = threadIdx.x; i < n; i += blockDim.x)
+            if (tokens[i] < 0 || tokens[i] >= vocab) s_bad = 1;
+        __syncthreads();
+        if (threadIdx.x == 0) *status = s_bad ? ATLAS_ERR_INVALID_ARG : ATLAS_OK;
+    }
+    int tok = tokens[t];
+    if (tok < 0 || tok >= vocab) tok = 0;
+    const uint2* row = reinterpret_cast<const uint2*>(emb + (size_t)tok * d);
+    for (int i = threadIdx.x; i < d / 4; i += blockDim.x) {
+        const uint2 v = row[i];
+        const float4 x = make_float4(bf16_bits_to_f32(v.x & 0xFFFFu), bf16_bits_to_f32(v.x >> 16),
+                                     bf16_bits_to_f32(v.y & 0xFFFFu), bf16_bits_to_f32(v.y >> 16));
+        reinterpret_cast<float4*>(X + (size_t)t * d)[i] = x;
+        store_split4(x, p_hi + (size_t)t * ldp + 4 * i, p_lo + (size_t)t * ldp + 4 * i);
+    }
+}
+
+// Full-projection QK RMSNorm, rotary embedding (x attention factor) at position
+// start_pos + t, q written back in place, k and v written to cache slot pos.
+__global__ __launch_bounds__(256) void pf_rope_kernel(PfRopeArgs a) {
+    constexpr int D = 128;
+    __shared__ float red[16];
+    __shared__ float s_cos[64], s_sin[64];
+    const int t = blockIdx.x, pos = a.start_pos + t;
+    const int nq = a.Hq * D, nk = a.Hkv * D;
+    float* row = a.qkv + (size_t)t * a.ld;
+    float sq = 0.f, sk = 0.f;
+    for (int i = threadIdx.x; i < nq; i += blockDim.x) sq = fmaf(row[i], row[i], sq);
+    for (int i = threadIdx.x; i < nk; i += blockDim.x) sk = fmaf(row[nq + i], row[nq + i], sk);
+    sq = block_sum(sq, red);
+    sk = block_sum(sk, red);
+    const float rq = 1.0f / sqrtf(sq / (float)nq + a.eps);
+    const float rk = 1.0f / sqrtf(sk / (float)nk + a.eps);
+    if (threadIdx.x < 64) {
+        const double ang = (double)pos * a.inv[threadIdx.x];
+        const double rr = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+        float sn, cs;
+        sincosf((float)rr, &sn, &cs);
+        s_cos[threadIdx.x] = cs * (float)a.mscale;
+        s_sin[threadIdx.x] = sn * (float)a.mscale;
+    }
+    __syncthreads();
+    const int npairs = (a.Hq + a.Hkv) * 64;
+    for (int u = threadIdx.x; u < npairs; u += blockDim.x) {
+        const int h = u >> 6, i = u & 63;
+        const bool isk = h >= a.Hq;
+        const float rr = isk ? rk : rq;
+        const float* g = isk ? a.g_k + (h - a.Hq) * D : a.g_q + h * D;
+        const int base = h * D;   // q heads, then k heads, in the projection row
+        const float x0 = g[i] * (row[base + i] * rr), x1 = g[i + 64] * (row[base + i + 64] * rr);
+        const float c = s_cos[i], sn = s_sin[i];
+        const float y0 = x0 * c - x1 * sn, y1 = x1 * c + x0 * sn;
+        if (isk) {
+            float* dst = a.k_cache + ((size_t)(h - a.Hq) * a.T_max + pos) * D;
+            dst[i] = y0;
+            dst[i + 64] = y1;
+        } else {
+            row[base + i] = y0;
+            row[base + i + 64] = y1;
+        }
+    }
+    for (int u = threadIdx.x; u < nk; u += blockDim.x) {
+        const int h = u / D, i = u % D;
+        a.v_cache[((size_t)h * a.T_max + pos) * D + i] = row[nq + nk + u];
+    }
+}
+
+// X[t] += g * A[t] / rms(A[t]) and the bf16 planes of the new X[t].
+__global__ __launch_bounds__(256) void pf_residual_kernel(float* X, const float* A, const float* g, int d, float eps,
+                                                         uint16_t* p_hi, uint16_t* p_lo, int ldp) {
+    __shared__ float red[16];
+    const int t = blockIdx.x;
+    const float4* a4 = reinterpret_cast<const float4*>(A + (size_t)t * d);
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < d / 4; i += blockDim.x) {
+        const float4 v = a4[i];
+        ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+    }
+    ss = block_sum(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+    float4* x4 = reinterpret_cast<float4*>(X + (size_t)t * d);
+    const float4* g4 = reinterpret_cast<const float4*>(g);
+    for (int i = threadIdx.x; i < d / 4; i += blockDim.x) {
+        const float4 v = a4[i], gg = g4[i], x = x4[i];
+        const float4 h = make_float4(x.x + gg.x * (v.x * r), x.y + gg.y * (v.y * r), x.z + gg.z * (v.z * r),
+                                     x.w + gg.w * (v.w * r));
+        x4[i] = h;
+        store_split4(h, p_hi + (size_t)t * ldp + 4 * i, p_lo + (size_t)t * ldp + 4 * i);
+    }
+}
+
+// bf16 planes of an f32 matrix [M][K] (row stride ldx) into [M][ldp]; K % 4 == 0.
+__global__ __launch_bounds__(256) void pf_split_kernel(const float* X, int K, int ldx, uint16_t* p_hi, uint16_t* p_lo,
+                                                      int ldp) {
+    const int t = blockIdx.x;
+    const float4* x4 = reinterpret_cast<const float4*>(X + (size_t)t * ldx);
+    for (int i = threadIdx.x; i < K / 4; i += blockDim.x)
+        store_split4(x4[i], p_hi + (size_t)t * ldp + 4 * i, p_lo + (size_t)t * ldp + 4 * i);
+}
+
+// ---- causal GQA attention over a block of 16 positions ------------------------------------
+//
+// grid (ceil(n / 16), Hkv), one wave per query head of the KV group. Keys come in
+// tiles of 16 through LDS (shared by the group's heads). Per wave: S (16 positions x
+// 16 keys) = Q K^T on f32 MFMA over the 128 dimensions, masked to each position's
+// window, online softmax per position, O += P V on f32 MFMA (P re-laid out through
+// LDS). The output is written as bf16 planes for the o projection.
+constexpr int PF_QT = 16;
+
+template <int G>
+__global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
+    constexpr int D = 128, KP = D + 4, VP = D + 16;
+    __shared__ float sK[16 * KP];
+    __shared__ float sV[16 * VP];
+    __shared__ float sP[G][16 * 17];
+    const int t0 = blockIdx.x * PF_QT, kv = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, l4 = lane >> 4;
+    const int head = kv * G + wave;
+    const int t_last = min(t0 + PF_QT, a.n) - 1;
+    const int p_first = a.start_pos + t0, p_last = a.start_pos + t_last;
+    const int klo = a.window > 0 ? max(0, p_first - a.window + 1) : 0;
+    const int khi = p_last;
+
+    // Q fragments: lane holds Q[position t0 + l16][4 s + l4], s < 32 (A operand layout)
+    float qf[32];
+    {
+        const float* q = a.qkv + (size_t)min(t0 + l16, a.n - 1) * a.ld_qkv + head * D;
+#pragma unroll
+        for (int s = 0; s < 32; s++) qf[s] = q[4 * s + l4];
+    }
+    float m[4], l[4];
+    f32x4_t o[8];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        m[r] = -INFINITY;
+        l[r] = 0.f;
+    }
+#pragma unroll
+    for (int gi = 0; gi < 8; gi++) o[gi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const float* Kh = a.k_cache + (size_t)kv * a.T_max * D;
+    const float* Vh = a.v_cache + (size_t)kv * a.T_max * D;
+    for (int kb = klo; kb <= khi; kb += 16) {
+        __syncthreads();
+        for (int u = tid; u < 16 * D / 4; u += blockDim.x) {
+            const int kr = u / (D / 4), c = u % (D / 4);
+            const size_t j = (size_t)min(kb + kr, khi);
+            *reinterpret_cast<float4*>(&sK[kr * KP + 4 * c]) = reinterpret_cast<const float4*>(Kh + j * D)[c];
+            *reinterpret_cast<float4*>(&sV[kr * VP + 4 * c]) = reinterpret_cast<const float4*>(Vh + j * D)[c];
+        }
+        __syncthreads();
+        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 32; s++) sc = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[s], sK[l16 * KP + 4 * s + l4], sc, 0, 0, 0);
+        // sc[r] = S[position 4 l4 + r][key kb + l16]
+        const int j = kb + l16;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int ti = t0 + 4 * l4 + r, pi = a.start_pos + ti;
+            const int lo_i = a.window > 0 ? max(0, pi - a.window + 1) : 0;
+            const bool valid = ti < a.n && j <= pi && j >= lo_i;
+            const float sv = valid ? sc[r] * a.scale : -INFINITY;
+            float mt = sv;
+            mt = fmaxf(mt, dpp_f<0xB1>(mt));
+            mt = fmaxf(mt, dpp_f<0x4E>(mt));
+            mt = fmaxf(mt, dpp_f<0x141>(mt));
+            mt = fmaxf(mt, dpp_f<0x140>(mt));
+            const float mn = fmaxf(m[r], mt);
+            const float corr = (mn == -INFINITY) ? 1.f : __expf(m[r] - mn);
+            const float p = valid ? __expf(sv - mn) : 0.f;
+            l[r] = fmaf(l[r], corr, row16_sum(p));
+            m[r] = mn;
+#pragma unroll
+            for (int gi = 0; gi < 8; gi++) o[gi][r] *= corr;
+            sP[wave][(4 * l4 + r) * 17 + l16] = p;
+        }
+        // O += P V: A operand P[position l16][key 4 s + l4], B operand V[key 4 s + l4][dim 16 gi + l16]
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            const float pa = sP[wave][l16 * 17 + 4 * s + l4];
+#pragma unroll
+            for (int gi = 0; gi < 8; gi++)
+                o[gi] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, sV[(4 * s + l4) * VP + 16 * gi + l16], o[gi], 0, 0, 0);
+        }
+    }
+    // o[gi][r] = O[position 4 l4 + r][dim 16 gi + l16]
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const int ti = t0 + 4 * l4 + r;
+        if (ti >= a.n) continue;
+        const float inv = 1.0f / l[r];
+        uint16_t* hi = a.o_hi + (size_t)ti * a.ldo + head * D;
+        uint16_t* lo = a.o_lo + (size_t)ti * a.ldo + head * D;
+#pragma unroll
+        for (int gi = 0; gi < 8; gi++) {
+            uint32_t h, lw;
+            pf_split(o[gi][r] * inv, h, lw);
+            hi[16 * gi + l16] = (uint16_t)h;
+            lo[16 * gi + l16] = (uint16_t)lw;
+        }
+    }
+}
+
+// ---- launchers ------------------------------------------------------------------------------
+
+int gemm_supported(int group) { return group >= 32 && (group == 32 || group % GM_BK == 0); }
+
+int launch_w4_gemm(const GemmArgs& a, int mode, hipStream_t st, const char* label) {
+    ATLAS_CHECK_SHAPE(gemm_supported(a.group), "prefill GEMM needs group 32 or a multiple of 64 (got %d)", a.group);
+    ATLAS_CHECK_SHAPE(a.K % 32 == 0 && a.K >= 32 && a.lda % 8 == 0, "prefill GEMM shape K=%d lda=%d", a.K, a.lda);
+    const int NW_ = mode ? GM_BN / 2 : GM_BN;
+    const int MT = (a.M + GM_BM - 1) / GM_BM, NT = (a.N + NW_ - 1) / NW_;
+    const int T = MT * NT, blocks = 8 * ((T + 7) / 8);
+    prof_mark(label, st);
+    if (mode == 0) ATLAS_KLAUNCH((w4_gemm_kernel<0>), dim3(blocks), dim3(GM_THREADS), 0, st, a);
+    else ATLAS_KLAUNCH((w4_gemm_kernel<1>), dim3(blocks), dim3(GM_THREADS), 0, st, a);
+    ATLAS_LAUNCH_CHECK("w4_gemm_kernel");
+    return ATLAS_OK;
+}
+
+int launch_pf_embed(const int32_t* tokens, int n, const uint16_t* emb, int vocab, int d, float* X, uint16_t* p_hi,
+                    uint16_t* p_lo, int ldp, int* status, hipStream_t st) {
+    prof_mark("pf_embed", st);
+    ATLAS_KLAUNCH(pf_embed_kernel, dim3(n), dim3(256), 0, st, tokens, n, emb, vocab, d, X, p_hi, p_lo, ldp, status);
+    ATLAS_LAUNCH_CHECK("pf_embed_kernel");
+    return ATLAS_OK;
+}
+
+int launch_pf_rope(const PfRopeArgs& a, hipStream_t st) {
+    prof_mark("pf_qk_norm_rope", st);
+    ATLAS_KLAUNCH(pf_rope_kernel, dim3(a.n), dim3(256), 0, st, a);
+    ATLAS_LAUNCH_CHECK("pf_rope_kernel");
+    return ATLAS_OK;
+}
+
+int launch_pf_attn(const PfAttnArgs& a, hipStream_t st) {
+    const int G = a.Hq / a.Hkv;
+    dim3 grid((a.n + PF_QT - 1) / PF_QT, a.Hkv);
+    prof_mark(a.window > 0 ? "pf_attn_window" : "pf_attn_full", st);
+    switch (G) {
+#define C(G_)                                                                   \
+    case G_:                                                                    \
+        ATLAS_KLAUNCH((pf_attn_kernel<G_>), grid, dim3(64 * G_), 0, st, a);    \
+        break;
+        C(1) C(2) C(3) C(4) C(5) C(6) C(7) C(8)
+#undef C
+        default: return fail(ATLAS_ERR_UNSUPPORTED_SHAPE, "Hq/Hkv=%d > 8", G);
+    }
+    ATLAS_LAUNCH_CHECK("pf_attn_kernel");
+    return ATLAS_OK;
+}
+
+int launch_pf_split(const float* X, int M, int K, int ldx, uint16_t* p_hi, uint16_t* p_lo, int ldp, hipStream_t st) {
+    prof_mark("pf_split", st);
+    ATLAS_KLAUNCH(pf_split_kernel, dim3(M), dim3(256), 0, st, X, K, ldx, p_hi, p_lo, ldp);
+    ATLAS_LAUNCH_CHECK("pf_split_kernel");
+    return ATLAS_OK;
+}
+
+int launch_pf_residual(float* X, const float* A, const float* g, int n, int d, float eps, uint16_t* p_hi,
+                       uint16_t* p_lo, int ldp, hipStream_t st) {
+    prof_mark("pf_residual_norm", st);
+    ATLAS_KLAUNCH(pf_residual_kernel, dim3(n), dim3(256), 0, st, X, A, g, d, eps, p_hi, p_lo, ldp);
+    ATLAS_LAUNCH_CHECK("pf_residual_kernel");
+    return ATLAS_OK;
+}
+
+}  // namespace atlas

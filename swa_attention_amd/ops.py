@@ -71,6 +71,24 @@ def atlas_w4_dequant(w: W4, out=None, stream=None):
     return out
 
 
+def atlas_w4_gemm_workspace_bytes(w: W4, M):
+    return L.lib().atlas_w4_gemm_workspace_bytes(ctypes.byref(w.c()), M)
+
+
+def atlas_w4_gemm(w: W4, A, C=None, ws=None, stream=None):
+    """C [M][N] = A [M][K] W^T on the matrix cores (A f32, row-major)."""
+    _dev(A, F32, "A")
+    M = A.shape[0]
+    if C is None:
+        C = torch.empty((M, w.N), dtype=F32, device=A.device)
+    _dev(C, F32, "C")
+    need = atlas_w4_gemm_workspace_bytes(w, M)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=A.device)
+    L.call("atlas_w4_gemm", ctypes.byref(w.c()), L.ptr(A), M, L.ptr(C), L.ptr(ws), ws.numel(), L.stream_ptr(stream))
+    return C
+
+
 # ---- norms, rotary, attention -------------------------------------------------------------------
 
 def atlas_rmsnorm_residual(x, g, resid=None, out=None, eps=1e-6, stream=None):

@@ -142,3 +142,58 @@ def test_prefill_equals_teacher_forced_decode_and_oracle():
     assert normwise(logits.cpu().numpy(), lg2.cpu().numpy()) < TOL
     for l in range(wl.model.n_layers):
         assert normwise(dm.layers[l].k_cache.cpu().numpy(), dm2.layers[l].k_cache.cpu().numpy()) < TOL
+
+
+def _prefill_vs_oracle(wl, n_tokens, dev):
+    toks = W.prompt_tokens(wl.model, wl.seed, n_tokens, stream=1)
+    dm = build_model(wl, dev)
+    d_toks = torch.from_numpy(toks).to(dev)
+    logits = torch.empty(wl.model.vocab, dtype=torch.float32, device=dev)
+    am = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(ops.atlas_prefill_workspace_bytes(dm, len(toks)), dtype=torch.uint8, device=dev)
+    ops.atlas_prefill(dm, d_toks, wl.n_cached, logits, am, ws)
+    torch.cuda.synchronize()
+    assert ops.atlas_device_status(ws) == 0
+    ref = R.run_prefill(wl, toks)
+    p0, p1 = wl.n_cached, wl.n_cached + n_tokens
+    for l in range(wl.model.n_layers):
+        gk, gv = dm.layers[l].k_cache.cpu().numpy(), dm.layers[l].v_cache.cpu().numpy()
+        assert normwise(gk[:, p0:p1], ref["K"][l][:, p0:p1]) < TOL, l
+        assert normwise(gv[:, p0:p1], ref["V"][l][:, p0:p1]) < TOL, l
+        np.testing.assert_array_equal(gk[:, :p0], ref["K"][l][:, :p0])   # earlier slots untouched
+        assert not np.any(gk[:, p1:])                                     # later slots untouched
+    assert normwise(logits.cpu().numpy(), ref["logits"]) < TOL
+    assert int(am.item()) == ref["argmax"]
+
+
+def test_prefill_long_prompt_crosses_the_window():
+    """100 tokens through the tiny 4-layer stack (window 64): the sliding window cuts
+    into the prompt itself, and the positions span seven 16-token attention tiles with
+    a ragged last one."""
+    dev = device()
+    announce("prefill tiny stack, 100 tokens, window 64")
+    _prefill_vs_oracle(_tiny_stack(n_cached=0, t_max=160), 100, dev)
+
+
+def test_prefill_continues_a_filled_cache():
+    """A prompt of 37 tokens after 50 cached positions (start_pos = 50): attention
+    reads the earlier cache, the window reaches back into it, and only slots 50..86
+    are written."""
+    dev = device()
+    announce("prefill tiny stack, 37 tokens after 50 cached")
+    _prefill_vs_oracle(_tiny_stack(n_cached=50, t_max=128), 37, dev)
+
+
+def test_prefill_bad_token_sets_status():
+    dev = device()
+    wl = _tiny_stack(n_cached=0, t_max=64)
+    announce("prefill with an out-of-range token id")
+    dm = build_model(wl, dev)
+    toks = W.prompt_tokens(wl.model, wl.seed, 8, stream=1)
+    toks[3] = wl.model.vocab + 5
+    d_toks = torch.from_numpy(toks).to(dev)
+    am = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(ops.atlas_prefill_workspace_bytes(dm, len(toks)), dtype=torch.uint8, device=dev)
+    ops.atlas_prefill(dm, d_toks, 0, None, am, ws)
+    torch.cuda.synchronize()
+    assert ops.atlas_device_status(ws) == 1

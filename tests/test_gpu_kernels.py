@@ -71,6 +71,43 @@ def test_gemv_matches_oracle(N, K):
     assert normwise(y, ref) < 1e-5
 
 
+@pytest.mark.parametrize("M,N,K,group,zeros,sd", [
+    (1, 96, 640, 128, True, 0), (17, 130, 640, 128, True, 0), (64, 256, 1728, 128, True, 0),
+    (130, 200, 640, 64, False, 1), (70, 64, 256, 32, True, 0), (200, 896, 640, 128, True, 0),
+    (65, 129, 5120, 128, True, 0)])
+def test_gemm_matches_oracle(M, N, K, group, zeros, sd):
+    """The matrix-core W4 GEMM (prefill projections) against the f64 oracle row by row:
+    ragged row and column tiles, a partial last group (K = 1,728), groups 32/64/128,
+    symmetric codes and bf16 scales. The activations pass through bf16 hi/lo planes
+    (16 significant bits), so the bar is 2e-5 normwise."""
+    dev = device()
+    announce(f"gemm M={M} N={N} K={K} group={group}")
+    c, s, z = _w4(N, K, 11, group, zeros, sd)
+    A = np.stack([synth.normal_f32(synth.key(11, 100 + i), K) for i in range(M)])
+    w = w4_to_device(c, s, z, K, dev, group, sd)
+    C = ops.atlas_w4_gemm(w, torch.from_numpy(A).to(dev)).cpu().numpy()
+    ref = np.stack([O.w4_gemv(c, s, z, K, A[i], group, sd) for i in range(M)])
+    assert normwise(C, ref) < 2e-5
+
+
+def test_gemm_one_hot_rows_bit_exact():
+    """Rows of A that are unit vectors e_j (exact in bf16, lo plane zero) give column j
+    of the dequantised matrix bit for bit: unpacking, zero point and scale selection
+    of the GEMM's dequantise-into-LDS path."""
+    dev = device()
+    N, K = 200, 1728
+    c, s, z = _w4(N, K, 12)
+    cols = [0, 1, 7, 8, 31, 32, 63, 64, 127, 128, 129, 1000, K - 65, K - 64, K - 1]
+    A = np.zeros((len(cols), K), dtype=np.float32)
+    for i, j in enumerate(cols):
+        A[i, j] = 1.0
+    w = w4_to_device(c, s, z, K, dev)
+    C = ops.atlas_w4_gemm(w, torch.from_numpy(A).to(dev)).cpu().numpy()
+    ref = O.dequant(c, s, z, K)
+    for i, j in enumerate(cols):
+        np.testing.assert_array_equal(C[i].view(np.uint32), ref[:, j].copy().view(np.uint32), err_msg=f"col {j}")
+
+
 def test_gemv_heavy_tailed_input():
     """Inputs spanning 12 orders of magnitude within a chunk stay at f32-level error."""
     dev = device()
