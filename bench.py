@@ -82,6 +82,57 @@ def cpu_baseline(wl, budget_s):
             "s_per_token": per_token}
 
 
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def measure_prefill(args, dm, cm, m, dev):
+    """Time-to-first-token of the 1,200-token prompt (same 64-layer model, positions
+    0..1,199, written over the decode cache after the decode timing): token ids on
+    device to the last row's logits and argmax."""
+    import torch
+    from synth import workloads as W
+    from swa_attention_amd import accounting as A
+    from swa_attention_amd import ops
+    pw = W.config(4)
+    n = pw.prompt_len
+    toks = torch.from_numpy(W.prompt_tokens(m, pw.seed, n)).to(dev)
+    ws = torch.empty(ops.atlas_prefill_workspace_bytes(dm, n), dtype=torch.uint8, device=dev)
+    logits = torch.empty(m.vocab, dtype=torch.float32, device=dev)
+    am = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def run():
+        ops.atlas_prefill(dm, toks, 0, logits, am, ws, cm=cm)
+
+    log(f"prefill {pw.name}: warm-up")
+    run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.prefill_reps):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.prefill_reps
+    assert ops.atlas_device_status(ws) == 0
+    ops.atlas_profile_start(100000)
+    run()
+    prof = ops.atlas_profile_stop()
+    log("prefill per-launch timing: " + ", ".join(f"{k} {v[0]}x {v[1] / v[0] * 1e3:.1f}us" for k, v in
+                                                  sorted(prof.items(), key=lambda kv: -kv[1][1])))
+    flops = A.prefill_flops(m, n)
+    out = {"workload": pw.name, "tokens": n, "ttft_ms": round(ms, 2), "reps": args.prefill_reps,
+           "algorithmic_tflop": round(flops / 1e12, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "mfma_frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    dom = "pf_gemm_gate_up"
+    if dom in prof:
+        cnt, tot = prof[dom]
+        f = 2.0 * n * 2 * m.dff * m.d   # algorithmic flops of one gate+up launch
+        ach = f / (tot / cnt * 1e-3) / 1e12
+        out["roofline"] = {"bound": "mfma", "kernel": "w4_gemm_kernel<1> (gate+up, SwiGLU)", "achieved": round(ach, 1),
+                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                           "avg_launch_us": round(tot / cnt * 1e3, 1),
+                           "note": "algorithmic flops; the bf16 hi/lo activation planes issue twice as many"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,6 +142,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle compute in the CPU leg")
     ap.add_argument("--profile-steps", type=int, default=3)
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 1,200-token prefill measurement")
+    ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (3 times); its HBM counters "
                          "calibrate the FETCH_SIZE/WRITE_SIZE readings of the decode kernels")
@@ -166,6 +219,10 @@ def main():
                 "kernel": f"gate_up_kernel (2 x {m.dff}x{m.d} W4 + SwiGLU)", "bytes_per_launch": per_launch,
                 "avg_launch_us": round(avg_s * 1e6, 2), "launches": cnt}
 
+    prefill = None
+    if not args.no_prefill and head and wl.use_tokens:
+        prefill = measure_prefill(args, dm, cm, m, dev)
+
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 18   # f32 elements
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -201,6 +258,7 @@ def main():
         "bytes_per_step": sb.total,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "prefill": prefill,
     }
     print(json.dumps(out), flush=True)
 
