@@ -1,0 +1,102 @@
+"""Parity at the full sizes the benchmark times (GPU).
+
+- The 64-layer decode step at 16,384 cached positions (the bench workload, same
+  launch configuration) against the oracle: logits normwise within 1e-3, identical
+  greedy argmax (the oracle's top-1/top-2 margin is printed), last hidden state.
+- The 1,200-token prefill on the matrix cores against 1,200 teacher-forced decode
+  steps of the GPU decode path (prefill's definition), at full size: the decode path
+  is itself checked against the oracle above, and the oracle is too slow for 1,200
+  positions of 64 layers. Logits, argmax and sampled KV slots are compared.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import runner as R
+from synth import workloads as W
+from synth.device import build_model
+from swa_attention_amd import ops
+from gpu_util import TOL, announce, device, normwise
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def olmo3_model():
+    dev = device()
+    wl = W.config(3)
+    announce("building the 64-layer OLMo-3-32B-shaped W4 model (16,385 KV slots per layer)")
+    dm = build_model(wl, dev)
+    torch.cuda.synchronize()
+    yield wl, dm
+    del dm
+    torch.cuda.empty_cache()
+
+
+def test_decode_64_layers_16k_matches_oracle(olmo3_model):
+    wl, dm = olmo3_model
+    dev = device()
+    m = wl.model
+    announce("decode step, 64 layers at 16,384 cached + lm_head vs oracle")
+    tok = R.decode_token(wl)
+    d_tok = torch.tensor([tok], dtype=torch.int32, device=dev)
+    pos = torch.tensor([wl.n_cached], dtype=torch.int32, device=dev)
+    logits = torch.empty(m.vocab, dtype=torch.float32, device=dev)
+    hidden = torch.empty(m.d, dtype=torch.float32, device=dev)
+    am = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(ops.atlas_decode_workspace_bytes(dm), dtype=torch.uint8, device=dev)
+    ops.atlas_decode_step(dm, pos, d_token=d_tok, hidden_out=hidden, logits=logits, argmax=am, ws=ws)
+    torch.cuda.synchronize()
+    assert ops.atlas_device_status(ws) == 0
+    ref = R.run_decode(wl)
+    lg = logits.cpu().numpy()
+    top2 = np.sort(ref["logits"])[-2:]
+    err_l = normwise(lg, ref["logits"])
+    err_y = normwise(hidden.cpu().numpy(), ref["y"])
+    print(f"logits normwise {err_l:.2e}, hidden normwise {err_y:.2e}, oracle top1-top2 margin {top2[1] - top2[0]:.3e}, "
+          f"max |logit err| {np.max(np.abs(lg - ref['logits'])):.3e}")
+    assert err_y < TOL
+    assert err_l < TOL
+    assert int(am.item()) == ref["argmax"]
+    # the new key/value went to slot 16,384 of every layer; slot 16,383 still holds the cache
+    k_new = dm.layers[63].k_cache[:, wl.n_cached]
+    assert torch.count_nonzero(k_new).item() > 0
+
+
+def test_prefill_1200_matches_teacher_forced_decode(olmo3_model):
+    wl, dm = olmo3_model
+    dev = device()
+    m = wl.model
+    pw = W.config(4)
+    n = pw.prompt_len
+    announce(f"prefill of {n} tokens (64 layers, matrix cores) vs {n} teacher-forced GPU decode steps")
+    toks = torch.from_numpy(W.prompt_tokens(m, pw.seed, n)).to(dev)
+    logits_p = torch.empty(m.vocab, dtype=torch.float32, device=dev)
+    am_p = torch.empty(1, dtype=torch.int32, device=dev)
+    ws_p = torch.empty(ops.atlas_prefill_workspace_bytes(dm, n), dtype=torch.uint8, device=dev)
+    ops.atlas_prefill(dm, toks, 0, logits_p, am_p, ws_p)
+    torch.cuda.synchronize()
+    assert ops.atlas_device_status(ws_p) == 0
+    sample_layers = [0, 3, 62, 63]
+    kv_p = {l: (dm.layers[l].k_cache[:, :n].cpu(), dm.layers[l].v_cache[:, :n].cpu()) for l in sample_layers}
+    del ws_p
+    # the decode path over the same positions (overwrites slots 0..n-1 with its own values)
+    logits_d = torch.empty_like(logits_p)
+    am_d = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(ops.atlas_decode_workspace_bytes(dm), dtype=torch.uint8, device=dev)
+    cm = dm.c()
+    pos = torch.arange(n, dtype=torch.int32, device=dev)
+    for t in range(n):
+        last = t == n - 1
+        ops.atlas_decode_step(dm, pos[t:t + 1], d_token=toks[t:t + 1], logits=logits_d if last else None,
+                              argmax=am_d if last else None, ws=ws, cm=cm)
+    torch.cuda.synchronize()
+    assert ops.atlas_device_status(ws) == 0
+    err = normwise(logits_p.cpu().numpy(), logits_d.cpu().numpy())
+    print(f"prefill vs decode logits normwise {err:.2e}")
+    assert err < TOL
+    assert int(am_p.item()) == int(am_d.item())
+    for l in sample_layers:
+        kp, vp = kv_p[l]
+        assert normwise(kp.numpy(), dm.layers[l].k_cache[:, :n].cpu().numpy()) < TOL, l
+        assert normwise(vp.numpy(), dm.layers[l].v_cache[:, :n].cpu().numpy()) < TOL, l
