@@ -172,6 +172,18 @@ __host__ __device__ inline XQ xq_view(void* base, int K) {
     return v;
 }
 
+// Byte k of the result r_k is byte k' of X[0..3] for k' = 0, 1, 2: r_k = [X0.k', X1.k',
+// X2.k', X3.k'] (v_perm_b32 selects bytes of the 8-byte pair {hi, lo}).
+__device__ __forceinline__ void xq_gather_bytes(const uint32_t (&X)[4], uint32_t& r0, uint32_t& r1, uint32_t& r2) {
+    const uint32_t a = __builtin_amdgcn_perm(X[1], X[0], 0x05010400u);   // X0.0 X1.0 X0.1 X1.1
+    const uint32_t b = __builtin_amdgcn_perm(X[3], X[2], 0x05010400u);   // X2.0 X3.0 X2.1 X3.1
+    const uint32_t c = __builtin_amdgcn_perm(X[1], X[0], 0x07030602u);   // X0.2 X1.2 X0.3 X1.3
+    const uint32_t d = __builtin_amdgcn_perm(X[3], X[2], 0x07030602u);   // X2.2 X3.2 X2.3 X3.3
+    r0 = __builtin_amdgcn_perm(b, a, 0x05040100u);
+    r1 = __builtin_amdgcn_perm(b, a, 0x07060302u);
+    r2 = __builtin_amdgcn_perm(d, c, 0x05040100u);
+}
+
 // Encode word `w` (8 elements x8[0..7]) of chunk `c`; the 4 threads of a chunk must
 // be lanes 4j..4j+3 of one wave (quad) and call this together.
 __device__ __forceinline__ void xq_encode_word(const float x8[8], XQ out, int c, int w) {
@@ -180,21 +192,33 @@ __device__ __forceinline__ void xq_encode_word(const float x8[8], XQ out, int c,
     for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(x8[i]));
     m = quad_max(m);
     int e = (m > 0.f) ? __builtin_amdgcn_frexp_expf(m) : 0;   // m < 2^e
-    // |v| <= 2^22, so b = v + 0x888888 lies in [0, 16^6): its nibbles n_p are the
-    // balanced digits of v plus 8 (v = sum_p (n_p - 8) 16^p), and the 4-bit pattern of
-    // the digit n_p - 8 is n_p ^ 8 (applied to whole plane words at the end)
-    uint32_t pl[XQ_PLANES] = {0u, 0u, 0u, 0u, 0u, 0u};
-    int s = 0;
+    // v = rint(x 2^(22-e)), |v| < 2^22: adding 1.5 * 2^23 rounds to the nearest even
+    // integer and leaves 0x4B400000 + v in the bits. b = v + 0x888888 lies in [0, 16^6):
+    // its nibbles n_p are the balanced digits of v plus 8 (v = sum_p (n_p - 8) 16^p), and
+    // the 4-bit pattern of the digit n_p - 8 is n_p ^ 8 (applied to whole plane words).
+    constexpr float ROUND = 12582912.0f;                      // 1.5 * 2^23
+    constexpr uint32_t ROUND_BITS = 0x4B400000u;
     const int sh = 22 - e;
+    uint32_t b[8], su = 0u;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        const int v = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(x8[i], sh));
-        s += v;
-        const uint32_t b = (uint32_t)(v + 0x888888);
-#pragma unroll
-        for (int p = 0; p < XQ_PLANES; p++) pl[p] |= ((b >> (4 * p)) & 15u) << (4 * i);
+        const uint32_t u = __float_as_uint(__builtin_amdgcn_ldexpf(x8[i], sh) + ROUND);
+        su += u;
+        b[i] = u + (0x888888u - ROUND_BITS);
     }
-    s = quad_sum_i(s);
+    int s = quad_sum_i((int)(su - 8u * ROUND_BITS));
+    // nibble transpose: plane p holds nibble p of the 8 values, value i in nibble i.
+    // Pair the values (2k, 2k+1) into bytes (E: even nibbles, O: odd nibbles of b), then
+    // gather byte k of the four pairs with byte permutes.
+    uint32_t E[4], O[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        E[k] = (b[2 * k] & 0x0F0F0F0Fu) | ((b[2 * k + 1] << 4) & 0xF0F0F0F0u);
+        O[k] = ((b[2 * k] >> 4) & 0x0F0F0F0Fu) | (b[2 * k + 1] & 0xF0F0F0F0u);
+    }
+    uint32_t pl[XQ_PLANES];
+    xq_gather_bytes(E, pl[0], pl[2], pl[4]);
+    xq_gather_bytes(O, pl[1], pl[3], pl[5]);
     uint32_t* dst = out.planes + (size_t)c * XQ_WORDS_PER_CHUNK + w * XQ_PLANES;
 #pragma unroll
     for (int p = 0; p < XQ_PLANES; p++) dst[p] = pl[p] ^ 0x88888888u;

@@ -90,8 +90,15 @@ int launch_sum_partials(const float* part, int S, int N, float* y, hipStream_t s
 }
 
 
+// at most 4 chunks per lane (the wider tiles hold fewer loads in flight); 5 only where
+// no split of K fits 4
+GemvShape standalone_shape(int N, int K) {
+    GemvShape p = gemv_shape(N, K, true, 256, 4);
+    return p.CPL ? p : gemv_shape(N, K, true, 256, 5);
+}
+
 size_t gemv_workspace_bytes(int N, int K) {
-    GemvShape p = gemv_shape(N, K, true, 256);
+    GemvShape p = standalone_shape(N, K);
     size_t b = align_up(xq_bytes(K), 256);
     if (p.S > 1) b += align_up((size_t)p.S * N * 4, 256);
     return b;
@@ -114,7 +121,7 @@ extern "C" int atlas_w4_gemv(const atlas_w4* W, const float* x, float* y, void* 
     ATLAS_CHECK_ARG(ws != nullptr, "null workspace");
     const size_t need = gemv_workspace_bytes(W->N, W->K);
     if (ws_bytes < need) return fail(ATLAS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu", ws_bytes, need);
-    GemvShape p = gemv_shape(W->N, W->K, true, 256);
+    GemvShape p = standalone_shape(W->N, W->K);
     ATLAS_CHECK_SHAPE(p.CPL > 0, "K=%d cannot be split into ranges the kernel supports", W->K);
     hipStream_t st = (hipStream_t)stream;
     XQ xq = xq_view(ws, W->K);
