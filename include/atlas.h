@@ -181,7 +181,9 @@ ATLAS_API int atlas_gqa_decode(const float* q, const float* k_cache, const float
  * d_hidden_out (f32 [d], may be NULL) receives the last layer's output. When
  * d_logits or d_argmax is non-NULL the final RMSNorm (g_final), the bf16 lm_head
  * GEMV (logits f32 [vocab]) and the greedy argmax (lowest index on ties, int32) run
- * as well. pos = *d_pos (device int32). ws: atlas_decode_workspace_bytes(m). */
+ * as well. pos = *d_pos (device int32). ws: atlas_decode_workspace_bytes(m).
+ * Shapes: head_dim 128, Hq % Hkv == 0 with Hq/Hkv <= 8, d a multiple of 32 in
+ * [32, 6144], dff a multiple of 32; otherwise ATLAS_ERR_UNSUPPORTED_SHAPE. */
 ATLAS_API size_t atlas_decode_workspace_bytes(const atlas_model* m);
 ATLAS_API int atlas_decode_step(const atlas_model* m, const int32_t* d_token, const float* d_hidden_in,
                       const int32_t* d_pos, float* d_hidden_out, float* d_logits, int32_t* d_argmax,

@@ -81,7 +81,7 @@ int validate_model(const atlas_model* m) {
     ATLAS_CHECK_SHAPE(m->hd == 128, "head_dim %d unsupported (128 only)", m->hd);
     ATLAS_CHECK_SHAPE(m->hq >= 1 && m->hkv >= 1 && m->hq % m->hkv == 0 && m->hq / m->hkv <= 8,
                       "head counts %d/%d unsupported", m->hq, m->hkv);
-    ATLAS_CHECK_SHAPE(m->d % 32 == 0 && m->d >= 32 && m->d <= 8192, "d=%d must be a multiple of 32 in [32, 8192]",
+    ATLAS_CHECK_SHAPE(m->d % 32 == 0 && m->d >= 32 && m->d <= 6144, "d=%d must be a multiple of 32 in [32, 6144]",
                       m->d);
     ATLAS_CHECK_SHAPE(m->dff % 32 == 0 && m->dff >= 32, "dff=%d must be a multiple of 32", m->dff);
     ATLAS_CHECK_ARG(m->t_max >= 1 && m->t_max <= (int64_t)1 << 30, "bad t_max");

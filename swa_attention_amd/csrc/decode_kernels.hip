@@ -213,7 +213,7 @@ struct GemvLds {
     }
 };
 
-constexpr int GEMV_NV4 = 8192 / 4 / GEMV_THREADS;   // float4 per thread for d <= 8192
+constexpr int GEMV_NV4 = 3;   // float4 per thread of an input vector: d <= 3 * 4 * GEMV_THREADS = 6144
 // register stages of the single-matrix kernels (CPL >= 4 tiles are larger: one stage less)
 template <int CPL>
 constexpr int gemv_stages() { return CPL >= 4 ? 3 : 4; }
