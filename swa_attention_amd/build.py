@@ -9,6 +9,9 @@ LIB = os.path.join(HERE, "libatlas.so")
 
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               # MFMA accumulators in ordinary VGPRs: no accvgpr copies around the
+               # per-group scaling of the prefill GEMM
+               "-mllvm", "-amdgpu-mfma-vgpr-form=1",
                "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
                "-fvisibility=hidden"]
 

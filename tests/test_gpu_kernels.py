@@ -108,6 +108,29 @@ def test_gemm_one_hot_rows_bit_exact():
         np.testing.assert_array_equal(C[i].view(np.uint32), ref[:, j].copy().view(np.uint32), err_msg=f"col {j}")
 
 
+@pytest.mark.parametrize("group", [64, 128])
+def test_gemm_large_grid_sampled_rows(group):
+    """A grid of 8,192 tiles (several per CU, tail round included): sampled rows of C
+    against the oracle, and one-hot rows bit for bit."""
+    dev = device()
+    M, N, K = 1024, 32768, 256
+    announce(f"gemm large grid M={M} N={N} K={K} group={group}")
+    c, s, z = _w4(N, K, 13, group)
+    A = np.stack([synth.normal_f32(synth.key(13, 100 + i), K) for i in range(M)])
+    onehot = [(5, 0), (100, 63), (517, 64), (1023, K - 1)]
+    for i, j in onehot:
+        A[i] = 0.0
+        A[i, j] = 1.0
+    w = w4_to_device(c, s, z, K, dev, group)
+    C = ops.atlas_w4_gemm(w, torch.from_numpy(A).to(dev)).cpu().numpy()
+    for i in [0, 1, 63, 64, 511, 700, 1000, 1022]:
+        ref = O.w4_gemv(c, s, z, K, A[i], group)
+        assert normwise(C[i], ref) < 2e-5, i
+    deq = O.dequant(c, s, z, K, group)
+    for i, j in onehot:
+        np.testing.assert_array_equal(C[i].view(np.uint32), deq[:, j].copy().view(np.uint32), err_msg=f"row {i}")
+
+
 def test_gemv_heavy_tailed_input():
     """Inputs spanning 12 orders of magnitude within a chunk stay at f32-level error."""
     dev = device()
