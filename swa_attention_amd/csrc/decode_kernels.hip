@@ -475,7 +475,11 @@ __global__ __launch_bounds__(GEMV_THREADS) void down_kernel(DownArgs a) {
 // groups of each wave are independent key streams with their own online softmax,
 // combined at the end. Queries stay in registers.
 
-constexpr int ATTN_KV_STAGES = 5;   // keys in flight per 16-lane stream: 4
+// Keys in flight per 16-lane stream: 1 (a ring of two). Deeper rings (2 and 4 keys) were
+// slower on both layer types: their registers (256 with spills at 4 keys) cost more
+// than the extra loads gain; 16 streams per block, two blocks per CU, already keep 32
+// keys (32 KB) in flight per CU.
+constexpr int ATTN_KV_STAGES = 2;
 constexpr int ATTN_SSQ_REGS = ATTN_SSQ_MAX_BLOCKS / ATTN_THREADS;   // sums-of-squares partials per thread
 constexpr int ATTN_QF_REGS = 8 * 128 / ATTN_THREADS;                 // query values per thread (G <= 8)
 
