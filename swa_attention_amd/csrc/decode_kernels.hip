@@ -214,10 +214,13 @@ struct GemvLds {
 };
 
 constexpr int GEMV_NV4 = 3;   // float4 per thread of an input vector: d <= 3 * 4 * GEMV_THREADS = 6144
-// register stages of the single-matrix kernels (CPL >= 4 tiles are larger: one stage less)
+// Register stages: two, i.e. one tile (gate/up: one tile pair) in flight per wave
+// beyond the one being reduced. Deeper rings (2-3 tiles in flight) were slower: a wave
+// spends longer issuing them before its prologue, and eight waves per CU already keep
+// the memory system busy.
 template <int CPL>
-constexpr int gemv_stages() { return CPL >= 4 ? 3 : 4; }
-constexpr int GU_STAGES = 3;                          // gate/up: 2 tile pairs in flight per wave
+constexpr int gemv_stages() { return 2; }
+constexpr int GU_STAGES = 2;
 
 // ---- qkv projection ----------------------------------------------------------------------
 
