@@ -483,20 +483,22 @@ __global__ __launch_bounds__(GEMV_THREADS) void down_kernel(DownArgs a) {
 // than the extra loads gain; 16 streams per block, two blocks per CU, already keep 32
 // keys (32 KB) in flight per CU.
 constexpr int ATTN_KV_STAGES = 2;
+constexpr int ATTN_WAVES = ATTN_THREADS / 64;
+constexpr int ATTN_STREAMS = 4 * ATTN_WAVES;                        // 16-lane key streams per block
 constexpr int ATTN_SSQ_REGS = ATTN_SSQ_MAX_BLOCKS / ATTN_THREADS;   // sums-of-squares partials per thread
 constexpr int ATTN_QF_REGS = 8 * 128 / ATTN_THREADS;                 // query values per thread (G <= 8)
 
 // FUSED: q/k/v come raw from the qkv projection (norm, rotary and KV append here);
 // otherwise q is final and the cache already holds the new key.
 template <int G, bool FUSED>
-__global__ __launch_bounds__(ATTN_THREADS, G <= 5 ? 2 : 1) void attn_kernel(AttnFusedArgs a) {
+__global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) void attn_kernel(AttnFusedArgs a) {
     constexpr int D = 128;
     __shared__ float s_q[G][D];
     __shared__ float s_kn[D], s_vn[D];
     __shared__ float s_cos[64], s_sin[64];
     __shared__ float red[16];
-    __shared__ float s_wm[4][G], s_wl[4][G];
-    __shared__ float s_wacc[4][G][D];
+    __shared__ float s_wm[ATTN_WAVES][G], s_wl[ATTN_WAVES][G];
+    __shared__ float s_wacc[ATTN_WAVES][G][D];
     const int s = blockIdx.x, kv = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane & 15, grp = lane >> 4;
@@ -577,7 +579,7 @@ __global__ __launch_bounds__(ATTN_THREADS, G <= 5 ? 2 : 1) void attn_kernel(Attn
     // during the prologue
     float4 rk[ATTN_KV_STAGES][2], rv[ATTN_KV_STAGES][2];
 #pragma unroll
-    for (int k = 0; k < ATTN_KV_STAGES - 1; k++) load_kv(stream + 16 * k, rk[k][0], rk[k][1], rv[k][0], rv[k][1]);
+    for (int k = 0; k < ATTN_KV_STAGES - 1; k++) load_kv(stream + ATTN_STREAMS * k, rk[k][0], rk[k][1], rv[k][0], rv[k][1]);
     // (keys past the stream's last one are clamped loads of valid rows, never consumed)
 
     if (FUSED) {
@@ -655,16 +657,16 @@ __global__ __launch_bounds__(ATTN_THREADS, G <= 5 ? 2 : 1) void attn_kernel(Attn
 #pragma unroll
         for (int i = 0; i < 8; i++) acc[h][i] = 0.f;
     }
-    // This stream's keys are stream, stream+16, ... (< cnt): nks of them. The ring holds
+    // This stream's keys are stream, stream + ATTN_STREAMS, ... (< cnt): nks of them. The ring holds
     // ATTN_KV_STAGES keys; each step loads the key ATTN_KV_STAGES-1 ahead and consumes
     // the oldest. Whole groups of ATTN_KV_STAGES keys run with unconditional (clamped)
     // loads so that the compiler's wait counting stays exact; the remainder is already
     // loaded. The new token's key and value come from LDS (the cache write above may
     // still be in flight).
     constexpr int NS = ATTN_KV_STAGES;
-    const int nks = cnt > stream ? (cnt - stream + 15) / 16 : 0;
+    const int nks = cnt > stream ? (cnt - stream + ATTN_STREAMS - 1) / ATTN_STREAMS : 0;
     auto consume = [&](int slot, int idx) {
-        const int j = k0 + stream + 16 * idx;
+        const int j = k0 + stream + ATTN_STREAMS * idx;
         float kx[8] = {rk[slot][0].x, rk[slot][0].y, rk[slot][0].z, rk[slot][0].w,
                        rk[slot][1].x, rk[slot][1].y, rk[slot][1].z, rk[slot][1].w};
         float vx[8] = {rv[slot][0].x, rv[slot][0].y, rv[slot][0].z, rv[slot][0].w,
@@ -696,7 +698,8 @@ __global__ __launch_bounds__(ATTN_THREADS, G <= 5 ? 2 : 1) void attn_kernel(Attn
 #pragma unroll
         for (int k = 0; k < NS; k++) {
             const int slot = (k + NS - 1) % NS;
-            load_kv(stream + 16 * min(ik + k + NS - 1, nks - 1), rk[slot][0], rk[slot][1], rv[slot][0], rv[slot][1]);
+            load_kv(stream + ATTN_STREAMS * min(ik + k + NS - 1, nks - 1), rk[slot][0], rk[slot][1], rv[slot][0],
+                    rv[slot][1]);
             __builtin_amdgcn_sched_barrier(0);
             consume(k, ik + k);
         }
@@ -732,10 +735,12 @@ __global__ __launch_bounds__(ATTN_THREADS, G <= 5 ? 2 : 1) void attn_kernel(Attn
     // combine the four waves and write the split partial
     for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
         const int h = t / D, dd = t % D;
-        float M = fmaxf(fmaxf(s_wm[0][h], s_wm[1][h]), fmaxf(s_wm[2][h], s_wm[3][h]));
+        float M = s_wm[0][h];
+#pragma unroll
+        for (int w = 1; w < ATTN_WAVES; w++) M = fmaxf(M, s_wm[w][h]);
         float l = 0.f, o = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; w++) {
+        for (int w = 0; w < ATTN_WAVES; w++) {
             const float e = (s_wm[w][h] == -INFINITY) ? 0.f : __expf(s_wm[w][h] - M);
             l = fmaf(s_wl[w][h], e, l);
             o = fmaf(s_wacc[w][h][dd], e, o);
@@ -1068,9 +1073,12 @@ int launch_down(const DownArgs& a0, const GemvShape& s, hipStream_t st) {
     GEMV_DISPATCH5(down_kernel, dim3(s.blocks, s.S), planes_lds_bytes(s.CW), st, a);
 }
 
+// Key splits per KV head: at least 64 keys each, and at most one block per CU over the
+// KV heads (more, smaller blocks measured slower: 512 blocks of 4 waves lost to 256).
+constexpr int ATTN_GRID_BLOCKS = 256;
 int attn_splits(int64_t maxkeys, int Hkv) {
     int64_t S = (maxkeys + 63) / 64;
-    const int64_t cap = std::max(1, (512 + Hkv - 1) / Hkv);
+    const int64_t cap = std::max(1, (ATTN_GRID_BLOCKS + Hkv - 1) / Hkv);
     if (S > cap) S = cap;
     if (S < 1) S = 1;
     return (int)S;
