@@ -765,8 +765,8 @@ __global__ __launch_bounds__(128) void merge_kernel(MergeArgs a) {
     const int h = blockIdx.x, d = threadIdx.x;
     const float* p = a.part + (size_t)h * a.S * ATTN_PART_F;
     // up to MERGE_REG_S split accumulators are loaded at once, in flight while the
-    // maxima are reduced
-    constexpr int MERGE_REG_S = 64;
+    // maxima are reduced (32: the split count of 8 KV heads at one block per CU)
+    constexpr int MERGE_REG_S = 32;
     const bool in_regs = a.S <= MERGE_REG_S;
     float accv[MERGE_REG_S];
     if (in_regs) {
