@@ -97,6 +97,65 @@ def test_decode_step_tiny_stack_with_head():
     assert int(am.item()) == ref["argmax"]
 
 
+def test_decode_steps_replay_from_a_hip_graph():
+    """One decode step (positions and token in device memory) captured into a HIP graph
+    replays a token-by-token decode: three replays, with eager work and synchronisation
+    between them, give bit-for-bit the logits, argmax and KV slots of three eager steps
+    (the step is deterministic: no atomics, fixed reduction orders)."""
+    dev = device()
+    wl = _tiny_stack()
+    announce("decode tiny 4-layer stack: eager steps vs HIP graph replays")
+    dm = build_model(wl, dev)
+    m = wl.model
+    tok = torch.tensor([R.decode_token(wl)], dtype=torch.int32, device=dev)
+    pos = torch.tensor([wl.n_cached], dtype=torch.int32, device=dev)
+    logits = torch.empty(m.vocab, dtype=torch.float32, device=dev)
+    ws = _ws(dm, dev)
+    cm = dm.c()
+    caches = [(L.k_cache.clone(), L.v_cache.clone()) for L in dm.layers]
+    tok0, pos0 = tok.clone(), pos.clone()
+
+    def step():
+        ops.atlas_decode_step(dm, pos, d_token=tok, logits=logits, argmax=tok, ws=ws, cm=cm)
+        pos.add_(1)
+
+    def restore():
+        for L, (k, v) in zip(dm.layers, caches):
+            L.k_cache.copy_(k)
+            L.v_cache.copy_(v)
+        tok.copy_(tok0)
+        pos.copy_(pos0)
+
+    eager = []
+    for _ in range(3):
+        step()
+        eager.append((logits.clone(), tok.clone()))
+    kv_eager = [L.k_cache[:, wl.n_cached:wl.n_cached + 3].clone() for L in dm.layers]
+    torch.cuda.synchronize()
+
+    restore()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                  # warm-up on the capture stream's pool
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    restore()
+    torch.cuda.synchronize()
+    for i in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(logits, eager[i][0]), f"replay {i}: logits"
+        assert torch.equal(tok, eager[i][1]), f"replay {i}: argmax"
+        assert int(pos.item()) == wl.n_cached + i + 1
+    for L, k in zip(dm.layers, kv_eager):
+        assert torch.equal(L.k_cache[:, wl.n_cached:wl.n_cached + 3], k)
+    assert ops.atlas_device_status(ws) == 0
+
+
 def test_bad_position_sets_status_and_leaves_cache():
     dev = device()
     wl = _tiny_stack(n_layers=1)
