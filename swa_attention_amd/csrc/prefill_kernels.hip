@@ -356,7 +356,8 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
     __shared__ float sK[16 * KP];
     __shared__ float sV[16 * VP];
     __shared__ float sP[G][16 * 17];
-    const int t0 = blockIdx.x * PF_QT, kv = blockIdx.y;
+    // longest query tiles (most causal keys) first, so that they start before the short ones
+    const int t0 = (gridDim.x - 1 - blockIdx.x) * PF_QT, kv = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, l4 = lane >> 4;
