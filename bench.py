@@ -8,9 +8,13 @@ token at position 16,384 (SWA layers read the last 4,096 keys, full layers all
 feeds back the previous step's argmax token. Inputs are seeded synthetic values
 resident in HBM before timing starts.
 
-Prints one JSON line: tokens/s, ms/step, achieved algorithmic HBM GB/s of the step,
-the roofline of the dominant kernel (the gate/up W4 GEMV) measured with HIP events
-on the launch stream, and the CPU oracle's throughput on a bounded sample.
+The timed steps replay one step captured in a HIP graph (the position and token live
+in device memory); HIP events between the replays give the per-step median, p10 and
+p90. Prints one JSON line: tokens/s, ms/step, achieved algorithmic HBM GB/s of the
+step, the roofline of the dominant kernel (the gate/up W4 GEMV) measured with
+dispatch-stamped HIP events on the launch stream, the read bandwidth a plain
+streaming kernel reaches on the same device, the 1,200-token prefill, and the CPU
+oracle's throughput on a bounded sample (all host threads and one thread).
 """
 import argparse
 import json
@@ -48,7 +52,37 @@ def measured_traffic():
     return rec["bytes_per_launch"] if h.hexdigest()[:16] == rec["source_sha256_16"] else None
 
 
-def cpu_baseline(wl, budget_s):
+def host_info():
+    """CPU model, logical CPUs and RAM of the host that runs the oracle."""
+    model, ram = "unknown", 0.0
+    try:
+        model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+        ram = next(int(l.split()[1]) for l in open("/proc/meminfo") if l.startswith("MemTotal")) / 2**20
+    except (OSError, StopIteration):
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "ram_GiB": round(ram, 1)}
+
+
+def oracle_block_seconds(config, n_blocks):
+    """Seconds of oracle compute for the first n_blocks [SWA,SWA,SWA,full] blocks of a
+    workload's decode step (inputs generated outside the timed region)."""
+    import oracle as O
+    from oracle import runner as R
+    from synth import workloads as W
+    wl = W.config(config)
+    m = wl.model
+    x = O.embed(W.embedding_rows(m, wl.seed, R.decode_token(wl), 1)[0])
+    t = 0.0
+    for l in range(4 * n_blocks):
+        T, Kc, Vc = R.layer_inputs(wl, l)
+        t0 = time.perf_counter()
+        x = O.layer_step(m, m.layer_types[l], T, x, Kc, Vc, wl.n_cached)
+        t += time.perf_counter() - t0
+        del T, Kc, Vc
+    return t
+
+
+def cpu_baseline(wl, budget_s, config):
     """Oracle (CPU, double accumulation, OpenMP) on whole [SWA,SWA,SWA,full] blocks of
     the same workload until ~budget_s of compute, plus the lm_head; extrapolated to
     the 64-layer token. Input generation is not timed."""
@@ -78,8 +112,25 @@ def cpu_baseline(wl, budget_s):
     sample = (f"{n_done} of {m.n_layers} layers ({n_done // 4} [SWA,SWA,SWA,full] blocks at 16,384 cached) "
               f"+ final norm + bf16 lm_head, timed {t_layers + t_head:.1f} s, extrapolated x{m.n_layers / n_done:g} "
               f"over layers")
-    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": threads, "kind": "oracle", "sample": sample,
-            "s_per_token": per_token}
+    out = {"value": 1.0 / per_token, "unit": "tokens/s", "cores": threads, "kind": "oracle", "sample": sample,
+           "s_per_token": per_token, "host": host_info()}
+    # the same oracle on one thread: one [SWA,SWA,SWA,full] block in a child process
+    # started with OMP_NUM_THREADS=1, scaled like the layers above (the head's share
+    # scaled by the same thread ratio as the layers)
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    try:
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-block-seconds", str(config)],
+                           env=env, capture_output=True, text=True, timeout=600)
+        t1 = float(r.stdout.strip().splitlines()[-1])
+        t_multi = t_layers * 4 / n_done
+        per_token_1 = t1 * m.n_layers / 4 + t_head * t1 / t_multi
+        out["single_thread"] = {"value": 1.0 / per_token_1, "unit": "tokens/s", "cores": 1,
+                                "sample": f"one [SWA,SWA,SWA,full] block at 16,384 cached, timed {t1:.1f} s, "
+                                          f"extrapolated x{m.n_layers // 4} over layers (head scaled alike)"}
+    except (subprocess.SubprocessError, ValueError, IndexError) as e:
+        log(f"single-thread oracle leg failed: {e}")
+    return out
 
 
 PEAK_BF16_TFLOPS = 2500.0
@@ -136,7 +187,7 @@ def measure_prefill(args, dm, cm, m, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, help="workload config (3 = 64-layer 16K decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -144,10 +195,17 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=3)
     ap.add_argument("--no-prefill", action="store_true", help="skip the 1,200-token prefill measurement")
     ap.add_argument("--prefill-reps", type=int, default=3)
+    ap.add_argument("--eager", action="store_true", help="time eager steps instead of HIP graph replays")
+    ap.add_argument("--stream-probe-gib", type=float, default=2.0,
+                    help="buffer size of the plain read-bandwidth probe (0 to skip)")
+    ap.add_argument("--oracle-block-seconds", type=int, default=None, help=argparse.SUPPRESS)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (3 times); its HBM counters "
                          "calibrate the FETCH_SIZE/WRITE_SIZE readings of the decode kernels")
     args = ap.parse_args()
+    if args.oracle_block_seconds is not None:   # the single-thread oracle leg (a child process)
+        print(oracle_block_seconds(args.oracle_block_seconds, 1))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
               "How the step would shard over several GPUs is described in DESIGN.md.", file=sys.stderr)
@@ -187,13 +245,36 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
+    run = step
+    if not args.eager:
+        # capture one step (warmed up on the capture stream first); replays run on the
+        # current stream like eager steps
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        run = graph.replay
+    log(f"timing {args.steps} steps ({'eager' if args.eager else 'HIP graph replays'})")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    evs[0].record()
+    for i in range(args.steps):
+        run()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms = dt * 1e3 / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    pct = lambda q: per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
+    step_ms = {"median": round(pct(0.5), 4), "p10": round(pct(0.1), 4), "p90": round(pct(0.9), 4)}
     assert ops.atlas_device_status(ws) == 0
 
     # per-launch timing pass: each dispatch stamps a start and a stop hipEvent on its stream
@@ -219,6 +300,27 @@ def main():
                 "kernel": f"gate_up_kernel (2 x {m.dff}x{m.d} W4 + SwiGLU)", "bytes_per_launch": per_launch,
                 "avg_launch_us": round(avg_s * 1e6, 2), "launches": cnt}
 
+    stream = None
+    if args.stream_probe_gib > 0:
+        nbytes = int(args.stream_probe_gib * 2**30) // 16 * 16
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        best = None
+        for blocks in (256, 512, 1024, 2048):
+            ops.atlas_stream_read(buf, blocks, sink)
+            ops.atlas_profile_start(64)
+            for _ in range(5):
+                ops.atlas_stream_read(buf, blocks, sink)
+            cnt, tot = ops.atlas_profile_stop()["stream_read"]
+            g = nbytes / (tot / cnt * 1e-3) / 1e9
+            if best is None or g > best[0]:
+                best = (g, blocks)
+        del buf, sink
+        stream = {"GBps": round(best[0], 1), "frac_of_peak": round(best[0] / PEAK_HBM_GBPS, 4), "bytes": nbytes,
+                  "blocks": best[1], "kernel": "stream_read_kernel (plain grid-stride read, 4 x 16 B in flight "
+                                               "per thread; best of 256-2,048 blocks)"}
+        log(f"plain read probe: {best[0]:.0f} GB/s with {best[1]} blocks")
+
     prefill = None
     if not args.no_prefill and head and wl.use_tokens:
         prefill = measure_prefill(args, dm, cm, m, dev)
@@ -236,7 +338,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("CPU oracle baseline (bounded sample)")
-        cpu = cpu_baseline(wl, args.cpu_budget)
+        cpu = cpu_baseline(wl, args.cpu_budget, args.config)
 
     out = {
         "metric": "decode tokens/s at batch 1, 32B W4, 16K ctx + achieved HBM GB/s vs peak",
@@ -246,6 +348,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms": step_ms,
+        "timing": "eager steps" if args.eager else "HIP graph replays of one captured step",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -257,6 +361,7 @@ def main():
         "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "bytes_per_step": sb.total,
         "roofline": roof,
+        "achievable_read": stream,
         "cpu_baseline": cpu,
         "prefill": prefill,
     }

@@ -210,6 +210,17 @@ ATLAS_API size_t atlas_prefill_workspace_bytes(const atlas_model* m, int32_t n_t
 ATLAS_API int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int32_t n_tokens, int32_t start_pos,
                   float* d_last_logits, int32_t* d_argmax, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- read-bandwidth probe (measurement aid) -------------------------------------------
+ * Reads `bytes` (a positive multiple of 16) of the device buffer d_buf (16-byte
+ * aligned) with a plain grid-stride streaming kernel of `blocks` blocks (1..65536) of
+ * 256 threads, and nothing else: the achievable read bandwidth that the decode
+ * kernels are compared with beside the device's peak. d_sink: one device uint32 that
+ * is written only in the rare case that the XOR of all words read equals a fixed
+ * sentinel. Asynchronous on `stream`; timed like any launch by atlas_profile_*
+ * (label "stream_read"). ATLAS_ERR_INVALID_ARG on a null pointer, misaligned buffer,
+ * bad size or block count. */
+ATLAS_API int atlas_stream_read(const void* d_buf, size_t bytes, uint32_t* d_sink, int32_t blocks, void* stream);
+
 /* ---- launch timing (measurement aid) -------------------------------------------------
  * Between atlas_profile_start(capacity) and atlas_profile_stop(), every kernel launch
  * of the library (at most `capacity` launches) carries a start and a stop hipEvent

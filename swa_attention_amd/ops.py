@@ -221,6 +221,20 @@ def atlas_prefill(m: Model, d_tokens, start_pos=0, logits=None, argmax=None, ws=
            L.ptr(argmax), L.ptr(ws), 0 if ws is None else ws.numel(), L.stream_ptr(stream))
 
 
+# ---- read-bandwidth probe (measurement aid) ------------------------------------------------------
+
+def atlas_stream_read(buf, blocks=512, sink=None, stream=None):
+    """Plain streaming read of the device tensor `buf` (its bytes, a multiple of 16) by
+    `blocks` blocks of 256 threads; returns the one-word sink."""
+    if not buf.is_cuda:
+        raise ValueError("buf must be a device tensor")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    L.call("atlas_stream_read", L.ptr(buf), buf.numel() * buf.element_size(), L.ptr(sink), blocks,
+           L.stream_ptr(stream))
+    return sink
+
+
 # ---- launch timing -------------------------------------------------------------------------------
 
 def atlas_profile_start(capacity=100000):

@@ -33,6 +33,19 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(syms) == set(L.exported_symbols())
 
 
+def test_stream_read_validation(lib):
+    def sr(buf=FAKE, n=1 << 20, sink=FAKE, blocks=512):
+        return lib.atlas_stream_read(buf, n, sink, blocks, None)
+    assert sr(buf=None) == L.ATLAS_ERR_INVALID_ARG
+    assert sr(sink=None) == L.ATLAS_ERR_INVALID_ARG
+    assert sr(n=0) == L.ATLAS_ERR_INVALID_ARG
+    assert sr(n=100) == L.ATLAS_ERR_INVALID_ARG           # not a multiple of 16
+    assert sr(buf=FAKE + 8) == L.ATLAS_ERR_INVALID_ARG    # misaligned
+    assert sr(blocks=0) == L.ATLAS_ERR_INVALID_ARG
+    assert sr(blocks=70000) == L.ATLAS_ERR_INVALID_ARG
+    assert b"blocks" in lib.atlas_last_error()
+
+
 def test_version_and_status_strings(lib):
     assert b"gfx950" in lib.atlas_version()
     assert lib.atlas_status_string(0) == b"ok"
@@ -120,6 +133,9 @@ def test_decode_step_validation(lib):
         L.ATLAS_ERR_UNSUPPORTED_SHAPE
     bad, keep4 = _fake_model(hd=64)
     assert lib.atlas_decode_workspace_bytes(ctypes.byref(bad)) == 0
+    wide, keep5 = _fake_model(d=6176, hq=1, hkv=1)          # the GEMV input vectors hold d <= 6144
+    assert step(ctypes.byref(wide), FAKE, None, FAKE, None, None, None, FAKE, need, None) == \
+        L.ATLAS_ERR_UNSUPPORTED_SHAPE
     pre = lib.atlas_prefill
     pneed = lib.atlas_prefill_workspace_bytes(ctypes.byref(mm), 8)
     assert pneed > 0
