@@ -14,13 +14,15 @@
 //     adds it to the output scaled by the group's scale;
 //   - QK RMSNorm, rotary embedding and the KV write run one block per position;
 //   - causal (windowed) GQA attention runs per (16 positions, KV head) with the
-//     query heads of the group in separate waves, on f32 MFMA (16x16x4);
+//     query heads of the group in separate waves, on bf16 MFMA with hi/lo operands
+//     (hi*hi + hi*lo + lo*hi: about 2^-16 relative per product);
 //   - the post-attention and post-MLP residual norms run one block per position.
 #include "prefill_kernels.h"
 
 namespace atlas {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));   // four bf16 (operand of the 16x16x16 MFMA)
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
@@ -344,18 +346,22 @@ __global__ __launch_bounds__(256) void pf_split_kernel(const float* X, int K, in
 // ---- causal GQA attention over a block of 16 positions ------------------------------------
 //
 // grid (ceil(n / 16), Hkv), one wave per query head of the KV group. Keys come in
-// tiles of 16 through LDS (shared by the group's heads). Per wave: S (16 positions x
-// 16 keys) = Q K^T on f32 MFMA over the 128 dimensions, masked to each position's
-// window, online softmax per position, O += P V on f32 MFMA (P re-laid out through
-// LDS). The output is written as bf16 planes for the o projection.
+// tiles of 16 through LDS (shared by the group's heads): K as bf16 hi/lo planes, V the
+// same but transposed ([dim][key]). Per wave: S (16 positions x 16 keys) = Q K^T over
+// the 128 dimensions on 16x16x32 bf16 MFMAs, masked to each position's window, online
+// softmax per position, O += P V on 16x16x16 bf16 MFMAs (P re-laid out through LDS);
+// each product is hi*hi + hi*lo + lo*hi of the split operands. The output is written
+// as bf16 planes for the o projection.
 constexpr int PF_QT = 16;
 
 template <int G>
 __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
-    constexpr int D = 128, KP = D + 4, VP = D + 16;
-    __shared__ float sK[16 * KP];
-    __shared__ float sV[16 * VP];
-    __shared__ float sP[G][16 * 17];
+    constexpr int D = 128, KPB = D + 8, VTP = 16 + 4, PP = 20;
+    __shared__ __align__(16) uint16_t sKh[16 * KPB];   // keys as bf16 planes: K = hi + lo
+    __shared__ __align__(16) uint16_t sKl[16 * KPB];
+    __shared__ __align__(16) uint16_t sVth[D * VTP];   // values transposed ([dim][key]) as bf16 planes
+    __shared__ __align__(16) uint16_t sVtl[D * VTP];
+    __shared__ __align__(16) float sP[G][16 * PP];
     // longest query tiles (most causal keys) first, so that they start before the short ones
     const int t0 = (gridDim.x - 1 - blockIdx.x) * PF_QT, kv = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -367,12 +373,28 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
     const int klo = a.window > 0 ? max(0, p_first - a.window + 1) : 0;
     const int khi = p_last;
 
-    // Q fragments: lane holds Q[position t0 + l16][4 s + l4], s < 32 (A operand layout)
-    float qf[32];
+    // Q fragments as bf16 planes (Q = hi + lo): lane holds Q[position t0 + l16][32 ks + 8 l4 + i],
+    // i < 8, for the k-step ks of 32 dims (A operand layout of the 16x16x32 bf16 MFMA)
+    bf16x8_t qh[4], ql[4];
     {
-        const float* q = a.qkv + (size_t)min(t0 + l16, a.n - 1) * a.ld_qkv + head * D;
+        const float4* q = reinterpret_cast<const float4*>(a.qkv + (size_t)min(t0 + l16, a.n - 1) * a.ld_qkv + head * D);
 #pragma unroll
-        for (int s = 0; s < 32; s++) qf[s] = q[4 * s + l4];
+        for (int ks = 0; ks < 4; ks++) {
+            const float4 u = q[8 * ks + 2 * l4], v = q[8 * ks + 2 * l4 + 1];
+            uint32_t h[8], lo[8];
+            pf_split(u.x, h[0], lo[0]);
+            pf_split(u.y, h[1], lo[1]);
+            pf_split(u.z, h[2], lo[2]);
+            pf_split(u.w, h[3], lo[3]);
+            pf_split(v.x, h[4], lo[4]);
+            pf_split(v.y, h[5], lo[5]);
+            pf_split(v.z, h[6], lo[6]);
+            pf_split(v.w, h[7], lo[7]);
+            qh[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                                             h[6] | (h[7] << 16)));
+            ql[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
+                                                             lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)));
+        }
     }
     float m[4], l[4];
     f32x4_t o[8];
@@ -391,13 +413,35 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
         for (int u = tid; u < 16 * D / 4; u += blockDim.x) {
             const int kr = u / (D / 4), c = u % (D / 4);
             const size_t j = (size_t)min(kb + kr, khi);
-            *reinterpret_cast<float4*>(&sK[kr * KP + 4 * c]) = reinterpret_cast<const float4*>(Kh + j * D)[c];
-            *reinterpret_cast<float4*>(&sV[kr * VP + 4 * c]) = reinterpret_cast<const float4*>(Vh + j * D)[c];
+            const float4 k4 = reinterpret_cast<const float4*>(Kh + j * D)[c];
+            uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+            pf_split(k4.x, h0, l0);
+            pf_split(k4.y, h1, l1);
+            pf_split(k4.z, h2, l2);
+            pf_split(k4.w, h3, l3);
+            *reinterpret_cast<uint2*>(&sKh[kr * KPB + 4 * c]) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+            *reinterpret_cast<uint2*>(&sKl[kr * KPB + 4 * c]) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+            const float4 v4 = reinterpret_cast<const float4*>(Vh + j * D)[c];
+            const float ve[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                uint32_t vh, vl;
+                pf_split(ve[e], vh, vl);
+                sVth[(4 * c + e) * VTP + kr] = (uint16_t)vh;
+                sVtl[(4 * c + e) * VTP + kr] = (uint16_t)vl;
+            }
         }
         __syncthreads();
+        // scores Q K^T: hi*hi + hi*lo + lo*hi (the lo*lo term is below 2^-16 of the product)
         f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 32; s++) sc = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[s], sK[l16 * KP + 4 * s + l4], sc, 0, 0, 0);
+        for (int ks = 0; ks < 4; ks++) {
+            const bf16x8_t kh = *reinterpret_cast<const bf16x8_t*>(&sKh[l16 * KPB + 32 * ks + 8 * l4]);
+            const bf16x8_t kl = *reinterpret_cast<const bf16x8_t*>(&sKl[l16 * KPB + 32 * ks + 8 * l4]);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[ks], kh, sc, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[ks], kl, sc, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[ks], kh, sc, 0, 0, 0);
+        }
         // sc[r] = S[position 4 l4 + r][key kb + l16]
         const int j = kb + l16;
 #pragma unroll
@@ -418,15 +462,27 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
             m[r] = mn;
 #pragma unroll
             for (int gi = 0; gi < 8; gi++) o[gi][r] *= corr;
-            sP[wave][(4 * l4 + r) * 17 + l16] = p;
+            sP[wave][(4 * l4 + r) * PP + l16] = p;
         }
-        // O += P V: A operand P[position l16][key 4 s + l4], B operand V[key 4 s + l4][dim 16 gi + l16]
+        // O += P V on 16x16x16 bf16 MFMAs, hi*hi + hi*lo + lo*hi: A operand P[position l16][key
+        // 4 l4 + i], B operand V[key 4 l4 + i][dim 16 gi + l16] (four keys of one dim: a row of V^T)
+        {
+            const float4 pv = *reinterpret_cast<const float4*>(&sP[wave][l16 * PP + 4 * l4]);
+            uint32_t h0, q0, h1, q1, h2, q2, h3, q3;
+            pf_split(pv.x, h0, q0);
+            pf_split(pv.y, h1, q1);
+            pf_split(pv.z, h2, q2);
+            pf_split(pv.w, h3, q3);
+            const bf16x4_t ph = __builtin_bit_cast(bf16x4_t, make_uint2(h0 | (h1 << 16), h2 | (h3 << 16)));
+            const bf16x4_t pl = __builtin_bit_cast(bf16x4_t, make_uint2(q0 | (q1 << 16), q2 | (q3 << 16)));
 #pragma unroll
-        for (int s = 0; s < 4; s++) {
-            const float pa = sP[wave][l16 * 17 + 4 * s + l4];
-#pragma unroll
-            for (int gi = 0; gi < 8; gi++)
-                o[gi] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, sV[(4 * s + l4) * VP + 16 * gi + l16], o[gi], 0, 0, 0);
+            for (int gi = 0; gi < 8; gi++) {
+                const bf16x4_t vh = *reinterpret_cast<const bf16x4_t*>(&sVth[(16 * gi + l16) * VTP + 4 * l4]);
+                const bf16x4_t vl = *reinterpret_cast<const bf16x4_t*>(&sVtl[(16 * gi + l16) * VTP + 4 * l4]);
+                o[gi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vh, o[gi], 0, 0, 0);
+                o[gi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vl, o[gi], 0, 0, 0);
+                o[gi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vh, o[gi], 0, 0, 0);
+            }
         }
     }
     // o[gi][r] = O[position 4 l4 + r][dim 16 gi + l16]
