@@ -710,19 +710,12 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
     // combine the four streams of the wave (lanes l, l^16, l^32, l^48)
 #pragma unroll
     for (int h = 0; h < G; h++) {
-        float M = fmaxf(mh[h], __shfl_xor(mh[h], 16, 64));
-        M = fmaxf(M, __shfl_xor(M, 32, 64));
+        // lane-swap butterflies (v_permlane16/32_swap): register moves, not LDS permutes
+        const float M = xor32_max(xor16_max(mh[h]));
         const float w = (M == -INFINITY) ? 0.f : __expf(mh[h] - M);
-        float l = lh[h] * w;
-        l += __shfl_xor(l, 16, 64);
-        l += __shfl_xor(l, 32, 64);
+        const float l = xor32_sum(xor16_sum(lh[h] * w));
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-            float v = acc[h][e] * w;
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
-            acc[h][e] = v;
-        }
+        for (int e = 0; e < 8; e++) acc[h][e] = xor32_sum(xor16_sum(acc[h][e] * w));
         if (lane == 0) {
             s_wm[wave][h] = M;
             s_wl[wave][h] = l;
