@@ -293,10 +293,10 @@ def main():
         cnt, tot = prof[dom]
         avg_s = tot / cnt * 1e-3
         # one launch streams the gate and the up matrix ([dff][d] each)
-        per_launch = 2 * A.w4_bytes(m.dff, m.d, m.group)
+        per_launch = 2 * A.w4_bytes(m.dff, m.d, m.group, 2, not m.symmetric)
         ach = per_launch / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(),
+                "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": measured_traffic() if args.config == 3 else None,
                 "kernel": f"gate_up_kernel (2 x {m.dff}x{m.d} W4 + SwiGLU)", "bytes_per_launch": per_launch,
                 "avg_launch_us": round(avg_s * 1e6, 2), "launches": cnt}
 
@@ -356,7 +356,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "layers": m.n_layers, "context": wl.n_cached, "batch": 1,
-                   "weights": "int4 group-128, f16 scales, uint4 zeros", "kv": "f32", "lm_head": "bf16"},
+                   "weights": (f"int4 group-{m.group}, {'bf16' if m.scale_dtype else 'f16'} scales, "
+                               + ("symmetric (zero point 8)" if m.symmetric else "uint4 zeros")),
+                   "kv": "f32", "lm_head": "bf16"},
         "achieved_GBps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "bytes_per_step": sb.total,

@@ -204,7 +204,8 @@ def layer_step(model, layer_type, T, x, Kc, Vc, pos, trace=None):
     'g_q', 'g_k', 'g_pa', 'g_pf'). Kc, Vc: [hkv][T_max][hd] caches, updated in place
     at slot pos. Returns y; fills ``trace`` (a dict) with the intermediates."""
     hq, hkv, hd, d, g = model.hq, model.hkv, model.hd, model.d, model.group
-    qkv = w4_gemv(*T["qkv"], d, x, g)
+    sd = getattr(model, "scale_dtype", 0)
+    qkv = w4_gemv(*T["qkv"], d, x, g, sd)
     q, k, v = qkv[:hq * hd], qkv[hq * hd:(hq + hkv) * hd], qkv[(hq + hkv) * hd:]
     qn = rmsnorm(q, T["g_q"], model.eps)
     kn = rmsnorm(k, T["g_k"], model.eps)
@@ -215,12 +216,12 @@ def layer_step(model, layer_type, T, x, Kc, Vc, pos, trace=None):
     Vc[:, pos, :] = v.reshape(hkv, hd)
     window = model.window if layer_type != FULL else 0
     o = attention(qr, Kc, Vc, hq, hkv, hd, pos, window)
-    a = w4_gemv(*T["o"], hq * hd, o, g)
+    a = w4_gemv(*T["o"], hq * hd, o, g, sd)
     h = rmsnorm_residual(a, T["g_pa"], x, model.eps)
-    u = w4_gemv(*T["gate"], d, h, g)
-    vv = w4_gemv(*T["up"], d, h, g)
+    u = w4_gemv(*T["gate"], d, h, g, sd)
+    vv = w4_gemv(*T["up"], d, h, g, sd)
     z = swiglu(u, vv)
-    mm = w4_gemv(*T["down"], model.dff, z, g)
+    mm = w4_gemv(*T["down"], model.dff, z, g, sd)
     y = rmsnorm_residual(mm, T["g_pf"], h, model.eps)
     if trace is not None:
         trace.update(qkv=qkv, q=qr, k=kr, v=v, o=o, a=a, h=h, u=u, up=vv, z=z, m=mm, y=y)

@@ -17,7 +17,10 @@ def w4_bytes(N, K, group=128, scale_bytes=2, zeros=True):
 
 
 def layer_w4_bytes(m):
-    return sum(w4_bytes(N, K, m.group) for _, _, N, K in m.linears())
+    """W4 bytes of one layer in the model's format (bf16 and f16 scales are both two
+    bytes; a symmetric model has no zero table)."""
+    zeros = not getattr(m, "symmetric", False)
+    return sum(w4_bytes(N, K, m.group, 2, zeros) for _, _, N, K in m.linears())
 
 
 def layer_weight_count(m):

@@ -36,7 +36,7 @@ def layer_to_device(model, seed, layer, n_cached, t_max, device, tensors=None):
     ws = {}
     for name, kind, N, K in model.linears():
         c, s, z = T[name]
-        ws[name] = w4_to_device(c, s, z, K, device, model.group)
+        ws[name] = w4_to_device(c, s, z, K, device, model.group, model.scale_dtype)
     Kc = torch.zeros((model.hkv, t_max, model.hd), dtype=torch.float32, device=device)
     Vc = torch.zeros_like(Kc)
     if n_cached > 0:

@@ -46,6 +46,8 @@ class Model:
     eps: float = 1e-6
     vocab: int = 100278
     model_id: int = 0
+    scale_dtype: int = 0              # 0: f16 group scales, 1: bf16
+    symmetric: bool = False           # True: no zero table, every zero point is 8
 
     @property
     def n_qkv(self):
@@ -64,6 +66,13 @@ def olmo3_32b(model_id=3, n_layers=64):
     types = [FULL if (l % 4) == 3 else SWA for l in range(n_layers)]
     return Model(d=5120, hq=40, hkv=8, hd=128, dff=27648, n_layers=n_layers, layer_types=types,
                  model_id=model_id)
+
+
+def card_format(m):
+    """The card's own W4 recipe on model m: symmetric codes (zero point 8, no zero
+    table), group 32, bf16 scales."""
+    m.group, m.scale_dtype, m.symmetric = 32, 1, True
+    return m
 
 
 def tiny(model_id=0):
@@ -86,8 +95,10 @@ class Workload:
 
 
 def config(i):
-    """The five workload configurations (0: tiny layer, 1: SWA layer at 4,096 keys,
-    2: full layer at 16,385 keys with YaRN, 3: 64-layer step at 16K, 4: prefill)."""
+    """The workload configurations. 0: tiny layer, 1: SWA layer at 4,096 keys, 2: full
+    layer at 16,385 keys with YaRN, 3: 64-layer step at 16K, 4: prefill of 1,200 tokens;
+    5: config 3 and 6: config 1 in the card's own W4 recipe (symmetric, group 32, bf16
+    scales)."""
     if i == 0:
         return Workload("tiny-swa-layer", tiny(0), seed=0, n_cached=256, t_max=257)
     if i == 1:
@@ -104,6 +115,13 @@ def config(i):
     if i == 4:
         return Workload("olmo3-32b-w4-prefill-1200", olmo3_32b(3), seed=0, n_cached=0,
                         t_max=1200, use_tokens=True, final_head=True, prompt_len=1200)
+    if i == 5:
+        return Workload("olmo3-32b-w4sym-g32-decode-16k", card_format(olmo3_32b(5)), seed=0, n_cached=16384,
+                        t_max=16385, use_tokens=True, final_head=True)
+    if i == 6:
+        m = card_format(olmo3_32b(model_id=6, n_layers=1))
+        m.layer_types = [SWA]
+        return Workload("olmo3-32b-w4sym-g32-swa-layer-4k", m, seed=0, n_cached=4096, t_max=4097)
     raise ValueError(i)
 
 
@@ -119,12 +137,15 @@ def key(wl_or_model, seed, layer, kind):
 # ---- per-layer inputs --------------------------------------------------------
 
 def w4_linear(model, seed, layer, kind, N, K):
-    """Packed codes [N][K/8] u32, f16 scale bits [N][G] u16, packed zeros [N][ceil(G/8)] u32.
-    Codes and zeros ~ U{0..15}; scales ~ U(0.002, 0.02) rounded to f16."""
+    """Packed codes [N][K/8] u32, scale bits [N][G] u16 (f16, or bf16 when
+    model.scale_dtype == 1), packed zeros [N][ceil(G/8)] u32 (None when the model is
+    symmetric). Codes and zeros ~ U{0..15}; scales ~ U(0.002, 0.02) rounded to the
+    scale type."""
     G = -(-K // model.group)
     codes = S.codes(S.key(seed, tid(model, layer, kind)), N * K // 8).reshape(N, K // 8)
-    scales = S.uniform_f16(S.key(seed, tid(model, layer, kind + 1)), N * G, 0.002, 0.02).reshape(N, G)
-    zeros = S.zeros(S.key(seed, tid(model, layer, kind + 2)), N, G)
+    uni = S.uniform_bf16 if model.scale_dtype == 1 else S.uniform_f16
+    scales = uni(S.key(seed, tid(model, layer, kind + 1)), N * G, 0.002, 0.02).reshape(N, G)
+    zeros = None if model.symmetric else S.zeros(S.key(seed, tid(model, layer, kind + 2)), N, G)
     return codes, scales, zeros
 
 

@@ -69,8 +69,8 @@ def test_decode_step_full_layer_yarn_full_size():
     assert err < TOL, err
 
 
-def _tiny_stack(n_layers=4, vocab=1000, n_cached=80, t_max=128, window=64, model_id=7):
-    m = W.tiny(model_id)
+def _tiny_stack(n_layers=4, vocab=1000, n_cached=80, t_max=128, window=64, model_id=7, card=False):
+    m = W.card_format(W.tiny(model_id)) if card else W.tiny(model_id)
     m.n_layers = n_layers
     m.layer_types = [W.FULL if l % 4 == 3 else W.SWA for l in range(n_layers)]
     m.vocab = vocab
@@ -154,6 +154,34 @@ def test_decode_steps_replay_from_a_hip_graph():
     for L, k in zip(dm.layers, kv_eager):
         assert torch.equal(L.k_cache[:, wl.n_cached:wl.n_cached + 3], k)
     assert ops.atlas_device_status(ws) == 0
+
+
+def test_card_format_swa_layer_full_size():
+    """The card's own W4 recipe (symmetric codes, group 32, bf16 scales, no zero table) on
+    a full-size SWA layer at 4,096 cached keys, against the oracle."""
+    dev = device()
+    announce("decode OLMo-3-32B SWA layer in the card's W4 recipe (symmetric, group 32, bf16 scales)")
+    err = _run_layer_case(W.config(6), dev)
+    print("normwise", err)
+    assert err < TOL, err
+
+
+def test_card_format_tiny_stack_decode_and_prefill():
+    """The card's W4 recipe through a tiny 4-layer stack with the head: one decode step
+    and a 40-token prefill (group-32 GEMM path), both against the oracle."""
+    dev = device()
+    announce("card W4 recipe: tiny 4-layer stack, decode + 40-token prefill")
+    wl = _tiny_stack(model_id=9, card=True)
+    dm = build_model(wl, dev)
+    d_tok = torch.tensor([R.decode_token(wl)], dtype=torch.int32, device=dev)
+    pos = torch.tensor([wl.n_cached], dtype=torch.int32, device=dev)
+    logits = torch.empty(wl.model.vocab, dtype=torch.float32, device=dev)
+    am = torch.empty(1, dtype=torch.int32, device=dev)
+    ops.atlas_decode_step(dm, pos, d_token=d_tok, logits=logits, argmax=am, ws=_ws(dm, dev))
+    ref = R.run_decode(wl)
+    assert normwise(logits.cpu().numpy(), ref["logits"]) < TOL
+    assert int(am.item()) == ref["argmax"]
+    _prefill_vs_oracle(_tiny_stack(model_id=9, card=True, n_cached=0, t_max=64), 40, dev)
 
 
 def test_bad_position_sets_status_and_leaves_cache():

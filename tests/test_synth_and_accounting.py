@@ -136,3 +136,19 @@ def test_our_layout_bytes():
     assert sb.kv == 48 * 33_554_432 + 16 * 134_225_920
     assert sb.lm_head == 1_026_846_720
     assert abs(sb.total / 1e9 - 21.0) < 0.01
+
+
+def test_card_format_layer_bytes_and_generator():
+    """The card's own W4 recipe (symmetric codes, group 32, bf16 scales): 0.5625 bytes per
+    weight, 274,268,160 per full-size layer (the 274.3 MB of the scope table); the
+    generator gives bf16 scale bits inside the scale range and no zero table."""
+    m = W.card_format(W.olmo3_32b())
+    assert A.layer_weight_count(m) == 487_587_840
+    assert A.layer_w4_bytes(m) == 487_587_840 * 9 // 16 == 274_268_160
+    c, sc, z = W.w4_linear(m, 0, 0, W.K_O, 64, 5120)
+    assert z is None and c.shape == (64, 640) and sc.shape == (64, 160)
+    v = (sc.astype(np.uint32) << 16).view(np.float32)
+    assert v.min() >= 0.002 * (1 - 2 ** -8) and v.max() <= 0.02 * (1 + 2 ** -8)
+    wl = W.config(5)
+    assert wl.model.symmetric and wl.model.group == 32 and wl.model.scale_dtype == 1
+    assert A.decode_step_bytes(wl.model, 16384).w4 == 64 * 274_268_160
