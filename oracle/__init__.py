@@ -55,6 +55,8 @@ def lib():
         L.orc_yarn_attention_factor.argtypes = [f64]
         L.orc_rope.argtypes = [vp, ci, ci, i64, vp, f64]
         L.orc_attention.argtypes = [vp, vp, vp, ci, ci, ci, i64, i64, i64, f64, vp]
+        L.orc_attention_kv.argtypes = [vp, vp, vp, ci, i64, ci, ci, ci, ci, i64, i64, f64, vp]
+        L.orc_round_bf16.argtypes = [vp, i64, vp]
         L.orc_swiglu.argtypes = [vp, vp, i64, vp]
         L.orc_argmax.restype = i64
         L.orc_argmax.argtypes = [vp, i64]
@@ -154,12 +156,37 @@ def rope(x, H, D, pos, inv, mscale=1.0):
 
 
 def attention(q, Kc, Vc, Hq, Hkv, D, pos, window, scale=None):
-    q, Kc, Vc = _c(q, np.float32), _c(Kc, np.float32), _c(Vc, np.float32)
-    T_max = Kc.size // (Hkv * D)
+    """Attention over f32 caches [Hkv][T_max][D] with key j in slot j."""
+    return attention_kv(q, _c(Kc, np.float32), _c(Vc, np.float32), Hq, Hkv, D, pos, window, False, scale)
+
+
+def attention_kv(q, Kc, Vc, Hq, Hkv, D, pos, window, ring, scale=None):
+    """Attention over caches [Hkv][slots][D] in storage layout: f32, or bf16 bits
+    (uint16 arrays); key j in slot j mod slots when ``ring``, else in slot j."""
+    q = _c(q, np.float32)
+    dt = 1 if Kc.dtype == np.uint16 else 0
+    Kc, Vc = _c(Kc, Kc.dtype), _c(Vc, Vc.dtype)
+    if Vc.dtype != Kc.dtype:
+        raise ValueError("K and V caches must share a dtype")
+    slots = Kc.size // (Hkv * D)
+    if not ring and pos >= slots:
+        raise ValueError("position beyond the cache")
+    if ring and not (0 < window <= slots):
+        raise ValueError("a ring must hold the whole window")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     out = np.empty(Hq * D, np.float32)
-    lib().orc_attention(_p(q), _p(Kc), _p(Vc), Hq, Hkv, D, T_max, pos, window, scale, _p(out))
+    lib().orc_attention_kv(_p(q), _p(Kc), _p(Vc), dt, slots, int(bool(ring)), Hq, Hkv, D, pos, window, scale,
+                           _p(out))
+    return out
+
+
+def round_bf16(x):
+    """bfloat16 bits of f32 values, rounded to nearest even (the store into a bf16
+    KV cache)."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().orc_round_bf16(_p(x), x.size, _p(out))
     return out
 
 
@@ -201,10 +228,14 @@ def layer_step(model, layer_type, T, x, Kc, Vc, pos, trace=None):
     """One decoder layer for the token at position ``pos``.
 
     T: the layer's tensors (W4 triples 'qkv', 'o', 'gate', 'up', 'down'; gains
-    'g_q', 'g_k', 'g_pa', 'g_pf'). Kc, Vc: [hkv][T_max][hd] caches, updated in place
-    at slot pos. Returns y; fills ``trace`` (a dict) with the intermediates."""
+    'g_q', 'g_k', 'g_pa', 'g_pf'). Kc, Vc: [hkv][slots][hd] caches in the model's KV
+    format (f32, or bf16 bits when model.kv_dtype == 1; on a sliding-window layer of
+    a model with swa_ring, a ring of `window` slots), updated in place at the slot
+    of pos. Returns y; fills ``trace`` (a dict) with the intermediates."""
     hq, hkv, hd, d, g = model.hq, model.hkv, model.hd, model.d, model.group
     sd = getattr(model, "scale_dtype", 0)
+    kv_dtype = getattr(model, "kv_dtype", 0)
+    ring = bool(getattr(model, "swa_ring", False)) and layer_type != FULL and model.window > 0
     qkv = w4_gemv(*T["qkv"], d, x, g, sd)
     q, k, v = qkv[:hq * hd], qkv[hq * hd:(hq + hkv) * hd], qkv[(hq + hkv) * hd:]
     qn = rmsnorm(q, T["g_q"], model.eps)
@@ -212,10 +243,15 @@ def layer_step(model, layer_type, T, x, Kc, Vc, pos, trace=None):
     inv, m = rope_params(model, layer_type)
     qr = rope(qn, hq, hd, pos, inv, m)
     kr = rope(kn, hkv, hd, pos, inv, m)
-    Kc[:, pos, :] = kr.reshape(hkv, hd)
-    Vc[:, pos, :] = v.reshape(hkv, hd)
+    slot = pos % Kc.shape[1] if ring else pos
+    if kv_dtype == 1:
+        Kc[:, slot, :] = round_bf16(kr).reshape(hkv, hd)
+        Vc[:, slot, :] = round_bf16(v).reshape(hkv, hd)
+    else:
+        Kc[:, slot, :] = kr.reshape(hkv, hd)
+        Vc[:, slot, :] = v.reshape(hkv, hd)
     window = model.window if layer_type != FULL else 0
-    o = attention(qr, Kc, Vc, hq, hkv, hd, pos, window)
+    o = attention_kv(qr, Kc, Vc, hq, hkv, hd, pos, window, ring)
     a = w4_gemv(*T["o"], hq * hd, o, g, sd)
     h = rmsnorm_residual(a, T["g_pa"], x, model.eps)
     u = w4_gemv(*T["gate"], d, h, g, sd)

@@ -10,6 +10,9 @@
  * Precision policy: inputs and outputs of every operation are f32 (the pages run
  * f32 activations and an f32 KV cache); every sum, product chain, norm, angle and
  * softmax inside an operation is evaluated in double and rounded to f32 once.
+ * The card's roadmap also plans a bf16 KV cache that keeps only the window on the
+ * sliding-window layers ("Limitations & roadmap"); when that format is selected, a
+ * key or value is rounded to bfloat16 when it is stored and read back exactly.
  *
  * Sources (titles of the pages):
  *  - "ATLAS-OLMo-3-32B-Think-v4" model card: "Quantization recipe" (packing of
@@ -207,15 +210,29 @@ void orc_rope(float* x, int H, int D, int64_t pos, const double* inv, double msc
 
 /* ---- attention ------------------------------------------------------------ */
 
-/* GQA decode attention for one new token at position pos.
- * q: [Hq][D]; K, V caches: [Hkv][T_max][D], with slot pos already holding the new
- * key/value. Query head h reads KV head h / (Hq / Hkv). The keys attended are
- * j in [lo, pos] with lo = max(0, pos - window + 1) when window > 0 (the window
- * counts the current token) and lo = 0 for full attention (window == 0).
+/* Value of element i of a cache stored as f32 (kv_dtype 0) or as bfloat16 bits
+ * (kv_dtype 1: the upper half of a binary32 pattern, so the value is exact). */
+static inline double kv_at(const void* base, int kv_dtype, int64_t i) {
+    if (kv_dtype == 1) {
+        uint32_t b = (uint32_t)((const uint16_t*)base)[i] << 16;
+        float f;
+        memcpy(&f, &b, 4);
+        return (double)f;
+    }
+    return (double)((const float*)base)[i];
+}
+
+/* GQA decode attention for one new token at position pos, over a cache in its
+ * storage layout: K, V are [Hkv][slots][D] of f32 or bfloat16 (kv_dtype), and key j
+ * is stored in slot j mod slots when ring != 0 (a sliding-window layer that keeps only
+ * its window) and in slot j otherwise. Slot of pos already holds the new key/value.
+ * Query head h reads KV head h / (Hq / Hkv). The keys attended are j in [lo, pos]
+ * with lo = max(0, pos - window + 1) when window > 0 (the window counts the current
+ * token) and lo = 0 for full attention (window == 0).
  *   s_j = scale * q . k_j ;  p = softmax(s) (max-subtracted) ;  o = sum_j p_j v_j
  * out: [Hq][D]. Everything in double. */
-void orc_attention(const float* q, const float* K, const float* V, int Hq, int Hkv, int D,
-                   int64_t T_max, int64_t pos, int64_t window, double scale, float* out) {
+void orc_attention_kv(const float* q, const void* K, const void* V, int kv_dtype, int64_t slots, int ring, int Hq,
+                      int Hkv, int D, int64_t pos, int64_t window, double scale, float* out) {
     int64_t lo = window > 0 ? pos - window + 1 : 0;
     if (lo < 0) lo = 0;
     int64_t n = pos - lo + 1;
@@ -224,14 +241,15 @@ void orc_attention(const float* q, const float* K, const float* V, int Hq, int H
     for (int h = 0; h < Hq; h++) {
         int kv = h / grp;
         const float* qh = q + (int64_t)h * D;
-        const float* Kh = K + (int64_t)kv * T_max * D;
-        const float* Vh = V + (int64_t)kv * T_max * D;
         double* s = (double*)malloc(sizeof(double) * (size_t)n);
+        int64_t* row = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);   /* element offset of key lo + t */
         double mx = -INFINITY;
         for (int64_t t = 0; t < n; t++) {
-            const float* kj = Kh + (lo + t) * D;
+            int64_t j = lo + t;
+            int64_t slot = ring ? j % slots : j;
+            row[t] = ((int64_t)kv * slots + slot) * D;
             double dot = 0.0;
-            for (int d = 0; d < D; d++) dot += (double)qh[d] * (double)kj[d];
+            for (int d = 0; d < D; d++) dot += (double)qh[d] * kv_at(K, kv_dtype, row[t] + d);
             s[t] = dot * scale;
             if (s[t] > mx) mx = s[t];
         }
@@ -242,10 +260,37 @@ void orc_attention(const float* q, const float* K, const float* V, int Hq, int H
         }
         for (int d = 0; d < D; d++) {
             double acc = 0.0;
-            for (int64_t t = 0; t < n; t++) acc += s[t] * (double)Vh[(lo + t) * D + d];
+            for (int64_t t = 0; t < n; t++) acc += s[t] * kv_at(V, kv_dtype, row[t] + d);
             out[(int64_t)h * D + d] = (float)(acc / den);
         }
+        free(row);
         free(s);
+    }
+}
+
+/* The same over an f32 cache [Hkv][T_max][D] with key j in slot j. */
+void orc_attention(const float* q, const float* K, const float* V, int Hq, int Hkv, int D, int64_t T_max,
+                   int64_t pos, int64_t window, double scale, float* out) {
+    orc_attention_kv(q, K, V, 0, T_max, 0, Hq, Hkv, D, pos, window, scale, out);
+}
+
+/* Storing an f32 value in a bfloat16 cache: round to nearest, ties to even. The
+ * upper 16 bits of the binary32 pattern are kept; one unit in their last place is
+ * added when the dropped lower 16 bits exceed half a unit, or equal half a unit and
+ * the kept pattern is odd. A carry out of the significand moves into the exponent,
+ * so values beyond the largest bfloat16 become infinity. A NaN stays a (quiet) NaN
+ * with its sign. */
+void orc_round_bf16(const float* x, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; i++) {
+        uint32_t b;
+        memcpy(&b, &x[i], 4);
+        if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x007FFFFFu)) {
+            out[i] = (uint16_t)((b >> 16) | 0x0040u);
+            continue;
+        }
+        uint32_t keep = b >> 16, rest = b & 0xFFFFu;
+        if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1;
+        out[i] = (uint16_t)keep;
     }
 }
 

@@ -44,6 +44,7 @@ def lib():
         L.synth_uniform_bf16.argtypes = [u64, i64, f64, f64, vp]
         L.synth_normal_f32_3d.argtypes = [u64, i64, i64, i64, i64, i64, f32, f32, vp]
         L.synth_normal_f32.argtypes = [u64, i64, f32, f32, vp]
+        L.synth_normal_kv.argtypes = [u64, i64, i64, i64, i64, i64, ctypes.c_int, f32, f32, vp]
         L.synth_normal_bf16_rows.argtypes = [u64, i64, i64, i64, f32, f32, vp]
         L.synth_tokens.argtypes = [u64, i64, i64, vp]
         L.synth_raw.argtypes = [u64, i64, vp]
@@ -113,6 +114,15 @@ def uniform_bf16(k, n, a, b):
 def normal_f32_3d_into(k, A, B, C, sa, sb, mu, sigma, dst):
     need = 4 * ((A - 1) * sa + (B - 1) * sb + C) if A and B and C else 0
     lib().synth_normal_f32_3d(k, A, B, C, sa, sb, mu, sigma, _ptr(dst, need))
+
+
+def normal_kv_into(k, A, B, C, j0, slots, dtype, mu, sigma, dst):
+    """Positions [j0, B) of an [A][B][C] N(mu, sigma) stream into slot j mod slots of
+    dst ([A][slots][C], f32 for dtype 0, bf16 bits for dtype 1); see synth.c."""
+    if not (0 <= j0 <= B and slots >= 1 and (B - j0) <= slots):
+        raise ValueError("positions do not fit the slots")
+    need = A * slots * C * (2 if dtype == 1 else 4)
+    lib().synth_normal_kv(k, A, B, C, j0, slots, dtype, mu, sigma, _ptr(dst, need))
 
 
 def normal_f32(k, n, mu=0.0, sigma=1.0):

@@ -147,6 +147,30 @@ void synth_normal_f32_3d(uint64_t key, int64_t A, int64_t B, int64_t C, int64_t 
     }
 }
 
+/* One layer's K or V cache in its storage layout. Element (a, j, c) of the N(mu, sigma)
+ * stream has the value index of synth_normal_f32_3d with B positions, (a*B + j)*C + c,
+ * so a position's values do not depend on the layout. Positions j in [j0, B) land in
+ * slot j mod slots of head a, out[(a*slots + j mod slots)*C + c], as f32 (dtype 0) or
+ * as bf16 bits rounded to nearest even (dtype 1). A flat cache is slots >= B, j0 = 0;
+ * a ring of W slots holding the last W positions is slots = W, j0 = max(0, B - W). */
+void synth_normal_kv(uint64_t key, int64_t A, int64_t B, int64_t C, int64_t j0, int64_t slots, int dtype,
+                     float mu, float sigma, void* out) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t a = 0; a < A; a++) {
+        for (int64_t j = j0; j < B; j++) {
+            const int64_t o = (a * slots + j % slots) * C;
+            const uint64_t base = (uint64_t)((a * B + j) * C);
+            for (int64_t c = 0; c < C; c++) {
+                float v = mu + sigma * irwin_hall12(key, base + (uint64_t)c);
+                if (dtype == 1)
+                    ((uint16_t*)out)[o + c] = f32_to_bf16_rne(v);
+                else
+                    ((float*)out)[o + c] = v;
+            }
+        }
+    }
+}
+
 void synth_normal_f32(uint64_t key, int64_t n, float mu, float sigma, float* out) {
     synth_normal_f32_3d(key, 1, 1, n, 0, 0, mu, sigma, out);
 }

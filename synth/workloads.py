@@ -48,6 +48,8 @@ class Model:
     model_id: int = 0
     scale_dtype: int = 0              # 0: f16 group scales, 1: bf16
     symmetric: bool = False           # True: no zero table, every zero point is 8
+    kv_dtype: int = 0                 # KV cache elements: 0 f32, 1 bf16
+    swa_ring: bool = False            # True: sliding-window layers keep a ring of `window` slots
 
     @property
     def n_qkv(self):
@@ -75,6 +77,13 @@ def card_format(m):
     return m
 
 
+def bf16_ring_kv(m):
+    """The card's planned KV format on model m: bf16 elements, and on the
+    sliding-window layers a ring of `window` slots (key j in slot j mod window)."""
+    m.kv_dtype, m.swa_ring = 1, True
+    return m
+
+
 def tiny(model_id=0):
     return Model(d=640, hq=5, hkv=1, hd=128, dff=1728, n_layers=1, layer_types=[SWA],
                  window=64, model_id=model_id)
@@ -98,7 +107,9 @@ def config(i):
     """The workload configurations. 0: tiny layer, 1: SWA layer at 4,096 keys, 2: full
     layer at 16,385 keys with YaRN, 3: 64-layer step at 16K, 4: prefill of 1,200 tokens;
     5: config 3 and 6: config 1 in the card's own W4 recipe (symmetric, group 32, bf16
-    scales)."""
+    scales); 7: config 3 with a bf16 KV cache and rings on the sliding-window layers;
+    8: the same at 65,535 cached tokens (the YaRN context limit of 65,536); 9: one
+    full-size SWA layer at 16,384 cached keys in that KV format (the ring has wrapped)."""
     if i == 0:
         return Workload("tiny-swa-layer", tiny(0), seed=0, n_cached=256, t_max=257)
     if i == 1:
@@ -122,6 +133,16 @@ def config(i):
         m = card_format(olmo3_32b(model_id=6, n_layers=1))
         m.layer_types = [SWA]
         return Workload("olmo3-32b-w4sym-g32-swa-layer-4k", m, seed=0, n_cached=4096, t_max=4097)
+    if i == 7:
+        return Workload("olmo3-32b-w4-decode-16k-bf16kv-ring", bf16_ring_kv(olmo3_32b(3)), seed=0,
+                        n_cached=16384, t_max=16385, use_tokens=True, final_head=True)
+    if i == 8:
+        return Workload("olmo3-32b-w4-decode-64k-bf16kv-ring", bf16_ring_kv(olmo3_32b(3)), seed=0,
+                        n_cached=65535, t_max=65536, use_tokens=True, final_head=True)
+    if i == 9:
+        m = bf16_ring_kv(olmo3_32b(model_id=1, n_layers=1))
+        m.layer_types = [SWA]
+        return Workload("olmo3-32b-swa-layer-16k-bf16kv-ring", m, seed=0, n_cached=16384, t_max=16385)
     raise ValueError(i)
 
 
@@ -166,18 +187,32 @@ def layer_tensors(model, seed, layer):
     return out
 
 
+def kv_slots(model, layer_type, t_max):
+    """Positions stored per KV head: `window` on a sliding-window layer kept as a ring,
+    else t_max."""
+    return model.window if (model.swa_ring and layer_type == SWA and model.window > 0) else t_max
+
+
+def kv_np_dtype(model):
+    return np.uint16 if model.kv_dtype == 1 else np.float32
+
+
 def kv_cache_into(model, seed, layer, n_cached, t_max, kdst, vdst):
-    """K and V caches [hkv][t_max][hd] f32; slots 0..n_cached-1 ~ N(0,1). Slots at or
-    past n_cached are left as the caller's buffer holds them."""
+    """K and V caches [hkv][slots][hd] in the model's KV format (f32, or bf16 bits)
+    holding positions 0..n_cached-1 ~ N(0,1) (a ring holds the last `slots` of them
+    at slot j mod slots). Slots not written are left as the caller's buffer holds them."""
+    slots = kv_slots(model, model.layer_types[layer], t_max)
+    j0 = max(0, n_cached - slots)
     for kind, dst in ((K_KC, kdst), (K_VC, vdst)):
         if n_cached > 0:
-            S.normal_f32_3d_into(S.key(seed, tid(model, layer, kind)), model.hkv, n_cached, model.hd,
-                                 t_max * model.hd, model.hd, 0.0, 1.0, dst)
+            S.normal_kv_into(S.key(seed, tid(model, layer, kind)), model.hkv, n_cached, model.hd, j0, slots,
+                             model.kv_dtype, 0.0, 1.0, dst)
 
 
 def kv_cache(model, seed, layer, n_cached, t_max):
-    Kc = np.zeros((model.hkv, t_max, model.hd), np.float32)
-    Vc = np.zeros((model.hkv, t_max, model.hd), np.float32)
+    slots = kv_slots(model, model.layer_types[layer], t_max)
+    Kc = np.zeros((model.hkv, slots, model.hd), kv_np_dtype(model))
+    Vc = np.zeros((model.hkv, slots, model.hd), kv_np_dtype(model))
     kv_cache_into(model, seed, layer, n_cached, t_max, Kc, Vc)
     return Kc, Vc
 
