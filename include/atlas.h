@@ -91,12 +91,14 @@ typedef struct atlas_rope {
 
 /* One decoder layer ([card] Architecture deep-dive; [kb]; [db]). qkv stacks the q
  * (Hq*D rows), k (Hkv*D) and v (Hkv*D) projections; gate and up are the two SwiGLU
- * inputs, down the output projection. Gains are f32. Caches are f32
- * [Hkv][T_max][D]. type: 0 = sliding window, 1 = full attention. */
+ * inputs, down the output projection. Gains are f32. The caches are [Hkv][slots][D]
+ * in the model's KV format (atlas_model.kv_dtype, swa_ring): slots = window on a
+ * sliding-window layer kept as a ring (key j in slot j mod window), else t_max (key j
+ * in slot j). type: 0 = sliding window, 1 = full attention. */
 typedef struct atlas_layer {
     atlas_w4 qkv, o, gate, up, down;
     const float *g_q, *g_k, *g_pa, *g_pf;
-    float *k_cache, *v_cache;
+    void *k_cache, *v_cache;
     int32_t type;
 } atlas_layer;
 
@@ -109,6 +111,13 @@ typedef struct atlas_model {
     const uint16_t* embedding;   /* bf16 [vocab][d] (device), or NULL */
     const float* g_final;        /* f32 [d] final RMSNorm gain (device), or NULL */
     const uint16_t* lm_head;     /* bf16 [vocab][d] (device), or NULL */
+    /* KV format ([card] Limitations & roadmap: a bf16 cache that keeps only the
+     * window on the sliding-window layers). kv_dtype 0: f32 elements; 1: bfloat16,
+     * rounded to nearest even (ties to even) when a key or value is stored and read
+     * back exactly. swa_ring != 0: every type-0 layer keeps a ring of `window` slots
+     * (needs window > 0); full layers always keep t_max. */
+    int32_t kv_dtype;
+    int32_t swa_ring;
 } atlas_model;
 
 ATLAS_API const char* atlas_version(void);
@@ -170,6 +179,24 @@ ATLAS_API size_t atlas_gqa_decode_workspace_bytes(int32_t Hq, int32_t Hkv, int32
 ATLAS_API int atlas_gqa_decode(const float* q, const float* k_cache, const float* v_cache, int32_t Hq, int32_t Hkv,
                      int32_t D, int64_t T_max, const int32_t* d_pos, int32_t window, float softmax_scale,
                      float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* The same over caches in any KV format ([card] Limitations & roadmap: bf16 KV and
+ * a window-sized cache on the sliding-window layers). layout (host memory):
+ *   kv_dtype 0 = f32, 1 = bfloat16 elements;
+ *   slots    = positions stored per KV head (caches are [Hkv][slots][D]);
+ *   ring     != 0: key j lives in slot j mod slots and any pos >= 0 is accepted
+ *              (needs 0 < window <= slots); else key j in slot j and pos < slots.
+ * Slot of pos must already hold the new key/value. ws: at least
+ * atlas_gqa_decode_workspace_bytes(Hq, Hkv, D, slots) bytes. A position outside the
+ * accepted range (checked on the device) makes every output row zero. */
+typedef struct atlas_kv_layout {
+    int32_t kv_dtype;
+    int32_t ring;
+    int64_t slots;
+} atlas_kv_layout;
+ATLAS_API int atlas_gqa_decode_kv(const float* q, const void* k_cache, const void* v_cache,
+                        const atlas_kv_layout* layout, int32_t Hq, int32_t Hkv, int32_t D, const int32_t* d_pos,
+                        int32_t window, float softmax_scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- decode step ------------------------------------------------------------------
  * One token through m->n_layers layers ([card] Architecture deep-dive; [kb]):

@@ -34,7 +34,11 @@ class atlas_model(ctypes.Structure):
                 ("n_layers", c_int32), ("window", c_int32), ("vocab", c_int32), ("eps", c_float),
                 ("t_max", c_int64), ("rope_swa", atlas_rope), ("rope_full", atlas_rope),
                 ("layers", ctypes.POINTER(atlas_layer)), ("embedding", c_void_p), ("g_final", c_void_p),
-                ("lm_head", c_void_p)]
+                ("lm_head", c_void_p), ("kv_dtype", c_int32), ("swa_ring", c_int32)]
+
+
+class atlas_kv_layout(ctypes.Structure):
+    _fields_ = [("kv_dtype", c_int32), ("ring", c_int32), ("slots", c_int64)]
 
 
 class atlas_profile_entry(ctypes.Structure):
@@ -57,6 +61,9 @@ _SIGS = {
     "atlas_gqa_decode_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int64]),
     "atlas_gqa_decode": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int64,
                                         c_void_p, c_int32, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "atlas_gqa_decode_kv": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, P(atlas_kv_layout), c_int32, c_int32,
+                                           c_int32, c_void_p, c_int32, c_float, c_void_p, c_void_p, c_size_t,
+                                           c_void_p]),
     "atlas_decode_workspace_bytes": (c_size_t, [P(atlas_model)]),
     "atlas_decode_step": (ctypes.c_int, [P(atlas_model), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_void_p, c_void_p, c_size_t, c_void_p]),

@@ -87,6 +87,8 @@ int validate_model(const atlas_model* m) {
     ATLAS_CHECK_ARG(m->t_max >= 1 && m->t_max <= (int64_t)1 << 30, "bad t_max");
     ATLAS_CHECK_ARG(m->window >= 0, "bad window");
     ATLAS_CHECK_ARG(m->eps >= 0.f, "bad eps");
+    ATLAS_CHECK_ARG(m->kv_dtype == 0 || m->kv_dtype == 1, "kv_dtype must be 0 (f32) or 1 (bf16)");
+    ATLAS_CHECK_ARG(!m->swa_ring || m->window > 0, "a sliding-window ring needs window > 0");
     const int nq = m->hq * m->hd, nqkv = (m->hq + 2 * m->hkv) * m->hd;
     const DecodePlan p = make_plan(m);
     ATLAS_CHECK_SHAPE(p.qkv.CPL && p.o.CPL && p.gu.CPL && p.down.CPL, "projection shapes unsupported");
@@ -159,6 +161,9 @@ int run_decode_layers(const atlas_model* m, const XSource& first, const int32_t*
         aa.k_cache = L.k_cache;
         aa.v_cache = L.v_cache;
         aa.T_max = m->t_max;
+        aa.ring = (m->swa_ring && L.type == 0) ? 1 : 0;
+        aa.slots = aa.ring ? m->window : m->t_max;
+        aa.kv_bf16 = m->kv_dtype;
         aa.d_pos = d_pos;
         aa.Hq = m->hq;
         aa.Hkv = m->hkv;

@@ -39,9 +39,12 @@ struct QkvArgs {
 struct AttnFusedArgs {
     const float* qkv;          // raw projection: q [Hq*D], k [Hkv*D], v [Hkv*D]
     const float *g_q, *g_k;
-    float* k_cache;
-    float* v_cache;
-    int64_t T_max;
+    void* k_cache;             // [Hkv][slots][D], f32 or bf16 (kv_bf16)
+    void* v_cache;
+    int64_t T_max;             // positions accepted: [0, T_max)
+    int64_t slots;             // positions stored per KV head
+    int ring;                  // 1: key j in slot j mod slots; 0: slot j
+    int kv_bf16;               // 1: bf16 elements, rounded to nearest even when stored
     const int32_t* d_pos;
     int Hq, Hkv, window, S;
     float scale, eps;

@@ -476,7 +476,35 @@ __global__ __launch_bounds__(GEMV_THREADS) void down_kernel(DownArgs a) {
 //
 // grid (S, Hkv), 256 threads. 16 lanes hold one key (8 dims each); the four 16-lane
 // groups of each wave are independent key streams with their own online softmax,
-// combined at the end. Queries stay in registers.
+// combined at the end. Queries stay in registers. The cache holds f32 or bf16
+// elements (KVB), and key j sits in slot j, or in slot j mod slots on a
+// sliding-window ring.
+
+// One key and value of a 16-lane stream as loaded: 8 f32 of each (two 16-byte
+// loads), or 8 bf16 of each (one 16-byte load), widened only when consumed so that
+// the loads stay in flight.
+template <bool KVB>
+struct KvRegs {
+    f32x4_t k0, k1, v0, v1;
+    __device__ __forceinline__ void unpack(float (&kx)[8], float (&vx)[8]) const {
+        kx[0] = k0.x; kx[1] = k0.y; kx[2] = k0.z; kx[3] = k0.w; kx[4] = k1.x; kx[5] = k1.y; kx[6] = k1.z; kx[7] = k1.w;
+        vx[0] = v0.x; vx[1] = v0.y; vx[2] = v0.z; vx[3] = v0.w; vx[4] = v1.x; vx[5] = v1.y; vx[6] = v1.z; vx[7] = v1.w;
+    }
+};
+template <>
+struct KvRegs<true> {
+    u32x4_t k, v;
+    __device__ __forceinline__ void unpack(float (&kx)[8], float (&vx)[8]) const {
+        const uint32_t kw[4] = {k.x, k.y, k.z, k.w}, vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {   // element 2i in the low half of word i
+            kx[2 * i] = __uint_as_float(kw[i] << 16);
+            kx[2 * i + 1] = __uint_as_float(kw[i] & 0xFFFF0000u);
+            vx[2 * i] = __uint_as_float(vw[i] << 16);
+            vx[2 * i + 1] = __uint_as_float(vw[i] & 0xFFFF0000u);
+        }
+    }
+};
 
 // Keys in flight per 16-lane stream: 1 (a ring of two). Deeper rings (2 and 4 keys) were
 // slower on both layer types: their registers (256 with spills at 4 keys) cost more
@@ -490,7 +518,7 @@ constexpr int ATTN_QF_REGS = 8 * 128 / ATTN_THREADS;                 // query va
 
 // FUSED: q/k/v come raw from the qkv projection (norm, rotary and KV append here);
 // otherwise q is final and the cache already holds the new key.
-template <int G, bool FUSED>
+template <int G, bool FUSED, bool KVB>
 __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) void attn_kernel(AttnFusedArgs a) {
     constexpr int D = 128;
     __shared__ float s_q[G][D];
@@ -543,7 +571,7 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
     }
     __builtin_amdgcn_sched_barrier(0);
     const int pos = __builtin_amdgcn_readfirstlane(pos_v);
-    const bool pos_ok = pos >= 0 && pos < a.T_max;
+    const bool pos_ok = pos >= 0 && pos < a.T_max && (a.ring || pos < a.slots);
     if (!pos_ok) {
         for (int t = threadIdx.x; t < G * (2 + D); t += blockDim.x) {
             const int h = t / (2 + D), e = t % (2 + D);
@@ -560,26 +588,35 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
     int cnt = min(Lk, lo + nkeys - k0);
     if (cnt < 0) cnt = 0;
     const int stream = wave * 4 + grp;
-    const float* Kh = a.k_cache + (size_t)kv * a.T_max * D;
-    const float* Vh = a.v_cache + (size_t)kv * a.T_max * D;
+    // Slots: key jb + i (jb the split's first key) is in slot sb + i, wrapped once on a
+    // ring. The keys of one call span at most `slots` positions (a ring holds the
+    // whole window), and on a flat cache jb + i <= pos < slots never wraps.
+    const int slots = (int)a.slots;
+    const int jb = cnt > 0 ? k0 : lo;
+    const int sb = a.ring ? jb % slots : jb;
+    const size_t head0 = (size_t)kv * a.slots * D;
     // K/V of key i of this split (clamped into the split)
-    auto load_kv = [&](int i, float4& ka, float4& kb, float4& va, float4& vb) {
-        const int j = cnt > 0 ? k0 + min(i, cnt - 1) : lo;
-        typedef float f32x4_t __attribute__((ext_vector_type(4)));
-        const f32x4_t* kp = reinterpret_cast<const f32x4_t*>(Kh + (size_t)j * D + 8 * sub);
-        const f32x4_t* vp = reinterpret_cast<const f32x4_t*>(Vh + (size_t)j * D + 8 * sub);
-        const f32x4_t k0v = __builtin_nontemporal_load(kp), k1v = __builtin_nontemporal_load(kp + 1);
-        const f32x4_t v0v = __builtin_nontemporal_load(vp), v1v = __builtin_nontemporal_load(vp + 1);
-        ka = make_float4(k0v.x, k0v.y, k0v.z, k0v.w);
-        kb = make_float4(k1v.x, k1v.y, k1v.z, k1v.w);
-        va = make_float4(v0v.x, v0v.y, v0v.z, v0v.w);
-        vb = make_float4(v1v.x, v1v.y, v1v.z, v1v.w);
+    auto load_kv = [&](int i, KvRegs<KVB>& r) {
+        int sl = sb + (cnt > 0 ? min(i, cnt - 1) : 0);
+        sl -= sl >= slots ? slots : 0;
+        const size_t e = head0 + (size_t)sl * D + 8 * sub;
+        if constexpr (KVB) {
+            r.k = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>((const uint16_t*)a.k_cache + e));
+            r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>((const uint16_t*)a.v_cache + e));
+        } else {
+            const f32x4_t* kp = reinterpret_cast<const f32x4_t*>((const float*)a.k_cache + e);
+            const f32x4_t* vp = reinterpret_cast<const f32x4_t*>((const float*)a.v_cache + e);
+            r.k0 = __builtin_nontemporal_load(kp);
+            r.k1 = __builtin_nontemporal_load(kp + 1);
+            r.v0 = __builtin_nontemporal_load(vp);
+            r.v1 = __builtin_nontemporal_load(vp + 1);
+        }
     };
     // ring of ATTN_KV_STAGES keys per stream; the first ATTN_KV_STAGES-1 are in flight
     // during the prologue
-    float4 rk[ATTN_KV_STAGES][2], rv[ATTN_KV_STAGES][2];
+    KvRegs<KVB> rkv[ATTN_KV_STAGES];
 #pragma unroll
-    for (int k = 0; k < ATTN_KV_STAGES - 1; k++) load_kv(stream + ATTN_STREAMS * k, rk[k][0], rk[k][1], rv[k][0], rv[k][1]);
+    for (int k = 0; k < ATTN_KV_STAGES - 1; k++) load_kv(stream + ATTN_STREAMS * k, rkv[k]);
     // (keys past the stream's last one are clamped loads of valid rows, never consumed)
 
     if (FUSED) {
@@ -608,7 +645,8 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
             s_cos[threadIdx.x] = cs * (float)a.mscale;
             s_sin[threadIdx.x] = sn * (float)a.mscale;
         }
-        if (threadIdx.x < D) s_vn[threadIdx.x] = vnew;
+        // a bf16 cache stores the rounded value, and the new token attends to what is stored
+        if (threadIdx.x < D) s_vn[threadIdx.x] = KVB ? bf16_bits_to_f32(f32_to_bf16_rne(vnew)) : vnew;
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < 2; r++) {
@@ -621,8 +659,8 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
                 const float c = s_cos[i], sn = s_sin[i];
                 const float y0 = x0 * c - x1 * sn, y1 = x1 * c + x0 * sn;
                 if (isk) {
-                    s_kn[i] = y0;
-                    s_kn[i + 64] = y1;
+                    s_kn[i] = KVB ? bf16_bits_to_f32(f32_to_bf16_rne(y0)) : y0;
+                    s_kn[i + 64] = KVB ? bf16_bits_to_f32(f32_to_bf16_rne(y1)) : y1;
                 } else {
                     s_q[hh][i] = y0;
                     s_q[hh][i + 64] = y1;
@@ -631,9 +669,14 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
         }
         __syncthreads();
         if (pos >= k0 && pos < k0 + cnt && threadIdx.x < D) {   // the split that holds the new token
-            const size_t off = ((size_t)kv * a.T_max + pos) * D + threadIdx.x;
-            a.k_cache[off] = s_kn[threadIdx.x];
-            a.v_cache[off] = s_vn[threadIdx.x];
+            const size_t off = head0 + (size_t)(a.ring ? pos % slots : pos) * D + threadIdx.x;
+            if constexpr (KVB) {   // already rounded: the upper half is the value
+                ((uint16_t*)a.k_cache)[off] = (uint16_t)(__float_as_uint(s_kn[threadIdx.x]) >> 16);
+                ((uint16_t*)a.v_cache)[off] = (uint16_t)(__float_as_uint(s_vn[threadIdx.x]) >> 16);
+            } else {
+                ((float*)a.k_cache)[off] = s_kn[threadIdx.x];
+                ((float*)a.v_cache)[off] = s_vn[threadIdx.x];
+            }
         }
     } else {
 #pragma unroll
@@ -667,10 +710,8 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
     const int nks = cnt > stream ? (cnt - stream + ATTN_STREAMS - 1) / ATTN_STREAMS : 0;
     auto consume = [&](int slot, int idx) {
         const int j = k0 + stream + ATTN_STREAMS * idx;
-        float kx[8] = {rk[slot][0].x, rk[slot][0].y, rk[slot][0].z, rk[slot][0].w,
-                       rk[slot][1].x, rk[slot][1].y, rk[slot][1].z, rk[slot][1].w};
-        float vx[8] = {rv[slot][0].x, rv[slot][0].y, rv[slot][0].z, rv[slot][0].w,
-                       rv[slot][1].x, rv[slot][1].y, rv[slot][1].z, rv[slot][1].w};
+        float kx[8], vx[8];
+        rkv[slot].unpack(kx, vx);
         if (FUSED && j == pos) {
 #pragma unroll
             for (int e = 0; e < 8; e++) {
@@ -698,8 +739,7 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
 #pragma unroll
         for (int k = 0; k < NS; k++) {
             const int slot = (k + NS - 1) % NS;
-            load_kv(stream + ATTN_STREAMS * min(ik + k + NS - 1, nks - 1), rk[slot][0], rk[slot][1], rv[slot][0],
-                    rv[slot][1]);
+            load_kv(stream + ATTN_STREAMS * min(ik + k + NS - 1, nks - 1), rkv[slot]);
             __builtin_amdgcn_sched_barrier(0);
             consume(k, ik + k);
         }
@@ -1083,8 +1123,13 @@ int launch_attn_fused(const AttnFusedArgs& a, int G, hipStream_t st) {
     switch (G) {
 #define C(G_)                                                                           \
     case G_:                                                                            \
-        if (a.fused) ATLAS_KLAUNCH((attn_kernel<G_, true>), grid, dim3(ATTN_THREADS), 0, st, a);    \
-        else ATLAS_KLAUNCH((attn_kernel<G_, false>), grid, dim3(ATTN_THREADS), 0, st, a);           \
+        if (a.kv_bf16) {                                                                            \
+            if (a.fused) ATLAS_KLAUNCH((attn_kernel<G_, true, true>), grid, dim3(ATTN_THREADS), 0, st, a); \
+            else ATLAS_KLAUNCH((attn_kernel<G_, false, true>), grid, dim3(ATTN_THREADS), 0, st, a);        \
+        } else {                                                                                    \
+            if (a.fused) ATLAS_KLAUNCH((attn_kernel<G_, true, false>), grid, dim3(ATTN_THREADS), 0, st, a); \
+            else ATLAS_KLAUNCH((attn_kernel<G_, false, false>), grid, dim3(ATTN_THREADS), 0, st, a);        \
+        }                                                                                           \
         break;
         C(1) C(2) C(3) C(4) C(5) C(6) C(7) C(8)
 #undef C

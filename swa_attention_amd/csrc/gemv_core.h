@@ -103,6 +103,7 @@ struct TileRegs {
 // once per step, so they are loaded non-temporally (streaming cache policy) and do not
 // push the activations and partial sums out of L2.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 template <int CPL, int RB>
 __device__ __forceinline__ void load_tile(TileRegs<CPL>& T, const W4View& W, const LaneMap<CPL, RB>& m, int row0) {
 #pragma unroll

@@ -22,6 +22,7 @@ struct PrefillWs {
     void* dec;       // decode workspace (status word, head partials)
     float *X, *QKV, *A;
     uint16_t *p1h, *p1l, *p2h, *p2l;
+    void *k_new, *v_new;   // prompt keys / values [Hkv][n][hd] in the cache's element type
     int ld1;
     size_t bytes;
 };
@@ -45,6 +46,9 @@ PrefillWs carve_prefill(const atlas_model* m, int n, void* base) {
     w.p1l = (uint16_t*)take((size_t)n * w.ld1 * 2);
     w.p2h = (uint16_t*)take((size_t)n * m->dff * 2);
     w.p2l = (uint16_t*)take((size_t)n * m->dff * 2);
+    const size_t kv_bytes = (size_t)m->hkv * n * m->hd * (m->kv_dtype == 1 ? 2 : 4);
+    w.k_new = take(kv_bytes);
+    w.v_new = take(kv_bytes);
     w.bytes = off;
     return w;
 }
@@ -120,7 +124,7 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
         qa.C = w.QKV;
         qa.ldc = nqkv;
         if ((rc = launch_w4_gemm(qa, 0, st, "pf_gemm_qkv"))) return rc;
-        // QK norm, rotary, KV slots start_pos .. start_pos + n - 1
+        // QK norm and rotary; the prompt keys/values into the prompt KV buffers
         PfRopeArgs ra{};
         ra.qkv = w.QKV;
         ra.ld = nqkv;
@@ -134,17 +138,23 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
         const RopeTable& rt = L.type == 1 ? rt_full : rt_swa;
         for (int i = 0; i < 64; i++) ra.inv[i] = rt.inv[i];
         ra.mscale = rt.mscale;
-        ra.k_cache = L.k_cache;
-        ra.v_cache = L.v_cache;
-        ra.T_max = m->t_max;
+        ra.k_new = w.k_new;
+        ra.v_new = w.v_new;
+        ra.kv_bf16 = m->kv_dtype;
         if ((rc = launch_pf_rope(ra, st))) return rc;
+        const bool ring = m->swa_ring && L.type == 0;
+        const int64_t slots = ring ? m->window : m->t_max;
         // causal attention; output planes for the o projection
         PfAttnArgs aa{};
         aa.qkv = w.QKV;
         aa.ld_qkv = nqkv;
         aa.k_cache = L.k_cache;
         aa.v_cache = L.v_cache;
-        aa.T_max = m->t_max;
+        aa.slots = slots;
+        aa.ring = ring ? 1 : 0;
+        aa.kv_bf16 = m->kv_dtype;
+        aa.k_new = w.k_new;
+        aa.v_new = w.v_new;
         aa.n = n;
         aa.start_pos = start_pos;
         aa.Hq = m->hq;
@@ -155,6 +165,19 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
         aa.o_lo = w.p1l;
         aa.ldo = w.ld1;
         if ((rc = launch_pf_attn(aa, st))) return rc;
+        // the prompt's keys and values into the cache, after every query has read them
+        PfCommitArgs ca{};
+        ca.k_new = w.k_new;
+        ca.v_new = w.v_new;
+        ca.k_cache = L.k_cache;
+        ca.v_cache = L.v_cache;
+        ca.slots = slots;
+        ca.ring = aa.ring;
+        ca.kv_bf16 = m->kv_dtype;
+        ca.n = n;
+        ca.start_pos = start_pos;
+        ca.Hkv = m->hkv;
+        if ((rc = launch_pf_commit(ca, st))) return rc;
         // o projection, h = x + RMSNorm_pa(a)
         GemmArgs oa = gemm(w.p1h, w.p1l, w.ld1, L.o, n);
         oa.C = w.A;

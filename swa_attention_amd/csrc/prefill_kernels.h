@@ -20,12 +20,18 @@ struct GemmArgs {
     int ldz;
 };
 
+// KV of the prompt: keys j < start_pos come from the layer's cache ([Hkv][slots][128],
+// key j in slot j or, on a ring, j mod slots), keys of the prompt from the prompt
+// buffers ([Hkv][n][128]); both hold f32 or bf16 elements (kv_bf16).
 struct PfAttnArgs {
     const float* qkv;          // [n][ld_qkv]: q rows already normalised and rotated
     int ld_qkv;
-    const float* k_cache;      // [Hkv][T_max][128]
-    const float* v_cache;
-    int64_t T_max;
+    const void* k_cache;
+    const void* v_cache;
+    int64_t slots;
+    int ring, kv_bf16;
+    const void* k_new;
+    const void* v_new;
     int n, start_pos, Hq, Hkv, window;
     float scale;
     uint16_t* o_hi;            // [n][ldo] bf16 planes of the attention output (Hq*128 used)
@@ -40,9 +46,21 @@ struct PfRopeArgs {
     float eps;
     double inv[64];
     double mscale;
-    float* k_cache;
-    float* v_cache;
-    int64_t T_max;
+    void* k_new;               // [Hkv][n][128] prompt keys / values, f32 or bf16 (kv_bf16)
+    void* v_new;
+    int kv_bf16;
+};
+
+// Prompt KV -> cache: positions j in [max(start_pos, start_pos + n - slots), start_pos + n)
+// on a ring (earlier prompt positions would be overwritten by later ones), all of
+// them otherwise.
+struct PfCommitArgs {
+    const void* k_new;
+    const void* v_new;
+    void* k_cache;
+    void* v_cache;
+    int64_t slots;
+    int ring, kv_bf16, n, start_pos, Hkv;
 };
 
 int gemm_supported(int group);
@@ -50,6 +68,7 @@ int launch_w4_gemm(const GemmArgs& a, int mode, hipStream_t st, const char* labe
 int launch_pf_embed(const int32_t* tokens, int n, const uint16_t* emb, int vocab, int d, float* X, uint16_t* p_hi,
                     uint16_t* p_lo, int ldp, int* status, hipStream_t st);
 int launch_pf_rope(const PfRopeArgs& a, hipStream_t st);
+int launch_pf_commit(const PfCommitArgs& a, hipStream_t st);
 int launch_pf_attn(const PfAttnArgs& a, hipStream_t st);
 int launch_pf_split(const float* X, int M, int K, int ldx, uint16_t* p_hi, uint16_t* p_lo, int ldp, hipStream_t st);
 int launch_pf_residual(float* X, const float* A, const float* g, int n, int d, float eps, uint16_t* p_hi,

@@ -23,12 +23,6 @@ namespace atlas {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short bf16x4_t __attribute__((ext_vector_type(4)));   // four bf16 (operand of the 16x16x16 MFMA)
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
-    const uint32_t u = __float_as_uint(x);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
 
 // x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (x - hi is exact in f32)
 __device__ __forceinline__ void pf_split(float x, uint32_t& hi, uint32_t& lo) {
@@ -261,7 +255,8 @@ __global__ __launch_bounds__(256) void pf_embed_kernel(const int32_t* tokens, in
 }
 
 // Full-projection QK RMSNorm, rotary embedding (x attention factor) at position
-// start_pos + t, q written back in place, k and v written to cache slot pos.
+// start_pos + t, q written back in place, k and v written to row t of the prompt KV
+// buffers (rounded to bf16 when the cache is bf16: what is stored is what attends).
 __global__ __launch_bounds__(256) void pf_rope_kernel(PfRopeArgs a) {
     constexpr int D = 128;
     __shared__ float red[16];
@@ -296,9 +291,14 @@ __global__ __launch_bounds__(256) void pf_rope_kernel(PfRopeArgs a) {
         const float c = s_cos[i], sn = s_sin[i];
         const float y0 = x0 * c - x1 * sn, y1 = x1 * c + x0 * sn;
         if (isk) {
-            float* dst = a.k_cache + ((size_t)(h - a.Hq) * a.T_max + pos) * D;
-            dst[i] = y0;
-            dst[i + 64] = y1;
+            const size_t e = ((size_t)(h - a.Hq) * a.n + t) * D + i;
+            if (a.kv_bf16) {
+                ((uint16_t*)a.k_new)[e] = (uint16_t)f32_to_bf16_rne(y0);
+                ((uint16_t*)a.k_new)[e + 64] = (uint16_t)f32_to_bf16_rne(y1);
+            } else {
+                ((float*)a.k_new)[e] = y0;
+                ((float*)a.k_new)[e + 64] = y1;
+            }
         } else {
             row[base + i] = y0;
             row[base + i + 64] = y1;
@@ -306,7 +306,31 @@ __global__ __launch_bounds__(256) void pf_rope_kernel(PfRopeArgs a) {
     }
     for (int u = threadIdx.x; u < nk; u += blockDim.x) {
         const int h = u / D, i = u % D;
-        a.v_cache[((size_t)h * a.T_max + pos) * D + i] = row[nq + nk + u];
+        const size_t e = ((size_t)h * a.n + t) * D + i;
+        const float v = row[nq + nk + u];
+        if (a.kv_bf16) ((uint16_t*)a.v_new)[e] = (uint16_t)f32_to_bf16_rne(v);
+        else ((float*)a.v_new)[e] = v;
+    }
+}
+
+// One block per committed position: copies its Hkv x 128 keys and values from the
+// prompt buffers into the cache slot (j mod slots on a ring).
+__global__ __launch_bounds__(256) void pf_commit_kernel(PfCommitArgs a) {
+    constexpr int D = 128;
+    const int end = a.start_pos + a.n;
+    const int first = a.ring ? max(a.start_pos, end - (int)a.slots) : a.start_pos;
+    const int j = first + blockIdx.x, t = j - a.start_pos;
+    const int slot = a.ring ? j % (int)a.slots : j;
+    const int esz = a.kv_bf16 ? 2 : 4;
+    const int nv = a.Hkv * D * esz / 16;   // 16-byte vectors per position and tensor
+    const int per_head = D * esz / 16;
+    for (int u = threadIdx.x; u < 2 * nv; u += blockDim.x) {
+        const int isv = u >= nv, w = isv ? u - nv : u, h = w / per_head, c = w % per_head;
+        const uint4* src = reinterpret_cast<const uint4*>((const char*)(isv ? a.v_new : a.k_new) +
+                                                          (((size_t)h * a.n + t) * D) * esz) + c;
+        uint4* dst = reinterpret_cast<uint4*>((char*)(isv ? a.v_cache : a.k_cache) +
+                                              (((size_t)h * a.slots + slot) * D) * esz) + c;
+        *dst = *src;
     }
 }
 
@@ -354,7 +378,37 @@ __global__ __launch_bounds__(256) void pf_split_kernel(const float* X, int K, in
 // as bf16 planes for the o projection.
 constexpr int PF_QT = 16;
 
-template <int G>
+// 4 consecutive K or V values (dims 4c..4c+3) of key j of KV head kv: from the cache
+// for j < start_pos (slot j, or j mod slots on a ring: start_pos - slots <= j there),
+// from the prompt buffer otherwise.
+template <bool KVB>
+__device__ __forceinline__ float4 pf_kv4(const void* cache, const void* fresh, const PfAttnArgs& a, int kv, int j,
+                                         int c, int sp) {
+    constexpr int D = 128;
+    size_t e;
+    const void* base;
+    if (j >= a.start_pos) {
+        base = fresh;
+        e = ((size_t)kv * a.n + (j - a.start_pos)) * D + 4 * c;
+    } else {
+        int sl = j;
+        if (a.ring) {   // sp = start_pos mod slots, 0 < start_pos - j <= slots
+            sl = sp - (a.start_pos - j);
+            sl += sl < 0 ? (int)a.slots : 0;
+        }
+        base = cache;
+        e = ((size_t)kv * a.slots + sl) * D + 4 * c;
+    }
+    if constexpr (KVB) {
+        const uint2 w = *reinterpret_cast<const uint2*>((const uint16_t*)base + e);
+        return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+                           __uint_as_float(w.y & 0xFFFF0000u));
+    } else {
+        return *reinterpret_cast<const float4*>((const float*)base + e);
+    }
+}
+
+template <int G, bool KVB>
 __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
     constexpr int D = 128, KPB = D + 8, VTP = 16 + 4, PP = 20;
     __shared__ __align__(16) uint16_t sKh[16 * KPB];   // keys as bf16 planes: K = hi + lo
@@ -406,14 +460,13 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
 #pragma unroll
     for (int gi = 0; gi < 8; gi++) o[gi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const float* Kh = a.k_cache + (size_t)kv * a.T_max * D;
-    const float* Vh = a.v_cache + (size_t)kv * a.T_max * D;
+    const int sp = a.ring ? a.start_pos % (int)a.slots : 0;
     for (int kb = klo; kb <= khi; kb += 16) {
         __syncthreads();
         for (int u = tid; u < 16 * D / 4; u += blockDim.x) {
             const int kr = u / (D / 4), c = u % (D / 4);
-            const size_t j = (size_t)min(kb + kr, khi);
-            const float4 k4 = reinterpret_cast<const float4*>(Kh + j * D)[c];
+            const int j = min(kb + kr, khi);
+            const float4 k4 = pf_kv4<KVB>(a.k_cache, a.k_new, a, kv, j, c, sp);
             uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
             pf_split(k4.x, h0, l0);
             pf_split(k4.y, h1, l1);
@@ -421,7 +474,7 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
             pf_split(k4.w, h3, l3);
             *reinterpret_cast<uint2*>(&sKh[kr * KPB + 4 * c]) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
             *reinterpret_cast<uint2*>(&sKl[kr * KPB + 4 * c]) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
-            const float4 v4 = reinterpret_cast<const float4*>(Vh + j * D)[c];
+            const float4 v4 = pf_kv4<KVB>(a.v_cache, a.v_new, a, kv, j, c, sp);
             const float ve[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
             for (int e = 0; e < 4; e++) {
@@ -535,6 +588,14 @@ int launch_pf_rope(const PfRopeArgs& a, hipStream_t st) {
     return ATLAS_OK;
 }
 
+int launch_pf_commit(const PfCommitArgs& a, hipStream_t st) {
+    const int npos = a.ring ? (int)std::min<int64_t>(a.n, a.slots) : a.n;
+    prof_mark("pf_kv_commit", st);
+    ATLAS_KLAUNCH(pf_commit_kernel, dim3(npos), dim3(256), 0, st, a);
+    ATLAS_LAUNCH_CHECK("pf_commit_kernel");
+    return ATLAS_OK;
+}
+
 int launch_pf_attn(const PfAttnArgs& a, hipStream_t st) {
     const int G = a.Hq / a.Hkv;
     dim3 grid((a.n + PF_QT - 1) / PF_QT, a.Hkv);
@@ -542,7 +603,8 @@ int launch_pf_attn(const PfAttnArgs& a, hipStream_t st) {
     switch (G) {
 #define C(G_)                                                                   \
     case G_:                                                                    \
-        ATLAS_KLAUNCH((pf_attn_kernel<G_>), grid, dim3(64 * G_), 0, st, a);    \
+        if (a.kv_bf16) ATLAS_KLAUNCH((pf_attn_kernel<G_, true>), grid, dim3(64 * G_), 0, st, a);    \
+        else ATLAS_KLAUNCH((pf_attn_kernel<G_, false>), grid, dim3(64 * G_), 0, st, a);              \
         break;
         C(1) C(2) C(3) C(4) C(5) C(6) C(7) C(8)
 #undef C

@@ -135,6 +135,36 @@ def atlas_gqa_decode(q, k_cache, v_cache, Hq, Hkv, D, T_max, d_pos, window, scal
     return out
 
 
+def atlas_gqa_decode_kv(q, k_cache, v_cache, Hq, Hkv, D, d_pos, window, ring=False, scale=None, out=None, ws=None,
+                        stream=None):
+    """Decode attention over caches [Hkv][slots][D] of f32 or bf16 (torch.bfloat16 or
+    raw int16/uint16 bits); ``ring``: key j in slot j mod slots."""
+    _dev(q, F32, "q")
+    if k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must share a dtype")
+    if k_cache.dtype == F32:
+        kv_dtype = 0
+    elif k_cache.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        kv_dtype = 1
+    else:
+        raise TypeError(f"unsupported cache dtype {k_cache.dtype}")
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, k_cache.dtype, n)
+    _dev(d_pos, I32, "d_pos")
+    slots = k_cache.numel() // (Hkv * D)
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty(Hq * D, dtype=F32, device=q.device)
+    need = atlas_gqa_decode_workspace_bytes(Hq, Hkv, D, slots)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    layout = L.atlas_kv_layout(kv_dtype, int(bool(ring)), slots)
+    L.call("atlas_gqa_decode_kv", L.ptr(q), L.ptr(k_cache), L.ptr(v_cache), ctypes.byref(layout), Hq, Hkv, D,
+           L.ptr(d_pos), window, scale, L.ptr(out), L.ptr(ws), ws.numel(), L.stream_ptr(stream))
+    return out
+
+
 # ---- model --------------------------------------------------------------------------------------
 
 @dataclass
@@ -175,6 +205,8 @@ class Model:
     embedding: Optional[torch.Tensor] = None
     g_final: Optional[torch.Tensor] = None
     lm_head: Optional[torch.Tensor] = None
+    kv_dtype: int = 0          # 0: f32 caches, 1: bf16
+    swa_ring: int = 0          # 1: sliding-window layers keep a ring of `window` slots
     _c: object = None
     _arr: object = None
 
@@ -187,7 +219,8 @@ class Model:
                                 ctypes.cast(arr, ctypes.POINTER(L.atlas_layer)),
                                 None if self.embedding is None else self.embedding.data_ptr(),
                                 None if self.g_final is None else self.g_final.data_ptr(),
-                                None if self.lm_head is None else self.lm_head.data_ptr())
+                                None if self.lm_head is None else self.lm_head.data_ptr(),
+                                self.kv_dtype, self.swa_ring)
         return self._c
 
 

@@ -37,14 +37,17 @@ def layer_to_device(model, seed, layer, n_cached, t_max, device, tensors=None):
     for name, kind, N, K in model.linears():
         c, s, z = T[name]
         ws[name] = w4_to_device(c, s, z, K, device, model.group, model.scale_dtype)
-    Kc = torch.zeros((model.hkv, t_max, model.hd), dtype=torch.float32, device=device)
+    # caches in the model's KV format: [hkv][slots][hd] f32, or bf16 bits held as int16
+    slots = W.kv_slots(model, model.layer_types[layer], t_max)
+    tdt = torch.int16 if model.kv_dtype == 1 else torch.float32
+    Kc = torch.zeros((model.hkv, slots, model.hd), dtype=tdt, device=device)
     Vc = torch.zeros_like(Kc)
     if n_cached > 0:
-        hk = np.zeros((model.hkv, t_max, model.hd), np.float32)
-        hv = np.zeros((model.hkv, t_max, model.hd), np.float32)
+        hk = np.zeros((model.hkv, slots, model.hd), W.kv_np_dtype(model))
+        hv = np.zeros((model.hkv, slots, model.hd), W.kv_np_dtype(model))
         W.kv_cache_into(model, seed, layer, n_cached, t_max, hk, hv)
-        Kc.copy_(torch.from_numpy(hk))
-        Vc.copy_(torch.from_numpy(hv))
+        Kc.copy_(torch.from_numpy(hk.view(np.int16) if model.kv_dtype == 1 else hk))
+        Vc.copy_(torch.from_numpy(hv.view(np.int16) if model.kv_dtype == 1 else hv))
     g = {k: _t(T[k], device) for k in ("g_q", "g_k", "g_pa", "g_pf")}
     return Layer(ws["qkv"], ws["o"], ws["gate"], ws["up"], ws["down"], g["g_q"], g["g_k"], g["g_pa"], g["g_pf"],
                  Kc, Vc, model.layer_types[layer])
@@ -68,7 +71,8 @@ def build_model(wl, device="cuda", n_layers=None, head=None, progress=None):
     n_layers = m.n_layers if n_layers is None else n_layers
     head = wl.final_head if head is None else head
     swa, full = rope_structs(m)
-    dm = Model(m.d, m.hq, m.hkv, m.hd, m.dff, m.window, m.vocab, m.eps, wl.t_max, swa, full)
+    dm = Model(m.d, m.hq, m.hkv, m.hd, m.dff, m.window, m.vocab, m.eps, wl.t_max, swa, full,
+               kv_dtype=m.kv_dtype, swa_ring=int(m.swa_ring))
     for l in range(n_layers):
         dm.layers.append(layer_to_device(m, wl.seed, l, wl.n_cached, wl.t_max, device))
         if progress:

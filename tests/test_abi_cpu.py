@@ -101,6 +101,23 @@ def test_attention_and_norm_validation(lib):
     assert q(FAKE, FAKE, FAKE, FAKE, 40, 8, 128, None, ctypes.byref(rope), 1e-6, None) == L.ATLAS_ERR_INVALID_ARG
 
 
+def test_kv_layout_attention_validation(lib):
+    g = lib.atlas_gqa_decode_kv
+    ws = lib.atlas_gqa_decode_workspace_bytes(40, 8, 128, 4096)
+
+    def call(layout, D=128, window=4096, ws_bytes=ws, pos=FAKE):
+        lay = None if layout is None else ctypes.byref(L.atlas_kv_layout(*layout))
+        return g(FAKE, FAKE, FAKE, lay, 40, 8, D, pos, window, 0.1, FAKE, FAKE, ws_bytes, None)
+    assert call(None) == L.ATLAS_ERR_INVALID_ARG
+    assert call((2, 1, 4096)) == L.ATLAS_ERR_INVALID_ARG              # element type
+    assert call((1, 1, 4096), window=0) == L.ATLAS_ERR_INVALID_ARG     # a ring needs a window
+    assert call((1, 1, 4096), window=4097) == L.ATLAS_ERR_INVALID_ARG  # ... that fits its slots
+    assert call((1, 1, 0)) == L.ATLAS_ERR_INVALID_ARG
+    assert call((1, 1, 4096), D=64) == L.ATLAS_ERR_UNSUPPORTED_SHAPE
+    assert call((1, 1, 4096), ws_bytes=16) == L.ATLAS_ERR_WORKSPACE_TOO_SMALL
+    assert call((1, 1, 4096), pos=None) == L.ATLAS_ERR_INVALID_ARG
+
+
 def _fake_model(n_layers=2, **over):
     m = dict(d=640, hq=5, hkv=1, hd=128, dff=1728)
     m.update(over)
@@ -136,8 +153,18 @@ def test_decode_step_validation(lib):
     wide, keep5 = _fake_model(d=6176, hq=1, hkv=1)          # the GEMV input vectors hold d <= 6144
     assert step(ctypes.byref(wide), FAKE, None, FAKE, None, None, None, FAKE, need, None) == \
         L.ATLAS_ERR_UNSUPPORTED_SHAPE
+    kvbad, keep6 = _fake_model()
+    kvbad.kv_dtype = 2
+    assert step(ctypes.byref(kvbad), FAKE, None, FAKE, None, None, None, FAKE, need, None) == L.ATLAS_ERR_INVALID_ARG
+    ringbad, keep7 = _fake_model()
+    ringbad.swa_ring, ringbad.window = 1, 0
+    assert step(ctypes.byref(ringbad), FAKE, None, FAKE, None, None, None, FAKE, need, None) == \
+        L.ATLAS_ERR_INVALID_ARG
     pre = lib.atlas_prefill
     pneed = lib.atlas_prefill_workspace_bytes(ctypes.byref(mm), 8)
+    bf, keep8 = _fake_model()
+    bf.kv_dtype = 1
+    assert 0 < lib.atlas_prefill_workspace_bytes(ctypes.byref(bf), 8) < pneed   # half-size prompt KV buffers
     assert pneed > 0
     assert pre(ctypes.byref(mm), FAKE, 8, 295, None, None, FAKE, pneed, None) == L.ATLAS_ERR_INVALID_ARG
     assert pre(ctypes.byref(mm), FAKE, 0, 0, None, None, FAKE, pneed, None) == L.ATLAS_ERR_INVALID_ARG
