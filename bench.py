@@ -136,7 +136,7 @@ def cpu_baseline(wl, budget_s, config):
 PEAK_BF16_TFLOPS = 2500.0
 
 
-def measure_prefill(args, dm, cm, m, dev):
+def measure_prefill(args, dm, cm, m, dev, wl_name):
     """Time-to-first-token of the 1,200-token prompt (same 64-layer model, positions
     0..1,199, written over the decode cache after the decode timing): token ids on
     device to the last row's logits and argmax."""
@@ -146,6 +146,9 @@ def measure_prefill(args, dm, cm, m, dev):
     from swa_attention_amd import ops
     pw = W.config(4)
     n = pw.prompt_len
+    # the prompt runs on the decode workload's model (its weight and KV formats)
+    name = pw.name if wl_name == W.config(3).name else wl_name.replace("decode-16k", "prefill-1200").replace(
+        "decode-64k", "prefill-1200")
     toks = torch.from_numpy(W.prompt_tokens(m, pw.seed, n)).to(dev)
     ws = torch.empty(ops.atlas_prefill_workspace_bytes(dm, n), dtype=torch.uint8, device=dev)
     logits = torch.empty(m.vocab, dtype=torch.float32, device=dev)
@@ -154,7 +157,7 @@ def measure_prefill(args, dm, cm, m, dev):
     def run():
         ops.atlas_prefill(dm, toks, 0, logits, am, ws, cm=cm)
 
-    log(f"prefill {pw.name}: warm-up")
+    log(f"prefill {name}: warm-up")
     run()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -169,7 +172,7 @@ def measure_prefill(args, dm, cm, m, dev):
     log("prefill per-launch timing: " + ", ".join(f"{k} {v[0]}x {v[1] / v[0] * 1e3:.1f}us" for k, v in
                                                   sorted(prof.items(), key=lambda kv: -kv[1][1])))
     flops = A.prefill_flops(m, n)
-    out = {"workload": pw.name, "tokens": n, "ttft_ms": round(ms, 2), "reps": args.prefill_reps,
+    out = {"workload": name, "tokens": n, "ttft_ms": round(ms, 2), "reps": args.prefill_reps,
            "algorithmic_tflop": round(flops / 1e12, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
            "mfma_frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     dom = "pf_gemm_gate_up"
@@ -323,7 +326,7 @@ def main():
 
     prefill = None
     if not args.no_prefill and head and wl.use_tokens:
-        prefill = measure_prefill(args, dm, cm, m, dev)
+        prefill = measure_prefill(args, dm, cm, m, dev, wl.name)
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 18   # f32 elements
@@ -358,7 +361,9 @@ def main():
         "config": {"workload": wl.name, "layers": m.n_layers, "context": wl.n_cached, "batch": 1,
                    "weights": (f"int4 group-{m.group}, {'bf16' if m.scale_dtype else 'f16'} scales, "
                                + ("symmetric (zero point 8)" if m.symmetric else "uint4 zeros")),
-                   "kv": "f32", "lm_head": "bf16"},
+                   "kv": ("bf16" if m.kv_dtype == 1 else "f32") + (
+                       f", ring of {m.window} slots on the sliding-window layers" if m.swa_ring else ""),
+                   "lm_head": "bf16"},
         "achieved_GBps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "bytes_per_step": sb.total,

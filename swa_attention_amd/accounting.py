@@ -2,7 +2,7 @@
 
 "Algorithmic" bytes are the bytes the step must move at least once per token: every
 W4 weight (packed codes, f16 group scales, packed uint4 zeros), the KV entries the
-attention reads, the bf16 lm_head, the norm gains and the embedding row. Achieved
+attention reads (f32 or bf16 elements), the bf16 lm_head, the norm gains and the embedding row. Achieved
 bandwidth is these bytes divided by measured time.
 """
 from dataclasses import dataclass
@@ -38,8 +38,13 @@ def keys_read(layer_type, pos, window):
     return min(window, pos + 1)
 
 
+def kv_elem_bytes(m):
+    """Bytes of one cached key or value element: 2 for a bf16 cache, else 4."""
+    return 2 if getattr(m, "kv_dtype", 0) == 1 else 4
+
+
 def layer_kv_read_bytes(m, layer_type, pos):
-    return 2 * m.hkv * m.hd * 4 * keys_read(layer_type, pos, m.window)
+    return 2 * m.hkv * m.hd * kv_elem_bytes(m) * keys_read(layer_type, pos, m.window)
 
 
 @dataclass
@@ -61,7 +66,7 @@ def decode_step_bytes(m, pos, n_layers=None, head=True):
     w4 = n_layers * layer_w4_bytes(m)
     kv = sum(layer_kv_read_bytes(m, m.layer_types[l], pos) for l in range(n_layers))
     # gains (f32), the new k/v written to the cache
-    small = n_layers * (4 * layer_gain_count(m) + 2 * m.hkv * m.hd * 4)
+    small = n_layers * (4 * layer_gain_count(m) + 2 * m.hkv * m.hd * kv_elem_bytes(m))
     lm = 0
     if head:
         lm = m.vocab * m.d * 2

@@ -511,6 +511,8 @@ struct KvRegs<true> {
 // than the extra loads gain; 16 streams per block, two blocks per CU, already keep 32
 // keys (32 KB) in flight per CU.
 constexpr int ATTN_KV_STAGES = 2;
+// A bf16 key and value take half the registers of f32 ones.
+constexpr int ATTN_KV_STAGES_BF16 = 3;
 constexpr int ATTN_WAVES = ATTN_THREADS / 64;
 constexpr int ATTN_STREAMS = 4 * ATTN_WAVES;                        // 16-lane key streams per block
 constexpr int ATTN_SSQ_REGS = ATTN_SSQ_MAX_BLOCKS / ATTN_THREADS;   // sums-of-squares partials per thread
@@ -612,11 +614,11 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
             r.v1 = __builtin_nontemporal_load(vp + 1);
         }
     };
-    // ring of ATTN_KV_STAGES keys per stream; the first ATTN_KV_STAGES-1 are in flight
-    // during the prologue
-    KvRegs<KVB> rkv[ATTN_KV_STAGES];
+    // ring of NS keys per stream; the first NS-1 are in flight during the prologue
+    constexpr int NS = KVB ? ATTN_KV_STAGES_BF16 : ATTN_KV_STAGES;
+    KvRegs<KVB> rkv[NS];
 #pragma unroll
-    for (int k = 0; k < ATTN_KV_STAGES - 1; k++) load_kv(stream + ATTN_STREAMS * k, rkv[k]);
+    for (int k = 0; k < NS - 1; k++) load_kv(stream + ATTN_STREAMS * k, rkv[k]);
     // (keys past the stream's last one are clamped loads of valid rows, never consumed)
 
     if (FUSED) {
@@ -706,7 +708,6 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
     // loads so that the compiler's wait counting stays exact; the remainder is already
     // loaded. The new token's key and value come from LDS (the cache write above may
     // still be in flight).
-    constexpr int NS = ATTN_KV_STAGES;
     const int nks = cnt > stream ? (cnt - stream + ATTN_STREAMS - 1) / ATTN_STREAMS : 0;
     auto consume = [&](int slot, int idx) {
         const int j = k0 + stream + ATTN_STREAMS * idx;
