@@ -1108,11 +1108,14 @@ int launch_down(const DownArgs& a0, const GemvShape& s, hipStream_t st) {
 }
 
 // Key splits per KV head: at least 64 keys each, and at most one block per CU over the
-// KV heads (more, smaller blocks measured slower: 512 blocks of 4 waves lost to 256).
+// KV heads (more, smaller blocks measured slower at 16K: 512 blocks of 4 waves lost to
+// 256). Past 1,024 keys per split the key loop outweighs the per-block prologue and two
+// blocks per CU pay off (65,536 keys, 8 KV heads: 64 us against 72 us).
 constexpr int ATTN_GRID_BLOCKS = 256;
 int attn_splits(int64_t maxkeys, int Hkv) {
     int64_t S = (maxkeys + 63) / 64;
-    const int64_t cap = std::max(1, (ATTN_GRID_BLOCKS + Hkv - 1) / Hkv);
+    int64_t cap = std::max(1, (ATTN_GRID_BLOCKS + Hkv - 1) / Hkv);
+    if (maxkeys > 1024 * cap) cap = std::max(1, (2 * ATTN_GRID_BLOCKS + Hkv - 1) / Hkv);
     if (S > cap) S = cap;
     if (S < 1) S = 1;
     return (int)S;

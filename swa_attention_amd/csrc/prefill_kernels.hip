@@ -374,16 +374,17 @@ __global__ __launch_bounds__(256) void pf_split_kernel(const float* X, int K, in
 // same but transposed ([dim][key]). Per wave: S (16 positions x 16 keys) = Q K^T over
 // the 128 dimensions on 16x16x32 bf16 MFMAs, masked to each position's window, online
 // softmax per position, O += P V on 16x16x16 bf16 MFMAs (P re-laid out through LDS);
-// each product is hi*hi + hi*lo + lo*hi of the split operands. The output is written
+// each product is hi*hi + hi*lo + lo*hi of the split operands (with a bf16 cache the
+// keys and values are exact in bf16, their lo planes vanish, and hi*hi + lo*hi
+// remain). The output is written
 // as bf16 planes for the o projection.
 constexpr int PF_QT = 16;
 
-// 4 consecutive K or V values (dims 4c..4c+3) of key j of KV head kv: from the cache
-// for j < start_pos (slot j, or j mod slots on a ring: start_pos - slots <= j there),
-// from the prompt buffer otherwise.
-template <bool KVB>
-__device__ __forceinline__ float4 pf_kv4(const void* cache, const void* fresh, const PfAttnArgs& a, int kv, int j,
-                                         int c, int sp) {
+// 4 consecutive K or V values (dims 4c..4c+3) of key j of KV head kv (f32 caches):
+// from the cache for j < start_pos (slot j, or j mod slots on a ring: start_pos - slots
+// < j there), from the prompt buffer otherwise.
+__device__ __forceinline__ float4 pf_kv4_f32(const void* cache, const void* fresh, const PfAttnArgs& a, int kv, int j,
+                                             int c, int sp) {
     constexpr int D = 128;
     size_t e;
     const void* base;
@@ -392,20 +393,35 @@ __device__ __forceinline__ float4 pf_kv4(const void* cache, const void* fresh, c
         e = ((size_t)kv * a.n + (j - a.start_pos)) * D + 4 * c;
     } else {
         int sl = j;
-        if (a.ring) {   // sp = start_pos mod slots, 0 < start_pos - j <= slots
+        if (a.ring) {   // sp = start_pos mod slots, 0 < start_pos - j < slots
             sl = sp - (a.start_pos - j);
             sl += sl < 0 ? (int)a.slots : 0;
         }
         base = cache;
         e = ((size_t)kv * a.slots + sl) * D + 4 * c;
     }
-    if constexpr (KVB) {
-        const uint2 w = *reinterpret_cast<const uint2*>((const uint16_t*)base + e);
-        return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
-                           __uint_as_float(w.y & 0xFFFF0000u));
+    return *reinterpret_cast<const float4*>((const float*)base + e);
+}
+
+// Raw bf16 bits of dims 8c..8c+7 of key j (bf16 caches), from the same places as pf_kv4_f32.
+__device__ __forceinline__ uint4 pf_kv8_bf16(const void* cache, const void* fresh, const PfAttnArgs& a, int kv, int j,
+                                             int c, int sp) {
+    constexpr int D = 128;
+    size_t e;
+    const void* base;
+    if (j >= a.start_pos) {
+        base = fresh;
+        e = ((size_t)kv * a.n + (j - a.start_pos)) * D + 8 * c;
     } else {
-        return *reinterpret_cast<const float4*>((const float*)base + e);
+        int sl = j;
+        if (a.ring) {
+            sl = sp - (a.start_pos - j);
+            sl += sl < 0 ? (int)a.slots : 0;
+        }
+        base = cache;
+        e = ((size_t)kv * a.slots + sl) * D + 8 * c;
     }
+    return *reinterpret_cast<const uint4*>((const uint16_t*)base + e);
 }
 
 template <int G, bool KVB>
@@ -463,25 +479,40 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
     const int sp = a.ring ? a.start_pos % (int)a.slots : 0;
     for (int kb = klo; kb <= khi; kb += 16) {
         __syncthreads();
-        for (int u = tid; u < 16 * D / 4; u += blockDim.x) {
-            const int kr = u / (D / 4), c = u % (D / 4);
-            const int j = min(kb + kr, khi);
-            const float4 k4 = pf_kv4<KVB>(a.k_cache, a.k_new, a, kv, j, c, sp);
-            uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-            pf_split(k4.x, h0, l0);
-            pf_split(k4.y, h1, l1);
-            pf_split(k4.z, h2, l2);
-            pf_split(k4.w, h3, l3);
-            *reinterpret_cast<uint2*>(&sKh[kr * KPB + 4 * c]) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-            *reinterpret_cast<uint2*>(&sKl[kr * KPB + 4 * c]) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
-            const float4 v4 = pf_kv4<KVB>(a.v_cache, a.v_new, a, kv, j, c, sp);
-            const float ve[4] = {v4.x, v4.y, v4.z, v4.w};
+        if constexpr (KVB) {   // a bf16 value is its own hi plane; its lo plane is zero and never staged
+            for (int u = tid; u < 16 * D / 8; u += blockDim.x) {
+                const int kr = u / (D / 8), c = u % (D / 8);
+                const int j = min(kb + kr, khi);
+                *reinterpret_cast<uint4*>(&sKh[kr * KPB + 8 * c]) = pf_kv8_bf16(a.k_cache, a.k_new, a, kv, j, c, sp);
+                const uint4 vw = pf_kv8_bf16(a.v_cache, a.v_new, a, kv, j, c, sp);
+                const uint32_t w[4] = {vw.x, vw.y, vw.z, vw.w};
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                uint32_t vh, vl;
-                pf_split(ve[e], vh, vl);
-                sVth[(4 * c + e) * VTP + kr] = (uint16_t)vh;
-                sVtl[(4 * c + e) * VTP + kr] = (uint16_t)vl;
+                for (int e = 0; e < 4; e++) {
+                    sVth[(8 * c + 2 * e) * VTP + kr] = (uint16_t)(w[e] & 0xFFFFu);
+                    sVth[(8 * c + 2 * e + 1) * VTP + kr] = (uint16_t)(w[e] >> 16);
+                }
+            }
+        } else {
+            for (int u = tid; u < 16 * D / 4; u += blockDim.x) {
+                const int kr = u / (D / 4), c = u % (D / 4);
+                const int j = min(kb + kr, khi);
+                const float4 k4 = pf_kv4_f32(a.k_cache, a.k_new, a, kv, j, c, sp);
+                uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+                pf_split(k4.x, h0, l0);
+                pf_split(k4.y, h1, l1);
+                pf_split(k4.z, h2, l2);
+                pf_split(k4.w, h3, l3);
+                *reinterpret_cast<uint2*>(&sKh[kr * KPB + 4 * c]) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                *reinterpret_cast<uint2*>(&sKl[kr * KPB + 4 * c]) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+                const float4 v4 = pf_kv4_f32(a.v_cache, a.v_new, a, kv, j, c, sp);
+                const float ve[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    uint32_t vh, vl;
+                    pf_split(ve[e], vh, vl);
+                    sVth[(4 * c + e) * VTP + kr] = (uint16_t)vh;
+                    sVtl[(4 * c + e) * VTP + kr] = (uint16_t)vl;
+                }
             }
         }
         __syncthreads();
@@ -490,9 +521,11 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 4; ks++) {
             const bf16x8_t kh = *reinterpret_cast<const bf16x8_t*>(&sKh[l16 * KPB + 32 * ks + 8 * l4]);
-            const bf16x8_t kl = *reinterpret_cast<const bf16x8_t*>(&sKl[l16 * KPB + 32 * ks + 8 * l4]);
             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[ks], kh, sc, 0, 0, 0);
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[ks], kl, sc, 0, 0, 0);
+            if constexpr (!KVB) {
+                const bf16x8_t kl = *reinterpret_cast<const bf16x8_t*>(&sKl[l16 * KPB + 32 * ks + 8 * l4]);
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[ks], kl, sc, 0, 0, 0);
+            }
             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[ks], kh, sc, 0, 0, 0);
         }
         // sc[r] = S[position 4 l4 + r][key kb + l16]
@@ -531,9 +564,11 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
 #pragma unroll
             for (int gi = 0; gi < 8; gi++) {
                 const bf16x4_t vh = *reinterpret_cast<const bf16x4_t*>(&sVth[(16 * gi + l16) * VTP + 4 * l4]);
-                const bf16x4_t vl = *reinterpret_cast<const bf16x4_t*>(&sVtl[(16 * gi + l16) * VTP + 4 * l4]);
                 o[gi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vh, o[gi], 0, 0, 0);
-                o[gi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vl, o[gi], 0, 0, 0);
+                if constexpr (!KVB) {
+                    const bf16x4_t vl = *reinterpret_cast<const bf16x4_t*>(&sVtl[(16 * gi + l16) * VTP + 4 * l4]);
+                    o[gi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vl, o[gi], 0, 0, 0);
+                }
                 o[gi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vh, o[gi], 0, 0, 0);
             }
         }
