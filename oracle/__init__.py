@@ -202,6 +202,36 @@ def argmax(x):
     return int(lib().orc_argmax(_p(x), x.size))
 
 
+def sample_top_p(logits, temperature, top_p, u):
+    """Token drawn from the logits with temperature and nucleus (top-p) filtering, the
+    card's sampling settings being temperature 0.6 and top-p 0.95 ("ATLAS-OLMo-3-32B-
+    Think-v4", Benchmarks; Prompting guide). In float64:
+
+      temperature <= 0: greedy, the first index of the maximum;
+      p_i proportional to e_i = exp((l_i - max l) / temperature);
+      nucleus: the fewest most-probable tokens whose mass reaches top_p (of the total),
+        tokens tied with the last one included, i.e. N = {i : e_i >= tau} with tau the
+        e of the k-th largest token, k the smallest count whose mass reaches top_p;
+      draw: u in [0, 1) is the uniform variate; the token is the first i of N, in
+        ascending index order, whose cumulative mass over N exceeds u * mass(N).
+
+    The random variate is an input, so the result is a function of (logits, u)."""
+    l = np.asarray(logits, np.float64)
+    if temperature <= 0:
+        return int(np.argmax(l))
+    e = np.exp((l - l.max()) / float(temperature))
+    total = e.sum()
+    order = np.argsort(-e, kind="stable")        # descending, ties by index
+    cum = np.cumsum(e[order])
+    k = int(np.searchsorted(cum, float(top_p) * total, side="left"))   # first prefix reaching top_p
+    k = min(k, e.size - 1)
+    tau = e[order[k]]
+    members = np.nonzero(e >= tau)[0]            # ascending index order
+    cn = np.cumsum(e[members])
+    target = float(u) * cn[-1]
+    return int(members[np.searchsorted(cn, target, side="right")])
+
+
 def embed(row_bits):
     r = _c(row_bits, np.uint16)
     x = np.empty(r.size, np.float32)
