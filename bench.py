@@ -303,6 +303,30 @@ def main():
                 "kernel": f"gate_up_kernel (2 x {m.dff}x{m.d} W4 + SwiGLU)", "bytes_per_launch": per_launch,
                 "avg_launch_us": round(avg_s * 1e6, 2), "launches": cnt}
 
+    sampling = None
+    if head:   # the on-device sampler at the card's settings, on this step's logits
+        wss = torch.empty(ops.atlas_sample_workspace_bytes(m.vocab), dtype=torch.uint8, device=dev)
+        du = torch.tensor([0.5], dtype=torch.float32, device=dev)
+        tok_s = torch.empty(1, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            ops.atlas_sample(logits, 0.6, 0.95, du, tok_s, wss)
+        torch.cuda.synchronize()
+        n_calls = 50
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n_calls):
+            ops.atlas_sample(logits, 0.6, 0.95, du, tok_s, wss)
+        e1.record()
+        torch.cuda.synchronize()
+        ops.atlas_profile_start(64)
+        ops.atlas_sample(logits, 0.6, 0.95, du, tok_s, wss)
+        sp = ops.atlas_profile_stop()
+        sampling = {"temperature": 0.6, "top_p": 0.95, "vocab": m.vocab,
+                    "us_per_call": round(e0.elapsed_time(e1) * 1e3 / n_calls, 2),
+                    "kernels_us": {k: round(v[1] / v[0] * 1e3, 2) for k, v in sp.items()},
+                    "note": "timed apart from the greedy step above"}
+        log(f"sampling: {sampling['us_per_call']} us per call")
+
     stream = None
     if args.stream_probe_gib > 0:
         nbytes = int(args.stream_probe_gib * 2**30) // 16 * 16
@@ -371,6 +395,7 @@ def main():
         "achievable_read": stream,
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "sampling": sampling,
     }
     print(json.dumps(out), flush=True)
 

@@ -237,6 +237,23 @@ ATLAS_API size_t atlas_prefill_workspace_bytes(const atlas_model* m, int32_t n_t
 ATLAS_API int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int32_t n_tokens, int32_t start_pos,
                   float* d_last_logits, int32_t* d_argmax, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- on-device sampling -------------------------------------------------------------
+ * Draws the next token from logits (f32 [vocab], device) with temperature and nucleus
+ * (top-p) filtering ([card] Benchmarks and Prompting guide: served with temperature
+ * 0.6, top-p 0.95). p_i is proportional to exp((l_i - max l) / temperature); the
+ * nucleus is the fewest most-probable tokens whose mass reaches top_p, with tokens
+ * tied with the last one included; the token is the first nucleus member, in
+ * ascending index order, whose cumulative mass exceeds u times the nucleus mass,
+ * u = *d_u (device float, clamped into [0, 1)). Masses are summed exactly in 2^-32
+ * units, so the draw is deterministic. temperature == 0: greedy (first index of the
+ * maximum; d_u and top_p unused). *d_token (device int32) receives the token.
+ * vocab in [1, 2^21]; top_p in (0, 1]; ws: atlas_sample_workspace_bytes(vocab) bytes
+ * of device memory. Asynchronous on `stream`; calls sharing a workspace must not
+ * overlap. */
+ATLAS_API size_t atlas_sample_workspace_bytes(int32_t vocab);
+ATLAS_API int atlas_sample(const float* d_logits, int32_t vocab, float temperature, float top_p, const float* d_u,
+                 int32_t* d_token, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- read-bandwidth probe (measurement aid) -------------------------------------------
  * Reads `bytes` (a positive multiple of 16) of the device buffer d_buf (16-byte
  * aligned) with a plain grid-stride streaming kernel of `blocks` blocks (1..65536) of

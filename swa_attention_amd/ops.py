@@ -256,6 +256,27 @@ def atlas_prefill(m: Model, d_tokens, start_pos=0, logits=None, argmax=None, ws=
 
 # ---- read-bandwidth probe (measurement aid) ------------------------------------------------------
 
+def atlas_sample_workspace_bytes(vocab):
+    return L.lib().atlas_sample_workspace_bytes(vocab)
+
+
+def atlas_sample(logits, temperature, top_p=1.0, d_u=None, token=None, ws=None, stream=None):
+    """Next token from device logits (f32 [vocab]) with temperature and nucleus
+    filtering; d_u: device f32 [1] uniform variate (unused when temperature == 0)."""
+    _dev(logits, F32, "logits")
+    if d_u is not None:
+        _dev(d_u, F32, "d_u")
+    if token is None:
+        token = torch.empty(1, dtype=I32, device=logits.device)
+    _dev(token, I32, "token")
+    V = logits.numel()
+    if ws is None:
+        ws = torch.empty(max(atlas_sample_workspace_bytes(V), 1), dtype=torch.uint8, device=logits.device)
+    L.call("atlas_sample", L.ptr(logits), V, float(temperature), float(top_p), L.ptr(d_u), L.ptr(token), L.ptr(ws),
+           ws.numel(), L.stream_ptr(stream))
+    return token
+
+
 def atlas_stream_read(buf, blocks=512, sink=None, stream=None):
     """Plain streaming read of the device tensor `buf` (its bytes, a multiple of 16) by
     `blocks` blocks of 256 threads; returns the one-word sink."""

@@ -118,6 +118,21 @@ def test_kv_layout_attention_validation(lib):
     assert call((1, 1, 4096), pos=None) == L.ATLAS_ERR_INVALID_ARG
 
 
+def test_sample_validation(lib):
+    ws = lib.atlas_sample_workspace_bytes(100278)
+    assert ws > 100278 * 4
+    assert lib.atlas_sample_workspace_bytes(0) == 0
+    s = lib.atlas_sample
+    assert s(None, 100278, 0.6, 0.95, FAKE, FAKE, FAKE, ws, None) == L.ATLAS_ERR_INVALID_ARG
+    assert s(FAKE, 0, 0.6, 0.95, FAKE, FAKE, FAKE, ws, None) == L.ATLAS_ERR_INVALID_ARG
+    assert s(FAKE, 100278, -1.0, 0.95, FAKE, FAKE, FAKE, ws, None) == L.ATLAS_ERR_INVALID_ARG
+    assert s(FAKE, 100278, float("nan"), 0.95, FAKE, FAKE, FAKE, ws, None) == L.ATLAS_ERR_INVALID_ARG
+    assert s(FAKE, 100278, 0.6, 0.0, FAKE, FAKE, FAKE, ws, None) == L.ATLAS_ERR_INVALID_ARG
+    assert s(FAKE, 100278, 0.6, 1.5, FAKE, FAKE, FAKE, ws, None) == L.ATLAS_ERR_INVALID_ARG
+    assert s(FAKE, 100278, 0.6, 0.95, None, FAKE, FAKE, ws, None) == L.ATLAS_ERR_INVALID_ARG   # needs u
+    assert s(FAKE, 100278, 0.6, 0.95, FAKE, FAKE, FAKE, ws - 1, None) == L.ATLAS_ERR_WORKSPACE_TOO_SMALL
+
+
 def _fake_model(n_layers=2, **over):
     m = dict(d=640, hq=5, hkv=1, hd=128, dff=1728)
     m.update(over)
