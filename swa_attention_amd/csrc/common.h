@@ -132,10 +132,18 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as
 // bfloat16 bits of x, rounded to nearest with ties to even (a carry from the
 // significand moves into the exponent, so overflow gives infinity); NaN stays a quiet
 // NaN with its sign.
+// Round to nearest even for finite x (the activation splits of the prefill).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne_finite(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// The same for any x, branch-free (values stored in a bf16 KV cache).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
     const uint32_t u = __float_as_uint(x);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet_nan = (u >> 16) | 0x40u;
+    return (u & 0x7FFFFFFFu) > 0x7F800000u ? quiet_nan : rounded;
 }
 
 __device__ __forceinline__ float scale_to_f32(uint16_t b, int scale_dtype) {

@@ -26,8 +26,8 @@ typedef short bf16x4_t __attribute__((ext_vector_type(4)));   // four bf16 (oper
 
 // x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (x - hi is exact in f32)
 __device__ __forceinline__ void pf_split(float x, uint32_t& hi, uint32_t& lo) {
-    hi = f32_to_bf16_rne(x);
-    lo = f32_to_bf16_rne(x - __uint_as_float(hi << 16));
+    hi = f32_to_bf16_rne_finite(x);
+    lo = f32_to_bf16_rne_finite(x - __uint_as_float(hi << 16));
 }
 
 // Store 4 consecutive values of a row as bf16 planes.
@@ -479,41 +479,66 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
     const int sp = a.ring ? a.start_pos % (int)a.slots : 0;
     for (int kb = klo; kb <= khi; kb += 16) {
         __syncthreads();
+        // A tile wholly inside the prompt (every tile when start_pos = 0) reads the prompt
+        // buffer directly; only a tile that reaches below start_pos goes through the
+        // per-key choice of buffer and the ring's slot map. kb is uniform: no divergence.
+        const bool fresh_tile = kb >= a.start_pos;
+        const size_t fresh0 = ((size_t)kv * a.n + (fresh_tile ? kb - a.start_pos : 0)) * D;
         if constexpr (KVB) {   // a bf16 value is its own hi plane; its lo plane is zero and never staged
-            for (int u = tid; u < 16 * D / 8; u += blockDim.x) {
-                const int kr = u / (D / 8), c = u % (D / 8);
-                const int j = min(kb + kr, khi);
-                *reinterpret_cast<uint4*>(&sKh[kr * KPB + 8 * c]) = pf_kv8_bf16(a.k_cache, a.k_new, a, kv, j, c, sp);
-                const uint4 vw = pf_kv8_bf16(a.v_cache, a.v_new, a, kv, j, c, sp);
-                const uint32_t w[4] = {vw.x, vw.y, vw.z, vw.w};
+            auto stage = [&](auto load8) {
+                for (int u = tid; u < 16 * D / 8; u += blockDim.x) {
+                    const int kr = u / (D / 8), c = u % (D / 8);
+                    const int j = min(kb + kr, khi);
+                    *reinterpret_cast<uint4*>(&sKh[kr * KPB + 8 * c]) = load8(a.k_cache, a.k_new, j, c);
+                    const uint4 vw = load8(a.v_cache, a.v_new, j, c);
+                    const uint32_t w[4] = {vw.x, vw.y, vw.z, vw.w};
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    sVth[(8 * c + 2 * e) * VTP + kr] = (uint16_t)(w[e] & 0xFFFFu);
-                    sVth[(8 * c + 2 * e + 1) * VTP + kr] = (uint16_t)(w[e] >> 16);
+                    for (int e = 0; e < 4; e++) {
+                        sVth[(8 * c + 2 * e) * VTP + kr] = (uint16_t)(w[e] & 0xFFFFu);
+                        sVth[(8 * c + 2 * e + 1) * VTP + kr] = (uint16_t)(w[e] >> 16);
+                    }
                 }
-            }
+            };
+            if (fresh_tile)
+                stage([&](const void*, const void* fresh, int j, int c) {
+                    return *reinterpret_cast<const uint4*>((const uint16_t*)fresh + fresh0 + (size_t)(j - kb) * D + 8 * c);
+                });
+            else
+                stage([&](const void* cache, const void* fresh, int j, int c) {
+                    return pf_kv8_bf16(cache, fresh, a, kv, j, c, sp);
+                });
         } else {
-            for (int u = tid; u < 16 * D / 4; u += blockDim.x) {
-                const int kr = u / (D / 4), c = u % (D / 4);
-                const int j = min(kb + kr, khi);
-                const float4 k4 = pf_kv4_f32(a.k_cache, a.k_new, a, kv, j, c, sp);
-                uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-                pf_split(k4.x, h0, l0);
-                pf_split(k4.y, h1, l1);
-                pf_split(k4.z, h2, l2);
-                pf_split(k4.w, h3, l3);
-                *reinterpret_cast<uint2*>(&sKh[kr * KPB + 4 * c]) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-                *reinterpret_cast<uint2*>(&sKl[kr * KPB + 4 * c]) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
-                const float4 v4 = pf_kv4_f32(a.v_cache, a.v_new, a, kv, j, c, sp);
-                const float ve[4] = {v4.x, v4.y, v4.z, v4.w};
+            auto stage = [&](auto load4) {
+                for (int u = tid; u < 16 * D / 4; u += blockDim.x) {
+                    const int kr = u / (D / 4), c = u % (D / 4);
+                    const int j = min(kb + kr, khi);
+                    const float4 k4 = load4(a.k_cache, a.k_new, j, c);
+                    uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+                    pf_split(k4.x, h0, l0);
+                    pf_split(k4.y, h1, l1);
+                    pf_split(k4.z, h2, l2);
+                    pf_split(k4.w, h3, l3);
+                    *reinterpret_cast<uint2*>(&sKh[kr * KPB + 4 * c]) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                    *reinterpret_cast<uint2*>(&sKl[kr * KPB + 4 * c]) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+                    const float4 v4 = load4(a.v_cache, a.v_new, j, c);
+                    const float ve[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    uint32_t vh, vl;
-                    pf_split(ve[e], vh, vl);
-                    sVth[(4 * c + e) * VTP + kr] = (uint16_t)vh;
-                    sVtl[(4 * c + e) * VTP + kr] = (uint16_t)vl;
+                    for (int e = 0; e < 4; e++) {
+                        uint32_t vh, vl;
+                        pf_split(ve[e], vh, vl);
+                        sVth[(4 * c + e) * VTP + kr] = (uint16_t)vh;
+                        sVtl[(4 * c + e) * VTP + kr] = (uint16_t)vl;
+                    }
                 }
-            }
+            };
+            if (fresh_tile)
+                stage([&](const void*, const void* fresh, int j, int c) {
+                    return *reinterpret_cast<const float4*>((const float*)fresh + fresh0 + (size_t)(j - kb) * D + 4 * c);
+                });
+            else
+                stage([&](const void* cache, const void* fresh, int j, int c) {
+                    return pf_kv4_f32(cache, fresh, a, kv, j, c, sp);
+                });
         }
         __syncthreads();
         // scores Q K^T: hi*hi + hi*lo + lo*hi (the lo*lo term is below 2^-16 of the product)

@@ -170,23 +170,41 @@ __global__ __launch_bounds__(SMP_SEL_THREADS) void sample_select_kernel(SampleAr
     for (int shift = 16; shift >= 0; shift -= 8) {
         if (t < 256) h[t] = 0;
         __syncthreads();
-        for (int i = t; i < a.V; i += SMP_SEL_THREADS) {
-            const float ev = a.e[i];
+        auto add = [&](float ev) {
             const uint32_t b = __float_as_uint(ev);
             if ((b >> (shift + 8)) == prefix) atomicAdd(&h[(b >> shift) & 255u], (unsigned long long)smp_mass(ev));
+        };
+        // 16-byte loads, several in flight per thread (e is 16-byte aligned)
+        const float4* e4 = reinterpret_cast<const float4*>(a.e);
+        const int V4 = a.V >> 2;
+#pragma unroll 4
+        for (int i = t; i < V4; i += SMP_SEL_THREADS) {
+            const float4 v = e4[i];
+            add(v.x);
+            add(v.y);
+            add(v.z);
+            add(v.w);
         }
+        for (int i = 4 * V4 + t; i < a.V; i += SMP_SEL_THREADS) add(a.e[i]);
         __syncthreads();
         smp_pick(h, suf, &s_target, &s_bin);
         prefix = (prefix << 8) | (uint32_t)s_bin;
     }
     const uint32_t tau = prefix;
-    // draw: chunk masses of the nucleus in index order, block scan, then the chunk
-    const int C = (a.V + SMP_SEL_THREADS - 1) / SMP_SEL_THREADS;
-    const int i0 = t * C, i1 = min(a.V, i0 + C);
+    // draw: chunk masses of the nucleus in index order, block scan, then the chunk;
+    // chunks are whole 16-byte groups
+    const int C = 4 * ((a.V + 4 * SMP_SEL_THREADS - 1) / (4 * SMP_SEL_THREADS));
+    const int i0 = min(a.V, t * C), i1 = min(a.V, i0 + C);
     unsigned long long m = 0;
-    for (int i = i0; i < i1; i++) {
-        const float ev = a.e[i];
-        if (__float_as_uint(ev) >= tau) m += smp_mass(ev);
+    {
+        auto nmass = [&](float ev) { return __float_as_uint(ev) >= tau ? smp_mass(ev) : 0ull; };
+        int i = i0;
+#pragma unroll 4
+        for (; i + 4 <= i1; i += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(a.e + i);
+            m += nmass(v.x) + nmass(v.y) + nmass(v.z) + nmass(v.w);
+        }
+        for (; i < i1; i++) m += nmass(a.e[i]);
     }
     chunk[t] = m;
     __syncthreads();
