@@ -237,6 +237,26 @@ ATLAS_API size_t atlas_prefill_workspace_bytes(const atlas_model* m, int32_t n_t
 ATLAS_API int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int32_t n_tokens, int32_t start_pos,
                   float* d_last_logits, int32_t* d_argmax, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- batched decode ------------------------------------------------------------------
+ * One token for each of `batch` sequences (1..16) through m->n_layers layers ([card]
+ * Limitations & roadmap: batched decode planned after batch-1 serving). By definition
+ * the result is `batch` independent decode steps (atlas_decode_step) with shared
+ * weights: sequence b feeds token d_tokens[b] at position d_pos[b] (device int32
+ * [batch]) into its own KV cache. Each layer's k_cache/v_cache hold the sequences back
+ * to back: [batch][Hkv][slots][D] in the model's KV format. The weights are read once
+ * per step for the whole batch: the projections run as W4 GEMMs on the matrix cores
+ * (the prefill's, split over K where the batch alone gives too few tiles), the lm_head
+ * as one bf16 matrix-core pass. Outputs (device, each may be NULL): d_hidden_out f32
+ * [batch][d] (last layer), d_logits f32 [batch][vocab], d_argmax int32 [batch] (first
+ * index of the maximum). Needs an embedding table, d % 64 == 0 and group 32 or a
+ * multiple of 64. ws: atlas_decode_batch_workspace_bytes(m, batch) bytes; its first
+ * word is the status word of atlas_device_status (ATLAS_ERR_INVALID_ARG for a token id
+ * or position out of range; such a sequence's cache is not written). */
+ATLAS_API size_t atlas_decode_batch_workspace_bytes(const atlas_model* m, int32_t batch);
+ATLAS_API int atlas_decode_batch(const atlas_model* m, const int32_t* d_tokens, const int32_t* d_pos, int32_t batch,
+                       float* d_hidden_out, float* d_logits, int32_t* d_argmax, void* ws, size_t ws_bytes,
+                       void* stream);
+
 /* ---- on-device sampling -------------------------------------------------------------
  * Draws the next token from logits (f32 [vocab], device) with temperature and nucleus
  * (top-p) filtering ([card] Benchmarks and Prompting guide: served with temperature

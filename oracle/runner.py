@@ -9,10 +9,10 @@ import oracle as O
 from synth import workloads as W
 
 
-def layer_inputs(wl, layer):
+def layer_inputs(wl, layer, n_cached=None, seq=0):
     m = wl.model
     T = W.layer_tensors(m, wl.seed, layer)
-    Kc, Vc = W.kv_cache(m, wl.seed, layer, wl.n_cached, wl.t_max)
+    Kc, Vc = W.kv_cache(m, wl.seed, layer, wl.n_cached if n_cached is None else n_cached, wl.t_max, seq)
     return T, Kc, Vc
 
 
@@ -31,27 +31,41 @@ def decode_token(wl):
     return int(W.prompt_tokens(wl.model, wl.seed, 1)[0])
 
 
-def run_decode(wl, n_layers=None, token=None, keep_hidden=False):
+def run_decode(wl, n_layers=None, token=None, keep_hidden=False, seq=0, keep_kv=False):
     """Full decode step: embed -> n_layers layers -> final norm -> bf16 lm_head ->
-    argmax. Returns dict(logits, argmax, y, hidden=[per-layer outputs])."""
+    argmax, for sequence ``seq`` of the workload (its own caches, at position
+    wl.seq_cached(seq)). Returns dict(logits, argmax, y, hidden=[per-layer outputs],
+    and with keep_kv the new key/value of every layer: kv=[(k, v)])."""
     m = wl.model
     n_layers = m.n_layers if n_layers is None else n_layers
     if token is None:
         token = decode_token(wl)
+    pos = wl.seq_cached(seq)
     x = O.embed(W.embedding_rows(m, wl.seed, token, 1)[0])
     hidden = []
+    kv = []
     for l in range(n_layers):
-        T, Kc, Vc = layer_inputs(wl, l)
-        x = O.layer_step(m, m.layer_types[l], T, x, Kc, Vc, wl.n_cached)
+        T, Kc, Vc = layer_inputs(wl, l, pos, seq)
+        tr = {} if keep_kv else None
+        x = O.layer_step(m, m.layer_types[l], T, x, Kc, Vc, pos, tr)
+        if keep_kv:
+            kv.append((tr["k"], tr["v"]))
         if keep_hidden:
             hidden.append(x.copy())
         del T, Kc, Vc
-    out = {"y": x, "token": token, "hidden": hidden}
+    out = {"y": x, "token": token, "hidden": hidden, "kv": kv}
     if wl.final_head:
         lm = W.lm_head_rows(m, wl.seed, 0, m.vocab)
         logits, yh = O.final_logits(x, W.final_gain(m, wl.seed), lm, m.eps)
         out.update(logits=logits, argmax=O.argmax(logits), y_hat=yh)
     return out
+
+
+def run_decode_batch(wl, n_layers=None, keep_kv=False):
+    """A batched decode step is, by definition, one independent decode step per
+    sequence (own token, position and caches; shared weights)."""
+    toks = W.batch_tokens(wl)
+    return [run_decode(wl, n_layers, int(toks[b]), seq=b, keep_kv=keep_kv) for b in range(wl.batch)]
 
 
 def run_prefill(wl, tokens, n_layers=None, final=True):

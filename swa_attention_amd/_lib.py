@@ -71,6 +71,9 @@ _SIGS = {
     "atlas_prefill_workspace_bytes": (c_size_t, [P(atlas_model), c_int32]),
     "atlas_prefill": (ctypes.c_int, [P(atlas_model), c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                      c_size_t, c_void_p]),
+    "atlas_decode_batch_workspace_bytes": (c_size_t, [P(atlas_model), c_int32]),
+    "atlas_decode_batch": (ctypes.c_int, [P(atlas_model), c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                          c_void_p, c_size_t, c_void_p]),
     "atlas_sample_workspace_bytes": (c_size_t, [c_int32]),
     "atlas_sample": (ctypes.c_int, [c_void_p, c_int32, c_float, c_float, c_void_p, c_void_p, c_void_p, c_size_t,
                                     c_void_p]),

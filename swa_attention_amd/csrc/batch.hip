@@ -1,0 +1,505 @@
+// Batched decode: one token for each of B sequences (own token, position and KV cache,
+// shared weights), the weights read once per step for all of them.
+//
+// Source: "ATLAS-OLMo-3-32B-Think-v4", Limitations & roadmap (batch-1 serving today,
+// batched decode planned). A batch is by definition B independent decode steps. With
+// B tokens the projections are skinny matrix products, so they run on the prefill's
+// matrix-core W4 GEMM over B rows (split over K for the narrow ones, so that the grid
+// still covers the chip), and the lm_head, read once for all rows, on bf16 matrix cores.
+// Per layer:
+//   w4_gemm (qkv, split-K) -> bd_rope (sum of the splits, QK norm, rotary at each
+//   row's position, k/v into that sequence's cache) -> attn_kernel over (splits, KV
+//   heads, sequences) -> merge -> pf_split -> w4_gemm (o, split-K) -> bd_residual ->
+//   w4_gemm (gate+up, SwiGLU) -> w4_gemm (down, split-K) -> bd_residual
+// then bd_final_norm -> bd_head (logits [B][V]) -> bd_argmax_rows.
+#include <cmath>
+
+#include "decode.h"
+#include "gemv.h"
+#include "norm_rope.h"
+#include "prefill_kernels.h"
+
+namespace atlas {
+
+typedef __bf16 bd_bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void bd_split(float x, uint32_t& hi, uint32_t& lo) {
+    hi = f32_to_bf16_rne_finite(x);
+    lo = f32_to_bf16_rne_finite(x - __uint_as_float(hi << 16));
+}
+
+// ---- QK norm, rotary and KV store per sequence -------------------------------------------------
+
+struct BdRopeArgs {
+    float* qkv;                // [B][ld]: the sum of the split partials; q rotated in place
+    const float* part;         // [parts][B][ld] partial projections
+    int parts;
+    size_t part_stride;
+    int ld, Hq, Hkv;
+    const float *g_q, *g_k;
+    float eps;
+    double inv[64];
+    double mscale;
+    const int32_t* d_pos;      // [B]
+    void* k_cache;             // [B][Hkv][slots][128], f32 or bf16
+    void* v_cache;
+    int64_t slots, seq_stride, T_max;
+    int ring, kv_bf16;
+    int* status;
+};
+
+__global__ __launch_bounds__(256) void bd_rope_kernel(BdRopeArgs a) {
+    constexpr int D = 128;
+    __shared__ float red[16];
+    __shared__ float s_cos[64], s_sin[64];
+    const int t = blockIdx.x;
+    const int pos = a.d_pos[t];
+    const int nq = a.Hq * D, nk = a.Hkv * D;
+    float* row = a.qkv + (size_t)t * a.ld;
+    for (int i = threadIdx.x; i < a.ld; i += blockDim.x) {
+        float sum = 0.f;
+        for (int p = 0; p < a.parts; p++) sum += a.part[p * a.part_stride + (size_t)t * a.ld + i];
+        row[i] = sum;
+    }
+    __syncthreads();
+    if (pos < 0 || pos >= a.T_max) {   // the attention of this row reports it too; nothing is stored
+        if (threadIdx.x == 0) *a.status = ATLAS_ERR_INVALID_ARG;
+        return;
+    }
+    float sq = 0.f, sk = 0.f;
+    for (int i = threadIdx.x; i < nq; i += blockDim.x) sq = fmaf(row[i], row[i], sq);
+    for (int i = threadIdx.x; i < nk; i += blockDim.x) sk = fmaf(row[nq + i], row[nq + i], sk);
+    sq = block_sum(sq, red);
+    sk = block_sum(sk, red);
+    const float rq = 1.0f / sqrtf(sq / (float)nq + a.eps);
+    const float rk = 1.0f / sqrtf(sk / (float)nk + a.eps);
+    if (threadIdx.x < 64) {
+        const double ang = (double)pos * a.inv[threadIdx.x];
+        const double rr = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+        float sn, cs;
+        sincosf((float)rr, &sn, &cs);
+        s_cos[threadIdx.x] = cs * (float)a.mscale;
+        s_sin[threadIdx.x] = sn * (float)a.mscale;
+    }
+    __syncthreads();
+    const int slot = a.ring ? pos % (int)a.slots : pos;
+    const size_t cache0 = (size_t)t * a.seq_stride + (size_t)slot * D;
+    const int npairs = (a.Hq + a.Hkv) * 64;
+    for (int u = threadIdx.x; u < npairs; u += blockDim.x) {
+        const int h = u >> 6, i = u & 63;
+        const bool isk = h >= a.Hq;
+        const float rr = isk ? rk : rq;
+        const float* g = isk ? a.g_k + (h - a.Hq) * D : a.g_q + h * D;
+        const int base = h * D;
+        const float x0 = g[i] * (row[base + i] * rr), x1 = g[i + 64] * (row[base + i + 64] * rr);
+        const float c = s_cos[i], sn = s_sin[i];
+        const float y0 = x0 * c - x1 * sn, y1 = x1 * c + x0 * sn;
+        if (isk) {
+            const size_t e = cache0 + (size_t)(h - a.Hq) * a.slots * D + i;
+            if (a.kv_bf16) {
+                ((uint16_t*)a.k_cache)[e] = (uint16_t)f32_to_bf16_rne(y0);
+                ((uint16_t*)a.k_cache)[e + 64] = (uint16_t)f32_to_bf16_rne(y1);
+            } else {
+                ((float*)a.k_cache)[e] = y0;
+                ((float*)a.k_cache)[e + 64] = y1;
+            }
+        } else {
+            row[base + i] = y0;
+            row[base + i + 64] = y1;
+        }
+    }
+    for (int u = threadIdx.x; u < nk; u += blockDim.x) {
+        const int h = u / D, i = u % D;
+        const size_t e = cache0 + (size_t)h * a.slots * D + i;
+        const float v = row[nq + nk + u];
+        if (a.kv_bf16) ((uint16_t*)a.v_cache)[e] = (uint16_t)f32_to_bf16_rne(v);
+        else ((float*)a.v_cache)[e] = v;
+    }
+}
+
+// ---- residual with split partials, final norm --------------------------------------------------
+
+// X[t] += g * A[t] / rms(A[t]) with A[t] the sum of `parts` partial rows; then the bf16
+// planes of the new X[t] for the next projection.
+__global__ __launch_bounds__(256) void bd_residual_kernel(float* X, const float* part, int parts, size_t part_stride,
+                                                         const float* g, int d, float eps, uint16_t* p_hi,
+                                                         uint16_t* p_lo, int ldp) {
+    extern __shared__ float s_a[];   // [d]
+    __shared__ float red[16];
+    const int t = blockIdx.x;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) {
+        float v = 0.f;
+        for (int p = 0; p < parts; p++) v += part[p * part_stride + (size_t)t * d + i];
+        s_a[i] = v;
+        ss = fmaf(v, v, ss);
+    }
+    ss = block_sum(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+    float* x = X + (size_t)t * d;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) {
+        const float h = x[i] + g[i] * (s_a[i] * r);
+        x[i] = h;
+        uint32_t hi, lo;
+        bd_split(h, hi, lo);
+        p_hi[(size_t)t * ldp + i] = (uint16_t)hi;
+        p_lo[(size_t)t * ldp + i] = (uint16_t)lo;
+    }
+}
+
+// y = g * X[t] / rms(X[t]) as bf16 planes (the final norm before the lm_head).
+__global__ __launch_bounds__(256) void bd_final_norm_kernel(const float* X, const float* g, int d, float eps,
+                                                           uint16_t* y_hi, uint16_t* y_lo, int ldy) {
+    __shared__ float red[16];
+    const int t = blockIdx.x;
+    const float* x = X + (size_t)t * d;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) ss = fmaf(x[i], x[i], ss);
+    ss = block_sum(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+    for (int i = threadIdx.x; i < d; i += blockDim.x) {
+        uint32_t hi, lo;
+        bd_split(g[i] * (x[i] * r), hi, lo);
+        y_hi[(size_t)t * ldy + i] = (uint16_t)hi;
+        y_lo[(size_t)t * ldy + i] = (uint16_t)lo;
+    }
+}
+
+// ---- lm_head over the batch: bf16 matrix cores, weights streamed once --------------------------
+
+// logits[m][n] = sum_k W[n][k] y[m][k] for m < B (<= 16), n < V. One wave per 16
+// vocabulary rows, on v_mfma_f32_16x16x32_bf16 with y = hi + lo: lane l holds the A
+// operand y[l % 16][k0 + 8 (l / 16) ..+8] and the B operand W[n0 + l % 16][same k],
+// both one 16-byte load, so the weights go from HBM to the matrix core without LDS;
+// each row is read 128 contiguous bytes per step (two k-steps of 32).
+constexpr int BD_HEAD_WAVES = 4;
+__global__ __launch_bounds__(64 * BD_HEAD_WAVES) void bd_head_kernel(const uint16_t* __restrict__ y_hi,
+                                                                      const uint16_t* __restrict__ y_lo, int ldy,
+                                                                      int B, const uint16_t* __restrict__ W, int V,
+                                                                      int d, float* __restrict__ logits) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n0 = (blockIdx.x * BD_HEAD_WAVES + wave) * 16;
+    if (n0 >= V) return;
+    const int l16 = lane & 15, kk = 8 * (lane >> 4);
+    const int n = min(n0 + l16, V - 1), m = min(l16, B - 1);
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4* wrow = reinterpret_cast<const u32x4*>(W + (size_t)n * d + kk);
+    const uint4* yh = reinterpret_cast<const uint4*>(y_hi + (size_t)m * ldy + kk);
+    const uint4* yl = reinterpret_cast<const uint4*>(y_lo + (size_t)m * ldy + kk);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int k0 = 0; k0 < d; k0 += 64) {
+        const int q = k0 / 8;   // in 16-byte units
+        const u32x4 w0 = __builtin_nontemporal_load(wrow + q), w1 = __builtin_nontemporal_load(wrow + q + 4);
+        const uint4 h0 = yh[q], l0 = yl[q], h1 = yh[q + 4], l1 = yl[q + 4];
+        const bd_bf16x8_t bw0 = __builtin_bit_cast(bd_bf16x8_t, w0), bw1 = __builtin_bit_cast(bd_bf16x8_t, w1);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bd_bf16x8_t, h0), bw0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bd_bf16x8_t, l0), bw0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bd_bf16x8_t, h1), bw1, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bd_bf16x8_t, l1), bw1, acc, 0, 0, 0);
+    }
+    // acc[r] = logits[row 4 (l / 16) + r][column n0 + l % 16]
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const int mm = 4 * (lane >> 4) + r, nn = n0 + l16;
+        if (mm < B && nn < V) logits[(size_t)mm * V + nn] = acc[r];
+    }
+}
+
+// First index of the maximum of each row of logits [B][V].
+__global__ __launch_bounds__(1024) void bd_argmax_rows_kernel(const float* logits, int V, int32_t* out) {
+    __shared__ float sv[1024];
+    __shared__ int si[1024];
+    const float* row = logits + (size_t)blockIdx.x * V;
+    float best = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int i = threadIdx.x; i < V; i += 1024) {
+        const float v = row[i];
+        if (v > best) {
+            best = v;
+            bi = i;
+        }
+    }
+    sv[threadIdx.x] = best;
+    si[threadIdx.x] = bi;
+    __syncthreads();
+    for (int o = 512; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) {
+            const float x = sv[threadIdx.x + o];
+            const int ix = si[threadIdx.x + o];
+            if (x > sv[threadIdx.x] || (x == sv[threadIdx.x] && ix < si[threadIdx.x])) {
+                sv[threadIdx.x] = x;
+                si[threadIdx.x] = ix;
+            }
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[blockIdx.x] = si[0];
+}
+
+// ---- host ----------------------------------------------------------------------------------------
+
+constexpr int BD_MAX_BATCH = 16;
+
+// Splits of K for a GEMM of `tiles` output tiles: the largest count (<= 16) that keeps
+// the grid within 320 blocks and each range a whole number of groups and 64-column tiles.
+int bd_ksplit(int tiles, int K, int group) {
+    int best = 1;
+    for (int s = 2; s <= 16; s++) {
+        if (tiles * s > 320) break;
+        if (K % s) continue;
+        const int c = K / s;
+        if (c % 64 || c % group) continue;
+        best = s;
+    }
+    return best;
+}
+
+struct BatchPlan {
+    int sq, so, sd;   // K splits of the qkv, o and down GEMMs
+    int S_swa, S_full, S_max;
+};
+
+static BatchPlan batch_plan(const atlas_model* m, int B) {
+    BatchPlan p{};
+    const int nq = m->hq * m->hd, nqkv = (m->hq + 2 * m->hkv) * m->hd;
+    const int MT = (B + 63) / 64;
+    p.sq = bd_ksplit(MT * ((nqkv + 127) / 128), m->d, m->layers[0].qkv.group);
+    p.so = bd_ksplit(MT * ((m->d + 127) / 128), nq, m->layers[0].o.group);
+    p.sd = bd_ksplit(MT * ((m->d + 127) / 128), m->dff, m->layers[0].down.group);
+    for (int l = 1; l < m->n_layers; l++) {   // one plan for every layer: take splits all layers allow
+        const atlas_layer& L = m->layers[l];
+        if (m->d % (p.sq * L.qkv.group) || (m->d / p.sq) % 64) p.sq = 1;
+        if (nq % (p.so * L.o.group) || (nq / p.so) % 64) p.so = 1;
+        if (m->dff % (p.sd * L.down.group) || (m->dff / p.sd) % 64) p.sd = 1;
+    }
+    const int64_t swa_keys = m->window > 0 ? std::min<int64_t>(m->window, m->t_max) : m->t_max;
+    p.S_swa = attn_splits(swa_keys, m->hkv * B);
+    p.S_full = attn_splits(m->t_max, m->hkv * B);
+    p.S_max = std::max(p.S_swa, p.S_full);
+    return p;
+}
+
+struct BatchWs {
+    int* status;
+    float *X, *qkv, *qkv_part, *o, *attn_part, *a_part, *logits;
+    uint16_t *p1h, *p1l, *p2h, *p2l;
+    int ld1;
+    size_t bytes;
+};
+
+static BatchWs carve_batch(const atlas_model* m, int B, const BatchPlan& p, void* base, bool need_logits) {
+    BatchWs w{};
+    char* b = (char*)base;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        void* q = b ? b + off : nullptr;
+        off += align_up(bytes, 256);
+        return q;
+    };
+    const int nq = m->hq * m->hd, nqkv = (m->hq + 2 * m->hkv) * m->hd;
+    w.ld1 = std::max(m->d, nq);
+    w.status = (int*)take(256);
+    w.X = (float*)take((size_t)B * m->d * 4);
+    w.qkv = (float*)take((size_t)B * nqkv * 4);
+    w.qkv_part = (float*)take((size_t)p.sq * B * nqkv * 4);
+    w.o = (float*)take((size_t)B * nq * 4);
+    w.attn_part = (float*)take((size_t)B * m->hq * p.S_max * ATTN_PART_F * 4);
+    w.a_part = (float*)take((size_t)std::max(p.so, p.sd) * B * m->d * 4);
+    w.p1h = (uint16_t*)take((size_t)B * w.ld1 * 2);
+    w.p1l = (uint16_t*)take((size_t)B * w.ld1 * 2);
+    w.p2h = (uint16_t*)take((size_t)B * m->dff * 2);
+    w.p2l = (uint16_t*)take((size_t)B * m->dff * 2);
+    w.logits = need_logits ? (float*)take((size_t)B * m->vocab * 4) : nullptr;
+    w.bytes = off;
+    return w;
+}
+
+static W4View bview(const atlas_w4& w) { return w4_view(w.qweight, w.scales, w.zeros, w.N, w.K, w.group, w.scale_dtype); }
+
+static GemmArgs bgemm(const uint16_t* hi, const uint16_t* lo, int lda, const atlas_w4& w, int M) {
+    GemmArgs g{};
+    g.a_hi = hi;
+    g.a_lo = lo;
+    g.lda = lda;
+    g.W0 = bview(w);
+    g.W1 = g.W0;
+    g.M = M;
+    g.N = w.N;
+    g.K = w.K;
+    g.group = w.group;
+    return g;
+}
+
+static int validate_batch(const atlas_model* m, int B) {
+    int rc = validate_model(m);
+    if (rc) return rc;
+    ATLAS_CHECK_ARG(B >= 1 && B <= BD_MAX_BATCH, "batch=%d outside [1, %d]", B, BD_MAX_BATCH);
+    ATLAS_CHECK_ARG(m->embedding, "batched decode needs an embedding table");
+    ATLAS_CHECK_SHAPE(m->d % 64 == 0, "batched decode needs d %% 64 == 0 (d=%d)", m->d);
+    for (int l = 0; l < m->n_layers; l++) {
+        const atlas_layer& L = m->layers[l];
+        const atlas_w4* ws[5] = {&L.qkv, &L.o, &L.gate, &L.up, &L.down};
+        for (const atlas_w4* w : ws)
+            ATLAS_CHECK_SHAPE(gemm_supported(w->group), "batched decode needs group 32 or a multiple of 64 (layer %d)",
+                              l);
+    }
+    return ATLAS_OK;
+}
+
+}  // namespace atlas
+
+using namespace atlas;
+
+extern "C" size_t atlas_decode_batch_workspace_bytes(const atlas_model* m, int32_t batch) {
+    if (validate_batch(m, batch) != ATLAS_OK) return 0;
+    return carve_batch(m, batch, batch_plan(m, batch), nullptr, true).bytes;
+}
+
+extern "C" int atlas_decode_batch(const atlas_model* m, const int32_t* d_tokens, const int32_t* d_pos, int32_t batch,
+                                  float* d_hidden_out, float* d_logits, int32_t* d_argmax, void* ws, size_t ws_bytes,
+                                  void* stream) {
+    int rc = validate_batch(m, batch);
+    if (rc) return rc;
+    ATLAS_CHECK_ARG(d_tokens && d_pos && ws, "null pointer");
+    const bool head = d_logits || d_argmax;
+    ATLAS_CHECK_ARG(!head || (m->lm_head && m->g_final && m->vocab >= 1), "lm_head/g_final/vocab missing");
+    const int B = batch;
+    const BatchPlan p = batch_plan(m, B);
+    const BatchWs w = carve_batch(m, B, p, ws, true);
+    if (ws_bytes < w.bytes) return fail(ATLAS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu", ws_bytes, w.bytes);
+    hipStream_t st = (hipStream_t)stream;
+    const int d = m->d, nq = m->hq * m->hd, nqkv = (m->hq + 2 * m->hkv) * m->hd;
+    RopeTable rt_swa, rt_full;
+    rope_table(&m->rope_swa, m->hd, &rt_swa);
+    rope_table(&m->rope_full, m->hd, &rt_full);
+    // the embedding kernel writes the status word first (ATLAS_OK, or a bad token id)
+    if ((rc = launch_pf_embed(d_tokens, B, m->embedding, m->vocab, d, w.X, w.p1h, w.p1l, w.ld1, w.status, st)))
+        return rc;
+    for (int l = 0; l < m->n_layers; l++) {
+        const atlas_layer& L = m->layers[l];
+        const bool ring = m->swa_ring && L.type == 0;
+        const int64_t slots = ring ? m->window : m->t_max;
+        const int64_t seq_stride = (int64_t)m->hkv * slots * m->hd;
+        // qkv projection of the B rows, split over K
+        GemmArgs qa = bgemm(w.p1h, w.p1l, w.ld1, L.qkv, B);
+        qa.C = w.qkv_part;
+        qa.ldc = nqkv;
+        qa.ksplit = p.sq;
+        qa.kchunk = d / p.sq;
+        qa.c_split = (size_t)B * nqkv;
+        if ((rc = launch_w4_gemm(qa, 0, st, "bd_gemm_qkv"))) return rc;
+        // QK norm, rotary at each row's position, k/v into each sequence's cache
+        BdRopeArgs ra{};
+        ra.qkv = w.qkv;
+        ra.part = w.qkv_part;
+        ra.parts = p.sq;
+        ra.part_stride = (size_t)B * nqkv;
+        ra.ld = nqkv;
+        ra.Hq = m->hq;
+        ra.Hkv = m->hkv;
+        ra.g_q = L.g_q;
+        ra.g_k = L.g_k;
+        ra.eps = m->eps;
+        const RopeTable& rt = L.type == 1 ? rt_full : rt_swa;
+        for (int i = 0; i < 64; i++) ra.inv[i] = rt.inv[i];
+        ra.mscale = rt.mscale;
+        ra.d_pos = d_pos;
+        ra.k_cache = L.k_cache;
+        ra.v_cache = L.v_cache;
+        ra.slots = slots;
+        ra.seq_stride = seq_stride;
+        ra.T_max = m->t_max;
+        ra.ring = ring ? 1 : 0;
+        ra.kv_bf16 = m->kv_dtype;
+        ra.status = w.status;
+        prof_mark("bd_qk_norm_rope", st);
+        ATLAS_KLAUNCH(bd_rope_kernel, dim3(B), dim3(256), 0, st, ra);
+        ATLAS_LAUNCH_CHECK("bd_rope_kernel");
+        // attention per sequence, then the merge into o rows
+        AttnFusedArgs aa{};
+        aa.k_cache = L.k_cache;
+        aa.v_cache = L.v_cache;
+        aa.T_max = m->t_max;
+        aa.slots = slots;
+        aa.ring = ring ? 1 : 0;
+        aa.kv_bf16 = m->kv_dtype;
+        aa.d_pos = d_pos;
+        aa.Hq = m->hq;
+        aa.Hkv = m->hkv;
+        aa.window = L.type == 1 ? 0 : m->window;
+        aa.S = L.type == 1 ? p.S_full : p.S_swa;
+        aa.scale = 1.0f / std::sqrt((float)m->hd);
+        aa.part = w.attn_part;
+        aa.status = w.status;
+        aa.fused = 0;
+        aa.q_final = w.qkv;
+        aa.batch = B;
+        aa.q_stride = nqkv;
+        aa.seq_stride = seq_stride;
+        aa.part_stride = (int64_t)m->hq * aa.S * ATTN_PART_F;
+        if ((rc = launch_attn_fused(aa, m->hq / m->hkv, st))) return rc;
+        MergeArgs ma{};
+        ma.part = w.attn_part;
+        ma.S = aa.S;
+        ma.Hq = m->hq;
+        ma.o = w.o;
+        ma.batch = B;
+        ma.part_stride = aa.part_stride;
+        ma.o_stride = nq;
+        if ((rc = launch_merge(ma, st))) return rc;
+        if ((rc = launch_pf_split(w.o, B, nq, nq, w.p1h, w.p1l, w.ld1, st))) return rc;
+        // o projection (split over K), h = x + RMSNorm_pa(a)
+        GemmArgs oa = bgemm(w.p1h, w.p1l, w.ld1, L.o, B);
+        oa.C = w.a_part;
+        oa.ldc = d;
+        oa.ksplit = p.so;
+        oa.kchunk = nq / p.so;
+        oa.c_split = (size_t)B * d;
+        if ((rc = launch_w4_gemm(oa, 0, st, "bd_gemm_o"))) return rc;
+        prof_mark("bd_residual_norm", st);
+        ATLAS_KLAUNCH(bd_residual_kernel, dim3(B), dim3(256), (size_t)d * 4, st, w.X, w.a_part, p.so, (size_t)B * d,
+                      L.g_pa, d, m->eps, w.p1h, w.p1l, w.ld1);
+        ATLAS_LAUNCH_CHECK("bd_residual_kernel");
+        // gate/up with SwiGLU, then down (split over K), y = h + RMSNorm_pf(m)
+        GemmArgs ga = bgemm(w.p1h, w.p1l, w.ld1, L.gate, B);
+        ga.W1 = bview(L.up);
+        ga.z_hi = w.p2h;
+        ga.z_lo = w.p2l;
+        ga.ldz = m->dff;
+        if ((rc = launch_w4_gemm(ga, 1, st, "bd_gemm_gate_up"))) return rc;
+        GemmArgs da = bgemm(w.p2h, w.p2l, m->dff, L.down, B);
+        da.C = w.a_part;
+        da.ldc = d;
+        da.ksplit = p.sd;
+        da.kchunk = m->dff / p.sd;
+        da.c_split = (size_t)B * d;
+        if ((rc = launch_w4_gemm(da, 0, st, "bd_gemm_down"))) return rc;
+        prof_mark("bd_residual_norm", st);
+        ATLAS_KLAUNCH(bd_residual_kernel, dim3(B), dim3(256), (size_t)d * 4, st, w.X, w.a_part, p.sd, (size_t)B * d,
+                      L.g_pf, d, m->eps, w.p1h, w.p1l, w.ld1);
+        ATLAS_LAUNCH_CHECK("bd_residual_kernel");
+    }
+    if (d_hidden_out) {
+        rc = hipMemcpyAsync(d_hidden_out, w.X, (size_t)B * d * 4, hipMemcpyDeviceToDevice, st) == hipSuccess
+                 ? ATLAS_OK
+                 : fail(ATLAS_ERR_HIP, "hidden copy failed");
+        if (rc) return rc;
+    }
+    if (!head) return ATLAS_OK;
+    prof_mark("bd_final_norm", st);
+    ATLAS_KLAUNCH(bd_final_norm_kernel, dim3(B), dim3(256), 0, st, w.X, m->g_final, d, m->eps, w.p1h, w.p1l, w.ld1);
+    ATLAS_LAUNCH_CHECK("bd_final_norm_kernel");
+    float* logits = d_logits ? d_logits : w.logits;
+    const int head_blocks = (m->vocab + 16 * BD_HEAD_WAVES - 1) / (16 * BD_HEAD_WAVES);
+    prof_mark("bd_lm_head", st);
+    ATLAS_KLAUNCH(bd_head_kernel, dim3(head_blocks), dim3(64 * BD_HEAD_WAVES), 0, st, w.p1h, w.p1l, w.ld1, B,
+                  m->lm_head, m->vocab, d, logits);
+    ATLAS_LAUNCH_CHECK("bd_head_kernel");
+    if (d_argmax) {
+        prof_mark("bd_argmax", st);
+        ATLAS_KLAUNCH(bd_argmax_rows_kernel, dim3(B), dim3(1024), 0, st, logits, m->vocab, d_argmax);
+        ATLAS_LAUNCH_CHECK("bd_argmax_rows_kernel");
+    }
+    return ATLAS_OK;
+}

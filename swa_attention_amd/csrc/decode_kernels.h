@@ -56,6 +56,10 @@ struct AttnFusedArgs {
     const float* q_final;      // fused == 0
     const float* ssq_part;     // fused: [n_ssq][2] sums of squares of q and k (qkv kernel)
     int n_ssq;
+    // batched decode (fused == 0): sequence z = blockIdx.z reads q_final + z * q_stride,
+    // position d_pos[z], caches + z * seq_stride elements, and writes part + z * part_stride
+    int batch;                 // 0 or 1: one sequence
+    int64_t q_stride, seq_stride, part_stride;
 };
 
 struct MergeArgs {
@@ -63,6 +67,9 @@ struct MergeArgs {
     int S, Hq;
     float* o;     // may be null
     XQ xq;        // planes may be null
+    // batched: sequence y = blockIdx.y reads part + y * part_stride, writes o + y * o_stride
+    int batch;    // 0 or 1: one sequence
+    int64_t part_stride, o_stride;
 };
 
 struct GemvPlanesArgs {    // encoded input already in global memory

@@ -529,14 +529,14 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
     __shared__ float red[16];
     __shared__ float s_wm[ATTN_WAVES][G], s_wl[ATTN_WAVES][G];
     __shared__ float s_wacc[ATTN_WAVES][G][D];
-    const int s = blockIdx.x, kv = blockIdx.y;
+    const int s = blockIdx.x, kv = blockIdx.y, bz = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane & 15, grp = lane >> 4;
     const int nq = a.Hq * D, nk = a.Hkv * D;
     // the position through a vector load (a scalar load would be waited for together
     // with the kernel arguments, before anything else is issued)
-    const int pos_v = a.d_pos[__builtin_amdgcn_mbcnt_lo(0u, 0u)];
-    float* part0 = a.part + (size_t)(kv * G) * a.S * ATTN_PART_F;
+    const int pos_v = a.d_pos[bz + (int)__builtin_amdgcn_mbcnt_lo(0u, 0u)];
+    float* part0 = a.part + (size_t)bz * a.part_stride + (size_t)(kv * G) * a.S * ATTN_PART_F;
     // Prologue inputs first (loads complete in issue order): the qkv kernel's per-block
     // sums of squares, this block's q heads and k/v head, and their gains. None depends
     // on the position, whose load is still in flight.
@@ -547,7 +547,8 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
     if (!FUSED) {
 #pragma unroll
         for (int r = 0; r < ATTN_QF_REGS; r++)
-            qf[r] = a.q_final[(size_t)kv * G * D + min((int)threadIdx.x + r * ATTN_THREADS, G * D - 1)];
+            qf[r] = a.q_final[(size_t)bz * a.q_stride + (size_t)kv * G * D +
+                              min((int)threadIdx.x + r * ATTN_THREADS, G * D - 1)];
     } else {
 #pragma unroll
         for (int j = 0; j < ATTN_SSQ_REGS; j++) {
@@ -596,7 +597,7 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
     const int slots = (int)a.slots;
     const int jb = cnt > 0 ? k0 : lo;
     const int sb = a.ring ? jb % slots : jb;
-    const size_t head0 = (size_t)kv * a.slots * D;
+    const size_t head0 = (size_t)bz * a.seq_stride + (size_t)kv * a.slots * D;
     // K/V of key i of this split (clamped into the split)
     auto load_kv = [&](int i, KvRegs<KVB>& r) {
         int sl = sb + (cnt > 0 ? min(i, cnt - 1) : 0);
@@ -797,7 +798,7 @@ __global__ __launch_bounds__(128) void merge_kernel(MergeArgs a) {
     __shared__ float s_o[128];
     __shared__ float s_M;
     const int h = blockIdx.x, d = threadIdx.x;
-    const float* p = a.part + (size_t)h * a.S * ATTN_PART_F;
+    const float* p = a.part + (size_t)blockIdx.y * a.part_stride + (size_t)h * a.S * ATTN_PART_F;
     // up to MERGE_REG_S split accumulators are loaded at once, in flight while the
     // maxima are reduced (32: the split count of 8 KV heads at one block per CU)
     constexpr int MERGE_REG_S = 32;
@@ -866,7 +867,7 @@ __global__ __launch_bounds__(128) void merge_kernel(MergeArgs a) {
         }
     }
     const float r = L > 0.f ? o / L : 0.f;
-    if (a.o) a.o[(size_t)h * 128 + d] = r;
+    if (a.o) a.o[(size_t)blockIdx.y * a.o_stride + (size_t)h * 128 + d] = r;
     if (a.xq.planes) {
         s_o[d] = r;
         __syncthreads();
@@ -1122,7 +1123,7 @@ int attn_splits(int64_t maxkeys, int Hkv) {
 }
 
 int launch_attn_fused(const AttnFusedArgs& a, int G, hipStream_t st) {
-    dim3 grid(a.S, a.Hkv);
+    dim3 grid(a.S, a.Hkv, std::max(1, a.batch));
     prof_mark(a.window > 0 ? "attn_window" : "attn_full", st);
     switch (G) {
 #define C(G_)                                                                           \
@@ -1146,7 +1147,7 @@ int launch_attn_fused(const AttnFusedArgs& a, int G, hipStream_t st) {
 int launch_merge(const MergeArgs& a, hipStream_t st) {
     if (a.S > MERGE_MAX_S) return fail(ATLAS_ERR_UNSUPPORTED_SHAPE, "too many key splits (%d)", a.S);
     prof_mark("attn_merge", st);
-    ATLAS_KLAUNCH(merge_kernel, dim3(a.Hq), dim3(128), 0, st, a);
+    ATLAS_KLAUNCH(merge_kernel, dim3(a.Hq, std::max(1, a.batch)), dim3(128), 0, st, a);
     ATLAS_LAUNCH_CHECK("merge_kernel");
     return ATLAS_OK;
 }

@@ -18,6 +18,10 @@ struct GemmArgs {
     uint16_t* z_hi;
     uint16_t* z_lo;
     int ldz;
+    // split-K (mode 0 only): ksplit ranges of kchunk columns (whole groups and k tiles);
+    // split s writes its partial product to C + s * c_split. ksplit = 1: no split.
+    int ksplit = 1, kchunk = 0;
+    size_t c_split = 0;
 };
 
 // KV of the prompt: keys j < start_pos come from the layer's cache ([Hkv][slots][128],

@@ -68,16 +68,18 @@ __global__ __launch_bounds__(GM_THREADS) void w4_gemm_kernel(GemmArgs a) {
     const int MT = (a.M + GM_BM - 1) / GM_BM;
     const int NW_ = MODE ? GM_BN / 2 : GM_BN;   // output columns per tile
     const int NT = (a.N + NW_ - 1) / NW_;
-    const int T = MT * NT, per = (T + 7) / 8;
-    const int L = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-    if (L >= T) return;
+    const int T = MT * NT, Wk = T * a.ksplit, per = (Wk + 7) / 8;
+    const int Lw = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (Lw >= Wk) return;
+    const int L = Lw % T, split = Lw / T;
+    const int k_lo = split * a.kchunk, k_hi = a.ksplit > 1 ? k_lo + a.kchunk : a.K;
     const int m0 = (L % MT) * GM_BM, n0 = (L / MT) * NW_;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     const int l16 = lane & 15, l4 = lane >> 4;
-    const int KT = (a.K + GM_BK - 1) / GM_BK;
+    const int KT = (k_hi - k_lo + GM_BK - 1) / GM_BK;
 
     // weight-tile row r -> matrix (second one for r >= 64 in mode 1) and row (clamped to N - 1)
     auto second = [&](int r) { return MODE && r >= GM_BN / 2; };
@@ -108,7 +110,7 @@ __global__ __launch_bounds__(GM_THREADS) void w4_gemm_kernel(GemmArgs a) {
     const size_t arow0 = (size_t)min(m0 + ar0, a.M - 1) * a.lda, arow1 = (size_t)min(m0 + ar1, a.M - 1) * a.lda;
 #define LOAD_TILE_K(kt_)                                                                                     \
     do {                                                                                                     \
-        const int kb_ = (kt_) * GM_BK;                                                                       \
+        const int kb_ = k_lo + (kt_) * GM_BK;                                                                \
         const size_t o0_ = arow0 + min(kb_ + ac0, a.K - 8), o1_ = arow1 + min(kb_ + ac1, a.K - 8);           \
         rAh0 = *reinterpret_cast<const uint4*>(a.a_hi + o0_);                                                \
         rAl0 = *reinterpret_cast<const uint4*>(a.a_lo + o0_);                                                \
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(GM_THREADS) void w4_gemm_kernel(GemmArgs a) {
 
     LOAD_TILE_K(0);
     for (int kt = 0; kt < KT; kt++) {
-        const int kb = kt * GM_BK, kn = min(GM_BK, a.K - kb);
+        const int kb = k_lo + kt * GM_BK, kn = min(GM_BK, k_hi - kb);
         __syncthreads();   // the previous tile's fragments have been read
         *reinterpret_cast<uint4*>(&sAh[ar0 * LDK + ac0]) = rAh0;
         *reinterpret_cast<uint4*>(&sAl[ar0 * LDK + ac0]) = rAl0;
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(GM_THREADS) void w4_gemm_kernel(GemmArgs a) {
                     accg[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[mf], b[nf], c, 0, 0, 0);
                 }
             const int kabs = kb + 32 * ks + 32;
-            if (kabs % a.group == 0 || kabs >= a.K) {   // group ends: scale and add
+            if (kabs % a.group == 0 || kabs >= k_hi) {   // group ends: scale and add
                 const int slot = a.group == 32 ? ks : 0;
 #pragma unroll
                 for (int nf = 0; nf < 4; nf++) {
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(GM_THREADS) void w4_gemm_kernel(GemmArgs a) {
 #pragma unroll
                 for (int nf = 0; nf < 4; nf++) {
                     const int col = n0 + bcol(nf) + l16;
-                    if (col < a.N) a.C[(size_t)row * a.ldc + col] = acc[mf][nf][r];
+                    if (col < a.N) a.C[split * a.c_split + (size_t)row * a.ldc + col] = acc[mf][nf][r];
                 }
             } else {
 #pragma unroll
@@ -625,7 +627,10 @@ int launch_w4_gemm(const GemmArgs& a, int mode, hipStream_t st, const char* labe
     ATLAS_CHECK_SHAPE(a.K % 32 == 0 && a.K >= 32 && a.lda % 8 == 0, "prefill GEMM shape K=%d lda=%d", a.K, a.lda);
     const int NW_ = mode ? GM_BN / 2 : GM_BN;
     const int MT = (a.M + GM_BM - 1) / GM_BM, NT = (a.N + NW_ - 1) / NW_;
-    const int T = MT * NT, blocks = 8 * ((T + 7) / 8);
+    ATLAS_CHECK_SHAPE(a.ksplit == 1 || (mode == 0 && a.ksplit > 1 && a.kchunk * a.ksplit == a.K &&
+                                        a.kchunk % GM_BK == 0 && a.kchunk % a.group == 0),
+                      "bad K split (%d x %d of K=%d)", a.ksplit, a.kchunk, a.K);
+    const int T = MT * NT * a.ksplit, blocks = 8 * ((T + 7) / 8);
     prof_mark(label, st);
     if (mode == 0) ATLAS_KLAUNCH((w4_gemm_kernel<0>), dim3(blocks), dim3(GM_THREADS), 0, st, a);
     else ATLAS_KLAUNCH((w4_gemm_kernel<1>), dim3(blocks), dim3(GM_THREADS), 0, st, a);

@@ -237,6 +237,30 @@ def atlas_decode_step(m: Model, d_pos, d_token=None, hidden_in=None, hidden_out=
            L.stream_ptr(stream))
 
 
+def atlas_decode_batch_workspace_bytes(m: Model, batch):
+    return L.lib().atlas_decode_batch_workspace_bytes(ctypes.byref(m.c()), batch)
+
+
+def atlas_decode_batch(m: Model, d_tokens, d_pos, hidden_out=None, logits=None, argmax=None, ws=None, stream=None,
+                       cm=None):
+    """One token for each of len(d_tokens) sequences; every layer's caches hold the
+    sequences back to back ([batch][Hkv][slots][D])."""
+    _dev(d_tokens, I32, "d_tokens")
+    _dev(d_pos, I32, "d_pos")
+    B = d_tokens.numel()
+    if d_pos.numel() != B:
+        raise ValueError("d_tokens and d_pos must have one entry per sequence")
+    for t, n, dt in ((hidden_out, "hidden_out", F32), (logits, "logits", F32), (argmax, "argmax", I32)):
+        _dev(t, dt, n)
+    c = cm if cm is not None else m.c()
+    if ws is None:
+        ws = torch.empty(max(L.lib().atlas_decode_batch_workspace_bytes(ctypes.byref(c), B), 1), dtype=torch.uint8,
+                         device=d_tokens.device)
+    L.call("atlas_decode_batch", ctypes.byref(c), L.ptr(d_tokens), L.ptr(d_pos), B, L.ptr(hidden_out), L.ptr(logits),
+           L.ptr(argmax), L.ptr(ws), ws.numel(), L.stream_ptr(stream))
+    return ws
+
+
 def atlas_device_status(ws, stream=None):
     out = ctypes.c_int32(-1)
     L.call("atlas_device_status", L.ptr(ws), L.stream_ptr(stream), ctypes.byref(out))

@@ -30,7 +30,10 @@ def rope_structs(model):
     return swa, full
 
 
-def layer_to_device(model, seed, layer, n_cached, t_max, device, tensors=None):
+def layer_to_device(model, seed, layer, n_cached, t_max, device, tensors=None, seq_cached=None):
+    """One layer's weights, gains and caches on the device. seq_cached: cached
+    positions of each sequence of a batch (the caches then hold the sequences back to
+    back, [batch][hkv][slots][hd]); None: one sequence with n_cached positions."""
     from swa_attention_amd.ops import Layer
     T = tensors if tensors is not None else W.layer_tensors(model, seed, layer)
     ws = {}
@@ -40,14 +43,19 @@ def layer_to_device(model, seed, layer, n_cached, t_max, device, tensors=None):
     # caches in the model's KV format: [hkv][slots][hd] f32, or bf16 bits held as int16
     slots = W.kv_slots(model, model.layer_types[layer], t_max)
     tdt = torch.int16 if model.kv_dtype == 1 else torch.float32
-    Kc = torch.zeros((model.hkv, slots, model.hd), dtype=tdt, device=device)
+    seqs = [n_cached] if seq_cached is None else list(seq_cached)
+    shape = (model.hkv, slots, model.hd) if seq_cached is None else (len(seqs), model.hkv, slots, model.hd)
+    Kc = torch.zeros(shape, dtype=tdt, device=device)
     Vc = torch.zeros_like(Kc)
-    if n_cached > 0:
-        hk = np.zeros((model.hkv, slots, model.hd), W.kv_np_dtype(model))
-        hv = np.zeros((model.hkv, slots, model.hd), W.kv_np_dtype(model))
-        W.kv_cache_into(model, seed, layer, n_cached, t_max, hk, hv)
-        Kc.copy_(torch.from_numpy(hk.view(np.int16) if model.kv_dtype == 1 else hk))
-        Vc.copy_(torch.from_numpy(hv.view(np.int16) if model.kv_dtype == 1 else hv))
+    for b, nc in enumerate(seqs):
+        if nc > 0:
+            hk = np.zeros((model.hkv, slots, model.hd), W.kv_np_dtype(model))
+            hv = np.zeros((model.hkv, slots, model.hd), W.kv_np_dtype(model))
+            W.kv_cache_into(model, seed, layer, nc, t_max, hk, hv, seq=b)
+            kd = Kc if seq_cached is None else Kc[b]
+            vd = Vc if seq_cached is None else Vc[b]
+            kd.copy_(torch.from_numpy(hk.view(np.int16) if model.kv_dtype == 1 else hk))
+            vd.copy_(torch.from_numpy(hv.view(np.int16) if model.kv_dtype == 1 else hv))
     g = {k: _t(T[k], device) for k in ("g_q", "g_k", "g_pa", "g_pf")}
     return Layer(ws["qkv"], ws["o"], ws["gate"], ws["up"], ws["down"], g["g_q"], g["g_k"], g["g_pa"], g["g_pf"],
                  Kc, Vc, model.layer_types[layer])
@@ -73,8 +81,9 @@ def build_model(wl, device="cuda", n_layers=None, head=None, progress=None):
     swa, full = rope_structs(m)
     dm = Model(m.d, m.hq, m.hkv, m.hd, m.dff, m.window, m.vocab, m.eps, wl.t_max, swa, full,
                kv_dtype=m.kv_dtype, swa_ring=int(m.swa_ring))
+    seq_cached = [wl.seq_cached(b) for b in range(wl.batch)] if wl.batch > 1 else None
     for l in range(n_layers):
-        dm.layers.append(layer_to_device(m, wl.seed, l, wl.n_cached, wl.t_max, device))
+        dm.layers.append(layer_to_device(m, wl.seed, l, wl.n_cached, wl.t_max, device, seq_cached=seq_cached))
         if progress:
             progress(l)
     if wl.use_tokens or head:

@@ -100,7 +100,13 @@ class Workload:
     use_tokens: bool = False   # config 3/4: embedding input; else x ~ N(0,1)
     final_head: bool = False   # final norm + lm_head + argmax
     prompt_len: int = 0        # prefill only
+    batch: int = 1             # batched decode: sequences decoded together
+    batch_gap: int = 0         # sequence b holds n_cached - b * batch_gap positions (ragged batch)
     extra: dict = field(default_factory=dict)
+
+    def seq_cached(self, b):
+        """Cached positions of sequence b of a batch (its new token sits there)."""
+        return self.n_cached - b * self.batch_gap
 
 
 def config(i):
@@ -146,8 +152,10 @@ def config(i):
     raise ValueError(i)
 
 
-def tid(model, layer, kind):
-    return (model.model_id << 48) | (layer << 16) | kind
+def tid(model, layer, kind, seq=0):
+    """Tensor id; ``seq`` numbers the sequences of a batch (their caches and tokens),
+    sequence 0 being the single-sequence workload's."""
+    return (model.model_id << 48) | (layer << 16) | (seq << 8) | kind
 
 
 def key(wl_or_model, seed, layer, kind):
@@ -197,23 +205,24 @@ def kv_np_dtype(model):
     return np.uint16 if model.kv_dtype == 1 else np.float32
 
 
-def kv_cache_into(model, seed, layer, n_cached, t_max, kdst, vdst):
+def kv_cache_into(model, seed, layer, n_cached, t_max, kdst, vdst, seq=0):
     """K and V caches [hkv][slots][hd] in the model's KV format (f32, or bf16 bits)
     holding positions 0..n_cached-1 ~ N(0,1) (a ring holds the last `slots` of them
-    at slot j mod slots). Slots not written are left as the caller's buffer holds them."""
+    at slot j mod slots); ``seq``: sequence of a batch. Slots not written are left as
+    the caller's buffer holds them."""
     slots = kv_slots(model, model.layer_types[layer], t_max)
     j0 = max(0, n_cached - slots)
     for kind, dst in ((K_KC, kdst), (K_VC, vdst)):
         if n_cached > 0:
-            S.normal_kv_into(S.key(seed, tid(model, layer, kind)), model.hkv, n_cached, model.hd, j0, slots,
+            S.normal_kv_into(S.key(seed, tid(model, layer, kind, seq)), model.hkv, n_cached, model.hd, j0, slots,
                              model.kv_dtype, 0.0, 1.0, dst)
 
 
-def kv_cache(model, seed, layer, n_cached, t_max):
+def kv_cache(model, seed, layer, n_cached, t_max, seq=0):
     slots = kv_slots(model, model.layer_types[layer], t_max)
     Kc = np.zeros((model.hkv, slots, model.hd), kv_np_dtype(model))
     Vc = np.zeros((model.hkv, slots, model.hd), kv_np_dtype(model))
-    kv_cache_into(model, seed, layer, n_cached, t_max, Kc, Vc)
+    kv_cache_into(model, seed, layer, n_cached, t_max, Kc, Vc, seq)
     return Kc, Vc
 
 
@@ -229,6 +238,12 @@ def final_gain(model, seed):
 
 def prompt_tokens(model, seed, n, stream=0):
     return S.tokens(S.key(seed, tid(model, GLOBAL_LAYER, K_TOK) + (stream << 8)), n, model.vocab)
+
+
+def batch_tokens(wl):
+    """The token each sequence of a batch feeds (sequence 0: the single-sequence
+    workload's token)."""
+    return np.array([int(prompt_tokens(wl.model, wl.seed, 1, stream=b * 16)[0]) for b in range(wl.batch)], np.int32)
 
 
 def embedding_rows(model, seed, r0, nr):

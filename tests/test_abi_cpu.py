@@ -175,6 +175,16 @@ def test_decode_step_validation(lib):
     ringbad.swa_ring, ringbad.window = 1, 0
     assert step(ctypes.byref(ringbad), FAKE, None, FAKE, None, None, None, FAKE, need, None) == \
         L.ATLAS_ERR_INVALID_ARG
+    bat = lib.atlas_decode_batch
+    bneed = lib.atlas_decode_batch_workspace_bytes(ctypes.byref(mm), 4)
+    assert bneed > 0
+    assert lib.atlas_decode_batch_workspace_bytes(ctypes.byref(mm), 0) == 0
+    assert lib.atlas_decode_batch_workspace_bytes(ctypes.byref(mm), 17) == 0
+    assert bat(ctypes.byref(mm), FAKE, FAKE, 0, None, None, None, FAKE, bneed, None) == L.ATLAS_ERR_INVALID_ARG
+    assert bat(ctypes.byref(mm), None, FAKE, 4, None, None, None, FAKE, bneed, None) == L.ATLAS_ERR_INVALID_ARG
+    assert bat(ctypes.byref(mm), FAKE, None, 4, None, None, None, FAKE, bneed, None) == L.ATLAS_ERR_INVALID_ARG
+    assert bat(ctypes.byref(mm), FAKE, FAKE, 4, None, None, None, FAKE, bneed - 1, None) == \
+        L.ATLAS_ERR_WORKSPACE_TOO_SMALL
     pre = lib.atlas_prefill
     pneed = lib.atlas_prefill_workspace_bytes(ctypes.byref(mm), 8)
     bf, keep8 = _fake_model()

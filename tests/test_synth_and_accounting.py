@@ -152,3 +152,21 @@ def test_card_format_layer_bytes_and_generator():
     wl = W.config(5)
     assert wl.model.symmetric and wl.model.group == 32 and wl.model.scale_dtype == 1
     assert A.decode_step_bytes(wl.model, 16384).w4 == 64 * 274_268_160
+
+
+def test_batch_sequence_zero_is_the_single_workload_and_others_differ():
+    """Sequence 0 of a batch has exactly the single-sequence workload's token and
+    caches; later sequences draw from their own streams, at their ragged positions."""
+    m = W.tiny(60)
+    single = W.Workload("s", m, seed=0, n_cached=100, t_max=120, use_tokens=True)
+    batch = W.Workload("b", m, seed=0, n_cached=100, t_max=120, use_tokens=True, batch=3, batch_gap=30)
+    assert [batch.seq_cached(b) for b in range(3)] == [100, 70, 40]
+    toks = W.batch_tokens(batch)
+    assert toks[0] == int(W.prompt_tokens(m, 0, 1)[0])
+    assert len(set(toks.tolist())) == 3
+    k0, v0 = W.kv_cache(m, 0, 0, 100, 120)
+    kb0, vb0 = W.kv_cache(m, 0, 0, 100, 120, seq=0)
+    kb1, _ = W.kv_cache(m, 0, 0, 70, 120, seq=1)
+    assert np.array_equal(k0, kb0) and np.array_equal(v0, vb0)
+    assert not np.array_equal(kb1[:, :70], k0[:, :70])
+    assert not np.any(kb1[:, 70:])
