@@ -234,16 +234,26 @@ def main():
     tok = torch.tensor([R.decode_token(wl)], dtype=torch.int32, device=dev)
     pos = torch.tensor([wl.n_cached], dtype=torch.int32, device=dev)
     head = wl.final_head
-    logits = torch.empty(m.vocab, dtype=torch.float32, device=dev) if head else None
+    B = wl.batch
+    if B > 1:   # batched decode: one token per sequence, every sequence at its own position
+        tok = torch.from_numpy(W.batch_tokens(wl)).to(dev)
+        pos = torch.tensor([wl.seq_cached(b) for b in range(B)], dtype=torch.int32, device=dev)
+    logits = torch.empty((B, m.vocab) if B > 1 else m.vocab, dtype=torch.float32, device=dev) if head else None
     am = tok if head else None      # each step feeds back its argmax
     hidden = torch.empty(m.d, dtype=torch.float32, device=dev)
     x_in = None if wl.use_tokens else torch.from_numpy(W.x_in(m, wl.seed)).to(dev)
-    ws = torch.empty(ops.atlas_decode_workspace_bytes(dm), dtype=torch.uint8, device=dev)
     cm = dm.c()
+    if B > 1:
+        ws = torch.empty(ops.atlas_decode_batch_workspace_bytes(dm, B), dtype=torch.uint8, device=dev)
+    else:
+        ws = torch.empty(ops.atlas_decode_workspace_bytes(dm), dtype=torch.uint8, device=dev)
 
     def step():
-        ops.atlas_decode_step(dm, pos, d_token=tok if wl.use_tokens else None, hidden_in=x_in,
-                              hidden_out=None if head else hidden, logits=logits, argmax=am, ws=ws, cm=cm)
+        if B > 1:
+            ops.atlas_decode_batch(dm, tok, pos, logits=logits, argmax=am, ws=ws, cm=cm)
+        else:
+            ops.atlas_decode_step(dm, pos, d_token=tok if wl.use_tokens else None, hidden_in=x_in,
+                                  hidden_out=None if head else hidden, logits=logits, argmax=am, ws=ws, cm=cm)
 
     for _ in range(args.warmup):
         step()
@@ -288,9 +298,12 @@ def main():
     log("per-launch timing: " + ", ".join(f"{k} {v[0]}x {v[1] / v[0] * 1e3:.1f}us" for k, v in
                                           sorted(prof.items(), key=lambda kv: -kv[1][1])))
 
-    sb = A.decode_step_bytes(m, wl.n_cached, head=head)
+    if B > 1:
+        sb = A.decode_batch_bytes(m, [wl.seq_cached(b) for b in range(B)], head=head)
+    else:
+        sb = A.decode_step_bytes(m, wl.n_cached, head=head)
     gbps = sb.total / (ms * 1e-3) / 1e9
-    dom = "w4_gemv_gate_up"
+    dom = "w4_gemv_gate_up" if B == 1 else "bd_gemm_gate_up"
     roof = None
     if dom in prof:
         cnt, tot = prof[dom]
@@ -300,11 +313,13 @@ def main():
         ach = per_launch / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": measured_traffic() if args.config == 3 else None,
-                "kernel": f"gate_up_kernel (2 x {m.dff}x{m.d} W4 + SwiGLU)", "bytes_per_launch": per_launch,
+                "kernel": (f"gate_up_kernel (2 x {m.dff}x{m.d} W4 + SwiGLU)" if B == 1 else
+                           f"w4_gemm_kernel<1> over {B} rows (2 x {m.dff}x{m.d} W4 + SwiGLU)"),
+                "bytes_per_launch": per_launch,
                 "avg_launch_us": round(avg_s * 1e6, 2), "launches": cnt}
 
     sampling = None
-    if head:   # the on-device sampler at the card's settings, on this step's logits
+    if head and B == 1:   # the on-device sampler at the card's settings, on this step's logits
         wss = torch.empty(ops.atlas_sample_workspace_bytes(m.vocab), dtype=torch.uint8, device=dev)
         du = torch.tensor([0.5], dtype=torch.float32, device=dev)
         tok_s = torch.empty(1, dtype=torch.int32, device=dev)
@@ -349,7 +364,7 @@ def main():
         log(f"plain read probe: {best[0]:.0f} GB/s with {best[1]} blocks")
 
     prefill = None
-    if not args.no_prefill and head and wl.use_tokens:
+    if not args.no_prefill and head and wl.use_tokens and B == 1:
         prefill = measure_prefill(args, dm, cm, m, dev, wl.name)
 
     if args.copy_probe_mib > 0:
@@ -368,8 +383,10 @@ def main():
         cpu = cpu_baseline(wl, args.cpu_budget, args.config)
 
     out = {
-        "metric": "decode tokens/s at batch 1, 32B W4, 16K ctx + achieved HBM GB/s vs peak",
-        "value": round(1e3 / ms, 3),
+        "metric": ("decode tokens/s at batch 1, 32B W4, 16K ctx + achieved HBM GB/s vs peak" if B == 1 else
+                   f"aggregate decode tokens/s at batch {B} (tokens of all sequences per second), 32B W4, "
+                   f"{wl.n_cached} ctx"),
+        "value": round(B * 1e3 / ms, 3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -382,7 +399,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "layers": m.n_layers, "context": wl.n_cached, "batch": 1,
+        "config": {"workload": wl.name, "layers": m.n_layers, "context": wl.n_cached, "batch": B,
                    "weights": (f"int4 group-{m.group}, {'bf16' if m.scale_dtype else 'f16'} scales, "
                                + ("symmetric (zero point 8)" if m.symmetric else "uint4 zeros")),
                    "kv": ("bf16" if m.kv_dtype == 1 else "f32") + (

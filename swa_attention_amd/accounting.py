@@ -74,6 +74,13 @@ def decode_step_bytes(m, pos, n_layers=None, head=True):
     return StepBytes(w4, kv, lm, small)
 
 
+def decode_batch_bytes(m, positions, n_layers=None, head=True):
+    """Algorithmic bytes of one batched step: the weights and lm_head once, the KV and
+    small vectors of every sequence (sequence b at positions[b])."""
+    per = [decode_step_bytes(m, p, n_layers, head) for p in positions]
+    return StepBytes(per[0].w4, sum(x.kv for x in per), per[0].lm_head, sum(x.small for x in per))
+
+
 def decode_flops(m, context, n_layers=None, head=True):
     """2 FLOPs per weight for every linear, 4 per (query head, dim, key) for the
     score and value products, plus the lm_head."""

@@ -23,6 +23,18 @@ namespace atlas {
 
 typedef __bf16 bd_bf16x8_t __attribute__((ext_vector_type(8)));
 
+// Sum of `parts` partial values at stride `stride` (split-K results): eight independent
+// accumulators, so that eight loads are in flight at once.
+__device__ __forceinline__ float bd_sum_parts(const float* p, int parts, size_t stride) {
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int q = 0;
+    for (; q + 8 <= parts; q += 8)
+#pragma unroll
+        for (int u = 0; u < 8; u++) s[u] += p[(size_t)(q + u) * stride];
+    for (; q < parts; q++) s[0] += p[(size_t)q * stride];
+    return ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+}
+
 __device__ __forceinline__ void bd_split(float x, uint32_t& hi, uint32_t& lo) {
     hi = f32_to_bf16_rne_finite(x);
     lo = f32_to_bf16_rne_finite(x - __uint_as_float(hi << 16));
@@ -48,7 +60,7 @@ struct BdRopeArgs {
     int* status;
 };
 
-__global__ __launch_bounds__(256) void bd_rope_kernel(BdRopeArgs a) {
+__global__ __launch_bounds__(1024) void bd_rope_kernel(BdRopeArgs a) {
     constexpr int D = 128;
     __shared__ float red[16];
     __shared__ float s_cos[64], s_sin[64];
@@ -57,9 +69,7 @@ __global__ __launch_bounds__(256) void bd_rope_kernel(BdRopeArgs a) {
     const int nq = a.Hq * D, nk = a.Hkv * D;
     float* row = a.qkv + (size_t)t * a.ld;
     for (int i = threadIdx.x; i < a.ld; i += blockDim.x) {
-        float sum = 0.f;
-        for (int p = 0; p < a.parts; p++) sum += a.part[p * a.part_stride + (size_t)t * a.ld + i];
-        row[i] = sum;
+        row[i] = bd_sum_parts(a.part + (size_t)t * a.ld + i, a.parts, a.part_stride);
     }
     __syncthreads();
     if (pos < 0 || pos >= a.T_max) {   // the attention of this row reports it too; nothing is stored
@@ -121,7 +131,7 @@ __global__ __launch_bounds__(256) void bd_rope_kernel(BdRopeArgs a) {
 
 // X[t] += g * A[t] / rms(A[t]) with A[t] the sum of `parts` partial rows; then the bf16
 // planes of the new X[t] for the next projection.
-__global__ __launch_bounds__(256) void bd_residual_kernel(float* X, const float* part, int parts, size_t part_stride,
+__global__ __launch_bounds__(1024) void bd_residual_kernel(float* X, const float* part, int parts, size_t part_stride,
                                                          const float* g, int d, float eps, uint16_t* p_hi,
                                                          uint16_t* p_lo, int ldp) {
     extern __shared__ float s_a[];   // [d]
@@ -129,8 +139,7 @@ __global__ __launch_bounds__(256) void bd_residual_kernel(float* X, const float*
     const int t = blockIdx.x;
     float ss = 0.f;
     for (int i = threadIdx.x; i < d; i += blockDim.x) {
-        float v = 0.f;
-        for (int p = 0; p < parts; p++) v += part[p * part_stride + (size_t)t * d + i];
+        const float v = bd_sum_parts(part + (size_t)t * d + i, parts, part_stride);
         s_a[i] = v;
         ss = fmaf(v, v, ss);
     }
@@ -148,7 +157,7 @@ __global__ __launch_bounds__(256) void bd_residual_kernel(float* X, const float*
 }
 
 // y = g * X[t] / rms(X[t]) as bf16 planes (the final norm before the lm_head).
-__global__ __launch_bounds__(256) void bd_final_norm_kernel(const float* X, const float* g, int d, float eps,
+__global__ __launch_bounds__(1024) void bd_final_norm_kernel(const float* X, const float* g, int d, float eps,
                                                            uint16_t* y_hi, uint16_t* y_lo, int ldy) {
     __shared__ float red[16];
     const int t = blockIdx.x;
@@ -163,6 +172,19 @@ __global__ __launch_bounds__(256) void bd_final_norm_kernel(const float* X, cons
         y_hi[(size_t)t * ldy + i] = (uint16_t)hi;
         y_lo[(size_t)t * ldy + i] = (uint16_t)lo;
     }
+}
+
+// z = silu(g) * u with g, u the sums of `parts` partial rows [parts][B][n], as the bf16
+// planes of the down projection's input. One thread per element.
+__global__ __launch_bounds__(256) void bd_swiglu_kernel(const float* gp, const float* up, int parts, size_t part_stride,
+                                                       int total, uint16_t* z_hi, uint16_t* z_lo) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const float g = bd_sum_parts(gp + i, parts, part_stride), u = bd_sum_parts(up + i, parts, part_stride);
+    uint32_t hi, lo;
+    bd_split(g / (1.0f + __expf(-g)) * u, hi, lo);
+    z_hi[i] = (uint16_t)hi;
+    z_lo[i] = (uint16_t)lo;
 }
 
 // ---- lm_head over the batch: bf16 matrix cores, weights streamed once --------------------------
@@ -213,13 +235,27 @@ __global__ __launch_bounds__(1024) void bd_argmax_rows_kernel(const float* logit
     const float* row = logits + (size_t)blockIdx.x * V;
     float best = -INFINITY;
     int bi = 0x7FFFFFFF;
-    for (int i = threadIdx.x; i < V; i += 1024) {
-        const float v = row[i];
+    auto see = [&](float v, int i) {   // i increases per thread: the first maximum is kept
         if (v > best) {
             best = v;
             bi = i;
         }
+    };
+    // up to three leading elements, then 16-byte loads (each thread's indices increase)
+    const int lead = min(V, (int)(((16 - ((uintptr_t)row & 15)) & 15) / 4));
+    if ((int)threadIdx.x < lead) see(row[threadIdx.x], threadIdx.x);
+    const float4* r4 = reinterpret_cast<const float4*>(row + lead);
+    const int V4 = (V - lead) >> 2;
+#pragma unroll 4
+    for (int i = threadIdx.x; i < V4; i += 1024) {
+        const float4 v = r4[i];
+        const int j = lead + 4 * i;
+        see(v.x, j);
+        see(v.y, j + 1);
+        see(v.z, j + 2);
+        see(v.w, j + 3);
     }
+    for (int i = lead + 4 * V4 + threadIdx.x; i < V; i += 1024) see(row[i], i);
     sv[threadIdx.x] = best;
     si[threadIdx.x] = bi;
     __syncthreads();
@@ -241,22 +277,25 @@ __global__ __launch_bounds__(1024) void bd_argmax_rows_kernel(const float* logit
 
 constexpr int BD_MAX_BATCH = 16;
 
-// Splits of K for a GEMM of `tiles` output tiles: the largest count (<= 16) that keeps
-// the grid within 320 blocks and each range a whole number of groups and 64-column tiles.
+// Splits of K for a GEMM of `tiles` output tiles over a few rows. With one tile row the
+// blocks are few and each is bound by the latency of its K loop, so the K range is cut
+// until about 1,024 blocks are in flight (at most 32 ranges, each a whole number of
+// groups and 64-column tiles): the smallest count that reaches 1,024 blocks, else the
+// largest that fits.
 int bd_ksplit(int tiles, int K, int group) {
     int best = 1;
-    for (int s = 2; s <= 16; s++) {
-        if (tiles * s > 320) break;
+    for (int s = 2; s <= 32; s++) {
         if (K % s) continue;
         const int c = K / s;
         if (c % 64 || c % group) continue;
         best = s;
+        if (tiles * s >= 1024) break;
     }
     return best;
 }
 
 struct BatchPlan {
-    int sq, so, sd;   // K splits of the qkv, o and down GEMMs
+    int sq, so, sg, sd;   // K splits of the qkv, o, gate/up and down GEMMs
     int S_swa, S_full, S_max;
 };
 
@@ -266,11 +305,13 @@ static BatchPlan batch_plan(const atlas_model* m, int B) {
     const int MT = (B + 63) / 64;
     p.sq = bd_ksplit(MT * ((nqkv + 127) / 128), m->d, m->layers[0].qkv.group);
     p.so = bd_ksplit(MT * ((m->d + 127) / 128), nq, m->layers[0].o.group);
+    p.sg = bd_ksplit(MT * ((m->dff + 127) / 128), m->d, m->layers[0].gate.group);
     p.sd = bd_ksplit(MT * ((m->d + 127) / 128), m->dff, m->layers[0].down.group);
     for (int l = 1; l < m->n_layers; l++) {   // one plan for every layer: take splits all layers allow
         const atlas_layer& L = m->layers[l];
         if (m->d % (p.sq * L.qkv.group) || (m->d / p.sq) % 64) p.sq = 1;
         if (nq % (p.so * L.o.group) || (nq / p.so) % 64) p.so = 1;
+        if (m->d % (p.sg * L.gate.group) || (m->d / p.sg) % 64) p.sg = 1;
         if (m->dff % (p.sd * L.down.group) || (m->dff / p.sd) % 64) p.sd = 1;
     }
     const int64_t swa_keys = m->window > 0 ? std::min<int64_t>(m->window, m->t_max) : m->t_max;
@@ -282,7 +323,7 @@ static BatchPlan batch_plan(const atlas_model* m, int B) {
 
 struct BatchWs {
     int* status;
-    float *X, *qkv, *qkv_part, *o, *attn_part, *a_part, *logits;
+    float *X, *qkv, *qkv_part, *o, *attn_part, *a_part, *g_part, *u_part, *logits;
     uint16_t *p1h, *p1l, *p2h, *p2l;
     int ld1;
     size_t bytes;
@@ -306,6 +347,8 @@ static BatchWs carve_batch(const atlas_model* m, int B, const BatchPlan& p, void
     w.o = (float*)take((size_t)B * nq * 4);
     w.attn_part = (float*)take((size_t)B * m->hq * p.S_max * ATTN_PART_F * 4);
     w.a_part = (float*)take((size_t)std::max(p.so, p.sd) * B * m->d * 4);
+    w.g_part = (float*)take((size_t)p.sg * B * m->dff * 4);
+    w.u_part = (float*)take((size_t)p.sg * B * m->dff * 4);
     w.p1h = (uint16_t*)take((size_t)B * w.ld1 * 2);
     w.p1l = (uint16_t*)take((size_t)B * w.ld1 * 2);
     w.p2h = (uint16_t*)take((size_t)B * m->dff * 2);
@@ -414,7 +457,7 @@ extern "C" int atlas_decode_batch(const atlas_model* m, const int32_t* d_tokens,
         ra.kv_bf16 = m->kv_dtype;
         ra.status = w.status;
         prof_mark("bd_qk_norm_rope", st);
-        ATLAS_KLAUNCH(bd_rope_kernel, dim3(B), dim3(256), 0, st, ra);
+        ATLAS_KLAUNCH(bd_rope_kernel, dim3(B), dim3(1024), 0, st, ra);
         ATLAS_LAUNCH_CHECK("bd_rope_kernel");
         // attention per sequence, then the merge into o rows
         AttnFusedArgs aa{};
@@ -458,16 +501,25 @@ extern "C" int atlas_decode_batch(const atlas_model* m, const int32_t* d_tokens,
         oa.c_split = (size_t)B * d;
         if ((rc = launch_w4_gemm(oa, 0, st, "bd_gemm_o"))) return rc;
         prof_mark("bd_residual_norm", st);
-        ATLAS_KLAUNCH(bd_residual_kernel, dim3(B), dim3(256), (size_t)d * 4, st, w.X, w.a_part, p.so, (size_t)B * d,
+        ATLAS_KLAUNCH(bd_residual_kernel, dim3(B), dim3(1024), (size_t)d * 4, st, w.X, w.a_part, p.so, (size_t)B * d,
                       L.g_pa, d, m->eps, w.p1h, w.p1l, w.ld1);
         ATLAS_LAUNCH_CHECK("bd_residual_kernel");
         // gate/up with SwiGLU, then down (split over K), y = h + RMSNorm_pf(m)
-        GemmArgs ga = bgemm(w.p1h, w.p1l, w.ld1, L.gate, B);
-        ga.W1 = bview(L.up);
-        ga.z_hi = w.p2h;
-        ga.z_lo = w.p2l;
-        ga.ldz = m->dff;
-        if ((rc = launch_w4_gemm(ga, 1, st, "bd_gemm_gate_up"))) return rc;
+        // gate and up as two split-K GEMMs into partials; SwiGLU sums them
+        const size_t gstride = (size_t)B * m->dff;
+        for (int which = 0; which < 2; which++) {
+            GemmArgs ga = bgemm(w.p1h, w.p1l, w.ld1, which ? L.up : L.gate, B);
+            ga.C = which ? w.u_part : w.g_part;
+            ga.ldc = m->dff;
+            ga.ksplit = p.sg;
+            ga.kchunk = d / p.sg;
+            ga.c_split = gstride;
+            if ((rc = launch_w4_gemm(ga, 0, st, which ? "bd_gemm_up" : "bd_gemm_gate"))) return rc;
+        }
+        prof_mark("bd_swiglu", st);
+        ATLAS_KLAUNCH(bd_swiglu_kernel, dim3((unsigned)((gstride + 255) / 256)), dim3(256), 0, st, w.g_part, w.u_part,
+                      p.sg, gstride, (int)gstride, w.p2h, w.p2l);
+        ATLAS_LAUNCH_CHECK("bd_swiglu_kernel");
         GemmArgs da = bgemm(w.p2h, w.p2l, m->dff, L.down, B);
         da.C = w.a_part;
         da.ldc = d;
@@ -476,7 +528,7 @@ extern "C" int atlas_decode_batch(const atlas_model* m, const int32_t* d_tokens,
         da.c_split = (size_t)B * d;
         if ((rc = launch_w4_gemm(da, 0, st, "bd_gemm_down"))) return rc;
         prof_mark("bd_residual_norm", st);
-        ATLAS_KLAUNCH(bd_residual_kernel, dim3(B), dim3(256), (size_t)d * 4, st, w.X, w.a_part, p.sd, (size_t)B * d,
+        ATLAS_KLAUNCH(bd_residual_kernel, dim3(B), dim3(1024), (size_t)d * 4, st, w.X, w.a_part, p.sd, (size_t)B * d,
                       L.g_pf, d, m->eps, w.p1h, w.p1l, w.ld1);
         ATLAS_LAUNCH_CHECK("bd_residual_kernel");
     }
@@ -488,7 +540,7 @@ extern "C" int atlas_decode_batch(const atlas_model* m, const int32_t* d_tokens,
     }
     if (!head) return ATLAS_OK;
     prof_mark("bd_final_norm", st);
-    ATLAS_KLAUNCH(bd_final_norm_kernel, dim3(B), dim3(256), 0, st, w.X, m->g_final, d, m->eps, w.p1h, w.p1l, w.ld1);
+    ATLAS_KLAUNCH(bd_final_norm_kernel, dim3(B), dim3(1024), 0, st, w.X, m->g_final, d, m->eps, w.p1h, w.p1l, w.ld1);
     ATLAS_LAUNCH_CHECK("bd_final_norm_kernel");
     float* logits = d_logits ? d_logits : w.logits;
     const int head_blocks = (m->vocab + 16 * BD_HEAD_WAVES - 1) / (16 * BD_HEAD_WAVES);

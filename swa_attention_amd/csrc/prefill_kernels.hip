@@ -227,6 +227,120 @@ __global__ __launch_bounds__(GM_THREADS) void w4_gemm_kernel(GemmArgs a) {
 #undef LOAD_TILE_K
 }
 
+// ---- the same product for a few rows ---------------------------------------------------------
+//
+// For M <= 16 (a decode batch) one 16-row MFMA tile covers A: the 64-row tile above would
+// spend 4x the matrix-core work on rows that do not exist. Mode 0 only, with split-K.
+// Per block: 16 rows x 128 columns; wave w owns columns 32w..32w+31 (two 16x16
+// fragments). Staging as above: codes dequantised to (c - z) in bf16 into LDS, A as bf16
+// hi/lo planes, per-group f32 accumulation scaled at the group's end, the next k tile's
+// loads in flight during the current one's products (deeper register rings were slower).
+__global__ __launch_bounds__(GM_THREADS) void w4_gemm16_kernel(GemmArgs a) {
+    constexpr int BM = 16, LDK = GM_BK + 8;
+    __shared__ __align__(16) uint16_t sAh[BM * LDK];
+    __shared__ __align__(16) uint16_t sAl[BM * LDK];
+    __shared__ __align__(16) uint16_t sB[GM_BN * LDK];
+    __shared__ float sS[2][GM_BN];
+    const int NT = (a.N + GM_BN - 1) / GM_BN;
+    const int Wk = NT * a.ksplit, per = (Wk + 7) / 8;
+    const int Lw = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (Lw >= Wk) return;
+    const int n0 = (Lw % NT) * GM_BN, split = Lw / NT;
+    const int k_lo = split * a.kchunk, k_hi = a.ksplit > 1 ? k_lo + a.kchunk : a.K;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, l4 = lane >> 4;
+    const int KT = (k_hi - k_lo + GM_BK - 1) / GM_BK;
+
+    // codes: W row br of the tile, 32 columns from bc (one uint4 per thread)
+    const int br = tid / (GM_BK / 32), bc = 32 * (tid % (GM_BK / 32));
+    const int brow = min(n0 + br, a.N - 1);
+    const int KW = a.W0.KW, GG = a.W0.G;
+    const int srow = tid & (GM_BN - 1), sslot = tid / GM_BN;
+    const uint16_t* s_p = a.W0.scales + (size_t)min(n0 + srow, a.N - 1) * GG;
+    // A: threads 0..127 stage the hi plane, 128..255 the lo plane: row ar, 8 columns from ac
+    const int pl = tid >> 7, ar = (tid & 127) / (GM_BK / 8), ac = 8 * (tid % (GM_BK / 8));
+    const uint16_t* a_src = (pl ? a.a_lo : a.a_hi) + (size_t)min(ar, a.M - 1) * a.lda;
+    uint16_t* a_dst = pl ? sAl : sAh;
+    uint4 rA, rB;
+    uint32_t rZ;
+    uint16_t rS;
+    auto load = [&](int kt) {
+        const int kb = k_lo + kt * GM_BK;
+        rA = *reinterpret_cast<const uint4*>(a_src + min(kb + ac, a.K - 8));
+        const int kc = min(kb + bc, a.K - 32);
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(a.W0.qweight + (size_t)brow * KW + kc / 8));
+        rB = make_uint4(v.x, v.y, v.z, v.w);
+        rZ = a.W0.zeros[(size_t)brow * a.W0.zstride + ((kc / a.group) >> 3)];
+        rS = s_p[min((kb + 32 * sslot) / a.group, GG - 1)];
+    };
+    f32x4_t acc[2], accg[2];
+#pragma unroll
+    for (int f = 0; f < 2; f++) {
+        acc[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        accg[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    load(0);
+    for (int kt = 0; kt < KT; kt++) {
+        const int kb = k_lo + kt * GM_BK, kn = min(GM_BK, k_hi - kb);
+        __syncthreads();   // the previous tile's fragments have been read
+        *reinterpret_cast<uint4*>(&a_dst[ar * LDK + ac]) = rA;
+        {
+            const int kc = min(kb + bc, a.K - 32);
+            const int z = a.W0.zsym ? 8 : (int)((rZ >> (((kc / a.group) & 7) * 4)) & 15u);
+            const uint32_t w4[4] = {rB.x, rB.y, rB.z, rB.w};
+            uint32_t o[16];
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const float v0 = (float)((int)((w4[q] >> (4 * e)) & 15u) - z);
+                    const float v1 = (float)((int)((w4[q] >> (4 * e + 4)) & 15u) - z);
+                    o[q * 4 + e / 2] = (__float_as_uint(v0) >> 16) | (__float_as_uint(v1) & 0xFFFF0000u);
+                }
+            uint4* dst = reinterpret_cast<uint4*>(&sB[br * LDK + bc]);
+#pragma unroll
+            for (int q = 0; q < 4; q++) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+        }
+        sS[sslot][srow] = scale_to_f32(rS, a.W0.scale_dtype);
+        __syncthreads();
+        if (kt + 1 < KT) load(kt + 1);   // in flight during the products below
+        for (int ks = 0; ks < kn / 32; ks++) {
+            const int k = ks * 32 + 8 * l4;
+            const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sAh[l16 * LDK + k]);
+            const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sAl[l16 * LDK + k]);
+#pragma unroll
+            for (int f = 0; f < 2; f++) {
+                const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(&sB[(wave * 32 + 16 * f + l16) * LDK + k]);
+                const f32x4_t c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, accg[f], 0, 0, 0);
+                accg[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, c, 0, 0, 0);
+            }
+            const int kabs = kb + 32 * ks + 32;
+            if (kabs % a.group == 0 || kabs >= k_hi) {   // group ends: scale and add
+                const int slot = a.group == 32 ? ks : 0;
+#pragma unroll
+                for (int f = 0; f < 2; f++) {
+                    const float sc = sS[slot][wave * 32 + 16 * f + l16];
+#pragma unroll
+                    for (int r = 0; r < 4; r++) acc[f][r] = fmaf(sc, accg[f][r], acc[f][r]);
+                    accg[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+    }
+    // D[row 4 l4 + r][column l16] of each fragment
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const int row = 4 * l4 + r;
+        if (row >= a.M) continue;
+#pragma unroll
+        for (int f = 0; f < 2; f++) {
+            const int col = n0 + wave * 32 + 16 * f + l16;
+            if (col < a.N) a.C[split * a.c_split + (size_t)row * a.ldc + col] = acc[f][r];
+        }
+    }
+}
+
 // ---- per-position kernels ----------------------------------------------------------------
 
 // X[t] = f32(embedding[tokens[t]]) and its bf16 planes. Block 0 also validates every
@@ -630,8 +744,14 @@ int launch_w4_gemm(const GemmArgs& a, int mode, hipStream_t st, const char* labe
     ATLAS_CHECK_SHAPE(a.ksplit == 1 || (mode == 0 && a.ksplit > 1 && a.kchunk * a.ksplit == a.K &&
                                         a.kchunk % GM_BK == 0 && a.kchunk % a.group == 0),
                       "bad K split (%d x %d of K=%d)", a.ksplit, a.kchunk, a.K);
-    const int T = MT * NT * a.ksplit, blocks = 8 * ((T + 7) / 8);
     prof_mark(label, st);
+    if (mode == 0 && a.M <= 16) {   // a few rows: one 16-row tile
+        const int T16 = NT * a.ksplit, b16 = 8 * ((T16 + 7) / 8);
+        ATLAS_KLAUNCH(w4_gemm16_kernel, dim3(b16), dim3(GM_THREADS), 0, st, a);
+        ATLAS_LAUNCH_CHECK("w4_gemm16_kernel");
+        return ATLAS_OK;
+    }
+    const int T = MT * NT * a.ksplit, blocks = 8 * ((T + 7) / 8);
     if (mode == 0) ATLAS_KLAUNCH((w4_gemm_kernel<0>), dim3(blocks), dim3(GM_THREADS), 0, st, a);
     else ATLAS_KLAUNCH((w4_gemm_kernel<1>), dim3(blocks), dim3(GM_THREADS), 0, st, a);
     ATLAS_LAUNCH_CHECK("w4_gemm_kernel");

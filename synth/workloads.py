@@ -115,7 +115,8 @@ def config(i):
     5: config 3 and 6: config 1 in the card's own W4 recipe (symmetric, group 32, bf16
     scales); 7: config 3 with a bf16 KV cache and rings on the sliding-window layers;
     8: the same at 65,535 cached tokens (the YaRN context limit of 65,536); 9: one
-    full-size SWA layer at 16,384 cached keys in that KV format (the ring has wrapped)."""
+    full-size SWA layer at 16,384 cached keys in that KV format (the ring has wrapped); 10:
+    config 7 for a batch of 8 sequences decoded together."""
     if i == 0:
         return Workload("tiny-swa-layer", tiny(0), seed=0, n_cached=256, t_max=257)
     if i == 1:
@@ -145,6 +146,9 @@ def config(i):
     if i == 8:
         return Workload("olmo3-32b-w4-decode-64k-bf16kv-ring", bf16_ring_kv(olmo3_32b(3)), seed=0,
                         n_cached=65535, t_max=65536, use_tokens=True, final_head=True)
+    if i == 10:
+        return Workload("olmo3-32b-w4-decode-16k-bf16kv-ring-batch8", bf16_ring_kv(olmo3_32b(3)), seed=0,
+                        n_cached=16384, t_max=16385, use_tokens=True, final_head=True, batch=8)
     if i == 9:
         m = bf16_ring_kv(olmo3_32b(model_id=1, n_layers=1))
         m.layer_types = [SWA]

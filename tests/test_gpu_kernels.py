@@ -74,7 +74,9 @@ def test_gemv_matches_oracle(N, K):
 @pytest.mark.parametrize("M,N,K,group,zeros,sd", [
     (1, 96, 640, 128, True, 0), (17, 130, 640, 128, True, 0), (64, 256, 1728, 128, True, 0),
     (130, 200, 640, 64, False, 1), (70, 64, 256, 32, True, 0), (200, 896, 640, 128, True, 0),
-    (65, 129, 5120, 128, True, 0)])
+    (65, 129, 5120, 128, True, 0),
+    # a few rows (the 16-row tile of batched decode)
+    (8, 300, 640, 32, False, 1), (5, 1001, 5120, 64, True, 0), (16, 7168, 1728, 128, True, 0)])
 def test_gemm_matches_oracle(M, N, K, group, zeros, sd):
     """The matrix-core W4 GEMM (prefill projections) against the f64 oracle row by row:
     ragged row and column tiles, a partial last group (K = 1,728), groups 32/64/128,
