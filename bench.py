@@ -303,18 +303,18 @@ def main():
     else:
         sb = A.decode_step_bytes(m, wl.n_cached, head=head)
     gbps = sb.total / (ms * 1e-3) / 1e9
-    dom = "w4_gemv_gate_up" if B == 1 else "bd_gemm_gate_up"
+    dom = "w4_gemv_gate_up" if B == 1 else "bd_gemm_gate"
     roof = None
     if dom in prof:
         cnt, tot = prof[dom]
         avg_s = tot / cnt * 1e-3
-        # one launch streams the gate and the up matrix ([dff][d] each)
-        per_launch = 2 * A.w4_bytes(m.dff, m.d, m.group, 2, not m.symmetric)
+        # one launch streams the gate and the up matrix ([dff][d] each); batched: the gate matrix
+        per_launch = (2 if B == 1 else 1) * A.w4_bytes(m.dff, m.d, m.group, 2, not m.symmetric)
         ach = per_launch / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": measured_traffic() if args.config == 3 else None,
                 "kernel": (f"gate_up_kernel (2 x {m.dff}x{m.d} W4 + SwiGLU)" if B == 1 else
-                           f"w4_gemm_kernel<1> over {B} rows (2 x {m.dff}x{m.d} W4 + SwiGLU)"),
+                           f"gate projection over {B} rows ({m.dff}x{m.d} W4, split over K)"),
                 "bytes_per_launch": per_launch,
                 "avg_launch_us": round(avg_s * 1e6, 2), "launches": cnt}
 

@@ -341,6 +341,136 @@ __global__ __launch_bounds__(GM_THREADS) void w4_gemm16_kernel(GemmArgs a) {
     }
 }
 
+// ---- a few rows, weights straight to the matrix cores --------------------------------------------
+//
+// The same product for M <= 16 without LDS staging or block barriers. The roles swap:
+// the W4 rows are the MFMA A operand (16 weight rows per tile) and the M activation rows
+// the B operand (16 columns), so each wave streams its own rows with no dependence on
+// other waves. A wave owns SK_TILES tiles (64 weight rows) and walks its K range 128
+// columns at a time:
+//  - lane l loads 16 bytes of codes of row l % 16 (columns 32 (l / 16) .. +32) per tile;
+//  - a per-wave 4 x 4 word transpose through LDS gives lane l, for k-step j, the 8 codes
+//    of columns 32 j + 8 (l / 16) .. +8, i.e. every k-step of 32 is a contiguous,
+//    group-aligned block of columns, so per-group scaling works as in the kernels above;
+//  - codes become (c - z) in bf16 (exact), the activations come as bf16 hi/lo planes
+//    (one 16-byte load per plane and k-step, shared by the wave's tiles);
+//  - per group: f32 products accumulated, then scaled by each weight row's group scale.
+// Needs the K range of every split to be a multiple of 128 (the dispatcher checks).
+constexpr int SK_TILES = 4, SK_WAVES = 4;
+
+// One 128-column step of a wave's tiles as loaded: codes (16 bytes per lane and tile),
+// the zero word, the scale of the lane's own row and 32-column group, the activations.
+struct SkStep {
+    u32x4_t cw[SK_TILES];
+    uint32_t zw[SK_TILES];
+    uint16_t sw[SK_TILES];
+    bf16x8_t bh[4], bl[4];
+};
+
+__global__ __launch_bounds__(64 * SK_WAVES) void w4_skinny_kernel(GemmArgs a) {
+    __shared__ __align__(16) uint32_t s_tr[SK_WAVES][SK_TILES * 16 * 16];   // code transpose, 1 KB per tile
+    __shared__ float s_sc[SK_WAVES][SK_TILES * 16 * 4];                     // scales [tile][row][k-step]
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int row = lane & 15, q = lane >> 4;
+    const int Nw = (a.N + 16 * SK_TILES - 1) / (16 * SK_TILES);   // wave tiles per split
+    const int gw = blockIdx.x * SK_WAVES + w;
+    if (gw >= Nw * a.ksplit) return;   // whole waves; no block barrier below
+    const int wt = gw % Nw, split = gw / Nw;
+    const int r_base = wt * 16 * SK_TILES;
+    const int k_lo = split * a.kchunk, k_hi = a.ksplit > 1 ? k_lo + a.kchunk : a.K;
+    const W4View& W = a.W0;
+    const int KW = W.KW, G = W.G;
+    uint32_t* tr = s_tr[w];
+    float* sc = s_sc[w];
+    const int m = min(row, a.M - 1);   // activation row of this lane's B operand
+    const uint16_t* xh = a.a_hi + (size_t)m * a.lda + 8 * q;
+    const uint16_t* xl = a.a_lo + (size_t)m * a.lda + 8 * q;
+    int wrow[SK_TILES];
+#pragma unroll
+    for (int t = 0; t < SK_TILES; t++) wrow[t] = min(r_base + 16 * t + row, a.N - 1);
+    auto load = [&](int k0, SkStep& S) {
+        k0 = min(k0, k_hi - 128);   // past the end: a valid step, never used
+#pragma unroll
+        for (int t = 0; t < SK_TILES; t++) {
+            S.cw[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(W.qweight + (size_t)wrow[t] * KW + (k0 + 32 * q) / 8));
+            S.zw[t] = W.zeros[(size_t)wrow[t] * W.zstride + ((k0 / a.group) >> 3)];
+            S.sw[t] = W.scales[(size_t)wrow[t] * G + (k0 + 32 * q) / a.group];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            S.bh[j] = *reinterpret_cast<const bf16x8_t*>(xh + k0 + 32 * j);
+            S.bl[j] = *reinterpret_cast<const bf16x8_t*>(xl + k0 + 32 * j);
+        }
+    };
+    f32x4_t acc[SK_TILES], accg[SK_TILES];
+#pragma unroll
+    for (int t = 0; t < SK_TILES; t++) {
+        acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        accg[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    auto compute = [&](int k0, const SkStep& S) {
+        // transpose: word j' of lane (row, q') to [t][row][j'][q']; lane (row, q) reads
+        // [t][row][q][0..3] = the codes of columns 32 j + 8 q, j = 0..3. Scales: lane
+        // (row, q) holds row's scale for k-step q; [t][row][q]
+#pragma unroll
+        for (int t = 0; t < SK_TILES; t++) {
+            const uint32_t wv[4] = {S.cw[t].x, S.cw[t].y, S.cw[t].z, S.cw[t].w};
+#pragma unroll
+            for (int j = 0; j < 4; j++) tr[((t * 16 + row) * 4 + j) * 4 + q] = wv[j];
+            sc[(t * 16 + row) * 4 + q] = scale_to_f32(S.sw[t], W.scale_dtype);
+        }
+        __builtin_amdgcn_wave_barrier();   // LDS accesses of one wave complete in order
+#pragma unroll
+        for (int t = 0; t < SK_TILES; t++) {
+            const uint4 tv = *reinterpret_cast<const uint4*>(&tr[((t * 16 + row) * 4 + q) * 4]);
+            const uint32_t tw[4] = {tv.x, tv.y, tv.z, tv.w};
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int g = (k0 + 32 * j) / a.group;
+                const int z = W.zsym ? 8 : (int)((S.zw[t] >> ((g & 7) * 4)) & 15u);
+                uint32_t o[4];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const float v0 = (float)((int)((tw[j] >> (4 * e)) & 15u) - z);
+                    const float v1 = (float)((int)((tw[j] >> (4 * e + 4)) & 15u) - z);
+                    o[e / 2] = (__float_as_uint(v0) >> 16) | (__float_as_uint(v1) & 0xFFFF0000u);
+                }
+                const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+                accg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, S.bh[j], accg[t], 0, 0, 0);
+                accg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, S.bl[j], accg[t], 0, 0, 0);
+                const int kabs = k0 + 32 * j + 32;
+                if (kabs % a.group == 0 || kabs >= k_hi) {   // group ends: scale each weight row
+#pragma unroll
+                    for (int r = 0; r < 4; r++) acc[t][r] = fmaf(sc[(t * 16 + 4 * q + r) * 4 + j], accg[t][r], acc[t][r]);
+                    accg[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();   // the reads finish before the next step's writes
+    };
+    // two steps in flight: the next step's loads are issued before this one is computed
+    SkStep S0, S1;
+    load(k_lo, S0);
+    for (int k0 = k_lo; k0 < k_hi; k0 += 256) {
+        load(k0 + 128, S1);
+        compute(k0, S0);
+        if (k0 + 128 < k_hi) {
+            load(k0 + 256, S0);
+            compute(k0 + 128, S1);
+        }
+    }
+    // D[weight row 4 q + r][activation row l % 16] of each tile
+    if (row < a.M) {
+#pragma unroll
+        for (int t = 0; t < SK_TILES; t++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int fr = r_base + 16 * t + 4 * q + r;
+                if (fr < a.N) a.C[split * a.c_split + (size_t)row * a.ldc + fr] = acc[t][r];
+            }
+    }
+}
+
 // ---- per-position kernels ----------------------------------------------------------------
 
 // X[t] = f32(embedding[tokens[t]]) and its bf16 planes. Block 0 also validates every
@@ -745,6 +875,14 @@ int launch_w4_gemm(const GemmArgs& a, int mode, hipStream_t st, const char* labe
                                         a.kchunk % GM_BK == 0 && a.kchunk % a.group == 0),
                       "bad K split (%d x %d of K=%d)", a.ksplit, a.kchunk, a.K);
     prof_mark(label, st);
+    const int krange = a.ksplit > 1 ? a.kchunk : a.K;
+    if (mode == 0 && a.M <= 16 && krange % 128 == 0) {   // a few rows: weights straight to the matrix cores
+        const int Nw = (a.N + 16 * SK_TILES - 1) / (16 * SK_TILES);
+        const int bs = (Nw * a.ksplit + SK_WAVES - 1) / SK_WAVES;
+        ATLAS_KLAUNCH(w4_skinny_kernel, dim3(bs), dim3(64 * SK_WAVES), 0, st, a);
+        ATLAS_LAUNCH_CHECK("w4_skinny_kernel");
+        return ATLAS_OK;
+    }
     if (mode == 0 && a.M <= 16) {   // a few rows: one 16-row tile
         const int T16 = NT * a.ksplit, b16 = 8 * ((T16 + 7) / 8);
         ATLAS_KLAUNCH(w4_gemm16_kernel, dim3(b16), dim3(GM_THREADS), 0, st, a);

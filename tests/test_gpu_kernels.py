@@ -92,20 +92,22 @@ def test_gemm_matches_oracle(M, N, K, group, zeros, sd):
     assert normwise(C, ref) < 2e-5
 
 
-def test_gemm_one_hot_rows_bit_exact():
+@pytest.mark.parametrize("K,group", [(1728, 128), (1280, 128), (1280, 32)])
+def test_gemm_one_hot_rows_bit_exact(K, group):
     """Rows of A that are unit vectors e_j (exact in bf16, lo plane zero) give column j
-    of the dequantised matrix bit for bit: unpacking, zero point and scale selection
-    of the GEMM's dequantise-into-LDS path."""
+    of the dequantised matrix bit for bit: unpacking, zero point and scale selection.
+    A few rows take the small-row paths: K = 1,728 the 16-row LDS tile, K a multiple
+    of 128 the kernel that feeds the codes to the matrix cores through a transpose."""
     dev = device()
-    N, K = 200, 1728
-    c, s, z = _w4(N, K, 12)
+    N = 200
+    c, s, z = _w4(N, K, 12, group)
     cols = [0, 1, 7, 8, 31, 32, 63, 64, 127, 128, 129, 1000, K - 65, K - 64, K - 1]
     A = np.zeros((len(cols), K), dtype=np.float32)
     for i, j in enumerate(cols):
         A[i, j] = 1.0
-    w = w4_to_device(c, s, z, K, dev)
+    w = w4_to_device(c, s, z, K, dev, group)
     C = ops.atlas_w4_gemm(w, torch.from_numpy(A).to(dev)).cpu().numpy()
-    ref = O.dequant(c, s, z, K)
+    ref = O.dequant(c, s, z, K, group)
     for i, j in enumerate(cols):
         np.testing.assert_array_equal(C[i].view(np.uint32), ref[:, j].copy().view(np.uint32), err_msg=f"col {j}")
 
