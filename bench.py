@@ -134,6 +134,7 @@ def cpu_baseline(wl, budget_s, config):
 
 
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_INT8_TOPS = 5000.0
 
 
 def measure_prefill(args, dm, cm, m, dev, wl_name):
@@ -180,10 +181,18 @@ def measure_prefill(args, dm, cm, m, dev, wl_name):
         cnt, tot = prof[dom]
         f = 2.0 * n * 2 * m.dff * m.d   # algorithmic flops of one gate+up launch
         ach = f / (tot / cnt * 1e-3) / 1e12
-        out["roofline"] = {"bound": "mfma", "kernel": "w4_gemm_kernel<1> (gate+up, SwiGLU)", "achieved": round(ach, 1),
-                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                           "avg_launch_us": round(tot / cnt * 1e3, 1),
-                           "note": "algorithmic flops; the bf16 hi/lo activation planes issue twice as many"}
+        if m.group % 128 == 0 and m.group <= 512 and m.d % m.group == 0:
+            # groups of 128-512: products on the int8 matrix cores, priced at the int8 peak
+            out["roofline"] = {"bound": "mfma", "kernel": "w4_gemm_i8_kernel<1> (gate+up, SwiGLU)",
+                               "achieved": round(ach, 1), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                               "frac": round(ach / PEAK_INT8_TOPS, 4), "avg_launch_us": round(tot / cnt * 1e3, 1),
+                               "note": "algorithmic multiply-adds x 2; the three int8 digit planes of the "
+                                       "activations issue three times as many"}
+        else:
+            out["roofline"] = {"bound": "mfma", "kernel": "w4_gemm_kernel<1> (gate+up, SwiGLU)",
+                               "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(ach / PEAK_BF16_TFLOPS, 4), "avg_launch_us": round(tot / cnt * 1e3, 1),
+                               "note": "algorithmic flops; the bf16 hi/lo activation planes issue twice as many"}
     return out
 
 

@@ -138,12 +138,20 @@ ATLAS_API int atlas_w4_dequant(const atlas_w4* W, float* out, void* stream);
 
 /* ---- W4 GEMM (the prefill projections) -------------------------------------------
  * C[m][n] = sum_k W[n][k] A[m][k] for M rows of f32 activations A [M][K] (row-major,
- * device) and an atlas_w4 W; C: f32 [M][N] (device). Runs on the matrix cores: A is
- * held as two bf16 planes (hi + lo, 16 significant bits), W is dequantised to exact
- * bf16 integers (code - zero) per quantisation group and each group's f32 sum is
- * scaled and accumulated; result within about 1e-5 relative of the f64 definition.
+ * device) and an atlas_w4 W; C: f32 [M][N] (device). Runs on the matrix cores, per
+ * quantisation group:
+ *   A is first held as two bf16 planes (hi + lo, 16 significant bits); then
+ *   - groups of 128, 256 or 512 dividing K, M > 16: int8 products. The planes are
+ *     rounded per row and group to 24-bit integers v times a power-of-two scale s
+ *     with max|A| / (127 * 2^16) <= s (error <= s/2 per element), carried as three int8
+ *     digit planes; the raw codes multiply each plane exactly in int32, the digit sums
+ *     and the zero point are combined in f32, and the group's sum is scaled and
+ *     accumulated in f32;
+ *   - other groups (32 or multiples of 64), or M <= 16: bf16 products of the planes
+ *     with W as exact bf16 integers (code - zero), per group summed in f32.
+ *   Either way the result is within about 1e-5 relative of the f64 definition.
  * Needs group == 32 or a multiple of 64 (else ATLAS_ERR_UNSUPPORTED_SHAPE).
- * ws: atlas_w4_gemm_workspace_bytes(W, M) bytes (the bf16 planes of A). */
+ * ws: atlas_w4_gemm_workspace_bytes(W, M) bytes (the planes of A). */
 ATLAS_API size_t atlas_w4_gemm_workspace_bytes(const atlas_w4* W, int32_t M);
 ATLAS_API int atlas_w4_gemm(const atlas_w4* W, const float* A, int32_t M, float* C, void* ws, size_t ws_bytes,
                             void* stream);

@@ -22,6 +22,8 @@ struct PrefillWs {
     void* dec;       // decode workspace (status word, head partials)
     float *X, *QKV, *A;
     uint16_t *p1h, *p1l, *p2h, *p2l;
+    int8_t *qh, *qm, *ql;  // int8 digit planes of the next GEMM's input [n][K]
+    float *qs, *qsum;      // and its per-(row, group) scales and sums [n][K / group]
     void *k_new, *v_new;   // prompt keys / values [Hkv][n][hd] in the cache's element type
     int ld1;
     size_t bytes;
@@ -46,6 +48,12 @@ PrefillWs carve_prefill(const atlas_model* m, int n, void* base) {
     w.p1l = (uint16_t*)take((size_t)n * w.ld1 * 2);
     w.p2h = (uint16_t*)take((size_t)n * m->dff * 2);
     w.p2l = (uint16_t*)take((size_t)n * m->dff * 2);
+    const int kmax = std::max(w.ld1, m->dff);
+    w.qh = (int8_t*)take((size_t)n * kmax);
+    w.qm = (int8_t*)take((size_t)n * kmax);
+    w.ql = (int8_t*)take((size_t)n * kmax);
+    w.qs = (float*)take((size_t)n * (kmax / 128 + 1) * 4);
+    w.qsum = (float*)take((size_t)n * (kmax / 128 + 1) * 4);
     const size_t kv_bytes = (size_t)m->hkv * n * m->hd * (m->kv_dtype == 1 ? 2 : 4);
     w.k_new = take(kv_bytes);
     w.v_new = take(kv_bytes);
@@ -80,6 +88,22 @@ GemmArgs gemm(const uint16_t* hi, const uint16_t* lo, int lda, const atlas_w4& w
     g.K = w.K;
     g.group = w.group;
     return g;
+}
+
+// Int8 digit planes of the GEMM input for groups of 128, 256 or 512 (the int8 matrix-core
+// kernel); other groups keep the bf16 planes.
+int attach_i8(GemmArgs& g, const PrefillWs& w, hipStream_t st) {
+    if (!gemm_i8_supported(g.group, g.K)) return ATLAS_OK;
+    const int rc = launch_pf_quant8(g.a_hi, g.a_lo, g.lda, g.M, g.K, g.group, w.qh, w.qm, w.ql, w.qs, w.qsum, st);
+    if (rc) return rc;
+    g.q_hi = w.qh;
+    g.q_mid = w.qm;
+    g.q_lo = w.ql;
+    g.q_s = w.qs;
+    g.q_sum = w.qsum;
+    g.ldq = g.K;
+    g.ldqs = g.K / g.group;
+    return ATLAS_OK;
 }
 
 }  // namespace
@@ -123,6 +147,7 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
         GemmArgs qa = gemm(w.p1h, w.p1l, w.ld1, L.qkv, n);
         qa.C = w.QKV;
         qa.ldc = nqkv;
+        if ((rc = attach_i8(qa, w, st))) return rc;
         if ((rc = launch_w4_gemm(qa, 0, st, "pf_gemm_qkv"))) return rc;
         // QK norm and rotary; the prompt keys/values into the prompt KV buffers
         PfRopeArgs ra{};
@@ -182,6 +207,7 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
         GemmArgs oa = gemm(w.p1h, w.p1l, w.ld1, L.o, n);
         oa.C = w.A;
         oa.ldc = d;
+        if ((rc = attach_i8(oa, w, st))) return rc;
         if ((rc = launch_w4_gemm(oa, 0, st, "pf_gemm_o"))) return rc;
         if ((rc = launch_pf_residual(w.X, w.A, L.g_pa, n, d, m->eps, w.p1h, w.p1l, w.ld1, st))) return rc;
         // gate/up with SwiGLU, then down
@@ -190,10 +216,12 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
         ga.z_hi = w.p2h;
         ga.z_lo = w.p2l;
         ga.ldz = m->dff;
+        if ((rc = attach_i8(ga, w, st))) return rc;
         if ((rc = launch_w4_gemm(ga, 1, st, "pf_gemm_gate_up"))) return rc;
         GemmArgs da = gemm(w.p2h, w.p2l, m->dff, L.down, n);
         da.C = w.A;
         da.ldc = d;
+        if ((rc = attach_i8(da, w, st))) return rc;
         if ((rc = launch_w4_gemm(da, 0, st, "pf_gemm_down"))) return rc;
         // y = h + RMSNorm_pf(m): the last layer leaves it to the head (last position only)
         if (!last || !head)
@@ -212,9 +240,37 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
 
 // ---- standalone W4 GEMM ---------------------------------------------------------------------
 
+namespace {
+struct GemmWs {
+    uint16_t *hi, *lo;   // bf16 planes [M][K]
+    int8_t *qh, *qm, *ql;   // int8 digit planes [M][K]
+    float *qs, *qsum;       // [M][K / 128 + 1]
+    size_t bytes;
+};
+GemmWs carve_gemm(int M, int K, void* base) {
+    GemmWs w{};
+    char* b = (char*)base;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        void* p = b ? b + off : nullptr;
+        off += align_up(bytes, 256);
+        return p;
+    };
+    w.hi = (uint16_t*)take((size_t)M * K * 2);
+    w.lo = (uint16_t*)take((size_t)M * K * 2);
+    w.qh = (int8_t*)take((size_t)M * K);
+    w.qm = (int8_t*)take((size_t)M * K);
+    w.ql = (int8_t*)take((size_t)M * K);
+    w.qs = (float*)take((size_t)M * (K / 128 + 1) * 4);
+    w.qsum = (float*)take((size_t)M * (K / 128 + 1) * 4);
+    w.bytes = off;
+    return w;
+}
+}  // namespace
+
 extern "C" size_t atlas_w4_gemm_workspace_bytes(const atlas_w4* W, int32_t M) {
     if (validate_w4(W) != ATLAS_OK || M < 1) return 0;
-    return 2 * align_up((size_t)M * W->K * 2, 256);
+    return carve_gemm(M, W->K, nullptr).bytes;
 }
 
 extern "C" int atlas_w4_gemm(const atlas_w4* W, const float* A, int32_t M, float* C, void* ws, size_t ws_bytes,
@@ -224,14 +280,25 @@ extern "C" int atlas_w4_gemm(const atlas_w4* W, const float* A, int32_t M, float
     ATLAS_CHECK_ARG(A && C && ws, "null pointer");
     ATLAS_CHECK_ARG(M >= 1, "M must be >= 1");
     ATLAS_CHECK_SHAPE(gemm_supported(W->group), "W4 GEMM needs group 32 or a multiple of 64 (got %d)", W->group);
-    const size_t plane = align_up((size_t)M * W->K * 2, 256);
-    if (ws_bytes < 2 * plane) return fail(ATLAS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu", ws_bytes, 2 * plane);
+    const GemmWs w = carve_gemm(M, W->K, ws);
+    if (ws_bytes < w.bytes) return fail(ATLAS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu", ws_bytes, w.bytes);
     hipStream_t st = (hipStream_t)stream;
-    uint16_t* hi = (uint16_t*)ws;
-    uint16_t* lo = (uint16_t*)((char*)ws + plane);
-    if ((rc = launch_pf_split(A, M, W->K, W->K, hi, lo, W->K, st))) return rc;
-    GemmArgs g = gemm(hi, lo, W->K, *W, M);
+    if ((rc = launch_pf_split(A, M, W->K, W->K, w.hi, w.lo, W->K, st))) return rc;
+    GemmArgs g = gemm(w.hi, w.lo, W->K, *W, M);
     g.C = C;
     g.ldc = W->N;
+    // more than 16 rows with groups of 128-512: the int8 matrix-core kernel; otherwise the
+    // bf16 kernels (a few rows take the small-row paths)
+    if (M > 16 && gemm_i8_supported(W->group, W->K)) {
+        if ((rc = launch_pf_quant8(w.hi, w.lo, W->K, M, W->K, W->group, w.qh, w.qm, w.ql, w.qs, w.qsum, st)))
+            return rc;
+        g.q_hi = w.qh;
+        g.q_mid = w.qm;
+        g.q_lo = w.ql;
+        g.q_s = w.qs;
+        g.q_sum = w.qsum;
+        g.ldq = W->K;
+        g.ldqs = W->K / W->group;
+    }
     return launch_w4_gemm(g, 0, st, "w4_gemm");
 }

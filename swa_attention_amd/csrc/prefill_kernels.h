@@ -22,6 +22,16 @@ struct GemmArgs {
     // split s writes its partial product to C + s * c_split. ksplit = 1: no split.
     int ksplit = 1, kchunk = 0;
     size_t c_split = 0;
+    // Int8 digit planes of A for w4_gemm_i8_kernel (null: the bf16 planes are used):
+    // A[m][k] ~ q_s[m][g] * (65536 q_hi + 256 q_mid + q_lo)[m][k] for group g of column
+    // k, the bytes of every 8 columns stored in the order 0,2,4,6,1,3,5,7; q_sum[m][g]
+    // is the sum of the group's 24-bit values. Row strides ldq (bytes), ldqs (groups).
+    const int8_t* q_hi = nullptr;
+    const int8_t* q_mid = nullptr;
+    const int8_t* q_lo = nullptr;
+    const float* q_s = nullptr;
+    const float* q_sum = nullptr;
+    int ldq = 0, ldqs = 0;
 };
 
 // KV of the prompt: keys j < start_pos come from the layer's cache ([Hkv][slots][128],
@@ -68,6 +78,9 @@ struct PfCommitArgs {
 };
 
 int gemm_supported(int group);
+int gemm_i8_supported(int group, int K);
+int launch_pf_quant8(const uint16_t* hi, const uint16_t* lo, int lda, int M, int K, int group, int8_t* q_hi,
+                     int8_t* q_mid, int8_t* q_lo, float* q_s, float* q_sum, hipStream_t st);
 int launch_w4_gemm(const GemmArgs& a, int mode, hipStream_t st, const char* label);
 int launch_pf_embed(const int32_t* tokens, int n, const uint16_t* emb, int vocab, int d, float* X, uint16_t* p_hi,
                     uint16_t* p_lo, int ldp, int* status, hipStream_t st);

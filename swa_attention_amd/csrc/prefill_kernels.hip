@@ -227,6 +227,272 @@ __global__ __launch_bounds__(GM_THREADS) void w4_gemm_kernel(GemmArgs a) {
 #undef LOAD_TILE_K
 }
 
+// ---- W4 GEMM on the int8 matrix cores ---------------------------------------------------------
+//
+// The same product with v_mfma_i32_16x16x64_i8, which does twice the bf16 rate's work per
+// instruction. A is a 24-bit fixed-point copy per row and quantisation group (A ~ s v,
+// v = 65536 h + 256 m + l, the digits as three int8 planes, see pf_quant8_kernel); the
+// weights enter as their raw 4-bit codes c in [0, 15] (a mask and a shift per word: the
+// low nibbles of a word are its columns 0,2,4,6 and the high nibbles 1,3,5,7, the byte
+// order of the A planes). Per group each digit plane's products are exact in int32;
+//   I = 65536 sum(c h) + 256 sum(c m) + sum(c l) - z sum(v)
+// is formed in f32 (about 2^-24 of its terms) and added to the output times s_w s_x. The tile is 64 rows of A x 128 rows of W
+// (mode 1: 64 of W0 and the same 64 of W1), four waves of 32 x 64, k tiles of 128 through
+// LDS (groups are multiples of 128), the next k tile in registers while the current one
+// is multiplied, tiles numbered XCD by XCD as in w4_gemm_kernel.
+constexpr int G8_BM = 64, G8_BN = 128, G8_BK = 128, G8_THREADS = 256;
+static_assert(G8_BM == GM_BM && G8_BN == GM_BN, "the launcher counts tiles of both kernels alike");
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+template <int MODE>
+__global__ __launch_bounds__(G8_THREADS) void w4_gemm_i8_kernel(GemmArgs a) {
+    constexpr int LDB = G8_BK + 16;   // padded LDS row in bytes
+    __shared__ __align__(16) int8_t sAh[G8_BM * LDB];
+    __shared__ __align__(16) int8_t sAm[G8_BM * LDB];
+    __shared__ __align__(16) int8_t sAl[G8_BM * LDB];
+    __shared__ __align__(16) int8_t sB[G8_BN * LDB];
+    __shared__ float sSw[G8_BN];
+    __shared__ int sZ[G8_BN];
+    __shared__ float sSx[G8_BM];
+    __shared__ float sSX[G8_BM];
+
+    const int MT = (a.M + G8_BM - 1) / G8_BM;
+    const int NW_ = MODE ? G8_BN / 2 : G8_BN;   // output columns per tile
+    const int NT = (a.N + NW_ - 1) / NW_;
+    const int T = MT * NT, per = (T + 7) / 8;
+    const int L = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (L >= T) return;
+    const int m0 = (L % MT) * G8_BM, n0 = (L / MT) * NW_;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    const int l16 = lane & 15, l4 = lane >> 4;
+    const int KT = a.K / G8_BK;
+
+    auto second = [&](int r) { return MODE && r >= G8_BN / 2; };
+    auto wrow = [&](int r) { return min(n0 + (second(r) ? r - G8_BN / 2 : r), a.N - 1); };
+    auto bcol = [&](int nf) { return MODE ? (nf < 2 ? wn * 32 + 16 * nf : 64 + wn * 32 + 16 * (nf - 2)) : wn * 64 + 16 * nf; };
+
+    // codes: thread t -> W row t/2, 64 columns from 64 (t % 2)
+    const int br = tid >> 1, bc = 64 * (tid & 1);
+    const uint32_t* b_q = (second(br) ? a.W1.qweight : a.W0.qweight) + (size_t)wrow(br) * a.W0.KW + bc / 8;
+    // the group's scale (threads < 128, W row t) or zero (threads >= 128, W row t - 128)
+    const int srow = tid & (G8_BN - 1);
+    const bool zthread = tid >= G8_BN;
+    const W4View& Ws = second(srow) ? a.W1 : a.W0;
+    const uint16_t* s_p = Ws.scales + (size_t)wrow(srow) * Ws.G;
+    const uint32_t* z_p = Ws.zeros + (size_t)wrow(srow) * Ws.zstride;
+    const int s_dtype = Ws.scale_dtype, zsym = Ws.zsym;
+    // A digits: thread t -> rows t/8 and t/8 + 32, 16 bytes from 16 (t % 8) of each plane
+    const int ar = tid >> 3, ac = 16 * (tid & 7);
+    const size_t ao0 = (size_t)min(m0 + ar, a.M - 1) * a.ldq + ac;
+    const size_t ao1 = (size_t)min(m0 + ar + 32, a.M - 1) * a.ldq + ac;
+    const size_t qo = (size_t)min(m0 + (tid & (G8_BM - 1)), a.M - 1) * a.ldqs;
+
+    uint4 rAh0, rAh1, rAm0, rAm1, rAl0, rAl1, rB0, rB1;
+    uint32_t rZ;
+    uint16_t rS;
+    float rSx, rSX;
+    auto load_k = [&](int kt) {
+        const int kb = kt * G8_BK, g = kb / a.group;
+        rAh0 = *reinterpret_cast<const uint4*>(a.q_hi + ao0 + kb);
+        rAh1 = *reinterpret_cast<const uint4*>(a.q_hi + ao1 + kb);
+        rAm0 = *reinterpret_cast<const uint4*>(a.q_mid + ao0 + kb);
+        rAm1 = *reinterpret_cast<const uint4*>(a.q_mid + ao1 + kb);
+        rAl0 = *reinterpret_cast<const uint4*>(a.q_lo + ao0 + kb);
+        rAl1 = *reinterpret_cast<const uint4*>(a.q_lo + ao1 + kb);
+        const u32x4_t* bp = reinterpret_cast<const u32x4_t*>(b_q + kb / 8);
+        const u32x4_t v0 = __builtin_nontemporal_load(bp), v1 = __builtin_nontemporal_load(bp + 1);
+        rB0 = make_uint4(v0.x, v0.y, v0.z, v0.w);
+        rB1 = make_uint4(v1.x, v1.y, v1.z, v1.w);
+        rS = s_p[g];
+        rZ = z_p[g >> 3];
+        rSx = a.q_s[qo + g];
+        rSX = a.q_sum[qo + g];
+    };
+
+    f32x4_t acc[2][4];
+    i32x4_t ah_acc[2][4], am_acc[2][4], al_acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            ah_acc[i][j] = i32x4_t{0, 0, 0, 0};
+            am_acc[i][j] = i32x4_t{0, 0, 0, 0};
+            al_acc[i][j] = i32x4_t{0, 0, 0, 0};
+        }
+
+    load_k(0);
+    for (int kt = 0; kt < KT; kt++) {
+        const int kb = kt * G8_BK;
+        __syncthreads();   // the previous tile's fragments have been read
+        *reinterpret_cast<uint4*>(&sAh[ar * LDB + ac]) = rAh0;
+        *reinterpret_cast<uint4*>(&sAh[(ar + 32) * LDB + ac]) = rAh1;
+        *reinterpret_cast<uint4*>(&sAm[ar * LDB + ac]) = rAm0;
+        *reinterpret_cast<uint4*>(&sAm[(ar + 32) * LDB + ac]) = rAm1;
+        *reinterpret_cast<uint4*>(&sAl[ar * LDB + ac]) = rAl0;
+        *reinterpret_cast<uint4*>(&sAl[(ar + 32) * LDB + ac]) = rAl1;
+        {
+            const uint32_t w[8] = {rB0.x, rB0.y, rB0.z, rB0.w, rB1.x, rB1.y, rB1.z, rB1.w};
+            uint4* dst = reinterpret_cast<uint4*>(&sB[br * LDB + bc]);
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+                dst[q] = make_uint4(w[2 * q] & 0x0F0F0F0Fu, (w[2 * q] >> 4) & 0x0F0F0F0Fu, w[2 * q + 1] & 0x0F0F0F0Fu,
+                                    (w[2 * q + 1] >> 4) & 0x0F0F0F0Fu);
+        }
+        if (zthread) sZ[srow] = zsym ? 8 : (int)((rZ >> (((kb / a.group) & 7) * 4)) & 15u);
+        else sSw[srow] = scale_to_f32(rS, s_dtype);
+        if (tid < G8_BM) {
+            sSx[tid] = rSx;
+            sSX[tid] = rSX;
+        }
+        __syncthreads();
+        if (kt + 1 < KT) load_k(kt + 1);   // in flight during the products below
+
+#pragma unroll
+        for (int ks = 0; ks < G8_BK / 64; ks++) {
+            const int k = ks * 64 + 16 * l4;
+            i32x4_t ah[2], am[2], al[2], b[4];
+#pragma unroll
+            for (int mf = 0; mf < 2; mf++) {
+                const int row = wm * 32 + mf * 16 + l16;
+                ah[mf] = *reinterpret_cast<const i32x4_t*>(&sAh[row * LDB + k]);
+                am[mf] = *reinterpret_cast<const i32x4_t*>(&sAm[row * LDB + k]);
+                al[mf] = *reinterpret_cast<const i32x4_t*>(&sAl[row * LDB + k]);
+            }
+#pragma unroll
+            for (int nf = 0; nf < 4; nf++) b[nf] = *reinterpret_cast<const i32x4_t*>(&sB[(bcol(nf) + l16) * LDB + k]);
+#pragma unroll
+            for (int mf = 0; mf < 2; mf++)
+#pragma unroll
+                for (int nf = 0; nf < 4; nf++) {
+                    ah_acc[mf][nf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[mf], b[nf], ah_acc[mf][nf], 0, 0, 0);
+                    am_acc[mf][nf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(am[mf], b[nf], am_acc[mf][nf], 0, 0, 0);
+                    al_acc[mf][nf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al[mf], b[nf], al_acc[mf][nf], 0, 0, 0);
+                }
+        }
+        if ((kb + G8_BK) % a.group == 0) {   // group ends: combine the digit sums, scale and add
+#pragma unroll
+            for (int nf = 0; nf < 4; nf++) {
+                const int n = bcol(nf) + l16;
+                const float sw = sSw[n];
+                const int z = sZ[n];
+#pragma unroll
+                for (int mf = 0; mf < 2; mf++) {
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        const int m = wm * 32 + mf * 16 + 4 * l4 + r;
+                        const float I = fmaf(65536.f, (float)ah_acc[mf][nf][r],
+                                             fmaf(256.f, (float)am_acc[mf][nf][r], (float)al_acc[mf][nf][r])) -
+                                        (float)z * sSX[m];
+                        acc[mf][nf][r] = fmaf(I, sw * sSx[m], acc[mf][nf][r]);
+                    }
+                    ah_acc[mf][nf] = i32x4_t{0, 0, 0, 0};
+                    am_acc[mf][nf] = i32x4_t{0, 0, 0, 0};
+                    al_acc[mf][nf] = i32x4_t{0, 0, 0, 0};
+                }
+            }
+        }
+    }
+
+    // epilogue: D[row 4*l4 + r][col l16] of each fragment
+#pragma unroll
+    for (int mf = 0; mf < 2; mf++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int row = m0 + wm * 32 + mf * 16 + 4 * l4 + r;
+            if (row >= a.M) continue;
+            if (MODE == 0) {
+#pragma unroll
+                for (int nf = 0; nf < 4; nf++) {
+                    const int col = n0 + bcol(nf) + l16;
+                    if (col < a.N) a.C[(size_t)row * a.ldc + col] = acc[mf][nf][r];
+                }
+            } else {
+#pragma unroll
+                for (int f = 0; f < 2; f++) {
+                    const int col = n0 + wn * 32 + 16 * f + l16;
+                    if (col < a.N) {
+                        const float gt = acc[mf][f][r], up = acc[mf][f + 2][r];
+                        uint32_t hi, lo;
+                        pf_split(gt / (1.0f + __expf(-gt)) * up, hi, lo);
+                        a.z_hi[(size_t)row * a.ldz + col] = (uint16_t)hi;
+                        a.z_lo[(size_t)row * a.ldz + col] = (uint16_t)lo;
+                    }
+                }
+            }
+        }
+}
+
+// Group-scaled 24-bit fixed point digits of A = hi + lo (bf16 planes) for
+// w4_gemm_i8_kernel. Each lane takes 8 consecutive columns, group/8 lanes of one wave a
+// group (group <= 512): s is the power of two with max|x| / Q8_MAX <= s (so x / s is
+// exact and only its rounding to an integer errs, by at most s / 2 <= max|x| / Q8_MAX),
+// v = rint(x / s) with |v| <= Q8_MAX = 127 * 65536, split into balanced digits
+// v = 65536 h + 256 m + l with l, m in [-128, 127] and h in [-127, 127]; bytes stored in
+// the order 0,2,4,6,1,3,5,7 of the 8 columns; q_sum = sum of v over the group (f32).
+constexpr float Q8_MAX = 8323072.f;
+__global__ __launch_bounds__(256) void pf_quant8_kernel(const uint16_t* hi, const uint16_t* lo, int lda, int M, int K,
+                                                        int group, int8_t* q_hi, int8_t* q_mid, int8_t* q_lo,
+                                                        float* q_s, float* q_sum) {
+    const int m = blockIdx.y;
+    const int b8 = blockIdx.x * 256 + threadIdx.x, nb = K / 8, lanes = group / 8;
+    const bool on = b8 < nb;   // whole groups are on or off (256 * 8 and K are multiples of group)
+    float x[8];
+    if (on) {
+        const uint4 h = *reinterpret_cast<const uint4*>(hi + (size_t)m * lda + 8 * b8);
+        const uint4 l = *reinterpret_cast<const uint4*>(lo + (size_t)m * lda + 8 * b8);
+        const uint32_t hw[4] = {h.x, h.y, h.z, h.w}, lw[4] = {l.x, l.y, l.z, l.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            x[2 * i] = bf16_bits_to_f32(hw[i] & 0xFFFFu) + bf16_bits_to_f32(lw[i] & 0xFFFFu);
+            x[2 * i + 1] = bf16_bits_to_f32(hw[i] >> 16) + bf16_bits_to_f32(lw[i] >> 16);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) x[i] = 0.f;
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) mx = fmaxf(mx, fabsf(x[i]));
+    for (int o = 1; o < lanes; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    int e;
+    (void)frexpf(mx / Q8_MAX, &e);   // s = 2^e >= max|x| / Q8_MAX (s = 1 for a zero group)
+    const float inv = ldexpf(1.f, -e);
+    int v[8];
+    double sum = 0.0;   // integers below 2^33: exact
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        v[i] = (int)fminf(fmaxf(rintf(x[i] * inv), -Q8_MAX), Q8_MAX);
+        sum += (double)v[i];
+    }
+    for (int o = 1; o < lanes; o <<= 1) sum += __shfl_xor(sum, o);
+    if (!on) return;
+    uint32_t H[2] = {0u, 0u}, Mw[2] = {0u, 0u}, Lw[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int ld = ((v[i] + 128) & 255) - 128;
+        const int v1 = (v[i] - ld) >> 8;   // exact: v - ld is a multiple of 256
+        const int md = ((v1 + 128) & 255) - 128;
+        const int hd = (v1 - md) >> 8;
+        const int word = i & 1, byte = i >> 1;   // column i -> position (i even: i/2, odd: 4 + i/2)
+        H[word] |= ((uint32_t)hd & 0xFFu) << (8 * byte);
+        Mw[word] |= ((uint32_t)md & 0xFFu) << (8 * byte);
+        Lw[word] |= ((uint32_t)ld & 0xFFu) << (8 * byte);
+    }
+    const size_t o8 = (size_t)m * K + 8 * b8;
+    *reinterpret_cast<uint2*>(q_hi + o8) = make_uint2(H[0], H[1]);
+    *reinterpret_cast<uint2*>(q_mid + o8) = make_uint2(Mw[0], Mw[1]);
+    *reinterpret_cast<uint2*>(q_lo + o8) = make_uint2(Lw[0], Lw[1]);
+    if (b8 % lanes == 0) {
+        const int ng = K / group;
+        q_s[(size_t)m * ng + b8 / lanes] = ldexpf(1.f, e);
+        q_sum[(size_t)m * ng + b8 / lanes] = (float)sum;
+    }
+}
+
 // ---- the same product for a few rows ---------------------------------------------------------
 //
 // For M <= 16 (a decode batch) one 16-row MFMA tile covers A: the 64-row tile above would
@@ -865,6 +1131,17 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
 // ---- launchers ------------------------------------------------------------------------------
 
 int gemm_supported(int group) { return group >= 32 && (group == 32 || group % GM_BK == 0); }
+int gemm_i8_supported(int group, int K) { return group % G8_BK == 0 && group <= 512 && K % group == 0; }
+
+int launch_pf_quant8(const uint16_t* hi, const uint16_t* lo, int lda, int M, int K, int group, int8_t* q_hi,
+                     int8_t* q_mid, int8_t* q_lo, float* q_s, float* q_sum, hipStream_t st) {
+    ATLAS_CHECK_SHAPE(gemm_i8_supported(group, K) && lda % 8 == 0 && lda >= K && M >= 1,
+                      "int8 planes need a group of 128, 256 or 512 dividing K (group %d, K %d, lda %d)", group, K, lda);
+    ATLAS_KLAUNCH(pf_quant8_kernel, dim3((K / 8 + 255) / 256, M), dim3(256), 0, st, hi, lo, lda, M, K, group, q_hi,
+                  q_mid, q_lo, q_s, q_sum);
+    ATLAS_LAUNCH_CHECK("pf_quant8_kernel");
+    return ATLAS_OK;
+}
 
 int launch_w4_gemm(const GemmArgs& a, int mode, hipStream_t st, const char* label) {
     ATLAS_CHECK_SHAPE(gemm_supported(a.group), "prefill GEMM needs group 32 or a multiple of 64 (got %d)", a.group);
@@ -875,6 +1152,16 @@ int launch_w4_gemm(const GemmArgs& a, int mode, hipStream_t st, const char* labe
                                         a.kchunk % GM_BK == 0 && a.kchunk % a.group == 0),
                       "bad K split (%d x %d of K=%d)", a.ksplit, a.kchunk, a.K);
     prof_mark(label, st);
+    if (a.q_hi) {   // int8 digit planes: the int8 matrix-core kernel
+        ATLAS_CHECK_SHAPE(gemm_i8_supported(a.group, a.K) && a.ksplit == 1 && a.ldq % 16 == 0 && a.ldq >= a.K &&
+                              a.ldqs >= a.K / a.group && a.q_mid && a.q_lo && a.q_s && a.q_sum,
+                          "int8 GEMM needs a group of 128, 256 or 512 dividing K, no K split, ldq %% 16 == 0");
+        const int T8 = MT * NT, b8 = 8 * ((T8 + 7) / 8);
+        if (mode == 0) ATLAS_KLAUNCH((w4_gemm_i8_kernel<0>), dim3(b8), dim3(G8_THREADS), 0, st, a);
+        else ATLAS_KLAUNCH((w4_gemm_i8_kernel<1>), dim3(b8), dim3(G8_THREADS), 0, st, a);
+        ATLAS_LAUNCH_CHECK("w4_gemm_i8_kernel");
+        return ATLAS_OK;
+    }
     const int krange = a.ksplit > 1 ? a.kchunk : a.K;
     if (mode == 0 && a.M <= 16 && krange % 128 == 0) {   // a few rows: weights straight to the matrix cores
         const int Nw = (a.N + 16 * SK_TILES - 1) / (16 * SK_TILES);
