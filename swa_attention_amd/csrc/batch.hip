@@ -277,22 +277,27 @@ __global__ __launch_bounds__(1024) void bd_argmax_rows_kernel(const float* logit
 
 constexpr int BD_MAX_BATCH = 16;
 
-// Splits of K for a GEMM of `tiles` output tiles over a few rows. With one tile row the
-// blocks are few and each is bound by the latency of its K loop, so the K range is cut
-// until about 1,024 blocks are in flight (at most 32 ranges, each a whole number of
-// groups and 64-column tiles): the smallest count that reaches 1,024 blocks, else the
-// largest that fits.
-int bd_ksplit(int tiles, int K, int group) {
+// Splits of K for a GEMM of `tiles` 128-row output tiles over a few rows. With one tile
+// row the blocks are few and each is bound by the latency of its K loop, so the K range
+// is cut (at most 32 ranges, each a whole number of groups and 64-column tiles): the
+// smallest count with tiles * s >= target, else the largest that fits.
+int bd_ksplit(int tiles, int K, int group, int target) {
     int best = 1;
     for (int s = 2; s <= 32; s++) {
         if (K % s) continue;
         const int c = K / s;
         if (c % 64 || c % group) continue;
         best = s;
-        if (tiles * s >= 1024) break;
+        if (tiles * s >= target) break;
     }
     return best;
 }
+// Split targets in 128-row tiles, measured at 8 sequences on the 32B shapes: the
+// small-row kernel runs two 4-wave blocks per CU, so gate/up (4 splits, 432 blocks) and
+// down (24 splits, 480 blocks) are best just under one 512-block round (5 and 27 splits
+// spill into a second: 63 and 69 us against 53 and 54); qkv and o are best at 8 and 10
+// splits (19 and 16 us against 25 and 18 at 20 and 40).
+constexpr int BD_SPLIT_TARGET_ATTN_PROJ = 384, BD_SPLIT_TARGET_MLP = 768;
 
 struct BatchPlan {
     int sq, so, sg, sd;   // K splits of the qkv, o, gate/up and down GEMMs
@@ -303,10 +308,10 @@ static BatchPlan batch_plan(const atlas_model* m, int B) {
     BatchPlan p{};
     const int nq = m->hq * m->hd, nqkv = (m->hq + 2 * m->hkv) * m->hd;
     const int MT = (B + 63) / 64;
-    p.sq = bd_ksplit(MT * ((nqkv + 127) / 128), m->d, m->layers[0].qkv.group);
-    p.so = bd_ksplit(MT * ((m->d + 127) / 128), nq, m->layers[0].o.group);
-    p.sg = bd_ksplit(MT * ((m->dff + 127) / 128), m->d, m->layers[0].gate.group);
-    p.sd = bd_ksplit(MT * ((m->d + 127) / 128), m->dff, m->layers[0].down.group);
+    p.sq = bd_ksplit(MT * ((nqkv + 127) / 128), m->d, m->layers[0].qkv.group, BD_SPLIT_TARGET_ATTN_PROJ);
+    p.so = bd_ksplit(MT * ((m->d + 127) / 128), nq, m->layers[0].o.group, BD_SPLIT_TARGET_ATTN_PROJ);
+    p.sg = bd_ksplit(MT * ((m->dff + 127) / 128), m->d, m->layers[0].gate.group, BD_SPLIT_TARGET_MLP);
+    p.sd = bd_ksplit(MT * ((m->d + 127) / 128), m->dff, m->layers[0].down.group, BD_SPLIT_TARGET_MLP);
     for (int l = 1; l < m->n_layers; l++) {   // one plan for every layer: take splits all layers allow
         const atlas_layer& L = m->layers[l];
         if (m->d % (p.sq * L.qkv.group) || (m->d / p.sq) % 64) p.sq = 1;
