@@ -43,7 +43,7 @@ PrefillWs carve_prefill(const atlas_model* m, int n, void* base) {
     w.dec = take(decode_ws_bytes(m));
     w.X = (float*)take((size_t)n * m->d * 4);
     w.QKV = (float*)take((size_t)n * nqkv * 4);
-    w.A = (float*)take((size_t)n * m->d * 4);
+    w.A = (float*)take((size_t)n * 2 * m->d * 4);   // o / down output: up to two K-split partials per row
     w.p1h = (uint16_t*)take((size_t)n * w.ld1 * 2);
     w.p1l = (uint16_t*)take((size_t)n * w.ld1 * 2);
     w.p2h = (uint16_t*)take((size_t)n * m->dff * 2);
@@ -88,6 +88,20 @@ GemmArgs gemm(const uint16_t* hi, const uint16_t* lo, int lda, const atlas_w4& w
     g.K = w.K;
     g.group = w.group;
     return g;
+}
+
+// K splits of the o and down GEMMs (1 or 2). Two halves of K double the tiles of these
+// N = d GEMMs (760 -> 1,520 at 1,200 positions: two rounds of the two-blocks-per-CU grid
+// filled instead of one and a half); the residual that reads them adds the halves.
+int pf_ksplit(const atlas_w4& w) {
+    const int c = w.K / 2;
+    return (w.K % 2 == 0 && c % w.group == 0 && c % 128 == 0) ? 2 : 1;
+}
+
+void set_split(GemmArgs& g, int S, int d) {
+    g.ksplit = S;
+    g.kchunk = S > 1 ? g.K / S : 0;
+    g.c_split = S > 1 ? (size_t)d : 0;   // partial s of row t at C + t ldc + s d
 }
 
 // Int8 digit planes of the GEMM input for groups of 128, 256 or 512 (the int8 matrix-core
@@ -206,10 +220,12 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
         // o projection, h = x + RMSNorm_pa(a)
         GemmArgs oa = gemm(w.p1h, w.p1l, w.ld1, L.o, n);
         oa.C = w.A;
-        oa.ldc = d;
+        oa.ldc = 2 * d;
+        const int so = pf_ksplit(L.o);
+        set_split(oa, so, d);
         if ((rc = attach_i8(oa, w, st))) return rc;
         if ((rc = launch_w4_gemm(oa, 0, st, "pf_gemm_o"))) return rc;
-        if ((rc = launch_pf_residual(w.X, w.A, L.g_pa, n, d, m->eps, w.p1h, w.p1l, w.ld1, st))) return rc;
+        if ((rc = launch_pf_residual(w.X, w.A, 2 * d, so, L.g_pa, n, d, m->eps, w.p1h, w.p1l, w.ld1, st))) return rc;
         // gate/up with SwiGLU, then down
         GemmArgs ga = gemm(w.p1h, w.p1l, w.ld1, L.gate, n);
         ga.W1 = view(L.up);
@@ -220,18 +236,21 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
         if ((rc = launch_w4_gemm(ga, 1, st, "pf_gemm_gate_up"))) return rc;
         GemmArgs da = gemm(w.p2h, w.p2l, m->dff, L.down, n);
         da.C = w.A;
-        da.ldc = d;
+        da.ldc = 2 * d;
+        const int sd = pf_ksplit(L.down);
+        set_split(da, sd, d);
         if ((rc = attach_i8(da, w, st))) return rc;
         if ((rc = launch_w4_gemm(da, 0, st, "pf_gemm_down"))) return rc;
         // y = h + RMSNorm_pf(m): the last layer leaves it to the head (last position only)
         if (!last || !head)
-            if ((rc = launch_pf_residual(w.X, w.A, L.g_pf, n, d, m->eps, w.p1h, w.p1l, w.ld1, st))) return rc;
+            if ((rc = launch_pf_residual(w.X, w.A, 2 * d, sd, L.g_pf, n, d, m->eps, w.p1h, w.p1l, w.ld1, st)))
+                return rc;
     }
     if (!head) return ATLAS_OK;
     XSource lastx{};
     lastx.mode = X_FROM_RESIDUAL;
-    lastx.m_part = w.A + (size_t)(n - 1) * d;
-    lastx.S = 1;
+    lastx.m_part = w.A + (size_t)(n - 1) * 2 * d;   // the down partials of the last row, d apart
+    lastx.S = pf_ksplit(m->layers[m->n_layers - 1].down);
     lastx.h = w.X + (size_t)(n - 1) * d;
     lastx.g = m->layers[m->n_layers - 1].g_pf;
     lastx.eps = m->eps;

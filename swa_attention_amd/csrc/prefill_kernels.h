@@ -88,7 +88,7 @@ int launch_pf_rope(const PfRopeArgs& a, hipStream_t st);
 int launch_pf_commit(const PfCommitArgs& a, hipStream_t st);
 int launch_pf_attn(const PfAttnArgs& a, hipStream_t st);
 int launch_pf_split(const float* X, int M, int K, int ldx, uint16_t* p_hi, uint16_t* p_lo, int ldp, hipStream_t st);
-int launch_pf_residual(float* X, const float* A, const float* g, int n, int d, float eps, uint16_t* p_hi,
-                       uint16_t* p_lo, int ldp, hipStream_t st);
+int launch_pf_residual(float* X, const float* A, int lda, int S, const float* g, int n, int d, float eps,
+                       uint16_t* p_hi, uint16_t* p_lo, int ldp, hipStream_t st);
 
 }  // namespace atlas

@@ -259,16 +259,18 @@ __global__ __launch_bounds__(G8_THREADS) void w4_gemm_i8_kernel(GemmArgs a) {
     const int MT = (a.M + G8_BM - 1) / G8_BM;
     const int NW_ = MODE ? G8_BN / 2 : G8_BN;   // output columns per tile
     const int NT = (a.N + NW_ - 1) / NW_;
-    const int T = MT * NT, per = (T + 7) / 8;
-    const int L = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-    if (L >= T) return;
+    const int T = MT * NT, Wk = T * a.ksplit, per = (Wk + 7) / 8;
+    const int Lw = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (Lw >= Wk) return;
+    const int L = Lw % T, split = Lw / T;
+    const int k_lo = split * a.kchunk, k_hi = a.ksplit > 1 ? k_lo + a.kchunk : a.K;
     const int m0 = (L % MT) * G8_BM, n0 = (L / MT) * NW_;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     const int l16 = lane & 15, l4 = lane >> 4;
-    const int KT = a.K / G8_BK;
+    const int KT = (k_hi - k_lo) / G8_BK;
 
     auto second = [&](int r) { return MODE && r >= G8_BN / 2; };
     auto wrow = [&](int r) { return min(n0 + (second(r) ? r - G8_BN / 2 : r), a.N - 1); };
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(G8_THREADS) void w4_gemm_i8_kernel(GemmArgs a) {
     uint16_t rS;
     float rSx, rSX;
     auto load_k = [&](int kt) {
-        const int kb = kt * G8_BK, g = kb / a.group;
+        const int kb = k_lo + kt * G8_BK, g = kb / a.group;
         rAh0 = *reinterpret_cast<const uint4*>(a.q_hi + ao0 + kb);
         rAh1 = *reinterpret_cast<const uint4*>(a.q_hi + ao1 + kb);
         rAm0 = *reinterpret_cast<const uint4*>(a.q_mid + ao0 + kb);
@@ -326,7 +328,7 @@ __global__ __launch_bounds__(G8_THREADS) void w4_gemm_i8_kernel(GemmArgs a) {
 
     load_k(0);
     for (int kt = 0; kt < KT; kt++) {
-        const int kb = kt * G8_BK;
+        const int kb = k_lo + kt * G8_BK;
         __syncthreads();   // the previous tile's fragments have been read
         *reinterpret_cast<uint4*>(&sAh[ar * LDB + ac]) = rAh0;
         *reinterpret_cast<uint4*>(&sAh[(ar + 32) * LDB + ac]) = rAh1;
@@ -408,7 +410,7 @@ __global__ __launch_bounds__(G8_THREADS) void w4_gemm_i8_kernel(GemmArgs a) {
 #pragma unroll
                 for (int nf = 0; nf < 4; nf++) {
                     const int col = n0 + bcol(nf) + l16;
-                    if (col < a.N) a.C[(size_t)row * a.ldc + col] = acc[mf][nf][r];
+                    if (col < a.N) a.C[split * a.c_split + (size_t)row * a.ldc + col] = acc[mf][nf][r];
                 }
             } else {
 #pragma unroll
@@ -847,14 +849,24 @@ __global__ __launch_bounds__(256) void pf_commit_kernel(PfCommitArgs a) {
 }
 
 // X[t] += g * A[t] / rms(A[t]) and the bf16 planes of the new X[t].
-__global__ __launch_bounds__(256) void pf_residual_kernel(float* X, const float* A, const float* g, int d, float eps,
-                                                         uint16_t* p_hi, uint16_t* p_lo, int ldp) {
+// A holds S (1 or 2) partial sums per row: row t's at A + t lda and A + t lda + d.
+__global__ __launch_bounds__(256) void pf_residual_kernel(float* X, const float* A, int lda, int S, const float* g,
+                                                         int d, float eps, uint16_t* p_hi, uint16_t* p_lo, int ldp) {
     __shared__ float red[16];
     const int t = blockIdx.x;
-    const float4* a4 = reinterpret_cast<const float4*>(A + (size_t)t * d);
+    const float4* a4 = reinterpret_cast<const float4*>(A + (size_t)t * lda);
+    const float4* b4 = reinterpret_cast<const float4*>(A + (size_t)t * lda + (S > 1 ? d : 0));
+    auto part = [&](int i) {
+        float4 v = a4[i];
+        if (S > 1) {
+            const float4 w = b4[i];
+            v = make_float4(v.x + w.x, v.y + w.y, v.z + w.z, v.w + w.w);
+        }
+        return v;
+    };
     float ss = 0.f;
     for (int i = threadIdx.x; i < d / 4; i += blockDim.x) {
-        const float4 v = a4[i];
+        const float4 v = part(i);
         ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
     }
     ss = block_sum(ss, red);
@@ -862,7 +874,7 @@ __global__ __launch_bounds__(256) void pf_residual_kernel(float* X, const float*
     float4* x4 = reinterpret_cast<float4*>(X + (size_t)t * d);
     const float4* g4 = reinterpret_cast<const float4*>(g);
     for (int i = threadIdx.x; i < d / 4; i += blockDim.x) {
-        const float4 v = a4[i], gg = g4[i], x = x4[i];
+        const float4 v = part(i), gg = g4[i], x = x4[i];
         const float4 h = make_float4(x.x + gg.x * (v.x * r), x.y + gg.y * (v.y * r), x.z + gg.z * (v.z * r),
                                      x.w + gg.w * (v.w * r));
         x4[i] = h;
@@ -1153,10 +1165,12 @@ int launch_w4_gemm(const GemmArgs& a, int mode, hipStream_t st, const char* labe
                       "bad K split (%d x %d of K=%d)", a.ksplit, a.kchunk, a.K);
     prof_mark(label, st);
     if (a.q_hi) {   // int8 digit planes: the int8 matrix-core kernel
-        ATLAS_CHECK_SHAPE(gemm_i8_supported(a.group, a.K) && a.ksplit == 1 && a.ldq % 16 == 0 && a.ldq >= a.K &&
+        ATLAS_CHECK_SHAPE(gemm_i8_supported(a.group, a.K) && (a.ksplit == 1 || a.kchunk % G8_BK == 0) &&
+                              a.ldq % 16 == 0 && a.ldq >= a.K &&
                               a.ldqs >= a.K / a.group && a.q_mid && a.q_lo && a.q_s && a.q_sum,
-                          "int8 GEMM needs a group of 128, 256 or 512 dividing K, no K split, ldq %% 16 == 0");
-        const int T8 = MT * NT, b8 = 8 * ((T8 + 7) / 8);
+                          "int8 GEMM needs a group of 128, 256 or 512 dividing K, K ranges of whole 128-column "
+                          "tiles, ldq %% 16 == 0");
+        const int T8 = MT * NT * a.ksplit, b8 = 8 * ((T8 + 7) / 8);
         if (mode == 0) ATLAS_KLAUNCH((w4_gemm_i8_kernel<0>), dim3(b8), dim3(G8_THREADS), 0, st, a);
         else ATLAS_KLAUNCH((w4_gemm_i8_kernel<1>), dim3(b8), dim3(G8_THREADS), 0, st, a);
         ATLAS_LAUNCH_CHECK("w4_gemm_i8_kernel");
@@ -1231,10 +1245,11 @@ int launch_pf_split(const float* X, int M, int K, int ldx, uint16_t* p_hi, uint1
     return ATLAS_OK;
 }
 
-int launch_pf_residual(float* X, const float* A, const float* g, int n, int d, float eps, uint16_t* p_hi,
-                       uint16_t* p_lo, int ldp, hipStream_t st) {
+int launch_pf_residual(float* X, const float* A, int lda, int S, const float* g, int n, int d, float eps,
+                       uint16_t* p_hi, uint16_t* p_lo, int ldp, hipStream_t st) {
+    ATLAS_CHECK_SHAPE((S == 1 || S == 2) && lda % 4 == 0 && lda >= S * d && d % 4 == 0, "residual partials");
     prof_mark("pf_residual_norm", st);
-    ATLAS_KLAUNCH(pf_residual_kernel, dim3(n), dim3(256), 0, st, X, A, g, d, eps, p_hi, p_lo, ldp);
+    ATLAS_KLAUNCH(pf_residual_kernel, dim3(n), dim3(256), 0, st, X, A, lda, S, g, d, eps, p_hi, p_lo, ldp);
     ATLAS_LAUNCH_CHECK("pf_residual_kernel");
     return ATLAS_OK;
 }
