@@ -271,6 +271,20 @@ def test_prefill_continues_a_filled_cache():
     _prefill_vs_oracle(_tiny_stack(n_cached=50, t_max=128), 37, dev)
 
 
+def test_prefill_split_k_shapes_match_oracle():
+    """A 2-layer stack with d = 1,024 (8 q / 2 KV heads) and dff = 2,048: half of the o
+    and down GEMMs' K is whole 128-column groups, so the prefill splits their K in two
+    (the residual kernel and the head add the halves) on the int8 kernel; 40 positions
+    after 20 cached, against the oracle."""
+    dev = device()
+    m = W.Model(d=1024, hq=8, hkv=2, hd=128, dff=2048, n_layers=2, layer_types=[W.SWA, W.FULL], window=64,
+                model_id=61)
+    m.vocab = 1000
+    wl = W.Workload("tiny-split-k", m, seed=0, n_cached=20, t_max=96, use_tokens=True, final_head=True)
+    announce("prefill 2-layer d=1024 stack, 40 tokens after 20 cached (split-K o/down)")
+    _prefill_vs_oracle(wl, 40, dev)
+
+
 def test_prefill_bad_token_sets_status():
     dev = device()
     wl = _tiny_stack(n_cached=0, t_max=64)
