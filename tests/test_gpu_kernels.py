@@ -168,6 +168,32 @@ def test_gemm_large_grid_sampled_rows(group):
         np.testing.assert_array_equal(C[i].view(np.uint32), deq[:, j].copy().view(np.uint32), err_msg=f"row {i}")
 
 
+@pytest.mark.parametrize("group", [128, 512])
+def test_gemm_int8_heavy_tailed_and_zero_groups(group):
+    """The int8 kernel's group-scaled fixed point on rows whose values span twelve
+    orders of magnitude, with whole groups of zeros and one group of a single huge
+    value: each group takes its own power-of-two scale, so normwise error stays at the
+    bf16 planes' level (2e-5), zero groups contribute exactly nothing, and rows that
+    are zero except for one group equal that group's product alone."""
+    dev = device()
+    M, N, K = 40, 256, 2048
+    c, s, z = _w4(N, K, 15, group)
+    r = np.random.default_rng(16)
+    A = (r.standard_normal((M, K)) * 10.0 ** r.uniform(-6, 6, (M, K))).astype(np.float32)
+    A[3, :] = 0.0
+    A[5, group:] = 0.0                    # only the first group is non-zero
+    A[7, :group] = 0.0
+    A[7, group + 3] = 3.0e7               # one huge value, the rest of its group at 1e-6..1e6
+    w = w4_to_device(c, s, z, K, dev, group)
+    C = ops.atlas_w4_gemm(w, torch.from_numpy(A).to(dev)).cpu().numpy()
+    ref = np.stack([O.w4_gemv(c, s, z, K, A[i], group) for i in range(M)])
+    for i in range(M):
+        if i == 3:
+            assert not C[i].any()
+        else:
+            assert normwise(C[i], ref[i]) < 2e-5, i
+
+
 def test_gemv_heavy_tailed_input():
     """Inputs spanning 12 orders of magnitude within a chunk stay at f32-level error."""
     dev = device()
