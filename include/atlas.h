@@ -235,9 +235,11 @@ ATLAS_API int atlas_device_status(const void* ws, void* stream, int32_t* status_
  * (int32, may be NULL). By definition it equals n_tokens teacher-forced decode
  * steps ([card] Limitations: prefill currently runs token by token through the
  * decode path, with a batched GEMM prefill as the planned fix); here the projections
- * run as W4 GEMMs on the matrix cores over all tokens (see atlas_w4_gemm), QK norm,
- * rotary and the KV write per token, and causal attention within each layer's
- * window on f32 matrix cores. Linear layers need group 32 or a multiple of 64.
+ * run as W4 GEMMs on the matrix cores over all tokens (see atlas_w4_gemm: int8
+ * products for groups of 128-512, bf16 otherwise), QK norm, rotary and the KV write
+ * per token, and causal attention within each layer's window on bf16 matrix cores
+ * with hi/lo operands (about 2^-16 per product). Linear layers need group 32 or a
+ * multiple of 64.
  * ws: atlas_prefill_workspace_bytes(m, n_tokens) bytes; its first word is the status
  * word of atlas_device_status (ATLAS_ERR_INVALID_ARG when a token id is out of range;
  * such ids read embedding row 0). */
