@@ -42,7 +42,7 @@ PrefillWs carve_prefill(const atlas_model* m, int n, void* base) {
     w.ld1 = std::max(m->d, nq);
     w.dec = take(decode_ws_bytes(m));
     w.X = (float*)take((size_t)n * m->d * 4);
-    w.QKV = (float*)take((size_t)n * nqkv * 4);
+    w.QKV = (float*)take((size_t)n * 4 * nqkv * 4);   // up to four K-split partials per row
     w.A = (float*)take((size_t)n * 2 * m->d * 4);   // o / down output: up to two K-split partials per row
     w.p1h = (uint16_t*)take((size_t)n * w.ld1 * 2);
     w.p1l = (uint16_t*)take((size_t)n * w.ld1 * 2);
@@ -90,12 +90,18 @@ GemmArgs gemm(const uint16_t* hi, const uint16_t* lo, int lda, const atlas_w4& w
     return g;
 }
 
-// K splits of the o and down GEMMs (1 or 2). Two halves of K double the tiles of these
-// N = d GEMMs (760 -> 1,520 at 1,200 positions: two rounds of the two-blocks-per-CU grid
-// filled instead of one and a half); the residual that reads them adds the halves.
-int pf_ksplit(const atlas_w4& w) {
-    const int c = w.K / 2;
-    return (w.K % 2 == 0 && c % w.group == 0 && c % 128 == 0) ? 2 : 1;
+// K splits of the qkv, o and down GEMMs: the most ranges up to `most` (two here) with whole
+// groups and 128-column tiles. At 1,200 positions the 64 x 128 tiles fill the
+// two-blocks-per-CU grid (512 per round) poorly: o and down have 760 tiles (1.5 rounds;
+// split in two, 2.97), qkv 1,064 (2.08 rounds; split in two, 4.16). The consumers add the
+// partials: the residual kernel (o, down), the head (the last down), the rotary kernel (qkv).
+// Four qkv ranges made the GEMM no faster than two and doubled the rotary kernel's reads.
+int pf_ksplit(const atlas_w4& w, int most) {
+    for (int s = most; s > 1; s--) {
+        const int c = w.K / s;
+        if (w.K % s == 0 && c % w.group == 0 && c % 128 == 0) return s;
+    }
+    return 1;
 }
 
 void set_split(GemmArgs& g, int S, int d) {
@@ -159,14 +165,18 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
         const bool last = l == m->n_layers - 1;
         // qkv projection of all positions
         GemmArgs qa = gemm(w.p1h, w.p1l, w.ld1, L.qkv, n);
+        const int sq = pf_ksplit(L.qkv, 2);
         qa.C = w.QKV;
-        qa.ldc = nqkv;
+        qa.ldc = sq * nqkv;
+        set_split(qa, sq, nqkv);
         if ((rc = attach_i8(qa, w, st))) return rc;
         if ((rc = launch_w4_gemm(qa, 0, st, "pf_gemm_qkv"))) return rc;
         // QK norm and rotary; the prompt keys/values into the prompt KV buffers
         PfRopeArgs ra{};
         ra.qkv = w.QKV;
-        ra.ld = nqkv;
+        ra.ld = sq * nqkv;
+        ra.S = sq;
+        ra.pstride = nqkv;
         ra.n = n;
         ra.start_pos = start_pos;
         ra.Hq = m->hq;
@@ -186,7 +196,7 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
         // causal attention; output planes for the o projection
         PfAttnArgs aa{};
         aa.qkv = w.QKV;
-        aa.ld_qkv = nqkv;
+        aa.ld_qkv = sq * nqkv;   // q rotated in place in the first partial
         aa.k_cache = L.k_cache;
         aa.v_cache = L.v_cache;
         aa.slots = slots;
@@ -221,7 +231,7 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
         GemmArgs oa = gemm(w.p1h, w.p1l, w.ld1, L.o, n);
         oa.C = w.A;
         oa.ldc = 2 * d;
-        const int so = pf_ksplit(L.o);
+        const int so = pf_ksplit(L.o, 2);
         set_split(oa, so, d);
         if ((rc = attach_i8(oa, w, st))) return rc;
         if ((rc = launch_w4_gemm(oa, 0, st, "pf_gemm_o"))) return rc;
@@ -237,7 +247,7 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
         GemmArgs da = gemm(w.p2h, w.p2l, m->dff, L.down, n);
         da.C = w.A;
         da.ldc = 2 * d;
-        const int sd = pf_ksplit(L.down);
+        const int sd = pf_ksplit(L.down, 2);
         set_split(da, sd, d);
         if ((rc = attach_i8(da, w, st))) return rc;
         if ((rc = launch_w4_gemm(da, 0, st, "pf_gemm_down"))) return rc;
@@ -250,7 +260,7 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
     XSource lastx{};
     lastx.mode = X_FROM_RESIDUAL;
     lastx.m_part = w.A + (size_t)(n - 1) * 2 * d;   // the down partials of the last row, d apart
-    lastx.S = pf_ksplit(m->layers[m->n_layers - 1].down);
+    lastx.S = pf_ksplit(m->layers[m->n_layers - 1].down, 2);
     lastx.h = w.X + (size_t)(n - 1) * d;
     lastx.g = m->layers[m->n_layers - 1].g_pf;
     lastx.eps = m->eps;

@@ -54,7 +54,8 @@ struct PfAttnArgs {
 };
 
 struct PfRopeArgs {
-    float* qkv;                // [n][ld]: q and k normalised/rotated in place
+    float* qkv;                // [n][ld]: S partial projections per row, pstride apart; q is
+                               // written back normalised and rotated into the first
     int ld, n, start_pos, Hq, Hkv;
     const float *g_q, *g_k;
     float eps;
@@ -63,6 +64,7 @@ struct PfRopeArgs {
     void* k_new;               // [Hkv][n][128] prompt keys / values, f32 or bf16 (kv_bf16)
     void* v_new;
     int kv_bf16;
+    int S = 1, pstride = 0;    // K-split partials of the qkv GEMM (1..4)
 };
 
 // Prompt KV -> cache: positions j in [max(start_pos, start_pos + n - slots), start_pos + n)

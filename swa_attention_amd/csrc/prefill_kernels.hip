@@ -771,16 +771,25 @@ __global__ __launch_bounds__(256) void pf_embed_kernel(const int32_t* tokens, in
 // Full-projection QK RMSNorm, rotary embedding (x attention factor) at position
 // start_pos + t, q written back in place, k and v written to row t of the prompt KV
 // buffers (rounded to bf16 when the cache is bf16: what is stored is what attends).
+// One block per position: the S partial projections are added into an LDS copy of the
+// row (dynamic shared memory, (Hq + 2 Hkv) * 128 floats), which every later read uses.
 __global__ __launch_bounds__(256) void pf_rope_kernel(PfRopeArgs a) {
     constexpr int D = 128;
+    extern __shared__ float s_row[];
     __shared__ float red[16];
     __shared__ float s_cos[64], s_sin[64];
     const int t = blockIdx.x, pos = a.start_pos + t;
-    const int nq = a.Hq * D, nk = a.Hkv * D;
+    const int nq = a.Hq * D, nk = a.Hkv * D, nqkv = nq + 2 * nk;
     float* row = a.qkv + (size_t)t * a.ld;
+    for (int i = threadIdx.x; i < nqkv; i += blockDim.x) {
+        float v = row[i];
+        for (int s = 1; s < a.S; s++) v += row[(size_t)s * a.pstride + i];
+        s_row[i] = v;
+    }
+    __syncthreads();
     float sq = 0.f, sk = 0.f;
-    for (int i = threadIdx.x; i < nq; i += blockDim.x) sq = fmaf(row[i], row[i], sq);
-    for (int i = threadIdx.x; i < nk; i += blockDim.x) sk = fmaf(row[nq + i], row[nq + i], sk);
+    for (int i = threadIdx.x; i < nq; i += blockDim.x) sq = fmaf(s_row[i], s_row[i], sq);
+    for (int i = threadIdx.x; i < nk; i += blockDim.x) sk = fmaf(s_row[nq + i], s_row[nq + i], sk);
     sq = block_sum(sq, red);
     sk = block_sum(sk, red);
     const float rq = 1.0f / sqrtf(sq / (float)nq + a.eps);
@@ -801,7 +810,7 @@ __global__ __launch_bounds__(256) void pf_rope_kernel(PfRopeArgs a) {
         const float rr = isk ? rk : rq;
         const float* g = isk ? a.g_k + (h - a.Hq) * D : a.g_q + h * D;
         const int base = h * D;   // q heads, then k heads, in the projection row
-        const float x0 = g[i] * (row[base + i] * rr), x1 = g[i + 64] * (row[base + i + 64] * rr);
+        const float x0 = g[i] * (s_row[base + i] * rr), x1 = g[i + 64] * (s_row[base + i + 64] * rr);
         const float c = s_cos[i], sn = s_sin[i];
         const float y0 = x0 * c - x1 * sn, y1 = x1 * c + x0 * sn;
         if (isk) {
@@ -821,7 +830,7 @@ __global__ __launch_bounds__(256) void pf_rope_kernel(PfRopeArgs a) {
     for (int u = threadIdx.x; u < nk; u += blockDim.x) {
         const int h = u / D, i = u % D;
         const size_t e = ((size_t)h * a.n + t) * D + i;
-        const float v = row[nq + nk + u];
+        const float v = s_row[nq + nk + u];
         if (a.kv_bf16) ((uint16_t*)a.v_new)[e] = (uint16_t)f32_to_bf16_rne(v);
         else ((float*)a.v_new)[e] = v;
     }
@@ -1206,8 +1215,12 @@ int launch_pf_embed(const int32_t* tokens, int n, const uint16_t* emb, int vocab
 }
 
 int launch_pf_rope(const PfRopeArgs& a, hipStream_t st) {
+    const int nqkv = (a.Hq + 2 * a.Hkv) * 128;
+    ATLAS_CHECK_SHAPE(a.S >= 1 && a.S <= 4 && (a.S == 1 || a.pstride >= nqkv) && a.ld >= (a.S - 1) * a.pstride + nqkv &&
+                          nqkv * 4 <= 64 * 1024,
+                      "qkv partials: S=%d pstride=%d ld=%d", a.S, a.pstride, a.ld);
     prof_mark("pf_qk_norm_rope", st);
-    ATLAS_KLAUNCH(pf_rope_kernel, dim3(a.n), dim3(256), 0, st, a);
+    ATLAS_KLAUNCH(pf_rope_kernel, dim3(a.n), dim3(256), (size_t)nqkv * 4, st, a);
     ATLAS_LAUNCH_CHECK("pf_rope_kernel");
     return ATLAS_OK;
 }
