@@ -82,6 +82,20 @@ def test_batch_tiny_stack_matches_oracle(kv_dtype, ring):
             assert _close_kv(gk[:, slot], hk) and _close_kv(gv[:, slot], hv), (b, l)
 
 
+def test_batch_of_sixteen_the_maximum():
+    """The largest batch (16 sequences, the 16-row MFMA tile full) at ragged positions
+    150 down to 0 through the tiny 4-layer stack with bf16 KV on rings: logits and argmax
+    of every sequence against the oracle."""
+    dev = device()
+    wl = _tiny_batch(1, True, batch=16, gap=10, model_id=53)
+    announce("batched decode, tiny 4-layer stack, 16 sequences at 150..0, bf16 ring")
+    dm, ws, before, logits, am, _ = _run_batch(wl, dev)
+    assert ops.atlas_device_status(ws) == 0
+    for b, ref in enumerate(R.run_decode_batch(wl)):
+        assert normwise(logits[b].cpu().numpy(), ref["logits"]) < TOL, b
+        assert int(am[b].item()) == ref["argmax"], b
+
+
 def test_batch_of_one_matches_the_single_step():
     dev = device()
     wl = _tiny_batch(0, False, batch=1, gap=0, model_id=51)
