@@ -271,18 +271,20 @@ def test_prefill_continues_a_filled_cache():
     _prefill_vs_oracle(_tiny_stack(n_cached=50, t_max=128), 37, dev)
 
 
-def test_prefill_split_k_shapes_match_oracle():
-    """A 2-layer stack with d = 1,024 (8 q / 2 KV heads) and dff = 2,048: half of the o
-    and down GEMMs' K is whole 128-column groups, so the prefill splits their K in two
-    (the residual kernel and the head add the halves) on the int8 kernel; 40 positions
-    after 20 cached, against the oracle."""
+@pytest.mark.parametrize("n_tokens,n_cached", [(40, 20), (1, 0), (1, 30), (17, 5)])
+def test_prefill_split_k_shapes_match_oracle(n_tokens, n_cached):
+    """A 2-layer stack with d = 1,024 (8 q / 2 KV heads) and dff = 2,048: half of the qkv,
+    o and down GEMMs' K is whole 128-column groups, so the prefill splits their K in two
+    (the rotary kernel, the residual kernel and the head add the halves) on the int8
+    kernel. Against the oracle: 40 positions after 20 cached; a one-token prompt on an
+    empty and on a filled cache (one GEMM row); 17 positions, one past a 16-row tile."""
     dev = device()
     m = W.Model(d=1024, hq=8, hkv=2, hd=128, dff=2048, n_layers=2, layer_types=[W.SWA, W.FULL], window=64,
                 model_id=61)
     m.vocab = 1000
-    wl = W.Workload("tiny-split-k", m, seed=0, n_cached=20, t_max=96, use_tokens=True, final_head=True)
-    announce("prefill 2-layer d=1024 stack, 40 tokens after 20 cached (split-K o/down)")
-    _prefill_vs_oracle(wl, 40, dev)
+    wl = W.Workload("tiny-split-k", m, seed=0, n_cached=n_cached, t_max=96, use_tokens=True, final_head=True)
+    announce(f"prefill 2-layer d=1024 stack, {n_tokens} tokens after {n_cached} cached (split-K GEMMs)")
+    _prefill_vs_oracle(wl, n_tokens, dev)
 
 
 def test_prefill_bad_token_sets_status():
