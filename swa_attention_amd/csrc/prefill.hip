@@ -29,6 +29,8 @@ struct PrefillWs {
     size_t bytes;
 };
 
+constexpr int PF_QKV_SPLIT_MAX = 2;   // K ranges of the qkv GEMM (see pf_ksplit)
+
 PrefillWs carve_prefill(const atlas_model* m, int n, void* base) {
     PrefillWs w{};
     char* b = (char*)base;
@@ -42,7 +44,7 @@ PrefillWs carve_prefill(const atlas_model* m, int n, void* base) {
     w.ld1 = std::max(m->d, nq);
     w.dec = take(decode_ws_bytes(m));
     w.X = (float*)take((size_t)n * m->d * 4);
-    w.QKV = (float*)take((size_t)n * 4 * nqkv * 4);   // up to four K-split partials per row
+    w.QKV = (float*)take((size_t)n * PF_QKV_SPLIT_MAX * nqkv * 4);   // K-split partials per row
     w.A = (float*)take((size_t)n * 2 * m->d * 4);   // o / down output: up to two K-split partials per row
     w.p1h = (uint16_t*)take((size_t)n * w.ld1 * 2);
     w.p1l = (uint16_t*)take((size_t)n * w.ld1 * 2);
@@ -165,7 +167,7 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
         const bool last = l == m->n_layers - 1;
         // qkv projection of all positions
         GemmArgs qa = gemm(w.p1h, w.p1l, w.ld1, L.qkv, n);
-        const int sq = pf_ksplit(L.qkv, 2);
+        const int sq = pf_ksplit(L.qkv, PF_QKV_SPLIT_MAX);
         qa.C = w.QKV;
         qa.ldc = sq * nqkv;
         set_split(qa, sq, nqkv);
