@@ -220,7 +220,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
-              "How the step would shard over several GPUs is described in DESIGN.md.", file=sys.stderr)
+              "The step would shard by KV head (attention local, two small all-reduces per layer); "
+              "only the one-GPU path is built.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -239,8 +240,8 @@ def main():
     torch.cuda.synchronize()
     log(f"model resident in {time.time() - t0:.1f} s, {torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
 
-    from oracle import runner as R   # only for the seeded first token id (no oracle arithmetic)
-    tok = torch.tensor([R.decode_token(wl)], dtype=torch.int32, device=dev)
+    # the seeded first token: the first draw of the workload's prompt stream
+    tok = torch.tensor([int(W.prompt_tokens(m, wl.seed, 1)[0])], dtype=torch.int32, device=dev)
     pos = torch.tensor([wl.n_cached], dtype=torch.int32, device=dev)
     head = wl.final_head
     B = wl.batch

@@ -24,9 +24,11 @@
  *    look back more than 4,096 tokens).
  *  - "Olmo 3 32B" (llm-architectures-explained): field table (post norms only,
  *    q_norm/k_norm, rotary on the full head, not parallel, untied embeddings).
- *  - "OLMo 3 32B" (LLM Architecture KB): reordered post-norm inside the residual
- *    branch; RMSNorm on Q and K before the attention dot product; YaRN only on
- *    the global layers.
+ *  - "OLMo 3 32B" (LLM Architecture KB), Architecture: the post-norm sits inside
+ *    each residual branch; the query and key projections are RMS-normalised
+ *    before their scores are taken (the page fixes no order against the rotary
+ *    step: norm first, then rotation, is the reading used here); YaRN applies to
+ *    the global layers alone.
  *  - "Olmo-3-1125-32B" (archdb): RMSNorm eps 1e-6, no projection biases,
  *    SwiGLU, YaRN on full-attention layers only.
  * Readings where the pages are silent are stated at each function.

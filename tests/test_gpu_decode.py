@@ -271,19 +271,27 @@ def test_prefill_continues_a_filled_cache():
     _prefill_vs_oracle(_tiny_stack(n_cached=50, t_max=128), 37, dev)
 
 
-@pytest.mark.parametrize("n_tokens,n_cached", [(40, 20), (1, 0), (1, 30), (17, 5)])
-def test_prefill_split_k_shapes_match_oracle(n_tokens, n_cached):
+@pytest.mark.parametrize("n_tokens,n_cached,fmt", [(40, 20, "g128"), (1, 0, "g128"), (1, 30, "g128"),
+                                                   (17, 5, "g128"), (40, 20, "card"), (17, 5, "card"),
+                                                   (23, 9, "g64")])
+def test_prefill_split_k_shapes_match_oracle(n_tokens, n_cached, fmt):
     """A 2-layer stack with d = 1,024 (8 q / 2 KV heads) and dff = 2,048: half of the qkv,
     o and down GEMMs' K is whole 128-column groups, so the prefill splits their K in two
-    (the rotary kernel, the residual kernel and the head add the halves) on the int8
-    kernel. Against the oracle: 40 positions after 20 cached; a one-token prompt on an
-    empty and on a filled cache (one GEMM row); 17 positions, one past a 16-row tile."""
+    (the rotary kernel, the residual kernel and the head add the halves). With groups of
+    128 this runs the int8 kernel; in the card's recipe (symmetric, group 32, bf16
+    scales) and with groups of 64 it runs the bf16 kernel's split path. Against the
+    oracle: 40 positions after 20 cached; a one-token prompt on an empty and on a filled
+    cache (one GEMM row); 17 positions, one past a 16-row tile; 23 after 9."""
     dev = device()
     m = W.Model(d=1024, hq=8, hkv=2, hd=128, dff=2048, n_layers=2, layer_types=[W.SWA, W.FULL], window=64,
                 model_id=61)
+    if fmt == "card":
+        W.card_format(m)
+    elif fmt == "g64":
+        m.group = 64
     m.vocab = 1000
     wl = W.Workload("tiny-split-k", m, seed=0, n_cached=n_cached, t_max=96, use_tokens=True, final_head=True)
-    announce(f"prefill 2-layer d=1024 stack, {n_tokens} tokens after {n_cached} cached (split-K GEMMs)")
+    announce(f"prefill 2-layer d=1024 stack ({fmt}), {n_tokens} tokens after {n_cached} cached (split-K GEMMs)")
     _prefill_vs_oracle(wl, n_tokens, dev)
 
 
@@ -300,3 +308,39 @@ def test_prefill_bad_token_sets_status():
     ops.atlas_prefill(dm, d_toks, 0, None, am, ws)
     torch.cuda.synchronize()
     assert ops.atlas_device_status(ws) == 1
+
+
+@pytest.mark.parametrize("rows", [(4800, 37), (26, 25), (4999, 1000, 999)])
+def test_argmax_ties_take_the_lowest_index(rows):
+    """Equal rows of the lm_head give bit-identical logits (same bits, same arithmetic).
+    Copies of twice the winning row are planted at rows far apart (handled by
+    different head blocks), at neighbouring rows (different waves of one block) and at
+    three rows; every copy then ties for the maximum, and the argmax must be the
+    lowest planted index (lowest index wins on ties)."""
+    dev = device()
+    wl = _tiny_stack(n_layers=1, vocab=5000)
+    announce(f"argmax ties at rows {rows}")
+    dm = build_model(wl, dev)
+    d_tok = torch.tensor([R.decode_token(wl)], dtype=torch.int32, device=dev)
+    pos = torch.tensor([wl.n_cached], dtype=torch.int32, device=dev)
+    logits = torch.empty(wl.model.vocab, dtype=torch.float32, device=dev)
+    am = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = _ws(dm, dev)
+    base_pos = pos.clone()
+    ops.atlas_decode_step(dm, pos, d_token=d_tok, logits=logits, argmax=am, ws=ws)
+    torch.cuda.synchronize()
+    win = int(am.item())
+    assert float(logits[win].item()) > 0.0
+    row2 = (dm.lm_head[win].view(torch.bfloat16).float() * 2.0).to(torch.bfloat16).view(torch.int16)
+    assert torch.equal(row2.view(torch.bfloat16).float(), dm.lm_head[win].view(torch.bfloat16).float() * 2.0)
+    for r in rows:
+        dm.lm_head[r].copy_(row2)
+    pos.copy_(base_pos)
+    ops.atlas_decode_step(dm, pos, d_token=d_tok, logits=logits, argmax=am, ws=ws)
+    torch.cuda.synchronize()
+    assert ops.atlas_device_status(ws) == 0
+    lg = logits.cpu()
+    vals = [lg[r].item() for r in rows]
+    assert all(v == vals[0] for v in vals), vals
+    assert vals[0] == lg.max().item()
+    assert int(am.item()) == min(rows)

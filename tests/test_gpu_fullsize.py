@@ -72,12 +72,15 @@ def test_decode_64_layers_bf16_ring_layer_by_layer(cfg):
     goes the other way on one side (both sides round their own f32 value, which
     agree to about 1e-6) moves that element by a whole bf16 unit; later layers
     amplify it. The oracle shows the same against itself: nudging its layer-0 input
-    by 1e-7 makes it differ from itself by 1.5e-4 after 32 of these layers, while the
-    f32 cache stays at 5e-7. End to end the two sides therefore differ by about the
-    tolerance at 64 layers (printed, not asserted). Each layer is checked on its own
-    instead, at full size and in the step's launch configuration: GPU layer l gets
-    the oracle's input to layer l, and its output is compared with the oracle's; the
-    head gets the oracle's last hidden state."""
+    by 1e-7 (relative, random signs) makes it differ from itself by 1.5e-4 after 32 of
+    these layers and by 1.03e-3 after all 64 (logits 9.1e-4, configuration 7), while
+    the f32 cache stays at 5e-7. So the 1e-3 bar tests the kernels layer by layer, at
+    full size and in the step's launch configuration: GPU layer l gets the oracle's
+    input to layer l, and its output is compared with the oracle's; the head gets the
+    oracle's last hidden state. End to end on fresh caches, the last hidden state is
+    held to 1e-2, ten times the oracle's own spread under that nudge, and the argmax
+    must match whenever the oracle's top-1/top-2 margin exceeds twice the largest
+    logit error (otherwise several tokens are within rounding of the maximum)."""
     import dataclasses
     dev = device()
     wl = W.config(cfg)
@@ -113,10 +116,20 @@ def test_decode_64_layers_bf16_ring_layer_by_layer(cfg):
     dm = build_model(wl, dev)
     ops.atlas_decode_step(dm, pos, d_token=d_tok, hidden_out=out, logits=logits, argmax=am, ws=ws)
     torch.cuda.synchronize()
+    assert ops.atlas_device_status(ws) == 0
     top2 = np.sort(ref["logits"])[-2:]
-    print(f"end to end: hidden normwise {normwise(out.cpu().numpy(), ref['y']):.2e}, logits "
-          f"{normwise(logits.cpu().numpy(), ref['logits']):.2e}, argmax {int(am.item())} vs {ref['argmax']} "
-          f"(oracle top1-top2 margin {top2[1] - top2[0]:.3e})")
+    margin = float(top2[1] - top2[0])
+    lg = logits.cpu().numpy()
+    max_err = float(np.max(np.abs(lg.astype(np.float64) - ref["logits"])))
+    err_y = normwise(out.cpu().numpy(), ref["y"])
+    print(f"end to end: hidden normwise {err_y:.2e}, logits {normwise(lg, ref['logits']):.2e}, "
+          f"argmax {int(am.item())} vs {ref['argmax']} (oracle top1-top2 margin {margin:.3e}, "
+          f"max |logit err| {max_err:.3e})")
+    assert err_y < 1e-2
+    if margin > 2.0 * max_err:
+        assert int(am.item()) == ref["argmax"]
+    else:
+        print("argmax not compared: the margin is within twice the logit error")
 
 
 def test_prefill_1200_matches_teacher_forced_decode(olmo3_model):
@@ -156,3 +169,47 @@ def test_prefill_1200_matches_teacher_forced_decode(olmo3_model):
         kp, vp = kv_p[l]
         assert normwise(kp.numpy(), dm.layers[l].k_cache[:, :n].cpu().numpy()) < TOL, l
         assert normwise(vp.numpy(), dm.layers[l].v_cache[:, :n].cpu().numpy()) < TOL, l
+
+
+def test_prefill_full_width_4_layers_matches_oracle():
+    """Prefill at full width against the oracle itself: 4 full-size layers
+    [SWA, SWA, SWA, full] of the 32B shape, a 20-token prompt after 3 cached positions.
+    At this width the GEMMs take their production paths: the int8 kernel for every
+    projection, the two-way K split of qkv, o and down (down's K = 27,648), and
+    gate+up's N = 55,296 with the SwiGLU epilogue; the prompt spans two 16-row
+    attention tiles. Every KV slot written and the last row's logits are compared at
+    the 1e-3 bar, with identical argmax."""
+    dev = device()
+    m = W.olmo3_32b(model_id=3, n_layers=4)
+    wl = W.Workload("olmo3-32b-4-layer-prefill", m, seed=0, n_cached=3, t_max=32, use_tokens=True,
+                    final_head=True)
+    n = 20
+    announce(f"prefill of {n} tokens after 3 cached through 4 full-size layers + lm_head vs oracle")
+    toks = W.prompt_tokens(m, wl.seed, n, stream=1)
+    dm = build_model(wl, dev)
+    d_toks = torch.from_numpy(toks).to(dev)
+    logits = torch.empty(m.vocab, dtype=torch.float32, device=dev)
+    am = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(ops.atlas_prefill_workspace_bytes(dm, n), dtype=torch.uint8, device=dev)
+    ops.atlas_prefill(dm, d_toks, wl.n_cached, logits, am, ws)
+    torch.cuda.synchronize()
+    assert ops.atlas_device_status(ws) == 0
+    kv = [(L.k_cache.cpu().numpy(), L.v_cache.cpu().numpy()) for L in dm.layers]
+    lg = logits.cpu().numpy()
+    del dm, ws
+    torch.cuda.empty_cache()
+    ref = R.run_prefill(wl, toks)
+    p0, p1 = wl.n_cached, wl.n_cached + n
+    errs = []
+    for l in range(m.n_layers):
+        gk, gv = kv[l]
+        errs.append(max(normwise(gk[:, p0:p1], ref["K"][l][:, p0:p1]), normwise(gv[:, p0:p1], ref["V"][l][:, p0:p1])))
+        np.testing.assert_array_equal(gk[:, :p0], ref["K"][l][:, :p0])
+        assert not np.any(gk[:, p1:])
+    err_l = normwise(lg, ref["logits"])
+    top2 = np.sort(ref["logits"])[-2:]
+    print(f"KV normwise per layer {['%.2e' % e for e in errs]}, logits {err_l:.2e}, "
+          f"oracle top1-top2 margin {top2[1] - top2[0]:.3e}")
+    assert max(errs) < TOL
+    assert err_l < TOL
+    assert int(am.item()) == ref["argmax"]

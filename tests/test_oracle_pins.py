@@ -466,6 +466,43 @@ def test_qk_norm_is_over_the_full_projection():
     np.testing.assert_array_equal(Vc[:, 0, :].reshape(-1), tr["v"])
 
 
+def test_qk_norm_comes_before_the_rotation():
+    """Norm first, then RoPE: with gains that differ between the two members of each
+    rotation pair (i, i + 64), the q and k the layer feeds to attention at position p
+    are a pure per-pair rotation of those at position 0, so every pair keeps its
+    length. Rotating first and normalising afterwards would scale the rotated pair by
+    unequal gains and change the lengths; the test computes that order too and checks
+    that the invariant catches it."""
+    wl = W.config(0)
+    m = wl.model
+    T = W.layer_tensors(m, 0, 0)
+    half = np.concatenate([np.ones(64), 3.0 * np.ones(64)]).astype(np.float32)
+    T["g_q"] = np.tile(half, m.hq)
+    T["g_k"] = np.tile(half, m.hkv)
+    x = W.x_in(m, 0)
+    outs = {}
+    for p in (0, 37):
+        Kc, Vc = W.kv_cache(m, 0, 0, 40, 64)
+        tr = {}
+        O.layer_step(m, 0, T, x, Kc, Vc, p, tr)
+        outs[p] = tr
+
+    def pair_len(v, H):
+        v = v.astype(np.float64).reshape(H, 2, 64)
+        return np.sqrt(v[:, 0] ** 2 + v[:, 1] ** 2)
+
+    for key, H in (("q", m.hq), ("k", m.hkv)):
+        l0, lp = pair_len(outs[0][key], H), pair_len(outs[37][key], H)
+        assert np.max(np.abs(lp - l0) / l0) < 1e-5
+        assert np.max(np.abs(outs[37][key] - outs[0][key])) > 1e-2   # position 37 does rotate
+    # the other order on the same projection: rotate, then normalise
+    q_raw = outs[37]["qkv"][:m.hq * m.hd]
+    inv, msc = O.rope_params(m, 0)
+    swapped = O.rmsnorm(O.rope(q_raw, m.hq, m.hd, 37, inv, msc), T["g_q"], m.eps)
+    ls = pair_len(swapped, m.hq)
+    assert np.max(np.abs(ls - pair_len(outs[0]["q"], m.hq)) / ls) > 1e-2
+
+
 def test_layer_types_use_yarn_only_on_full_layers():
     m = W.olmo3_32b(n_layers=8)
     assert m.layer_types == [0, 0, 0, 1, 0, 0, 0, 1]
