@@ -224,6 +224,27 @@ ATLAS_API int atlas_decode_step(const atlas_model* m, const int32_t* d_token, co
                       const int32_t* d_pos, float* d_hidden_out, float* d_logits, int32_t* d_argmax,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* ---- decode step without a workspace argument -------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation. The same step as
+ * atlas_decode_step (same arguments, results and shape limits), with its workspace
+ * taken from a scratch area of ATLAS_NOALLOC_SCRATCH_BYTES (4 MiB) that the library
+ * keeps in device memory, one per GPU, until the process ends. The call allocates
+ * nothing and every step writes the parts of the scratch area it reads, so a call
+ * does not depend on what an earlier call left there.
+ *  - A model whose atlas_decode_workspace_bytes() exceeds the scratch size returns
+ *    ATLAS_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (the 32B shape needs
+ *    about 1.4 MB at 16,385 slots and 2.1 MB at 65,536).
+ *  - d_status_out (device int32, may be NULL) receives the step's status word, the
+ *    value atlas_device_status() reads from a workspace, at the end of the step.
+ *  - All calls on one GPU share that GPU's scratch area: calls that overlap in time on
+ *    one GPU (from other streams or threads) race and must be serialised by the
+ *    caller. Calls on different GPUs are independent. */
+#define ATLAS_NOALLOC_SCRATCH_BYTES (4u << 20)
+ATLAS_API int atlas_decode_step_noalloc(const atlas_model* m, const int32_t* d_token, const float* d_hidden_in,
+                              const int32_t* d_pos, float* d_hidden_out, float* d_logits, int32_t* d_argmax,
+                              int32_t* d_status_out, void* stream);
+
 /* Device status word of the last step that used this workspace (ATLAS_OK, or
  * ATLAS_ERR_INVALID_ARG when a position was out of range). Synchronises stream. */
 ATLAS_API int atlas_device_status(const void* ws, void* stream, int32_t* status_out);

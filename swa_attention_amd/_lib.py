@@ -68,6 +68,8 @@ _SIGS = {
     "atlas_decode_step": (ctypes.c_int, [P(atlas_model), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_void_p, c_void_p, c_size_t, c_void_p]),
     "atlas_device_status": (ctypes.c_int, [c_void_p, c_void_p, P(c_int32)]),
+    "atlas_decode_step_noalloc": (ctypes.c_int, [P(atlas_model), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                 c_void_p, c_void_p, c_void_p]),
     "atlas_prefill_workspace_bytes": (c_size_t, [P(atlas_model), c_int32]),
     "atlas_prefill": (ctypes.c_int, [P(atlas_model), c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                      c_size_t, c_void_p]),

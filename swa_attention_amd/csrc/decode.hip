@@ -263,9 +263,10 @@ extern "C" size_t atlas_decode_workspace_bytes(const atlas_model* m) {
     return decode_ws_bytes(m);
 }
 
-extern "C" int atlas_decode_step(const atlas_model* m, const int32_t* d_token, const float* d_hidden_in,
-                                 const int32_t* d_pos, float* d_hidden_out, float* d_logits, int32_t* d_argmax,
-                                 void* ws, size_t ws_bytes, void* stream) {
+namespace atlas {
+
+int check_decode_args(const atlas_model* m, const int32_t* d_token, const float* d_hidden_in, const int32_t* d_pos,
+                      const float* d_logits, const int32_t* d_argmax) {
     int rc = validate_model(m);
     if (rc) return rc;
     ATLAS_CHECK_ARG(d_pos != nullptr, "null d_pos");
@@ -273,6 +274,16 @@ extern "C" int atlas_decode_step(const atlas_model* m, const int32_t* d_token, c
     ATLAS_CHECK_ARG(!d_token || m->embedding, "token input needs an embedding table");
     const bool head = d_logits || d_argmax;
     ATLAS_CHECK_ARG(!head || (m->lm_head && m->g_final && m->vocab >= 1), "lm_head/g_final/vocab missing");
+    return ATLAS_OK;
+}
+
+}  // namespace atlas
+
+extern "C" int atlas_decode_step(const atlas_model* m, const int32_t* d_token, const float* d_hidden_in,
+                                 const int32_t* d_pos, float* d_hidden_out, float* d_logits, int32_t* d_argmax,
+                                 void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_decode_args(m, d_token, d_hidden_in, d_pos, d_logits, d_argmax);
+    if (rc) return rc;
     ATLAS_CHECK_ARG(ws != nullptr, "null workspace");
     const size_t need = decode_ws_bytes(m);
     if (ws_bytes < need) return fail(ATLAS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu", ws_bytes, need);

@@ -237,6 +237,18 @@ def atlas_decode_step(m: Model, d_pos, d_token=None, hidden_in=None, hidden_out=
            L.stream_ptr(stream))
 
 
+def atlas_decode_step_noalloc(m: Model, d_pos, d_token=None, hidden_in=None, hidden_out=None, logits=None,
+                              argmax=None, status_out=None, stream=None, cm=None):
+    """One decode step on the library's fixed scratch area (no workspace argument)."""
+    for t, n, dt in ((d_pos, "d_pos", I32), (d_token, "d_token", I32), (hidden_in, "hidden_in", F32),
+                     (hidden_out, "hidden_out", F32), (logits, "logits", F32), (argmax, "argmax", I32),
+                     (status_out, "status_out", I32)):
+        _dev(t, dt, n)
+    cm = cm if cm is not None else m.c()
+    L.call("atlas_decode_step_noalloc", ctypes.byref(cm), L.ptr(d_token), L.ptr(hidden_in), L.ptr(d_pos),
+           L.ptr(hidden_out), L.ptr(logits), L.ptr(argmax), L.ptr(status_out), L.stream_ptr(stream))
+
+
 def atlas_decode_batch_workspace_bytes(m: Model, batch):
     return L.lib().atlas_decode_batch_workspace_bytes(ctypes.byref(m.c()), batch)
 

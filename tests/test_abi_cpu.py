@@ -148,6 +148,26 @@ def _fake_model(n_layers=2, **over):
     return mm, layers
 
 
+def test_decode_step_noalloc_validation(lib):
+    """The no-allocation decode step checks its arguments like atlas_decode_step and
+    rejects a model whose workspace exceeds its fixed scratch area before touching
+    the device."""
+    mm, keep = _fake_model()
+    step = lib.atlas_decode_step_noalloc
+    assert step(None, FAKE, None, FAKE, None, None, None, None, None) == L.ATLAS_ERR_INVALID_ARG
+    assert step(ctypes.byref(mm), None, None, FAKE, None, None, None, None, None) == L.ATLAS_ERR_INVALID_ARG
+    assert step(ctypes.byref(mm), FAKE, None, None, None, None, None, None, None) == L.ATLAS_ERR_INVALID_ARG
+    bad, keep2 = _fake_model(type=2)
+    assert step(ctypes.byref(bad), FAKE, None, FAKE, None, None, None, None, None) == L.ATLAS_ERR_INVALID_ARG
+    big, keep3 = _fake_model()
+    big.vocab = 2_000_000                                  # logits alone: 8 MB of workspace
+    need = lib.atlas_decode_workspace_bytes(ctypes.byref(big))
+    assert need > 4 << 20
+    assert step(ctypes.byref(big), FAKE, None, FAKE, None, FAKE, FAKE, None, None) == L.ATLAS_ERR_WORKSPACE_TOO_SMALL
+    assert b"scratch" in lib.atlas_last_error()
+    assert lib.atlas_decode_workspace_bytes(ctypes.byref(mm)) <= 4 << 20
+
+
 def test_decode_step_validation(lib):
     mm, keep = _fake_model()
     need = lib.atlas_decode_workspace_bytes(ctypes.byref(mm))
