@@ -206,6 +206,7 @@ int run_decode_layers(const atlas_model* m, const XSource& first, const int32_t*
         ga.d = m->d;
         ga.group = L.gate.group;
         ga.h_out = w.h;
+        ga.old_frac = GEMV_OLD_FRAC;
         ga.z = w.z;
         if ((rc = launch_gate_up(ga, p.gu, st))) return rc;
         // 6. down projection (split-K partials)
@@ -214,6 +215,7 @@ int run_decode_layers(const atlas_model* m, const XSource& first, const int32_t*
         da.z = w.z;
         da.group = L.down.group;
         da.m_part = w.m_part;
+        da.old_frac = GEMV_OLD_FRAC;
         if ((rc = launch_down(da, p.down, st))) return rc;
     }
     XSource lo{};

@@ -8,6 +8,11 @@ constexpr int GEMV_THREADS = 512;   // 8 waves per GEMV block
 constexpr int ATTN_THREADS = 256;   // 4 waves = 16 key streams per attention block
 constexpr int ATTN_PART_F = 130;    // m, l, acc[128] per (query head, split)
 constexpr int ATTN_SSQ_MAX_BLOCKS = 512;   // qkv blocks whose sums of squares attention reads
+// Share of a GEMV block's row tiles given to its older waves (the first of the two
+// waves of each SIMD). Measured on the gate/up projection (2 x 27,648 x 5,120): an even
+// split leaves the younger waves streaming alone for ~5.5 us at the end; 0.63 is the
+// shortest.
+constexpr float GEMV_OLD_FRAC = 0.63f;
 
 // How a QKV block obtains the layer input x.
 enum XMode { X_FROM_EMBED = 0, X_FROM_HIDDEN = 1, X_FROM_RESIDUAL = 2 };
@@ -84,6 +89,7 @@ struct GateUpArgs {
     const float *a, *x, *g;     // h = x + g * a / rms(a)
     float eps;
     int d, group, CW, tiles_per_block;
+    float old_frac;             // share of a block's tiles streamed by its older waves
     float* h_out;               // block 0
     float* z;                   // [dff]
 };
@@ -92,6 +98,7 @@ struct DownArgs {
     W4View W;
     const float* z;             // f32 [K]
     int group, CW, tiles_per_block;
+    float old_frac;             // share of a block's tiles streamed by its older waves
     float* m_part;              // [S][N]
 };
 

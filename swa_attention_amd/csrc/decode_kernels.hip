@@ -320,6 +320,26 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_planes_kernel(GemvPlanesArg
     stream_rows<CPL, RB, gemv_stages<CPL>()>(a.W, m, P, R, t, nt, NW, a.y + (size_t)kr * a.W.N, lane);
 }
 
+// ---- older / younger wave split ----------------------------------------------------------
+// Tiles of a block split between its older and younger waves. On each SIMD the wave
+// dispatched first (waves 0 .. NW/2 - 1 of a 512-thread block) is served first by the
+// memory system and streams faster while both run; with equal shares the younger waves
+// finish several microseconds later, streaming alone at a fraction of the bandwidth.
+// The older waves take the fraction `old_frac` of the block's tiles, strided over
+// NW/2 waves, the younger ones the rest.
+struct WaveRange {
+    int t, nt, stride;
+};
+__device__ __forceinline__ WaveRange wave_range(int t_begin, int t_end, int wave, int NW, float old_frac) {
+    WaveRange r;
+    const int HW = NW / 2, nb = max(t_end - t_begin, 0);
+    const int n_old = min(nb, (int)(nb * old_frac + 0.5f));
+    r.stride = HW;
+    r.t = wave < HW ? t_begin + wave : t_begin + n_old + (wave - HW);
+    r.nt = wave_tiles(r.t, wave < HW ? t_begin + n_old : t_end, HW);
+    return r;
+}
+
 // ---- gate/up projections + SwiGLU ---------------------------------------------------------
 
 template <int CPL, int RB>
@@ -343,7 +363,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void gate_up_kernel(GateUpArgs a) {
     m.init(lane, 0, a.CW, a.group);
     const int T = (a.Wg.N + RB - 1) / RB;
     const int t_begin = blockIdx.x * a.tiles_per_block, t_end = min(T, t_begin + a.tiles_per_block);
-    const int t = t_begin + wave, nt = wave_tiles(t, t_end, NW);
+    const WaveRange wr = wave_range(t_begin, t_end, wave, NW, a.old_frac);
+    const int t = wr.t, nt = wr.nt, TS = wr.stride;
     // h = x + g * a / rms(a): inputs loaded first, then the weight prefetch
     const int n4 = a.d >> 2, bd = blockDim.x;
     float4 va[GEMV_NV4], vx[GEMV_NV4], vg[GEMV_NV4];
@@ -361,8 +382,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void gate_up_kernel(GateUpArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     TileRegs<CPL> RG[GU_STAGES], RU[GU_STAGES];
-    prefetch_tiles<CPL, RB, GU_STAGES>(RG, a.Wg, m, t, nt, NW);
-    prefetch_tiles<CPL, RB, GU_STAGES>(RU, a.Wu, m, t, nt, NW);
+    prefetch_tiles<CPL, RB, GU_STAGES>(RG, a.Wg, m, t, nt, TS);
+    prefetch_tiles<CPL, RB, GU_STAGES>(RU, a.Wu, m, t, nt, TS);
     {
         float ss = 0.f;
 #pragma unroll
@@ -399,14 +420,14 @@ __global__ __launch_bounds__(GEMV_THREADS) void gate_up_kernel(GateUpArgs a) {
     for (; i + GU_STAGES <= nt; i += GU_STAGES) {
 #pragma unroll
         for (int k = 0; k < GU_STAGES; k++) {
-            const int rl = (t + min(i + k + GU_STAGES - 1, nt - 1) * NW) * RB;
+            const int rl = (t + min(i + k + GU_STAGES - 1, nt - 1) * TS) * RB;
             load_tile(RG[(k + GU_STAGES - 1) % GU_STAGES], a.Wg, m, rl);
             load_tile(RU[(k + GU_STAGES - 1) % GU_STAGES], a.Wu, m, rl);
             __builtin_amdgcn_sched_barrier(0);
             float ag[RB], au[RB];
             tile_dot(RG[k], P, m, a.Wg, ag);
             tile_dot(RU[k], P, m, a.Wu, au);
-            swiglu_rows<CPL, RB>(ag, au, (t + (i + k) * NW) * RB, a.Wg.N, a.z, lane);
+            swiglu_rows<CPL, RB>(ag, au, (t + (i + k) * TS) * RB, a.Wg.N, a.z, lane);
         }
     }
 #pragma unroll
@@ -415,7 +436,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gate_up_kernel(GateUpArgs a) {
             float ag[RB], au[RB];
             tile_dot(RG[k], P, m, a.Wg, ag);
             tile_dot(RU[k], P, m, a.Wu, au);
-            swiglu_rows<CPL, RB>(ag, au, (t + (i + k) * NW) * RB, a.Wg.N, a.z, lane);
+            swiglu_rows<CPL, RB>(ag, au, (t + (i + k) * TS) * RB, a.Wg.N, a.z, lane);
         }
     }
 }
@@ -436,7 +457,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void down_kernel(DownArgs a) {
     m.init(lane, C0, a.CW, a.group);
     const int T = (a.W.N + RB - 1) / RB;
     const int t_begin = blockIdx.x * a.tiles_per_block, t_end = min(T, t_begin + a.tiles_per_block);
-    const int t = t_begin + wave, nt = wave_tiles(t, t_end, NW);
+    const WaveRange wr = wave_range(t_begin, t_end, wave, NW, a.old_frac);
+    const int t = wr.t, nt = wr.nt;
     // this block's range of z, loaded before the weight prefetch and encoded into LDS
     const int nwords = a.CW * 4;
     float4 u[DOWN_MAX_ROUNDS], v[DOWN_MAX_ROUNDS];
@@ -451,7 +473,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void down_kernel(DownArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     TileRegs<CPL> R[gemv_stages<CPL>()];
-    prefetch_tiles<CPL, RB, gemv_stages<CPL>()>(R, a.W, m, t, nt, NW);
+    prefetch_tiles<CPL, RB, gemv_stages<CPL>()>(R, a.W, m, t, nt, wr.stride);
     {
         XQ o;
         o.planes = L.s_pl;
@@ -469,7 +491,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void down_kernel(DownArgs a) {
     __syncthreads();
     LanePlanes<CPL> P;
     P.load(m, L.s_pl, L.s_qs, L.s_is, C0);
-    stream_rows<CPL, RB, gemv_stages<CPL>()>(a.W, m, P, R, t, nt, NW, a.m_part + (size_t)kr * a.W.N, lane);
+    stream_rows<CPL, RB, gemv_stages<CPL>()>(a.W, m, P, R, t, nt, wr.stride, a.m_part + (size_t)kr * a.W.N, lane);
 }
 
 // ---- attention ---------------------------------------------------------------------------------
