@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode64_16k_hbm_traffic.md")
+KERNEL_TRACE_PROFILE = os.path.join(ROOT, "profiles", "decode64_16k_kernel_stats.md")
 KERNEL_SOURCES = ["swa_attention_amd/csrc/gemv_core.h", "swa_attention_amd/csrc/decode_kernels.hip",
                   "swa_attention_amd/csrc/decode_kernels.h", "swa_attention_amd/csrc/common.h"]
 
@@ -50,6 +51,22 @@ def measured_traffic():
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return rec["bytes_per_launch"] if h.hexdigest()[:16] == rec["source_sha256_16"] else None
+
+
+def profiled_replay_us():
+    """Average gate/up launch duration over the timed graph replays of the committed
+    rocprofv3 kernel trace, or None when the kernel sources have changed since."""
+    import hashlib
+    try:
+        line = [l for l in open(KERNEL_TRACE_PROFILE) if l.startswith("roofline-json: ")][0]
+    except (OSError, IndexError):
+        return None
+    rec = json.loads(line[len("roofline-json: "):])
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return rec["graph_replay_avg_us"] if h.hexdigest()[:16] == rec["source_sha256_16"] else None
 
 
 def host_info():
@@ -133,6 +150,122 @@ def cpu_baseline(wl, budget_s, config):
     return out
 
 
+def oracle_layer_configs(configs=(0, 1, 2), runs=3):
+    """Median seconds of one oracle layer step for the single-layer workloads (config 0:
+    the tiny layer; 1: a full-size SWA layer at 4,096 keys; 2: a full-size full-attention
+    layer at 16,385 keys with YaRN), inputs generated outside the timed region."""
+    import statistics
+    import oracle as O
+    from oracle import runner as R
+    from synth import workloads as W
+    from swa_attention_amd import accounting as A
+    out = {}
+    for c in configs:
+        wl = W.config(c)
+        m = wl.model
+        T, Kc, Vc = R.layer_inputs(wl, 0)
+        x = W.x_in(m, wl.seed)
+        ts = []
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            O.layer_step(m, m.layer_types[0], T, x, Kc, Vc, wl.n_cached)
+            ts.append(time.perf_counter() - t0)
+        med = statistics.median(ts)
+        b = A.decode_step_bytes(m, wl.n_cached, head=False).total
+        out[str(c)] = {"workload": wl.name, "us_per_step": round(med * 1e6, 1), "runs": runs,
+                       "GBps": round(b / med / 1e9, 3), "bytes_per_step": b}
+        del T, Kc, Vc
+    return out
+
+
+def oracle_prefill_baseline(budget_tokens=16):
+    """The oracle's prefill (its definition: teacher-forced decode) on the 4-layer
+    [SWA, SWA, SWA, full] truncation of the 1,200-token workload, for the first
+    budget_tokens tokens; extrapolated linearly over tokens (the weight GEMVs, not the
+    attention over <= 1,200 keys, dominate each position) and x16 over layers."""
+    import oracle as O
+    from oracle import runner as R
+    from synth import workloads as W
+    pw = W.config(4)
+    m = pw.model
+    toks = W.prompt_tokens(m, pw.seed, budget_tokens)
+    Ts = [W.layer_tensors(m, pw.seed, l) for l in range(4)]
+    caches = [W.kv_cache(m, pw.seed, l, 0, budget_tokens) for l in range(4)]
+    rows = {int(t): W.embedding_rows(m, pw.seed, int(t), 1)[0] for t in toks}
+    t_sum = 0.0
+    for t, tok in enumerate(toks):
+        x = O.embed(rows[int(tok)])
+        t0 = time.perf_counter()
+        for l in range(4):
+            x = O.layer_step(m, m.layer_types[l], Ts[l], x, caches[l][0], caches[l][1], t)
+        t_sum += time.perf_counter() - t0
+    ttft_s = t_sum * (pw.prompt_len / budget_tokens) * (m.n_layers / 4)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    threads = min(threads, len(os.sched_getaffinity(0)))
+    return {"value": round(pw.prompt_len / ttft_s, 3), "unit": "prompt tokens/s", "ttft_s": round(ttft_s, 1),
+            "cores": threads, "kind": "oracle",
+            "sample": f"4-layer [SWA,SWA,SWA,full] truncation, first {budget_tokens} of {pw.prompt_len} tokens "
+                      f"timed {t_sum:.1f} s; extrapolated x{pw.prompt_len / budget_tokens:g} over tokens and "
+                      f"x{m.n_layers // 4} over layers (lm_head not included)"}
+
+
+def measure_layer_configs(dev, steps=30, copies=3):
+    """Decode step of one full-size layer (config 1: SWA at 4,096 keys; config 2: full
+    attention at 16,385 keys with YaRN), timed over `copies` independent device copies
+    of the layer's weights and KV cache taken in turn, so that a step never finds its
+    layer in the ~256 MB memory-side cache left by the previous step. HIP graph of one
+    step per copy, replayed."""
+    import torch
+    from synth import workloads as W
+    from synth.device import build_model
+    from swa_attention_amd import accounting as A
+    from swa_attention_amd import ops
+    out = {}
+    for c in (1, 2):
+        wl = W.config(c)
+        m = wl.model
+        dms = [build_model(wl, dev) for _ in range(copies)]   # same seeded values at distinct addresses
+        cms = [d.c() for d in dms]
+        x = torch.from_numpy(W.x_in(m, wl.seed)).to(dev)
+        pos = torch.tensor([wl.n_cached], dtype=torch.int32, device=dev)
+        ws = torch.empty(ops.atlas_decode_workspace_bytes(dms[0]), dtype=torch.uint8, device=dev)
+
+        def one_round():
+            for d, cm in zip(dms, cms):
+                ops.atlas_decode_step(d, pos, hidden_in=x, ws=ws, cm=cm)
+
+        one_round()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            one_round()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            one_round()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        assert ops.atlas_device_status(ws) == 0
+        us = e0.elapsed_time(e1) * 1e3 / (steps * copies)
+        b = A.decode_step_bytes(m, wl.n_cached, head=False).total
+        out[str(c)] = {"workload": wl.name, "us_per_step": round(us, 2), "GBps": round(b / (us * 1e-6) / 1e9, 1),
+                       "frac_of_peak": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4), "bytes_per_step": b,
+                       "method": f"{copies} device copies of the layer ({copies} x {b / 1e6:.1f} MB) taken in turn, "
+                                 f"HIP graph replays ({steps} x {copies} steps)"}
+        log(f"layer config {c}: {us:.1f} us per step, {out[str(c)]['GBps']} GB/s")
+        del dms, cms, ws, g
+        torch.cuda.empty_cache()
+    return out
+
+
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_INT8_TOPS = 5000.0
 
@@ -174,6 +307,7 @@ def measure_prefill(args, dm, cm, m, dev, wl_name):
                                                   sorted(prof.items(), key=lambda kv: -kv[1][1])))
     flops = A.prefill_flops(m, n)
     out = {"workload": name, "tokens": n, "ttft_ms": round(ms, 2), "reps": args.prefill_reps,
+           "tokens_per_s": round(n / (ms * 1e-3), 1),
            "algorithmic_tflop": round(flops / 1e12, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
            "mfma_frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     dom = "pf_gemm_gate_up"
@@ -208,6 +342,12 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the 1,200-token prefill measurement")
     ap.add_argument("--prefill-reps", type=int, default=3)
     ap.add_argument("--eager", action="store_true", help="time eager steps instead of HIP graph replays")
+    ap.add_argument("--no-sampling", action="store_true", help="skip the on-device sampling measurement")
+    ap.add_argument("--no-layer-configs", action="store_true",
+                    help="skip the single-layer workloads (full-size SWA and full-attention layers)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode step: no sampling, read probe, layer configs, prefill or CPU legs "
+                         "(for profiler runs)")
     ap.add_argument("--stream-probe-gib", type=float, default=2.0,
                     help="buffer size of the plain read-bandwidth probe (0 to skip)")
     ap.add_argument("--oracle-block-seconds", type=int, default=None, help=argparse.SUPPRESS)
@@ -218,6 +358,9 @@ def main():
     if args.oracle_block_seconds is not None:   # the single-thread oracle leg (a child process)
         print(oracle_block_seconds(args.oracle_block_seconds, 1))
         return
+    if args.decode_only:
+        args.no_sampling = args.no_layer_configs = args.no_prefill = args.no_cpu_baseline = True
+        args.stream_probe_gib = 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
               "The step would shard by KV head (attention local, two small all-reduces per layer); "
@@ -326,10 +469,15 @@ def main():
                 "kernel": (f"gate_up_kernel (2 x {m.dff}x{m.d} W4 + SwiGLU)" if B == 1 else
                            f"gate projection over {B} rows ({m.dff}x{m.d} W4, split over K)"),
                 "bytes_per_launch": per_launch,
-                "avg_launch_us": round(avg_s * 1e6, 2), "launches": cnt}
+                "avg_launch_us": round(avg_s * 1e6, 2), "launches": cnt,
+                "duration_source": "dispatch-stamped HIP events on the launch stream, eager timing steps"}
+        rp = profiled_replay_us() if (args.config == 3 and B == 1) else None
+        if rp:   # the committed rocprofv3 trace of the same command, timed graph replays only
+            roof["rocprof_graph_replay_avg_us"] = rp
+            roof["rocprof_frac"] = round(per_launch / (rp * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
 
     sampling = None
-    if head and B == 1:   # the on-device sampler at the card's settings, on this step's logits
+    if head and B == 1 and not args.no_sampling:   # the on-device sampler at the card's settings
         wss = torch.empty(ops.atlas_sample_workspace_bytes(m.vocab), dtype=torch.uint8, device=dev)
         du = torch.tensor([0.5], dtype=torch.float32, device=dev)
         tok_s = torch.empty(1, dtype=torch.int32, device=dev)
@@ -377,6 +525,10 @@ def main():
     if not args.no_prefill and head and wl.use_tokens and B == 1:
         prefill = measure_prefill(args, dm, cm, m, dev, wl.name)
 
+    layer_cfgs = None
+    if not args.no_layer_configs and args.config == 3:
+        layer_cfgs = measure_layer_configs(dev)
+
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 18   # f32 elements
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -391,6 +543,12 @@ def main():
     if not args.no_cpu_baseline:
         log("CPU oracle baseline (bounded sample)")
         cpu = cpu_baseline(wl, args.cpu_budget, args.config)
+        if args.config == 3:
+            log("CPU oracle: single-layer configurations (median of 3)")
+            cpu["layer_configs"] = oracle_layer_configs()
+            if prefill is not None:
+                log("CPU oracle: prefill on the 4-layer truncation (bounded sample)")
+                prefill["cpu_baseline"] = oracle_prefill_baseline()
 
     out = {
         "metric": ("decode tokens/s at batch 1, 32B W4, 16K ctx + achieved HBM GB/s vs peak" if B == 1 else
@@ -422,6 +580,7 @@ def main():
         "achievable_read": stream,
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "layer_configs": layer_cfgs,
         "sampling": sampling,
     }
     print(json.dumps(out), flush=True)

@@ -9,37 +9,92 @@
 // the token is the first nucleus member, in ascending index order, whose cumulative
 // mass exceeds u times the nucleus mass. T = 0 is greedy (lowest index on ties).
 //
-// No sort. Masses are summed as 64-bit integers (e_i in units of 2^-32, truncated), so
-// every sum is exact and independent of order: the result is deterministic and a
-// replayed graph draws the same token. tau is found by a radix select over the bit
-// pattern of e (positive floats order like their patterns), one byte per pass:
-//   1. sample_max_kernel   (256 blocks): per-block max and its lowest index;
-//   2. sample_exp_kernel   (256 blocks): e_i = exp((l_i - max) / T) to the workspace
-//      and a per-block histogram of the top byte of e_i weighted by its mass;
-//   3. sample_select_kernel (one block): the top byte from the histograms, the other
-//      three bytes by passes over e restricted to the prefix chosen so far, then the
-//      draw: per-thread chunk masses, a block scan, and one scan inside the chunk
-//      that holds the target.
+// No sort of the vocabulary. Masses are summed as 64-bit integers (e_i in units of
+// 2^-32, truncated), so every sum is exact and independent of order: the result is
+// deterministic and a replayed graph draws the same token. tau is the bit pattern of e
+// (positive floats order like their patterns) where the mass counted from the top
+// first reaches ceil(top_p * total). Each block of the first three kernels owns a
+// contiguous slice of the vocabulary:
+//   1. sample_max_kernel  (256 blocks): per-slice max and its lowest index; clears the
+//      histogram;
+//   2. sample_exp_kernel  (256 blocks): e_i to the workspace and its mass added to a
+//      histogram over the top 12 bits of e's pattern (sign, exponent and 3 mantissa
+//      bits): an LDS histogram per block, then one integer atomic per non-empty bin;
+//   3. sample_bin_kernel  (256 blocks): every block finds the 12-bit bin that holds
+//      tau, sums the mass of its slice above that bin (certainly in the nucleus) and
+//      writes the (index, e) of its elements inside the bin, the candidates, to its own
+//      region in index order;
+//   4. sample_draw_kernel (one block): the low 20 bits of tau by radix passes of 8, 8
+//      and 4 bits over the candidates (staged in LDS); each slice's nucleus mass (its
+//      certain mass plus its candidates at or above tau); the slice holding the target
+//      u * mass from a scan of the 256 slice masses; the token from a scan inside it.
 #include <cmath>
 
 #include "common.h"
 
 namespace atlas {
 
-constexpr int SMP_BLOCKS = 256, SMP_THREADS = 256, SMP_SEL_THREADS = 1024;
+constexpr int SMP_BLOCKS = 256, SMP_THREADS = 256, SMP_DRAW_THREADS = 256;
+// e <= 1, so the top 12 bits of its pattern are at most 0x3F8: 1,024 bins hold them.
+constexpr int SMP_BINS = 1024, SMP_SHIFT = 20;
+// The histogram is kept in one copy per XCD (block b adds to copy b mod 8, the XCD it
+// runs on), so the atomics of different XCDs never contend for one address.
+constexpr int SMP_COPIES = 8;
+constexpr int SMP_CAND_LDS = 4096;         // candidates staged in LDS by the draw (more: from memory)
 constexpr double SMP_FIX = 4294967296.0;   // 2^32: mass units per unit of e (e <= 1)
 static_assert(SMP_THREADS == SMP_BLOCKS, "sample_exp_kernel reduces one block maximum per thread");
 
 __device__ __forceinline__ uint64_t smp_mass(float e) { return (uint64_t)((double)e * SMP_FIX); }
+__device__ __forceinline__ uint64_t smp_mass_bits(uint32_t b) { return smp_mass(__uint_as_float(b)); }
 
-// ---- 1. block maxima ----------------------------------------------------------------------
-__global__ __launch_bounds__(SMP_THREADS) void sample_max_kernel(const float* __restrict__ l, int V, float* bmax,
-                                                                 int* bidx) {
+// Contiguous slice of block b: [b * sl, min(V, (b + 1) * sl)).
+__host__ __device__ inline int smp_slice(int V) { return ((V + SMP_BLOCKS - 1) / SMP_BLOCKS + 3) & ~3; }
+
+struct SampleWs {
+    float* bmax;
+    int* bidx;
+    float* e;                  // [V]
+    uint64_t* hist;            // [SMP_COPIES][SMP_BINS] masses by the top 12 bits of e's pattern
+    uint64_t* certain;         // [SMP_BLOCKS] nucleus mass above tau's bin, per slice
+    uint32_t* ncand;           // [SMP_BLOCKS] candidates of each slice
+    uint2* cand;               // [SMP_BLOCKS][slice] (index, bits of e) of each slice's elements
+                               //   inside tau's bin, in index order
+    uint64_t* sel;             // [4]: bin, remaining target, total mass
+};
+
+// Block-wide exclusive scan of one 64-bit value per thread (blockDim.x a multiple of 64,
+// at most 1024), with the total: shuffle scans inside each wave, then the wave totals
+// through LDS. wsum: LDS [16]. Every thread of the block calls it.
+__device__ uint64_t block_excl_scan(uint64_t v, uint64_t* wsum, uint64_t* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    uint64_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    uint64_t off = 0, tot = 0;
+    for (int i = 0; i < nw; i++) {
+        const uint64_t sw = wsum[i];
+        off += i < w ? sw : 0ull;
+        tot += sw;
+    }
+    *total = tot;
+    __syncthreads();   // wsum is free for the next call
+    return off + x - v;
+}
+
+// ---- 1. slice maxima --------------------------------------------------------------------
+__global__ __launch_bounds__(SMP_THREADS) void sample_max_kernel(const float* __restrict__ l, int V, SampleWs w,
+                                                                 int clear) {
     __shared__ float sv[SMP_THREADS];
     __shared__ int si[SMP_THREADS];
+    const int sl = smp_slice(V), i0 = blockIdx.x * sl, i1 = min(V, i0 + sl);
     float best = -INFINITY;
     int bi = 0x7FFFFFFF;
-    for (int i = blockIdx.x * SMP_THREADS + threadIdx.x; i < V; i += SMP_BLOCKS * SMP_THREADS) {
+    for (int i = i0 + threadIdx.x; i < i1; i += SMP_THREADS) {
         const float v = l[i];
         if (v > best) {   // i increases, so the first index of a maximum is kept
             best = v;
@@ -48,6 +103,10 @@ __global__ __launch_bounds__(SMP_THREADS) void sample_max_kernel(const float* __
     }
     sv[threadIdx.x] = best;
     si[threadIdx.x] = bi;
+    if (clear) {   // the histogram starts at zero
+        for (int b = blockIdx.x * SMP_THREADS + threadIdx.x; b < SMP_COPIES * SMP_BINS; b += SMP_BLOCKS * SMP_THREADS)
+            w.hist[b] = 0;
+    }
     __syncthreads();
     for (int o = SMP_THREADS / 2; o > 0; o >>= 1) {
         if (threadIdx.x < o) {
@@ -61,171 +120,233 @@ __global__ __launch_bounds__(SMP_THREADS) void sample_max_kernel(const float* __
         __syncthreads();
     }
     if (threadIdx.x == 0) {
-        bmax[blockIdx.x] = sv[0];
-        bidx[blockIdx.x] = si[0];
+        w.bmax[blockIdx.x] = sv[0];
+        w.bidx[blockIdx.x] = si[0];
     }
 }
 
-// ---- 2. e and the top-byte histogram ------------------------------------------------------------
-__global__ __launch_bounds__(SMP_THREADS) void sample_exp_kernel(const float* __restrict__ l, int V,
-                                                                 const float* __restrict__ bmax, float invT,
-                                                                 float* __restrict__ e, uint64_t* __restrict__ hist) {
+// ---- 2. e and the histogram ------------------------------------------------------------------
+__global__ __launch_bounds__(SMP_THREADS) void sample_exp_kernel(const float* __restrict__ l, int V, float invT,
+                                                                 SampleWs w) {
     __shared__ float red[SMP_THREADS];
-    __shared__ unsigned long long h[256];
-    red[threadIdx.x] = bmax[threadIdx.x];   // SMP_THREADS == SMP_BLOCKS
-    h[threadIdx.x] = 0;
+    __shared__ unsigned long long hb[SMP_BINS];
+    red[threadIdx.x] = w.bmax[threadIdx.x];   // SMP_THREADS == SMP_BLOCKS
+    for (int b = threadIdx.x; b < SMP_BINS; b += SMP_THREADS) hb[b] = 0;
     __syncthreads();
     for (int o = SMP_THREADS / 2; o > 0; o >>= 1) {
         if (threadIdx.x < o) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + o]);
         __syncthreads();
     }
     const float M = red[0];
-    for (int i = blockIdx.x * SMP_THREADS + threadIdx.x; i < V; i += SMP_BLOCKS * SMP_THREADS) {
+    const int sl = smp_slice(V), i0 = blockIdx.x * sl, i1 = min(V, i0 + sl);
+    for (int i = i0 + threadIdx.x; i < i1; i += SMP_THREADS) {
         const float v = expf((l[i] - M) * invT);
         const float ev = fminf(v, 1.0f);   // the maximum gives exactly 1
-        e[i] = ev;
-        atomicAdd(&h[__float_as_uint(ev) >> 24], (unsigned long long)smp_mass(ev));
+        w.e[i] = ev;
+        const uint64_t ms = smp_mass(ev);
+        if (ms) atomicAdd(&hb[__float_as_uint(ev) >> SMP_SHIFT], (unsigned long long)ms);
     }
     __syncthreads();
-    hist[(size_t)blockIdx.x * 256 + threadIdx.x] = h[threadIdx.x];
+    uint64_t* dst = w.hist + (size_t)(blockIdx.x % SMP_COPIES) * SMP_BINS;
+    for (int b = threadIdx.x; b < SMP_BINS; b += SMP_THREADS)
+        if (hb[b]) atomicAdd((unsigned long long*)&dst[b], hb[b]);
 }
 
-// ---- 3. threshold and draw (one block) -----------------------------------------------------------
-
-// Chooses the bin (0..255) where the mass counted from the top bin down first reaches
-// *target, and lowers *target by the mass of the bins above it. h: LDS [256]; every
-// thread of the block calls it.
-__device__ void smp_pick(unsigned long long* h, unsigned long long* suf, uint64_t* target, int* bin) {
+// ---- 3. tau's bin, certain masses and the candidate list ---------------------------------------
+__global__ __launch_bounds__(SMP_THREADS) void sample_bin_kernel(int V, double top_p, SampleWs w) {
+    __shared__ uint64_t tmp[16];
+    __shared__ int s_bin;
+    __shared__ uint64_t s_rem;
     const int t = threadIdx.x;
-    if (t < 256) suf[t] = h[t];
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {   // suffix sums: suf[b] = sum of h[b..255]
-        unsigned long long add = 0;
-        if (t < 256 && t + o < 256) add = suf[t + o];
-        __syncthreads();
-        if (t < 256) suf[t] += add;
-        __syncthreads();
-    }
-    const uint64_t tg = *target;   // read by every thread before the one below lowers it
-    __syncthreads();
-    if (t < 256) {   // suf is non-increasing and suf[0] >= tg >= 1: exactly one bin matches
-        const uint64_t above = t < 255 ? suf[t + 1] : 0;
-        if (suf[t] >= tg && above < tg) {
-            *bin = t;
-            *target = tg - above;
+    // thread t holds the 4 bins [4 (255 - t), 4 (255 - t) + 4): thread 0 the highest
+    constexpr int BPT = SMP_BINS / SMP_THREADS;
+    const int b0 = (SMP_THREADS - 1 - t) * BPT;
+    uint64_t hv[BPT] = {};
+#pragma unroll
+    for (int c = 0; c < SMP_COPIES; c++)
+#pragma unroll
+        for (int k = 0; k < BPT; k++) hv[k] += w.hist[(size_t)c * SMP_BINS + b0 + k];
+    uint64_t own = 0;
+#pragma unroll
+    for (int k = 0; k < BPT; k++) own += hv[k];
+    uint64_t total;
+    const uint64_t above = block_excl_scan(own, tmp, &total);
+    uint64_t tg = (uint64_t)ceil(top_p * (double)total);   // total < 2^53: exact enough
+    tg = tg < 1 ? 1 : (tg > total ? total : tg);
+    if (above < tg && above + own >= tg) {   // exactly one thread (own > 0)
+        uint64_t c = above;
+        for (int k = BPT - 1; k >= 0; k--) {
+            if (c + hv[k] >= tg) {
+                s_bin = b0 + k;
+                s_rem = tg - c;
+                break;
+            }
+            c += hv[k];
         }
     }
     __syncthreads();
+    const uint32_t bin = (uint32_t)s_bin;
+    if (blockIdx.x == 0 && t == 0) {
+        w.sel[0] = bin;
+        w.sel[1] = s_rem;
+        w.sel[2] = total;
+    }
+    // this slice: mass above the bin, and its candidates in index order (thread t takes
+    // the consecutive elements [i0 + t * per, i0 + (t + 1) * per) of the slice)
+    const int sl = smp_slice(V), i0 = blockIdx.x * sl, i1 = min(V, i0 + sl);
+    const int per = (sl + SMP_THREADS - 1) / SMP_THREADS;
+    const int j0 = min(i1, i0 + t * per), j1 = min(i1, j0 + per);
+    uint64_t cm = 0, nmine = 0;
+    for (int i = j0; i < j1; i++) {
+        const uint32_t bits = __float_as_uint(w.e[i]);
+        const uint32_t hbin = bits >> SMP_SHIFT;
+        if (hbin > bin) cm += smp_mass_bits(bits);
+        nmine += hbin == bin;
+    }
+    uint64_t nblk, blk;
+    uint32_t pos = (uint32_t)block_excl_scan(nmine, tmp, &nblk);
+    uint2* dst = w.cand + (size_t)blockIdx.x * sl;
+    for (int i = j0; i < j1 && nmine; i++) {
+        const uint32_t bits = __float_as_uint(w.e[i]);
+        if ((bits >> SMP_SHIFT) == bin) dst[pos++] = make_uint2((uint32_t)i, bits);
+    }
+    block_excl_scan(cm, tmp, &blk);   // block sum
+    if (t == 0) {
+        w.certain[blockIdx.x] = blk;
+        w.ncand[blockIdx.x] = (uint32_t)nblk;
+    }
 }
 
-struct SampleArgs {
-    const float* e;
+// ---- 4. tau and the draw (one block) --------------------------------------------------------------
+
+struct DrawArgs {
+    SampleWs w;
     int V;
-    const uint64_t* hist;   // [SMP_BLOCKS][256]
-    const float* bmax;
-    const int* bidx;
     int greedy;
-    double top_p;
     const float* d_u;
     int32_t* out;
 };
 
-__global__ __launch_bounds__(SMP_SEL_THREADS) void sample_select_kernel(SampleArgs a) {
-    __shared__ unsigned long long h[256], suf[256];
-    __shared__ unsigned long long chunk[SMP_SEL_THREADS];
-    __shared__ uint64_t s_target;
-    __shared__ int s_bin;
+__global__ __launch_bounds__(SMP_DRAW_THREADS) void sample_draw_kernel(DrawArgs a) {
+    __shared__ unsigned long long h[256];
+    __shared__ unsigned long long s_nm[SMP_BLOCKS];
+    __shared__ uint32_t s_off[SMP_BLOCKS], s_cnt[SMP_BLOCKS];
+    __shared__ uint2 s_cand[SMP_CAND_LDS];
+    __shared__ uint64_t tmp[16];
+    __shared__ uint64_t s_target, s_lo;
+    __shared__ int s_bin, s_blk;
     const int t = threadIdx.x;
-    if (a.greedy) {   // first index of the maximum over the block partials
+    const SampleWs& w = a.w;
+    if (a.greedy) {   // first index of the maximum over the slice partials
         if (t == 0) {
-            float best = a.bmax[0];
-            int bi = a.bidx[0];
+            float best = w.bmax[0];
+            int bi = w.bidx[0];
             for (int b = 1; b < SMP_BLOCKS; b++)
-                if (a.bmax[b] > best || (a.bmax[b] == best && a.bidx[b] < bi)) {
-                    best = a.bmax[b];
-                    bi = a.bidx[b];
+                if (w.bmax[b] > best || (w.bmax[b] == best && w.bidx[b] < bi)) {
+                    best = w.bmax[b];
+                    bi = w.bidx[b];
                 }
             *a.out = bi;
         }
         return;
     }
-    // top byte: sum the block histograms
-    if (t < 256) {
-        unsigned long long s = 0;
-        for (int b = 0; b < SMP_BLOCKS; b++) s += a.hist[(size_t)b * 256 + t];
-        h[t] = s;
+    // candidate counts of the slices -> offsets of a dense candidate list. The first
+    // SMP_DRAW_THREADS / SMP_BLOCKS candidates of every slice are loaded with the counts
+    // (thread t: slice t mod 256, rank t / 256), before it is known which exist.
+    const int sl = smp_slice(a.V);
+    const int pb = t % SMP_BLOCKS, pk = t / SMP_BLOCKS;
+    const uint2 pre = w.cand[(size_t)pb * sl + min(pk, sl - 1)];
+    const uint32_t cnt = t < SMP_BLOCKS ? w.ncand[t] : 0u;
+    if (t < SMP_BLOCKS) s_nm[t] = w.certain[t];
+    if (t == 0) s_target = w.sel[1];
+    float u = *a.d_u;
+    uint64_t nc64;
+    const uint32_t off = (uint32_t)block_excl_scan(cnt, tmp, &nc64);
+    if (t < SMP_BLOCKS) {
+        s_off[t] = off;
+        s_cnt[t] = cnt;
     }
     __syncthreads();
-    if (t == 0) {
-        unsigned long long tot = 0;
-        for (int b = 0; b < 256; b++) tot += h[b];
-        // tot < 2^53 (V < 2^21 tokens of mass <= 2^32), so the product is exact enough
-        uint64_t tg = (uint64_t)ceil(a.top_p * (double)tot);
-        s_target = tg < 1 ? 1 : (tg > tot ? tot : tg);
+    const uint32_t nc = (uint32_t)nc64;
+    // candidate c lives in slice b with s_off[b] <= c < s_off[b + 1] (binary search)
+    auto cand_at = [&](uint32_t c) {
+        int lo = 0, hi = SMP_BLOCKS - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= c) lo = mid;
+            else hi = mid - 1;
+        }
+        return w.cand[(size_t)lo * sl + (c - s_off[lo])];
+    };
+    const bool staged = nc <= (uint32_t)SMP_CAND_LDS;
+    if (staged) {
+        constexpr uint32_t NPRE = SMP_DRAW_THREADS / SMP_BLOCKS;
+        const uint32_t cb = s_cnt[pb], ob = s_off[pb];
+        if ((uint32_t)pk < cb) s_cand[ob + pk] = pre;
+        for (uint32_t k = pk + NPRE; k < cb; k += NPRE)   // slices with more candidates than were prefetched
+            s_cand[ob + k] = w.cand[(size_t)pb * sl + k];
     }
     __syncthreads();
-    smp_pick(h, suf, &s_target, &s_bin);
-    uint32_t prefix = (uint32_t)s_bin;   // bits selected so far
-    // bytes 2..4 of the threshold pattern
-    for (int shift = 16; shift >= 0; shift -= 8) {
+    auto cand_get = [&](uint32_t c) { return staged ? s_cand[c] : cand_at(c); };
+    // low 20 bits of tau: radix passes over bits [19:12], [11:4] and [3:0] of the
+    // candidates matching the prefix chosen so far
+    uint32_t prefix = (uint32_t)w.sel[0];
+    for (int pass = 0; pass < 3; pass++) {
+        const int shift = pass == 0 ? 12 : pass == 1 ? 4 : 0, width = pass == 2 ? 4 : 8;
         if (t < 256) h[t] = 0;
         __syncthreads();
-        auto add = [&](float ev) {
-            const uint32_t b = __float_as_uint(ev);
-            if ((b >> (shift + 8)) == prefix) atomicAdd(&h[(b >> shift) & 255u], (unsigned long long)smp_mass(ev));
-        };
-        // 16-byte loads, several in flight per thread (e is 16-byte aligned)
-        const float4* e4 = reinterpret_cast<const float4*>(a.e);
-        const int V4 = a.V >> 2;
-#pragma unroll 4
-        for (int i = t; i < V4; i += SMP_SEL_THREADS) {
-            const float4 v = e4[i];
-            add(v.x);
-            add(v.y);
-            add(v.z);
-            add(v.w);
+        for (uint32_t c = t; c < nc; c += SMP_DRAW_THREADS) {
+            const uint32_t b = cand_get(c).y;
+            if ((b >> (shift + width)) == prefix)
+                atomicAdd(&h[(b >> shift) & ((1u << width) - 1u)], (unsigned long long)smp_mass_bits(b));
         }
-        for (int i = 4 * V4 + t; i < a.V; i += SMP_SEL_THREADS) add(a.e[i]);
         __syncthreads();
-        smp_pick(h, suf, &s_target, &s_bin);
-        prefix = (prefix << 8) | (uint32_t)s_bin;
+        // the bin (of 2^width, highest first) where the mass from the top reaches the
+        // remaining target; thread t holds bin 255 - t (bins past 2^width are empty)
+        const uint64_t own = t < 256 ? h[255 - t] : 0ull;
+        const uint64_t tg = s_target;
+        uint64_t tot;
+        const uint64_t above = block_excl_scan(own, tmp, &tot);
+        if (above < tg && above + own >= tg) {   // exactly one thread (own > 0)
+            s_bin = 255 - t;
+            s_target = tg - above;
+        }
+        __syncthreads();
+        prefix = (prefix << width) | (uint32_t)s_bin;
     }
     const uint32_t tau = prefix;
-    // draw: chunk masses of the nucleus in index order, block scan, then the chunk;
-    // chunks are whole 16-byte groups
-    const int C = 4 * ((a.V + 4 * SMP_SEL_THREADS - 1) / (4 * SMP_SEL_THREADS));
-    const int i0 = min(a.V, t * C), i1 = min(a.V, i0 + C);
-    unsigned long long m = 0;
-    {
-        auto nmass = [&](float ev) { return __float_as_uint(ev) >= tau ? smp_mass(ev) : 0ull; };
-        int i = i0;
-#pragma unroll 4
-        for (; i + 4 <= i1; i += 4) {
-            const float4 v = *reinterpret_cast<const float4*>(a.e + i);
-            m += nmass(v.x) + nmass(v.y) + nmass(v.z) + nmass(v.w);
-        }
-        for (; i < i1; i++) m += nmass(a.e[i]);
+    // nucleus mass of every slice: its certain mass plus its candidates at or above tau
+    for (uint32_t c = t; c < nc; c += SMP_DRAW_THREADS) {
+        const uint2 cv = cand_get(c);
+        if (cv.y >= tau) atomicAdd(&s_nm[cv.x / (uint32_t)sl], (unsigned long long)smp_mass_bits(cv.y));
     }
-    chunk[t] = m;
     __syncthreads();
-    for (int o = 1; o < SMP_SEL_THREADS; o <<= 1) {   // inclusive scan
-        const unsigned long long add = t >= o ? chunk[t - o] : 0ull;
-        __syncthreads();
-        chunk[t] += add;
-        __syncthreads();
-    }
-    const unsigned long long total = chunk[SMP_SEL_THREADS - 1];
-    float u = *a.d_u;
+    uint64_t total;
+    const uint64_t lo_b = block_excl_scan(t < SMP_BLOCKS ? s_nm[t] : 0ull, tmp, &total);
     u = u > 0.f ? u : 0.f;                      // u outside [0, 1) is clamped into it
     u = u < 1.f ? u : 0.99999994f;
-    const unsigned long long tgt = (unsigned long long)((double)u * (double)total);   // < total
-    const unsigned long long lo = t > 0 ? chunk[t - 1] : 0ull;
-    if (lo <= tgt && tgt < chunk[t]) {          // exactly one thread: the chunk holding the target
-        unsigned long long c = lo;
-        for (int i = i0; i < i1; i++) {
-            const float ev = a.e[i];
-            if (__float_as_uint(ev) >= tau) {
-                c += smp_mass(ev);
+    const uint64_t tgt = (uint64_t)((double)u * (double)total);   // < total
+    if (t < SMP_BLOCKS && lo_b <= tgt && tgt < lo_b + s_nm[t]) {   // exactly one slice
+        s_blk = t;
+        s_lo = lo_b;
+    }
+    __syncthreads();
+    // inside that slice: consecutive elements per thread, index order
+    const int i0 = s_blk * sl, i1 = min(a.V, i0 + sl);
+    const int per = (sl + SMP_DRAW_THREADS - 1) / SMP_DRAW_THREADS;
+    const int j0 = min(i1, i0 + t * per), j1 = min(i1, j0 + per);
+    uint64_t m = 0;
+    for (int i = j0; i < j1; i++) {
+        const uint32_t b = __float_as_uint(w.e[i]);
+        m += b >= tau ? smp_mass_bits(b) : 0ull;
+    }
+    const uint64_t lo_t = s_lo + block_excl_scan(m, tmp, &total);
+    if (lo_t <= tgt && tgt < lo_t + m) {   // exactly one thread: the elements holding the target
+        uint64_t c = lo_t;
+        for (int i = j0; i < j1; i++) {
+            const uint32_t b = __float_as_uint(w.e[i]);
+            if (b >= tau) {
+                c += smp_mass_bits(b);
                 if (c > tgt) {
                     *a.out = i;
                     break;
@@ -235,9 +356,24 @@ __global__ __launch_bounds__(SMP_SEL_THREADS) void sample_select_kernel(SampleAr
     }
 }
 
-size_t sample_ws_bytes(int V) {
-    return align_up((size_t)SMP_BLOCKS * 4, 256) * 2 + align_up((size_t)V * 4, 256) +
-           align_up((size_t)SMP_BLOCKS * 256 * 8, 256);
+static size_t carve_ws(void* base, int V, SampleWs* w) {
+    size_t off = 0;
+    auto take = [&](size_t n) {
+        void* p = base ? (char*)base + off : nullptr;
+        off += align_up(n, 256);
+        return p;
+    };
+    SampleWs s{};
+    s.bmax = (float*)take((size_t)SMP_BLOCKS * 4);
+    s.bidx = (int*)take((size_t)SMP_BLOCKS * 4);
+    s.e = (float*)take((size_t)V * 4);
+    s.hist = (uint64_t*)take((size_t)SMP_COPIES * SMP_BINS * 8);
+    s.certain = (uint64_t*)take((size_t)SMP_BLOCKS * 8);
+    s.ncand = (uint32_t*)take((size_t)SMP_BLOCKS * 4);
+    s.cand = (uint2*)take((size_t)SMP_BLOCKS * smp_slice(V) * 8);
+    s.sel = (uint64_t*)take(4 * 8);
+    if (w) *w = s;
+    return off;
 }
 
 }  // namespace atlas
@@ -246,7 +382,7 @@ using namespace atlas;
 
 extern "C" size_t atlas_sample_workspace_bytes(int32_t vocab) {
     if (vocab < 1 || vocab > (1 << 21)) return 0;
-    return sample_ws_bytes(vocab);
+    return carve_ws(nullptr, vocab, nullptr);
 }
 
 extern "C" int atlas_sample(const float* d_logits, int32_t vocab, float temperature, float top_p, const float* d_u,
@@ -257,35 +393,31 @@ extern "C" int atlas_sample(const float* d_logits, int32_t vocab, float temperat
     const bool greedy = temperature == 0.f;
     ATLAS_CHECK_ARG(greedy || (top_p > 0.f && top_p <= 1.f), "top_p must be in (0, 1]");
     ATLAS_CHECK_ARG(greedy || d_u, "sampling needs the uniform variate d_u");
-    const size_t need = sample_ws_bytes(vocab);
+    const size_t need = carve_ws(nullptr, vocab, nullptr);
     if (ws_bytes < need) return fail(ATLAS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu", ws_bytes, need);
-    char* base = (char*)ws;
-    float* bmax = (float*)base;
-    int* bidx = (int*)(base + align_up((size_t)SMP_BLOCKS * 4, 256));
-    float* e = (float*)(base + 2 * align_up((size_t)SMP_BLOCKS * 4, 256));
-    uint64_t* hist = (uint64_t*)((char*)e + align_up((size_t)vocab * 4, 256));
+    SampleWs w{};
+    carve_ws(ws, vocab, &w);
     hipStream_t st = (hipStream_t)stream;
     prof_mark("sample_max", st);
-    ATLAS_KLAUNCH(sample_max_kernel, dim3(SMP_BLOCKS), dim3(SMP_THREADS), 0, st, d_logits, vocab, bmax, bidx);
+    ATLAS_KLAUNCH(sample_max_kernel, dim3(SMP_BLOCKS), dim3(SMP_THREADS), 0, st, d_logits, vocab, w, greedy ? 0 : 1);
     ATLAS_LAUNCH_CHECK("sample_max_kernel");
     if (!greedy) {
         prof_mark("sample_exp", st);
-        ATLAS_KLAUNCH(sample_exp_kernel, dim3(SMP_BLOCKS), dim3(SMP_THREADS), 0, st, d_logits, vocab, bmax,
-                      1.0f / temperature, e, hist);
+        ATLAS_KLAUNCH(sample_exp_kernel, dim3(SMP_BLOCKS), dim3(SMP_THREADS), 0, st, d_logits, vocab,
+                      1.0f / temperature, w);
         ATLAS_LAUNCH_CHECK("sample_exp_kernel");
+        prof_mark("sample_bin", st);
+        ATLAS_KLAUNCH(sample_bin_kernel, dim3(SMP_BLOCKS), dim3(SMP_THREADS), 0, st, vocab, (double)top_p, w);
+        ATLAS_LAUNCH_CHECK("sample_bin_kernel");
     }
-    SampleArgs a{};
-    a.e = e;
+    DrawArgs a{};
+    a.w = w;
     a.V = vocab;
-    a.hist = hist;
-    a.bmax = bmax;
-    a.bidx = bidx;
     a.greedy = greedy ? 1 : 0;
-    a.top_p = top_p;
     a.d_u = d_u;
     a.out = d_token;
-    prof_mark("sample_select", st);
-    ATLAS_KLAUNCH(sample_select_kernel, dim3(1), dim3(SMP_SEL_THREADS), 0, st, a);
-    ATLAS_LAUNCH_CHECK("sample_select_kernel");
+    prof_mark("sample_draw", st);
+    ATLAS_KLAUNCH(sample_draw_kernel, dim3(1), dim3(SMP_DRAW_THREADS), 0, st, a);
+    ATLAS_LAUNCH_CHECK("sample_draw_kernel");
     return ATLAS_OK;
 }

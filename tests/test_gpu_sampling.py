@@ -145,3 +145,40 @@ def test_graph_replays_draw_like_eager_calls():
         replayed = int(tok.item())
         eager = _draw(lt, 0.6, 0.95, float(np.float32(u)), ws, dev)
         assert replayed == eager
+
+
+@pytest.mark.parametrize("case", ["all_equal", "threshold_ties", "two_levels"])
+def test_many_tied_values_at_the_threshold(case):
+    """Inputs whose nucleus threshold sits among many equal probabilities, so the
+    candidate list that pins the threshold's low bits is long: every logit equal (the
+    nucleus is the whole vocabulary and the draw is uniform over it), half of the
+    vocabulary tied just below a few large logits, and values spread over two
+    adjacent binary orders of magnitude. Every draw must be valid by the oracle's own
+    arithmetic (as in the full-vocabulary test: f32 against f64 probabilities can move
+    a draw that lies within ~1e-7 of a boundary); where every probability is exactly 1
+    the draw must equal the oracle's."""
+    dev = device()
+    r = np.random.default_rng(17)
+    if case == "all_equal":
+        l = np.zeros(V_FULL, np.float32)
+    elif case == "threshold_ties":
+        l = np.full(V_FULL, -1.0, np.float32)
+        l[r.choice(V_FULL, V_FULL // 2, replace=False)] = 0.25
+        l[r.choice(V_FULL, 5, replace=False)] = 6.0
+    else:
+        l = (np.log(1.0 + r.random(V_FULL)) * 0.6).astype(np.float32)
+    lt = torch.from_numpy(l).to(dev)
+    ws = torch.empty(ops.atlas_sample_workspace_bytes(V_FULL), dtype=torch.uint8, device=dev)
+    announce(f"sampling with many ties ({case})")
+    for T, p in ((0.6, 0.95), (1.0, 0.5), (1.0, 1.0)):
+        e, tau, inN, cN = _oracle_structures(l, T, p)
+        S = cN[-1]
+        for u in (0.0, 0.1234, 0.5, 0.87654, 0.99999994):
+            u32 = float(np.float32(u))
+            t = _draw(lt, T, p, u32, ws, dev)
+            o = O.sample_top_p(l, T, p, u32)
+            if case == "all_equal":
+                assert t == o, (u, T, p)
+            assert e[t] >= tau * (1 - 1e-5), (case, u, T, p, t, o)
+            lo, hi = cN[t] - (e[t] if inN[t] else 0.0), cN[t]
+            assert lo - 1e-5 * S <= np.float32(u) * S <= hi + 1e-5 * S, (case, u, T, p, t, o)
