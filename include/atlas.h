@@ -132,6 +132,19 @@ ATLAS_API const char* atlas_last_error(void);
 ATLAS_API size_t atlas_w4_gemv_workspace_bytes(const atlas_w4* W);
 ATLAS_API int atlas_w4_gemv(const atlas_w4* W, const float* x, float* y, void* ws, size_t ws_bytes, void* stream);
 
+/* Batched W4 GEMV: y[v][n] = sum_k W[n][k] x[v][k] for B <= 8 activation vectors, the
+ * weights read once for all of them (the projections of batched decode, [card]
+ * Limitations & roadmap: batched decode after the batch-1 path). x: f32 [B][K], y: f32
+ * [B][N] (device, row-major). Requires K % 64 == 0 and a group that is a multiple of
+ * 128; else ATLAS_ERR_UNSUPPORTED_SHAPE. Each x[v] is encoded per block of 128 columns
+ * as 24-bit block fixed point (n = rint(x / 2^e) with |n| < 2^23) and multiplied on the
+ * int8 matrix cores in exact integer digit sums; result within 1e-6 relative of the f64
+ * definition. ws: device workspace of atlas_w4_gemv_batch_workspace_bytes(W, B) bytes
+ * (0 when the shape is unsupported). */
+ATLAS_API size_t atlas_w4_gemv_batch_workspace_bytes(const atlas_w4* W, int32_t B);
+ATLAS_API int atlas_w4_gemv_batch(const atlas_w4* W, const float* x, int32_t B, float* y, void* ws, size_t ws_bytes,
+                                  void* stream);
+
 /* Materialise the dequantised matrix out[N][K] f32 (device); exact (bit-for-bit
  * (code - zero) * scale). For checking the unpacking. */
 ATLAS_API int atlas_w4_dequant(const atlas_w4* W, float* out, void* stream);

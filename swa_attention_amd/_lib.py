@@ -53,6 +53,8 @@ _SIGS = {
     "atlas_w4_gemv_workspace_bytes": (c_size_t, [P(atlas_w4)]),
     "atlas_w4_gemv": (ctypes.c_int, [P(atlas_w4), c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "atlas_w4_dequant": (ctypes.c_int, [P(atlas_w4), c_void_p, c_void_p]),
+    "atlas_w4_gemv_batch_workspace_bytes": (c_size_t, [P(atlas_w4), c_int32]),
+    "atlas_w4_gemv_batch": (ctypes.c_int, [P(atlas_w4), c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "atlas_w4_gemm_workspace_bytes": (c_size_t, [P(atlas_w4), c_int32]),
     "atlas_w4_gemm": (ctypes.c_int, [P(atlas_w4), c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "atlas_rmsnorm_residual": (ctypes.c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_void_p]),

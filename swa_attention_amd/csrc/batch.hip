@@ -14,6 +14,7 @@
 // then bd_final_norm -> bd_head (logits [B][V]) -> bd_argmax_rows.
 #include <cmath>
 
+#include "bgemv.h"
 #include "decode.h"
 #include "gemv.h"
 #include "norm_rope.h"
@@ -187,6 +188,73 @@ __global__ __launch_bounds__(256) void bd_swiglu_kernel(const float* gp, const f
     z_lo[i] = (uint16_t)lo;
 }
 
+// ---- the same for the int8-plane projections (B <= 8, see bgemv.hip) -------------------------
+
+// Sum of `parts` partial rows at 8 consecutive columns, in split order.
+__device__ __forceinline__ void bd_sum8(const float* p, int parts, size_t stride, float out[8]) {
+    float4 s0 = *reinterpret_cast<const float4*>(p), s1 = *reinterpret_cast<const float4*>(p + 4);
+    for (int q = 1; q < parts; q++) {
+        const float4 a = *reinterpret_cast<const float4*>(p + (size_t)q * stride);
+        const float4 b = *reinterpret_cast<const float4*>(p + (size_t)q * stride + 4);
+        s0.x += a.x; s0.y += a.y; s0.z += a.z; s0.w += a.w;
+        s1.x += b.x; s1.y += b.y; s1.z += b.z; s1.w += b.w;
+    }
+    out[0] = s0.x; out[1] = s0.y; out[2] = s0.z; out[3] = s0.w;
+    out[4] = s1.x; out[5] = s1.y; out[6] = s1.z; out[7] = s1.w;
+}
+
+// X[t] += g * A[t] / rms(A[t]) (A[t] the sum of `parts` partial rows), then X[t] encoded
+// for the next projection. One block of whole waves per row; thread i holds columns
+// 8 i .. 8 i + 7, and the block covers the encoding's padded width (16 threads per 128
+// columns).
+__global__ __launch_bounds__(1024) void bd_residual_q_kernel(float* X, const float* part, int parts,
+                                                           size_t part_stride, const float* g, int d, float eps,
+                                                           BQ q) {
+    __shared__ float red[16];
+    const int t = blockIdx.x, col0 = 8 * threadIdx.x;
+    const bool on = col0 < d;
+    float a[8], x[8];
+    float ss = 0.f;
+    if (on) {
+        bd_sum8(part + (size_t)t * d + col0, parts, part_stride, a);
+#pragma unroll
+        for (int j = 0; j < 8; j++) ss = fmaf(a[j], a[j], ss);
+    }
+    ss = block_sum(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+    if (on) {
+        float* xr = X + (size_t)t * d + col0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            x[j] = xr[j] + g[col0 + j] * (a[j] * r);
+            xr[j] = x[j];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; j++) x[j] = 0.f;
+    }
+    if (col0 < q.ldq) bq_encode_row16(x, q, t, col0, threadIdx.x >> 4);   // whole rows of 16 lanes
+}
+
+// z = silu(g) * u (g, u the sums of `parts` partial rows [parts][B][n]), encoded for the
+// down projection. Grid (blocks over 16 threads per 128 columns, B).
+__global__ __launch_bounds__(256) void bd_swiglu_q_kernel(const float* gp, const float* up, int parts,
+                                                         size_t part_stride, int n, BQ q) {
+    const int t = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x, col0 = 8 * i;
+    float z[8];
+    if (col0 < n) {
+        float gv[8], uv[8];
+        bd_sum8(gp + (size_t)t * n + col0, parts, part_stride, gv);
+        bd_sum8(up + (size_t)t * n + col0, parts, part_stride, uv);
+#pragma unroll
+        for (int j = 0; j < 8; j++) z[j] = gv[j] / (1.0f + __expf(-gv[j])) * uv[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; j++) z[j] = 0.f;
+    }
+    if (col0 < q.ldq) bq_encode_row16(z, q, t, col0, i >> 4);   // whole rows of 16 lanes
+}
+
 // ---- lm_head over the batch: bf16 matrix cores, weights streamed once --------------------------
 
 // logits[m][n] = sum_k W[n][k] y[m][k] for m < B (<= 16), n < V. One wave per 16
@@ -300,13 +368,30 @@ int bd_ksplit(int tiles, int K, int group, int target) {
 constexpr int BD_SPLIT_TARGET_ATTN_PROJ = 384, BD_SPLIT_TARGET_MLP = 768;
 
 struct BatchPlan {
-    int sq, so, sg, sd;   // K splits of the qkv, o, gate/up and down GEMMs
+    int sq, so, sg, sd;   // K splits of the qkv, o, gate/up and down projections
     int S_swa, S_full, S_max;
+    bool bq;              // projections on int8 planes (bgemv.hip); else the bf16-plane GEMM
 };
+
+// Whether every projection of every layer takes the int8-plane batched GEMV.
+static bool batch_bq_ok(const atlas_model* m, int B) {
+    if (B > BG_MAX_B || m->d % 64 || m->d > 8192) return false;
+    for (int l = 0; l < m->n_layers; l++) {
+        const atlas_layer& L = m->layers[l];
+        const atlas_w4* ws[5] = {&L.qkv, &L.o, &L.gate, &L.up, &L.down};
+        for (const atlas_w4* w : ws) {
+            const W4View v = w4_view(w->qweight, w->scales, w->zeros, w->N, w->K, w->group, w->scale_dtype);
+            if (!bgemv_supported(v, w->group)) return false;
+        }
+        if (L.gate.group != L.up.group) return false;
+    }
+    return true;
+}
 
 static BatchPlan batch_plan(const atlas_model* m, int B) {
     BatchPlan p{};
     const int nq = m->hq * m->hd, nqkv = (m->hq + 2 * m->hkv) * m->hd;
+    p.bq = batch_bq_ok(m, B);
     const int MT = (B + 63) / 64;
     p.sq = bd_ksplit(MT * ((nqkv + 127) / 128), m->d, m->layers[0].qkv.group, BD_SPLIT_TARGET_ATTN_PROJ);
     p.so = bd_ksplit(MT * ((m->d + 127) / 128), nq, m->layers[0].o.group, BD_SPLIT_TARGET_ATTN_PROJ);
@@ -318,6 +403,12 @@ static BatchPlan batch_plan(const atlas_model* m, int B) {
         if (nq % (p.so * L.o.group) || (nq / p.so) % 64) p.so = 1;
         if (m->d % (p.sg * L.gate.group) || (m->d / p.sg) % 64) p.sg = 1;
         if (m->dff % (p.sd * L.down.group) || (m->dff / p.sd) % 64) p.sd = 1;
+    }
+    if (p.bq) {   // the int8-plane GEMV picks its own K split
+        p.sq = bgemv_splits(m->d, nqkv);
+        p.so = bgemv_splits(nq, m->d);
+        p.sg = bgemv_splits(m->d, m->dff, m->dff);
+        p.sd = bgemv_splits(m->dff, m->d);
     }
     const int64_t swa_keys = m->window > 0 ? std::min<int64_t>(m->window, m->t_max) : m->t_max;
     // key splits sized as for half the (KV head, sequence) blocks: at 8 sequences, 8 on the
@@ -334,6 +425,7 @@ struct BatchWs {
     float *X, *qkv, *qkv_part, *o, *attn_part, *a_part, *g_part, *u_part, *logits;
     uint16_t *p1h, *p1l, *p2h, *p2l;
     int ld1;
+    void* bq;             // int8 planes of the current projection input (plan.bq)
     size_t bytes;
 };
 
@@ -362,6 +454,7 @@ static BatchWs carve_batch(const atlas_model* m, int B, const BatchPlan& p, void
     w.p2h = (uint16_t*)take((size_t)B * m->dff * 2);
     w.p2l = (uint16_t*)take((size_t)B * m->dff * 2);
     w.logits = need_logits ? (float*)take((size_t)B * m->vocab * 4) : nullptr;
+    w.bq = p.bq ? take(bq_bytes(B, std::max(std::max(m->d, nq), m->dff))) : nullptr;
     w.bytes = off;
     return w;
 }
@@ -427,19 +520,31 @@ extern "C" int atlas_decode_batch(const atlas_model* m, const int32_t* d_tokens,
     // the embedding kernel writes the status word first (ATLAS_OK, or a bad token id)
     if ((rc = launch_pf_embed(d_tokens, B, m->embedding, m->vocab, d, w.X, w.p1h, w.p1l, w.ld1, w.status, st)))
         return rc;
+    const BQ q_d = p.bq ? bq_carve(w.bq, B, d) : BQ{};       // inputs of qkv and gate/up
+    const BQ q_nq = p.bq ? bq_carve(w.bq, B, nq) : BQ{};     // input of o
+    const BQ q_ff = p.bq ? bq_carve(w.bq, B, m->dff) : BQ{}; // input of down
+    if (p.bq && (rc = launch_bq_encode(w.X, d, B, d, q_d, st))) return rc;
+    // whole waves (the block sum reads every lane), covering the encoding's padded width
+    const unsigned res_threads = (unsigned)align_up((size_t)16 * ((d + 127) / 128), 64);
     for (int l = 0; l < m->n_layers; l++) {
         const atlas_layer& L = m->layers[l];
         const bool ring = m->swa_ring && L.type == 0;
         const int64_t slots = ring ? m->window : m->t_max;
         const int64_t seq_stride = (int64_t)m->hkv * slots * m->hd;
         // qkv projection of the B rows, split over K
-        GemmArgs qa = bgemm(w.p1h, w.p1l, w.ld1, L.qkv, B);
-        qa.C = w.qkv_part;
-        qa.ldc = nqkv;
-        qa.ksplit = p.sq;
-        qa.kchunk = d / p.sq;
-        qa.c_split = (size_t)B * nqkv;
-        if ((rc = launch_w4_gemm(qa, 0, st, "bd_gemm_qkv"))) return rc;
+        if (p.bq) {
+            const BgemvOut o{w.qkv_part, (size_t)B * nqkv, nqkv};
+            if ((rc = launch_bgemv(bview(L.qkv), L.qkv.group, nullptr, q_d, B, o, nullptr, st, "bd_gemv_qkv")))
+                return rc;
+        } else {
+            GemmArgs qa = bgemm(w.p1h, w.p1l, w.ld1, L.qkv, B);
+            qa.C = w.qkv_part;
+            qa.ldc = nqkv;
+            qa.ksplit = p.sq;
+            qa.kchunk = d / p.sq;
+            qa.c_split = (size_t)B * nqkv;
+            if ((rc = launch_w4_gemm(qa, 0, st, "bd_gemm_qkv"))) return rc;
+        }
         // QK norm, rotary at each row's position, k/v into each sequence's cache
         BdRopeArgs ra{};
         ra.qkv = w.qkv;
@@ -494,11 +599,37 @@ extern "C" int atlas_decode_batch(const atlas_model* m, const int32_t* d_tokens,
         ma.part = w.attn_part;
         ma.S = aa.S;
         ma.Hq = m->hq;
-        ma.o = w.o;
+        ma.o = p.bq ? nullptr : w.o;
+        if (p.bq) ma.bq = q_nq;   // the o projection's input, encoded by the merge
         ma.batch = B;
         ma.part_stride = aa.part_stride;
         ma.o_stride = nq;
         if ((rc = launch_merge(ma, st))) return rc;
+        if (p.bq) {
+            // o projection, h = x + RMSNorm_pa(a); gate/up, SwiGLU; down, y = h + RMSNorm_pf(m)
+            const BgemvOut oo{w.a_part, (size_t)B * d, d};
+            if ((rc = launch_bgemv(bview(L.o), L.o.group, nullptr, q_nq, B, oo, nullptr, st, "bd_gemv_o"))) return rc;
+            prof_mark("bd_residual_norm", st);
+            ATLAS_KLAUNCH(bd_residual_q_kernel, dim3(B), dim3(res_threads), 0, st, w.X, w.a_part, p.so, (size_t)B * d,
+                          L.g_pa, d, m->eps, q_d);
+            ATLAS_LAUNCH_CHECK("bd_residual_q_kernel");
+            const size_t gstride = (size_t)B * m->dff;
+            const BgemvOut og{w.g_part, gstride, m->dff}, ou{w.u_part, gstride, m->dff};
+            const W4View wu = bview(L.up);
+            if ((rc = launch_bgemv(bview(L.gate), L.gate.group, &wu, q_d, B, og, &ou, st, "bd_gemv_gate_up"))) return rc;
+            prof_mark("bd_swiglu", st);
+            ATLAS_KLAUNCH(bd_swiglu_q_kernel, dim3((unsigned)((q_ff.ldq / 8 + 255) / 256), B), dim3(256), 0, st,
+                          w.g_part, w.u_part, p.sg, gstride, m->dff, q_ff);
+            ATLAS_LAUNCH_CHECK("bd_swiglu_q_kernel");
+            const BgemvOut od{w.a_part, (size_t)B * d, d};
+            if ((rc = launch_bgemv(bview(L.down), L.down.group, nullptr, q_ff, B, od, nullptr, st, "bd_gemv_down")))
+                return rc;
+            prof_mark("bd_residual_norm", st);
+            ATLAS_KLAUNCH(bd_residual_q_kernel, dim3(B), dim3(res_threads), 0, st, w.X, w.a_part, p.sd, (size_t)B * d,
+                          L.g_pf, d, m->eps, q_d);
+            ATLAS_LAUNCH_CHECK("bd_residual_q_kernel");
+            continue;
+        }
         if ((rc = launch_pf_split(w.o, B, nq, nq, w.p1h, w.p1l, w.ld1, st))) return rc;
         // o projection (split over K), h = x + RMSNorm_pa(a)
         GemmArgs oa = bgemm(w.p1h, w.p1l, w.ld1, L.o, B);

@@ -1,5 +1,6 @@
 // Fused kernels of the decode step (internal interface).
 #pragma once
+#include "bgemv.h"
 #include "gemv_core.h"
 
 namespace atlas {
@@ -72,6 +73,7 @@ struct MergeArgs {
     int S, Hq;
     float* o;     // may be null
     XQ xq;        // planes may be null
+    BQ bq;        // p may be null: o of sequence blockIdx.y as int8 planes (one head = one 128-column block)
     // batched: sequence y = blockIdx.y reads part + y * part_stride, writes o + y * o_stride
     int batch;    // 0 or 1: one sequence
     int64_t part_stride, o_stride;

@@ -900,6 +900,16 @@ __global__ __launch_bounds__(128) void merge_kernel(MergeArgs a) {
             xq_encode_word(x8, a.xq, h * 4 + (d >> 2), d & 3);
         }
     }
+    if (a.bq.p) {
+        s_o[d] = r;
+        __syncthreads();
+        if (d < 16) {   // one row of 16 lanes encodes the head's 128 values
+            float x8[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) x8[i] = s_o[8 * d + i];
+            bq_encode_row16(x8, a.bq, blockIdx.y, h * 128 + 8 * d, h);
+        }
+    }
 }
 
 // ---- final norm, bf16 lm_head and argmax partials ------------------------------------------------

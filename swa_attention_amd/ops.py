@@ -63,6 +63,27 @@ def atlas_w4_gemv(w: W4, x, y=None, ws=None, stream=None):
     return y
 
 
+def atlas_w4_gemv_batch_workspace_bytes(w: W4, B: int):
+    return L.lib().atlas_w4_gemv_batch_workspace_bytes(ctypes.byref(w.c()), int(B))
+
+
+def atlas_w4_gemv_batch(w: W4, x, y=None, ws=None, stream=None):
+    """x: f32 [B][K] on the device; returns y f32 [B][N]."""
+    _dev(x, F32, "x")
+    if x.dim() != 2 or x.shape[1] != w.K or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B][K] tensor")
+    B = x.shape[0]
+    if y is None:
+        y = torch.empty((B, w.N), dtype=F32, device=x.device)
+    _dev(y, F32, "y")
+    need = atlas_w4_gemv_batch_workspace_bytes(w, B)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    L.call("atlas_w4_gemv_batch", ctypes.byref(w.c()), L.ptr(x), B, L.ptr(y), L.ptr(ws), ws.numel(),
+           L.stream_ptr(stream))
+    return y
+
+
 def atlas_w4_dequant(w: W4, out=None, stream=None):
     if out is None:
         out = torch.empty((w.N, w.K), dtype=F32, device=w.qweight.device)

@@ -76,6 +76,25 @@ def test_w4_gemv_validation(lib):
     assert b"workspace" in lib.atlas_last_error()
 
 
+def test_w4_gemv_batch_validation(lib):
+    def gb(W, B=4, ws_bytes=1 << 24, ws=FAKE, x=FAKE, y=FAKE):
+        return lib.atlas_w4_gemv_batch(ctypes.byref(W) if W is not None else None, x, B, y, ws, ws_bytes, None)
+    assert gb(None) == L.ATLAS_ERR_INVALID_ARG
+    assert gb(w4(), B=0) == L.ATLAS_ERR_INVALID_ARG
+    assert gb(w4(), B=9) == L.ATLAS_ERR_INVALID_ARG
+    assert gb(w4(K=96)) == L.ATLAS_ERR_UNSUPPORTED_SHAPE            # K % 64 != 0
+    assert gb(w4(group=64)) == L.ATLAS_ERR_UNSUPPORTED_SHAPE        # group not a multiple of 128
+    assert gb(w4(group=32)) == L.ATLAS_ERR_UNSUPPORTED_SHAPE
+    assert gb(w4(), x=None) == L.ATLAS_ERR_INVALID_ARG
+    assert gb(w4(), ws=None) == L.ATLAS_ERR_INVALID_ARG
+    assert lib.atlas_w4_gemv_batch_workspace_bytes(ctypes.byref(w4(group=64)), 4) == 0
+    assert lib.atlas_w4_gemv_batch_workspace_bytes(ctypes.byref(w4()), 9) == 0
+    for N, K, B in ((7168, 5120, 8), (5120, 27648, 8), (640, 1728, 3), (64, 256, 1)):
+        need = lib.atlas_w4_gemv_batch_workspace_bytes(ctypes.byref(w4(N, K)), B)
+        assert need > 0
+        assert gb(w4(N, K), B=B, ws_bytes=need - 1) == L.ATLAS_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_workspace_sizes_are_positive_for_real_shapes(lib):
     for N, K in ((7168, 5120), (5120, 5120), (27648, 5120), (5120, 27648), (896, 640), (640, 1728)):
         assert lib.atlas_w4_gemv_workspace_bytes(ctypes.byref(w4(N, K))) > 0

@@ -71,6 +71,64 @@ def test_gemv_matches_oracle(N, K):
     assert normwise(y, ref) < 1e-5
 
 
+@pytest.mark.parametrize("N,K,B,group,zeros,sd", [
+    (896, 640, 3, 128, True, 0), (1728, 640, 8, 128, True, 0), (640, 1728, 5, 128, True, 0),
+    (33, 640, 7, 128, False, 1), (1001, 1024, 2, 256, False, 1), (300, 2048, 1, 512, True, 0),
+    (130, 4096, 8, 1024, True, 0), (7168, 5120, 8, 128, True, 0), (5120, 6144, 4, 128, True, 0),
+    (5120, 27648, 8, 128, True, 0), (27648, 5120, 6, 128, True, 0)])
+def test_gemv_batch_matches_oracle(N, K, B, group, zeros, sd):
+    """The batched W4 GEMV (int8 matrix cores, 24-bit block fixed-point activations)
+    against the f64 oracle, vector by vector: ragged row tiles, a 64-column last block
+    (K = 1,728), groups of 128 to 1,024, symmetric codes and bf16 scales, chunks split
+    over blocks (K = 27,648), 1 to 8 vectors. The only deviation is the 24-bit encoding
+    of x and f32 summation, so the single GEMV's 1e-5 bar applies."""
+    dev = device()
+    announce(f"gemv batch N={N} K={K} B={B} group={group}")
+    c, s, z = _w4(N, K, 11, group, zeros, sd)
+    w = w4_to_device(c, s, z, K, dev, group, sd)
+    xs = np.stack([synth.normal_f32(synth.key(11, 100 + v), K) for v in range(B)])
+    y = ops.atlas_w4_gemv_batch(w, torch.from_numpy(xs).to(dev)).cpu().numpy()
+    for v in range(B):
+        ref = O.w4_gemv(c, s, z, K, xs[v], group, sd)
+        assert normwise(y[v], ref) < 1e-5, v
+
+
+def test_gemv_batch_one_hot_columns_bit_exact():
+    """Eight one-hot vectors at once: each output row is its column of the dequantised
+    matrix bit for bit (code and zero selection, scale, the digit recombination; the
+    power-of-two block scale makes the encoding exact)."""
+    dev = device()
+    N, K = 1001, 1728
+    announce(f"gemv batch one-hot N={N} K={K}")
+    c, s, z = _w4(N, K, 12)
+    w = w4_to_device(c, s, z, K, dev)
+    ref = O.dequant(c, s, z, K)
+    for cols in ([0, 1, 7, 8, 31, 32, 127, 128], [129, 511, 512, 640, 1023, K - 65, K - 64, K - 1]):
+        x = np.zeros((8, K), dtype=np.float32)
+        for v, j in enumerate(cols):
+            x[v, j] = 1.0
+        y = ops.atlas_w4_gemv_batch(w, torch.from_numpy(x).to(dev)).cpu().numpy()
+        for v, j in enumerate(cols):
+            np.testing.assert_array_equal(y[v].view(np.uint32), ref[:, j].copy().view(np.uint32), err_msg=f"col {j}")
+
+
+def test_gemv_batch_heavy_tailed_and_zero_rows():
+    """Inputs spanning 12 orders of magnitude, an all-zero vector and a vector of equal
+    values: the block encoding keeps f32-level error, and a zero vector gives exact
+    zeros."""
+    dev = device()
+    N, K = 512, 5120
+    c, s, z = _w4(N, K, 13)
+    r = np.random.default_rng(6)
+    xs = np.stack([(r.standard_normal(K) * 10.0 ** r.uniform(-6, 6, K)).astype(np.float32),
+                   np.zeros(K, dtype=np.float32), np.full(K, 0.37, dtype=np.float32)])
+    w = w4_to_device(c, s, z, K, dev)
+    y = ops.atlas_w4_gemv_batch(w, torch.from_numpy(xs).to(dev)).cpu().numpy()
+    assert normwise(y[0], O.w4_gemv(c, s, z, K, xs[0])) < 1e-5
+    assert not y[1].any()
+    assert normwise(y[2], O.w4_gemv(c, s, z, K, xs[2])) < 1e-5
+
+
 @pytest.mark.parametrize("M,N,K,group,zeros,sd", [
     (1, 96, 640, 128, True, 0), (17, 130, 640, 128, True, 0), (64, 256, 1728, 128, True, 0),
     (130, 200, 640, 64, False, 1), (70, 64, 256, 32, True, 0), (200, 896, 640, 128, True, 0),
