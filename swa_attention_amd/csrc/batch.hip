@@ -61,30 +61,33 @@ struct BdRopeArgs {
     int* status;
 };
 
+// One block per sequence; the summed row stays in LDS (dynamic, ld floats) between the
+// norms and the rotation, and every global load of the partials is issued before the
+// first barrier.
 __global__ __launch_bounds__(1024) void bd_rope_kernel(BdRopeArgs a) {
     constexpr int D = 128;
-    __shared__ float red[16];
+    extern __shared__ float s_row[];   // [ld]
+    __shared__ float red[2][16];
     __shared__ float s_cos[64], s_sin[64];
     const int t = blockIdx.x;
     const int pos = a.d_pos[t];
     const int nq = a.Hq * D, nk = a.Hkv * D;
-    float* row = a.qkv + (size_t)t * a.ld;
-    for (int i = threadIdx.x; i < a.ld; i += blockDim.x) {
-        row[i] = bd_sum_parts(a.part + (size_t)t * a.ld + i, a.parts, a.part_stride);
-    }
-    __syncthreads();
-    if (pos < 0 || pos >= a.T_max) {   // the attention of this row reports it too; nothing is stored
-        if (threadIdx.x == 0) *a.status = ATLAS_ERR_INVALID_ARG;
-        return;
-    }
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
     float sq = 0.f, sk = 0.f;
-    for (int i = threadIdx.x; i < nq; i += blockDim.x) sq = fmaf(row[i], row[i], sq);
-    for (int i = threadIdx.x; i < nk; i += blockDim.x) sk = fmaf(row[nq + i], row[nq + i], sk);
-    sq = block_sum(sq, red);
-    sk = block_sum(sk, red);
-    const float rq = 1.0f / sqrtf(sq / (float)nq + a.eps);
-    const float rk = 1.0f / sqrtf(sk / (float)nk + a.eps);
-    if (threadIdx.x < 64) {
+    for (int i = 4 * threadIdx.x; i < a.ld; i += 4 * blockDim.x) {   // ld, nq, nk multiples of 4
+        const float* p = a.part + (size_t)t * a.ld + i;
+        float4 v = *reinterpret_cast<const float4*>(p);
+        for (int q = 1; q < a.parts; q++) {
+            const float4 u = *reinterpret_cast<const float4*>(p + (size_t)q * a.part_stride);
+            v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+        }
+        *reinterpret_cast<float4*>(&s_row[i]) = v;
+        const float ss = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        if (i < nq) sq += ss;
+        else if (i < nq + nk) sk += ss;
+    }
+    const bool ok = pos >= 0 && pos < a.T_max;
+    if (threadIdx.x < 64 && ok) {
         const double ang = (double)pos * a.inv[threadIdx.x];
         const double rr = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
         float sn, cs;
@@ -92,7 +95,27 @@ __global__ __launch_bounds__(1024) void bd_rope_kernel(BdRopeArgs a) {
         s_cos[threadIdx.x] = cs * (float)a.mscale;
         s_sin[threadIdx.x] = sn * (float)a.mscale;
     }
+    sq = wave_sum(sq);
+    sk = wave_sum(sk);
+    if (lane == 0) {
+        red[0][w] = sq;
+        red[1][w] = sk;
+    }
     __syncthreads();
+    float* row = a.qkv + (size_t)t * a.ld;
+    if (!ok) {   // the attention of this row reports it too; nothing is stored in the cache
+        for (int i = threadIdx.x; i < nq; i += blockDim.x) row[i] = s_row[i];
+        if (threadIdx.x == 0) *a.status = ATLAS_ERR_INVALID_ARG;
+        return;
+    }
+    sq = 0.f;
+    sk = 0.f;
+    for (int i = 0; i < nw; i++) {
+        sq += red[0][i];
+        sk += red[1][i];
+    }
+    const float rq = 1.0f / sqrtf(sq / (float)nq + a.eps);
+    const float rk = 1.0f / sqrtf(sk / (float)nk + a.eps);
     const int slot = a.ring ? pos % (int)a.slots : pos;
     const size_t cache0 = (size_t)t * a.seq_stride + (size_t)slot * D;
     const int npairs = (a.Hq + a.Hkv) * 64;
@@ -102,7 +125,7 @@ __global__ __launch_bounds__(1024) void bd_rope_kernel(BdRopeArgs a) {
         const float rr = isk ? rk : rq;
         const float* g = isk ? a.g_k + (h - a.Hq) * D : a.g_q + h * D;
         const int base = h * D;
-        const float x0 = g[i] * (row[base + i] * rr), x1 = g[i + 64] * (row[base + i + 64] * rr);
+        const float x0 = g[i] * (s_row[base + i] * rr), x1 = g[i + 64] * (s_row[base + i + 64] * rr);
         const float c = s_cos[i], sn = s_sin[i];
         const float y0 = x0 * c - x1 * sn, y1 = x1 * c + x0 * sn;
         if (isk) {
@@ -122,7 +145,7 @@ __global__ __launch_bounds__(1024) void bd_rope_kernel(BdRopeArgs a) {
     for (int u = threadIdx.x; u < nk; u += blockDim.x) {
         const int h = u / D, i = u % D;
         const size_t e = cache0 + (size_t)h * a.slots * D + i;
-        const float v = row[nq + nk + u];
+        const float v = s_row[nq + nk + u];
         if (a.kv_bf16) ((uint16_t*)a.v_cache)[e] = (uint16_t)f32_to_bf16_rne(v);
         else ((float*)a.v_cache)[e] = v;
     }
@@ -213,9 +236,14 @@ __global__ __launch_bounds__(1024) void bd_residual_q_kernel(float* X, const flo
     __shared__ float red[16];
     const int t = blockIdx.x, col0 = 8 * threadIdx.x;
     const bool on = col0 < d;
-    float a[8], x[8];
+    float a[8], x[8], gv[8];
     float ss = 0.f;
-    if (on) {
+    float* xr = X + (size_t)t * d + col0;
+    if (on) {   // the residual and the gain are loaded before the block sum, with the partials
+        const float4 x0 = *reinterpret_cast<const float4*>(xr), x1 = *reinterpret_cast<const float4*>(xr + 4);
+        x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w; x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+#pragma unroll
+        for (int j = 0; j < 8; j++) gv[j] = g[col0 + j];   // the caller's gains: 4-byte aligned only
         bd_sum8(part + (size_t)t * d + col0, parts, part_stride, a);
 #pragma unroll
         for (int j = 0; j < 8; j++) ss = fmaf(a[j], a[j], ss);
@@ -223,12 +251,10 @@ __global__ __launch_bounds__(1024) void bd_residual_q_kernel(float* X, const flo
     ss = block_sum(ss, red);
     const float r = 1.0f / sqrtf(ss / (float)d + eps);
     if (on) {
-        float* xr = X + (size_t)t * d + col0;
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            x[j] = xr[j] + g[col0 + j] * (a[j] * r);
-            xr[j] = x[j];
-        }
+        for (int j = 0; j < 8; j++) x[j] = x[j] + gv[j] * (a[j] * r);
+        *reinterpret_cast<float4*>(xr) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4*>(xr + 4) = make_float4(x[4], x[5], x[6], x[7]);
     } else {
 #pragma unroll
         for (int j = 0; j < 8; j++) x[j] = 0.f;
@@ -570,7 +596,7 @@ extern "C" int atlas_decode_batch(const atlas_model* m, const int32_t* d_tokens,
         ra.kv_bf16 = m->kv_dtype;
         ra.status = w.status;
         prof_mark("bd_qk_norm_rope", st);
-        ATLAS_KLAUNCH(bd_rope_kernel, dim3(B), dim3(1024), 0, st, ra);
+        ATLAS_KLAUNCH(bd_rope_kernel, dim3(B), dim3(1024), (size_t)nqkv * 4, st, ra);
         ATLAS_LAUNCH_CHECK("bd_rope_kernel");
         // attention per sequence, then the merge into o rows
         AttnFusedArgs aa{};
