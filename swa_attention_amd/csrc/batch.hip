@@ -283,43 +283,63 @@ __global__ __launch_bounds__(256) void bd_swiglu_q_kernel(const float* gp, const
 
 // ---- lm_head over the batch: bf16 matrix cores, weights streamed once --------------------------
 
-// logits[m][n] = sum_k W[n][k] y[m][k] for m < B (<= 16), n < V. One wave per 16
-// vocabulary rows, on v_mfma_f32_16x16x32_bf16 with y = hi + lo: lane l holds the A
-// operand y[l % 16][k0 + 8 (l / 16) ..+8] and the B operand W[n0 + l % 16][same k],
-// both one 16-byte load, so the weights go from HBM to the matrix core without LDS;
-// each row is read 128 contiguous bytes per step (two k-steps of 32).
-constexpr int BD_HEAD_WAVES = 4;
+// logits[m][n] = sum_k W[n][k] y[m][k] for m < B (<= 16), n < V. One wave per
+// BD_HEAD_TILES x 16 vocabulary rows, on v_mfma_f32_16x16x32_bf16 with y = hi + lo: lane l
+// holds the A operand y[l % 16][k0 + 8 (l / 16) ..+8] and the B operands W[n0 + 16 i +
+// l % 16][same k], each one 16-byte load, so the weights go from HBM to the matrix core
+// without LDS, and one load of y (from L2) serves BD_HEAD_TILES weight tiles. The weight
+// loads run BD_HEAD_AHEAD steps of 32 columns ahead of the products (plain loads: with
+// 16 rows x 64 bytes per wave instruction they stream faster than nontemporal ones).
+constexpr int BD_HEAD_WAVES = 4, BD_HEAD_TILES = 4, BD_HEAD_AHEAD = 4;
 __global__ __launch_bounds__(64 * BD_HEAD_WAVES) void bd_head_kernel(const uint16_t* __restrict__ y_hi,
                                                                       const uint16_t* __restrict__ y_lo, int ldy,
                                                                       int B, const uint16_t* __restrict__ W, int V,
                                                                       int d, float* __restrict__ logits) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n0 = (blockIdx.x * BD_HEAD_WAVES + wave) * 16;
+    const int n0 = (blockIdx.x * BD_HEAD_WAVES + wave) * 16 * BD_HEAD_TILES;
     if (n0 >= V) return;
     const int l16 = lane & 15, kk = 8 * (lane >> 4);
-    const int n = min(n0 + l16, V - 1), m = min(l16, B - 1);
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4* wrow = reinterpret_cast<const u32x4*>(W + (size_t)n * d + kk);
+    const int m = min(l16, B - 1);
+    const uint4* wrow[BD_HEAD_TILES];
+#pragma unroll
+    for (int i = 0; i < BD_HEAD_TILES; i++)
+        wrow[i] = reinterpret_cast<const uint4*>(W + (size_t)min(n0 + 16 * i + l16, V - 1) * d + kk);
     const uint4* yh = reinterpret_cast<const uint4*>(y_hi + (size_t)m * ldy + kk);
     const uint4* yl = reinterpret_cast<const uint4*>(y_lo + (size_t)m * ldy + kk);
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-    for (int k0 = 0; k0 < d; k0 += 64) {
-        const int q = k0 / 8;   // in 16-byte units
-        const u32x4 w0 = __builtin_nontemporal_load(wrow + q), w1 = __builtin_nontemporal_load(wrow + q + 4);
-        const uint4 h0 = yh[q], l0 = yl[q], h1 = yh[q + 4], l1 = yl[q + 4];
-        const bd_bf16x8_t bw0 = __builtin_bit_cast(bd_bf16x8_t, w0), bw1 = __builtin_bit_cast(bd_bf16x8_t, w1);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bd_bf16x8_t, h0), bw0, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bd_bf16x8_t, l0), bw0, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bd_bf16x8_t, h1), bw1, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bd_bf16x8_t, l1), bw1, acc, 0, 0, 0);
-    }
-    // acc[r] = logits[row 4 (l / 16) + r][column n0 + l % 16]
+    const int steps = d / 32;   // 32 columns (4 x 16 bytes per row) per step
+    uint4 wv[BD_HEAD_AHEAD][BD_HEAD_TILES];
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-        const int mm = 4 * (lane >> 4) + r, nn = n0 + l16;
-        if (mm < B && nn < V) logits[(size_t)mm * V + nn] = acc[r];
+    for (int s = 0; s < BD_HEAD_AHEAD; s++)
+#pragma unroll
+        for (int i = 0; i < BD_HEAD_TILES; i++) wv[s][i] = wrow[i][4 * min(s, steps - 1)];
+    f32x4_t acc[BD_HEAD_TILES];
+#pragma unroll
+    for (int i = 0; i < BD_HEAD_TILES; i++) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < steps; s0 += BD_HEAD_AHEAD) {
+#pragma unroll
+        for (int s = 0; s < BD_HEAD_AHEAD; s++) {
+            const int st = s0 + s;
+            if (st < steps) {
+                const uint4 h = yh[4 * st], lo = yl[4 * st];
+                const int nx = 4 * min(st + BD_HEAD_AHEAD, steps - 1);   // the step BD_HEAD_AHEAD on
+#pragma unroll
+                for (int i = 0; i < BD_HEAD_TILES; i++) {
+                    const bd_bf16x8_t bw = __builtin_bit_cast(bd_bf16x8_t, wv[s][i]);
+                    wv[s][i] = wrow[i][nx];
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bd_bf16x8_t, h), bw, acc[i], 0, 0, 0);
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bd_bf16x8_t, lo), bw, acc[i], 0, 0, 0);
+                }
+            }
+        }
     }
+    // acc[i][r] = logits[row 4 (l / 16) + r][column n0 + 16 i + l % 16]
+#pragma unroll
+    for (int i = 0; i < BD_HEAD_TILES; i++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int mm = 4 * (lane >> 4) + r, nn = n0 + 16 * i + l16;
+            if (mm < B && nn < V) logits[(size_t)mm * V + nn] = acc[i][r];
+        }
 }
 
 // First index of the maximum of each row of logits [B][V].
@@ -708,7 +728,7 @@ extern "C" int atlas_decode_batch(const atlas_model* m, const int32_t* d_tokens,
     ATLAS_KLAUNCH(bd_final_norm_kernel, dim3(B), dim3(1024), 0, st, w.X, m->g_final, d, m->eps, w.p1h, w.p1l, w.ld1);
     ATLAS_LAUNCH_CHECK("bd_final_norm_kernel");
     float* logits = d_logits ? d_logits : w.logits;
-    const int head_blocks = (m->vocab + 16 * BD_HEAD_WAVES - 1) / (16 * BD_HEAD_WAVES);
+    const int head_blocks = (m->vocab + 16 * BD_HEAD_TILES * BD_HEAD_WAVES - 1) / (16 * BD_HEAD_TILES * BD_HEAD_WAVES);
     prof_mark("bd_lm_head", st);
     ATLAS_KLAUNCH(bd_head_kernel, dim3(head_blocks), dim3(64 * BD_HEAD_WAVES), 0, st, w.p1h, w.p1l, w.ld1, B,
                   m->lm_head, m->vocab, d, logits);

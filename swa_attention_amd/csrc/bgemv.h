@@ -4,20 +4,23 @@
 
 namespace atlas {
 
-// A few activation vectors x[v] (v < B) of K columns as 24-bit block fixed point:
-// per block of 128 columns, s = 2^e and integers n = rint(x / s) with |n| <= 127 * 2^16,
-// split into balanced digits n = 65536 h + 256 m + l (h, m, l int8). Planes [3][rows][ldq]
-// (h, m, l) with the bytes of every 8 columns stored in the order 0,2,4,6,1,3,5,7, and
-// per (vector, block): sy = sum of (256 h + m), sl = sum of l, sx = s. Columns past K up
-// to ldq (a multiple of 128) hold zero digits.
+// A few activation vectors x[v] (v < 8) of K columns as 24-bit block fixed point: per
+// block of 128 columns, s = 2^e and integers n = rint(x / s) with |n| <= 127 * 2^16,
+// split into balanced digits n = 65536 h + 256 m + l (h, m, l int8). The digits are
+// stored in the order the batched GEMV's MFMA B operand takes them, 4 KB per block:
+// fragment (block b, k-step u of the block, MFMA j) is 64 lanes x 16 bytes at
+// ((b * 2 + u) * 2 + j) * 1024, lane 16 q + c holding columns 32 q + 16 u .. + 15 of the
+// block (the bytes of every 8 columns in the order 0,2,4,6,1,3,5,7) of plane
+// (16 j + c) / 8 of vector (16 j + c) % 8; the slots of plane 3 and of absent vectors
+// are never written (the GEMV does not load them). Per (vector, block): sy = sum of
+// (256 h + m), sl = sum of l, sx = s.
 struct BQ {
     int8_t* p;
-    size_t pstride;   // bytes between planes
-    int ldq;          // bytes per vector row
+    int ldq;          // K rounded up to a multiple of 128 (the encoded width)
     int* sy;
     int* sl;
     float* sx;
-    int nbs;          // blocks per vector row of sy, sl, sx
+    int nbs;          // blocks per vector row of sy, sl, sx (ldq / 128)
 };
 
 constexpr int BG_MAX_B = 8;          // vectors per launch
@@ -92,10 +95,14 @@ __device__ __forceinline__ void bq_encode_row16(const float x[8], const BQ& q, i
     }
     sy = row16_sum_i(sy);
     sl = row16_sum_i(sl);
-    int8_t* base = q.p + (size_t)v * q.ldq + col0;
-    *reinterpret_cast<uint2*>(base) = make_uint2(H[0], H[1]);
-    *reinterpret_cast<uint2*>(base + q.pstride) = make_uint2(M[0], M[1]);
-    *reinterpret_cast<uint2*>(base + 2 * q.pstride) = make_uint2(L[0], L[1]);
+    // columns 8 j16 .. + 7 of the block (j16 = lane in the row): k-step u = (j16 / 2) % 2,
+    // lane quarter q = j16 / 4, byte half j16 % 2 of the 16-byte fragment slot; plane P of
+    // vector v sits in slot 8 P + v (MFMA (8 P + v) / 16, column (8 P + v) % 16)
+    const int j16 = threadIdx.x & 15, u = (j16 >> 1) & 1, qq = j16 >> 2;
+    int8_t* base = q.p + (size_t)blk * 4096 + u * 2048 + (size_t)qq * 256 + 8 * (j16 & 1);
+    *reinterpret_cast<uint2*>(base + v * 16) = make_uint2(H[0], H[1]);             // slot v: MFMA 0
+    *reinterpret_cast<uint2*>(base + (8 + v) * 16) = make_uint2(M[0], M[1]);       // slot 8 + v: MFMA 0
+    *reinterpret_cast<uint2*>(base + 1024 + v * 16) = make_uint2(L[0], L[1]);      // slot 16 + v: MFMA 1
     if ((threadIdx.x & 15) == 0) {
         const size_t o = (size_t)v * q.nbs + blk;
         q.sy[o] = sy;

@@ -9,7 +9,8 @@
 // (a mask and a shift per code word: low nibbles are a word's columns 0,2,4,6, high
 // nibbles 1,3,5,7) and B = 16 columns of activation digits: columns 0-7 of the first
 // MFMA are the h digits of vectors 0-7, columns 8-15 their m digits, columns 0-7 of the
-// second the l digits (see BQ). Per 128-column block and row the three digit sums are
+// second the l digits (see BQ: the encoders store them fragment by fragment, so each
+// B operand is one contiguous kilobyte). Per 128-column block and row the three digit sums are
 // exact in int32; with Y = 256 sum(c h) + sum(c m) and L = sum(c l),
 //   sum((c - z) n) = 256 (Y - z sy) + (L - z sl)
 // is formed from two exact integers and one f32 fma, then scaled by s_w s_x into the
@@ -33,18 +34,17 @@ namespace atlas {
 typedef int bg_i32x4 __attribute__((ext_vector_type(4)));
 
 size_t bq_bytes(int rows, int K) {
-    const int ldq = (int)align_up((size_t)K, 128), nb = ldq / 128;
-    return align_up((size_t)3 * rows * ldq, 256) + 3 * align_up((size_t)rows * nb * 4, 256);
+    const int nb = (K + 127) / 128;
+    return (size_t)nb * 4096 + 3 * align_up((size_t)rows * nb * 4, 256);
 }
 
 BQ bq_carve(void* base, int rows, int K) {
     BQ q{};
-    q.ldq = (int)align_up((size_t)K, 128);
-    q.nbs = q.ldq / 128;
+    q.nbs = (K + 127) / 128;
+    q.ldq = q.nbs * 128;
     char* b = (char*)base;
     q.p = (int8_t*)b;
-    q.pstride = (size_t)rows * q.ldq;
-    size_t off = align_up((size_t)3 * rows * q.ldq, 256);
+    const size_t off = (size_t)q.nbs * 4096;
     const size_t sb = align_up((size_t)rows * q.nbs * 4, 256);
     q.sy = (int*)(b + off);
     q.sl = (int*)(b + off + sb);
@@ -149,8 +149,7 @@ __global__ __launch_bounds__(512) void bgemv_kernel(BgemvArgs a) {
 #pragma unroll
                 for (int j = 0; j < 2; j++) {
                     const int idx = 16 * j + c, pl = idx >> 3, vec = idx & 7;
-                    const int8_t* src = a.x.p + (size_t)min(pl, 2) * a.x.pstride + (size_t)min(vec, B - 1) * a.x.ldq +
-                                        min(kc0 + 128 * tt, a.x.ldq - 128) + 32 * q + 16 * u;
+                    const int8_t* src = a.x.p + (size_t)((blk0 + tt) * 2 + u) * 2048 + j * 1024 + 16 * lane;
                     bf[2 * t + u][j] = bg_i32x4{0, 0, 0, 0};
                     if (pl < 3 && vec < B && t < nb) bf[2 * t + u][j] = *reinterpret_cast<const bg_i32x4*>(src);
                 }
