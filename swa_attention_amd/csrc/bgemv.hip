@@ -96,6 +96,7 @@ struct BgemvArgs {
     int B, K, group;
     int NBT;                // blocks of 128 columns (the last may hold 64)
     int NB, CB, S, TPB;     // blocks per chunk, waves (chunks) per block, K splits, tiles per block
+    int NBy;                // > 0: waves 4-7 take chunks of NBy blocks, waves 0-3 of NB (CB = 8)
     BgemvOut o0, o1;
 };
 
@@ -126,8 +127,12 @@ __global__ __launch_bounds__(512) void bgemv_kernel(BgemvArgs a) {
     const int c = lane & 15, q = lane >> 4;
     const int split = (int)blockIdx.x % a.S, tb = (int)blockIdx.x / a.S;
     const int chunk = split * a.CB + w;
-    const int blk0 = chunk * NB;                       // first block of the chunk
-    const int nb = max(0, min(NB, a.NBT - blk0));      // blocks of this wave (0: idle wave)
+    // first block and length of this wave's chunk. With NBy > 0 the older wave of each
+    // SIMD (waves 0-3, served first by the memory system) takes the longer chunk, so that
+    // the two waves of a SIMD finish together
+    const int w4 = w & 3;
+    const int blk0 = a.NBy ? split * 4 * (NB + a.NBy) + (w < 4 ? w4 * NB : 4 * NB + w4 * a.NBy) : chunk * NB;
+    const int nb = max(0, min(a.NBy && w >= 4 ? a.NBy : NB, a.NBT - blk0));   // blocks of this wave
     const int kc0 = blk0 * 128;
     const bool tail = (a.K & 127) != 0 && blk0 + nb == a.NBT;   // its last block holds 64 columns
     const int Ttot = a.T0 + a.T1;
@@ -280,6 +285,7 @@ bool bgemv_supported(const W4View& W, int group) {
 
 struct BgShape {
     int NBT, NB, CB, S;
+    int NBy = 0;   // > 0: chunks of NB blocks for waves 0-3 and NBy for waves 4-7 (CB = 8)
 };
 
 // Waves per SIMD that the registers of a chunk of NB blocks allow (at the stage counts
@@ -306,6 +312,20 @@ static BgShape bg_shape(int K, int tiles) {
     static const int wide[6] = {6, 5, 4, 3, 2, 1}, narrow_short[6] = {4, 3, 2, 6, 5, 1},
                      narrow_long[6] = {6, 4, 3, 2, 5, 1};
     const bool is_wide = tiles >= 1024;
+    if (is_wide && sh.NBT % 40 == 0 && sh.NBT / 40 <= 1) {   // 6 + 4 blocks per SIMD's wave pair
+        sh.NB = 6;
+        sh.NBy = 4;
+        sh.CB = 8;
+        sh.S = sh.NBT / 40;
+        return sh;
+    }
+    if (!is_wide && K > 8192 && sh.NBT % 36 == 0) {   // 5 + 4 blocks per SIMD's wave pair, K split
+        sh.NB = 5;
+        sh.NBy = 4;
+        sh.CB = 8;
+        sh.S = sh.NBT / 36;
+        return sh;
+    }
     const int* order = is_wide ? wide : (K <= 8192 ? narrow_short : narrow_long);
     for (int i = 0; i < 6; i++) {
         const int nb = order[i];
@@ -378,6 +398,7 @@ int launch_bgemv(const W4View& W0, int group, const W4View* W1, const BQ& x, int
     a.group = group;
     a.NBT = sh.NBT;
     a.NB = sh.NB;
+    a.NBy = sh.NBy;
     a.CB = sh.CB;
     a.S = sh.S;
     a.TPB = bg_tiles_per_block(a.T0 + a.T1, a.S, a.CB, a.NB);
