@@ -309,6 +309,9 @@ def measure_prefill(args, dm, cm, m, dev, wl_name):
     out = {"workload": name, "tokens": n, "ttft_ms": round(ms, 2), "reps": args.prefill_reps,
            "tokens_per_s": round(n / (ms * 1e-3), 1),
            "algorithmic_tflop": round(flops / 1e12, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "dtype": ("int8 matrix cores for the W4 projections (activations as 24-bit fixed point per row and "
+                     "group of 128 in three int8 digit planes, exact int32 sums, f32 accumulation); bf16 matrix "
+                     "cores for attention with hi/lo operand planes (about 16 significant bits per product)"),
            "mfma_frac_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     dom = "pf_gemm_gate_up"
     if dom in prof:
@@ -569,6 +572,14 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "dtype_detail": (
+            "W4 projections: activations as 24-bit block fixed point per 32 columns, exact integer dot "
+            "products with the 4-bit codes, f32 accumulation; attention, norms and the bf16 lm_head in f32"
+            if B == 1 else
+            "W4 projections: activations as 24-bit block fixed point per 128 columns in three int8 digit "
+            "planes on the int8 matrix cores (exact int32 digit sums), f32 accumulation; attention and norms "
+            "in f32; bf16 lm_head with activations as bf16 hi/lo planes" if B <= 8 else
+            "W4 projections on bf16 matrix cores with activations as bf16 hi/lo planes (16 significant bits)"),
         "data": "synthetic",
         "config": {"workload": wl.name, "layers": m.n_layers, "context": wl.n_cached, "batch": B,
                    "weights": (f"int4 group-{m.group}, {'bf16' if m.scale_dtype else 'f16'} scales, "
