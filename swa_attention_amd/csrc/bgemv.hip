@@ -85,9 +85,12 @@ int launch_bq_encode(const float* X, int ldx, int B, int K, const BQ& q, hipStre
 
 constexpr int BG_NBM = 6;   // blocks of 128 columns per wave chunk, at most (template NB)
 // tiles in flight per wave (register stages): four, three for 6-block chunks (whose
-// fourth stage would not fit in 256 registers)
+// fourth stage would not fit in 256 registers); two for waves of at most BG_SHORT_TPB
+// tiles, whose first loads are most of their work (a deeper ring only makes the
+// launch's opening burst larger)
 template <int NB>
 constexpr int bg_stages() { return NB >= 6 ? 3 : 4; }
+constexpr int BG_SHORT_TPB = 4;
 
 struct BgemvArgs {
     W4View W0, W1;
@@ -120,7 +123,7 @@ __device__ __forceinline__ uint32_t bg_bcast16(uint32_t v) {   // lane SRC of ea
     return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x10 | (SRC << 5));
 }
 
-template <int NB>
+template <int NB, int NS>
 __global__ __launch_bounds__(512) void bgemv_kernel(BgemvArgs a) {
     extern __shared__ float4 s_part[];   // [TPB][CB][64]
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -247,7 +250,6 @@ __global__ __launch_bounds__(512) void bgemv_kernel(BgemvArgs a) {
     // multiplied. Every load is issued (past the last tile they re-read its addresses,
     // from L2), so the compiler can count the loads in flight and waits only for the
     // oldest stage.
-    constexpr int NS = bg_stages<NB>();
     BgStage<NB> S[NS];
 #pragma unroll
     for (int k = 0; k < NS - 1; k++) load(k, S[k]);
@@ -377,6 +379,19 @@ static int bg_tiles_per_block(int Ttot, int S, int CB, int NB) {
     return best;
 }
 
+template <int NB, int NS>
+static int bg_launch(const BgemvArgs& a, int blocks, size_t lds, hipStream_t st) {
+    static bool attr_set = false;   // per instantiation: LDS partials above 64 KB
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void*)bgemv_kernel<NB, NS>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                160 * 1024) != hipSuccess)
+            return fail(ATLAS_ERR_HIP, "bgemv: LDS attribute");
+        attr_set = true;
+    }
+    ATLAS_KLAUNCH((bgemv_kernel<NB, NS>), dim3(blocks), dim3(64 * a.CB), lds, st, a);
+    return ATLAS_OK;
+}
+
 int launch_bgemv(const W4View& W0, int group, const W4View* W1, const BQ& x, int B, const BgemvOut& o0,
                  const BgemvOut* o1, hipStream_t st, const char* label) {
     ATLAS_CHECK_SHAPE(B >= 1 && B <= BG_MAX_B, "batched GEMV: B=%d", B);
@@ -407,17 +422,15 @@ int launch_bgemv(const W4View& W0, int group, const W4View* W1, const BQ& x, int
     const int blocks = a.S * ((a.T0 + a.T1 + a.TPB - 1) / a.TPB);
     const size_t lds = (size_t)a.TPB * a.CB * 64 * sizeof(float4);
     prof_mark(label, st);
+    const bool short_run = a.TPB <= BG_SHORT_TPB;
     switch (a.NB) {
 #define BGL(nb_)                                                                                           \
     case nb_: {                                                                                            \
-        static bool attr_set = false;                                                                      \
-        if (!attr_set) {                                                                                   \
-            if (hipFuncSetAttribute((const void*)bgemv_kernel<nb_>, hipFuncAttributeMaxDynamicSharedMemorySize, \
-                                    160 * 1024) != hipSuccess)                                             \
-                return fail(ATLAS_ERR_HIP, "bgemv: LDS attribute");                                        \
-            attr_set = true;                                                                               \
+        if (short_run) {                                                                                   \
+            if (int rc_ = bg_launch<nb_, 2>(a, blocks, lds, st)) return rc_;                               \
+        } else if (int rc_ = bg_launch<nb_, bg_stages<nb_>()>(a, blocks, lds, st)) {                       \
+            return rc_;                                                                                    \
         }                                                                                                  \
-        ATLAS_KLAUNCH(bgemv_kernel<nb_>, dim3(blocks), dim3(64 * a.CB), lds, st, a);                       \
         break;                                                                                             \
     }
         BGL(1) BGL(2) BGL(3) BGL(4) BGL(5) BGL(6)
