@@ -129,6 +129,34 @@ def test_batch_full_size_swa_layer():
         assert err < TOL
 
 
+def test_batch_full_size_4_layers_8_sequences_bf16_ring():
+    """The config-10 format at full size: four layers [SWA, SWA, SWA, full] of the 32B
+    shape, bf16 KV with window rings, eight sequences at 16,384 down to 5,884 cached
+    positions (the int8 matrix-core projections at their largest batch, the full layer
+    over 16K keys, rings wrapped). Each sequence's last hidden state against the
+    oracle, and each layer's new key and value in that sequence's ring slot."""
+    dev = device()
+    m = W.bf16_ring_kv(W.olmo3_32b(model_id=10, n_layers=4))
+    wl = W.Workload("olmo3-32b-4-layers-bf16kv-ring-batch8", m, seed=0, n_cached=16384, t_max=16385,
+                    use_tokens=True, batch=8, batch_gap=1500)
+    announce("batched decode, 4 full-size layers, 8 sequences, bf16 KV rings, 16K")
+    dm, ws, _, _, _, hid = _run_batch(wl, dev, hidden=True)
+    assert ops.atlas_device_status(ws) == 0
+    refs = R.run_decode_batch(wl, keep_kv=True)
+    for b, ref in enumerate(refs):
+        err = normwise(hid[b].cpu().numpy(), ref["y"])
+        print(f"sequence {b} at {wl.seq_cached(b)}: normwise {err:.2e}")
+        assert err < TOL
+        pos = wl.seq_cached(b)
+        import oracle as O
+        for l, L in enumerate(dm.layers):
+            slot = pos % L.k_cache.shape[2] if m.layer_types[l] == W.SWA else pos
+            k, v = ref["kv"][l]
+            hk, hv = O.round_bf16(k.reshape(m.hkv, -1)), O.round_bf16(v.reshape(m.hkv, -1))
+            assert _close_kv(L.k_cache[b][:, slot].cpu().numpy(), hk), (b, l)
+            assert _close_kv(L.v_cache[b][:, slot].cpu().numpy(), hv), (b, l)
+
+
 def test_batch_bad_position_sets_status_and_spares_the_cache():
     dev = device()
     wl = _tiny_batch(0, False, batch=2, gap=10, model_id=52)
