@@ -533,8 +533,11 @@ struct KvRegs<true> {
 // than the extra loads gain; 16 streams per block, two blocks per CU, already keep 32
 // keys (32 KB) in flight per CU.
 constexpr int ATTN_KV_STAGES = 2;
-// A bf16 key and value take half the registers of f32 ones.
-constexpr int ATTN_KV_STAGES_BF16 = 3;
+// A bf16 key and value take half the registers of f32 ones: the ring holds two pairs of
+// keys, and each online-softmax update takes a pair (one rescale of the accumulators per
+// two keys, which trims the VALU work per key where that work, not HBM, sets the pace).
+constexpr int ATTN_KV_STAGES_BF16 = 2;
+constexpr int ATTN_KEYS_PER_STEP_BF16 = 2;
 constexpr int ATTN_WAVES = ATTN_THREADS / 64;
 constexpr int ATTN_STREAMS = 4 * ATTN_WAVES;                        // 16-lane key streams per block
 constexpr int ATTN_SSQ_REGS = ATTN_SSQ_MAX_BLOCKS / ATTN_THREADS;   // sums-of-squares partials per thread
@@ -637,11 +640,15 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
             r.v1 = __builtin_nontemporal_load(vp + 1);
         }
     };
-    // ring of NS keys per stream; the first NS-1 are in flight during the prologue
+    // ring of NS steps of KP keys per stream; the first NS-1 steps are in flight during
+    // the prologue
     constexpr int NS = KVB ? ATTN_KV_STAGES_BF16 : ATTN_KV_STAGES;
-    KvRegs<KVB> rkv[NS];
+    constexpr int KP = KVB ? ATTN_KEYS_PER_STEP_BF16 : 1;
+    KvRegs<KVB> rkv[NS][KP];
 #pragma unroll
-    for (int k = 0; k < NS - 1; k++) load_kv(stream + ATTN_STREAMS * k, rkv[k]);
+    for (int k = 0; k < NS - 1; k++)
+#pragma unroll
+        for (int e = 0; e < KP; e++) load_kv(stream + ATTN_STREAMS * (k * KP + e), rkv[k][e]);
     // (keys past the stream's last one are clamped loads of valid rows, never consumed)
 
     if (FUSED) {
@@ -725,52 +732,72 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
 #pragma unroll
         for (int i = 0; i < 8; i++) acc[h][i] = 0.f;
     }
-    // This stream's keys are stream, stream + ATTN_STREAMS, ... (< cnt): nks of them. The ring holds
-    // ATTN_KV_STAGES keys; each step loads the key ATTN_KV_STAGES-1 ahead and consumes
-    // the oldest. Whole groups of ATTN_KV_STAGES keys run with unconditional (clamped)
+    // This stream's keys are stream, stream + ATTN_STREAMS, ... (< cnt): nks of them, in
+    // nst steps of KP keys. The ring holds NS steps; each step loads the step NS-1 ahead
+    // and consumes the oldest. Whole groups of NS steps run with unconditional (clamped)
     // loads so that the compiler's wait counting stays exact; the remainder is already
     // loaded. The new token's key and value come from LDS (the cache write above may
     // still be in flight).
     const int nks = cnt > stream ? (cnt - stream + ATTN_STREAMS - 1) / ATTN_STREAMS : 0;
-    auto consume = [&](int slot, int idx) {
-        const int j = k0 + stream + ATTN_STREAMS * idx;
-        float kx[8], vx[8];
-        rkv[slot].unpack(kx, vx);
-        if (FUSED && j == pos) {
+    const int nst = (nks + KP - 1) / KP;
+    auto consume = [&](int slot, int st) {
+        float kx[KP][8], vx[KP][8];
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
-                kx[e] = s_kn[8 * sub + e];
-                vx[e] = s_vn[8 * sub + e];
+        for (int e = 0; e < KP; e++) {
+            rkv[slot][e].unpack(kx[e], vx[e]);
+            if (FUSED && k0 + stream + ATTN_STREAMS * (st * KP + e) == pos) {
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    kx[e][i] = s_kn[8 * sub + i];
+                    vx[e][i] = s_vn[8 * sub + i];
+                }
             }
         }
 #pragma unroll
         for (int h = 0; h < G; h++) {
-            float dsum = 0.f;
+            float sc[KP], mn = mh[h];
 #pragma unroll
-            for (int e = 0; e < 8; e++) dsum = fmaf(q[h][e], kx[e], dsum);
-            const float sc = row16_sum(dsum) * a.scale;
-            const float mn = fmaxf(mh[h], sc);
+            for (int e = 0; e < KP; e++) {
+                float dsum = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; i++) dsum = fmaf(q[h][i], kx[e][i], dsum);
+                sc[e] = row16_sum(dsum) * a.scale;
+                if (KP > 1 && st * KP + e >= nks) sc[e] = -INFINITY;   // past the stream's last key
+                mn = fmaxf(mn, sc[e]);
+            }
             const float c = __expf(mh[h] - mn);
-            const float p = __expf(sc - mn);
-            lh[h] = fmaf(lh[h], c, p);
+            float p[KP], psum = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; e++) acc[h][e] = fmaf(acc[h][e], c, p * vx[e]);
+            for (int e = 0; e < KP; e++) {
+                p[e] = __expf(sc[e] - mn);
+                psum += p[e];
+            }
+            lh[h] = fmaf(lh[h], c, psum);
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                float t = p[KP - 1] * vx[KP - 1][i];
+#pragma unroll
+                for (int e = KP - 2; e >= 0; e--) t = fmaf(p[e], vx[e][i], t);
+                acc[h][i] = fmaf(acc[h][i], c, t);
+            }
             mh[h] = mn;
         }
     };
-    int ik = 0;
-    for (; ik + NS <= nks; ik += NS) {
+    int it = 0;
+    for (; it + NS <= nst; it += NS) {
 #pragma unroll
         for (int k = 0; k < NS; k++) {
             const int slot = (k + NS - 1) % NS;
-            load_kv(stream + ATTN_STREAMS * min(ik + k + NS - 1, nks - 1), rkv[slot]);
+#pragma unroll
+            for (int e = 0; e < KP; e++)
+                load_kv(stream + ATTN_STREAMS * min((it + k + NS - 1) * KP + e, nks - 1), rkv[slot][e]);
             __builtin_amdgcn_sched_barrier(0);
-            consume(k, ik + k);
+            consume(k, it + k);
         }
     }
 #pragma unroll
     for (int k = 0; k < NS - 1; k++)
-        if (ik + k < nks) consume(k, ik + k);
+        if (it + k < nst) consume(k, it + k);
     // combine the four streams of the wave (lanes l, l^16, l^32, l^48)
 #pragma unroll
     for (int h = 0; h < G; h++) {
