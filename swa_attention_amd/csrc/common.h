@@ -49,9 +49,11 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // row mirror: every lane ends with its row's total), then two lane-xor exchanges
 // across rows.
 
+// Every control used here reads a valid lane for every lane; bound_ctrl with a zero old
+// value lets the compiler fold the move into the consuming add or max (v_add_f32_dpp).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ float row16_sum(float v) {

@@ -528,6 +528,9 @@ struct KvRegs<true> {
     }
 };
 
+// 2^x on the hardware exponential (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Keys in flight per 16-lane stream: 1 (a ring of two). Deeper rings (2 and 4 keys) were
 // slower on both layer types: their registers (256 with spills at 4 keys) cost more
 // than the extra loads gain; 16 streams per block, two blocks per CU, already keep 32
@@ -719,11 +722,14 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
         __syncthreads();
     }
 
+    // scores in base-2 units: q carries the softmax scale and log2(e), so each
+    // exponential is one exp2; the partial's maximum goes back to natural units
+    const float qs = a.scale * 1.4426950408889634f;
     float q[G][8];
 #pragma unroll
     for (int h = 0; h < G; h++)
 #pragma unroll
-        for (int i = 0; i < 8; i++) q[h][i] = s_q[h][8 * sub + i];
+        for (int i = 0; i < 8; i++) q[h][i] = s_q[h][8 * sub + i] * qs;
     float mh[G], lh[G], acc[G][8];
 #pragma unroll
     for (int h = 0; h < G; h++) {
@@ -761,15 +767,15 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
                 float dsum = 0.f;
 #pragma unroll
                 for (int i = 0; i < 8; i++) dsum = fmaf(q[h][i], kx[e][i], dsum);
-                sc[e] = row16_sum(dsum) * a.scale;
+                sc[e] = row16_sum(dsum);
                 if (KP > 1 && st * KP + e >= nks) sc[e] = -INFINITY;   // past the stream's last key
                 mn = fmaxf(mn, sc[e]);
             }
-            const float c = __expf(mh[h] - mn);
+            const float c = exp2_fast(mh[h] - mn);
             float p[KP], psum = 0.f;
 #pragma unroll
             for (int e = 0; e < KP; e++) {
-                p[e] = __expf(sc[e] - mn);
+                p[e] = exp2_fast(sc[e] - mn);
                 psum += p[e];
             }
             lh[h] = fmaf(lh[h], c, psum);
@@ -803,7 +809,7 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
     for (int h = 0; h < G; h++) {
         // lane-swap butterflies (v_permlane16/32_swap): register moves, not LDS permutes
         const float M = xor32_max(xor16_max(mh[h]));
-        const float w = (M == -INFINITY) ? 0.f : __expf(mh[h] - M);
+        const float w = (M == -INFINITY) ? 0.f : exp2_fast(mh[h] - M);
         const float l = xor32_sum(xor16_sum(lh[h] * w));
 #pragma unroll
         for (int e = 0; e < 8; e++) acc[h][e] = xor32_sum(xor16_sum(acc[h][e] * w));
@@ -825,14 +831,14 @@ __global__ __launch_bounds__(ATTN_THREADS, ATTN_WAVES <= 4 && G <= 5 ? 2 : 1) vo
         float l = 0.f, o = 0.f;
 #pragma unroll
         for (int w = 0; w < ATTN_WAVES; w++) {
-            const float e = (s_wm[w][h] == -INFINITY) ? 0.f : __expf(s_wm[w][h] - M);
+            const float e = (s_wm[w][h] == -INFINITY) ? 0.f : exp2_fast(s_wm[w][h] - M);
             l = fmaf(s_wl[w][h], e, l);
             o = fmaf(s_wacc[w][h][dd], e, o);
         }
         float* dst = part0 + ((size_t)h * a.S + s) * ATTN_PART_F;
         dst[2 + dd] = o;
         if (dd == 0) {
-            dst[0] = M;
+            dst[0] = M * 0.6931471805599453f;
             dst[1] = l;
         }
     }
