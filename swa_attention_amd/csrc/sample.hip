@@ -41,6 +41,8 @@ constexpr int SMP_BINS = 1024, SMP_SHIFT = 20;
 // runs on), so the atomics of different XCDs never contend for one address.
 constexpr int SMP_COPIES = 8;
 constexpr int SMP_CAND_LDS = 4096;         // candidates staged in LDS by the draw (more: from memory)
+constexpr int SMP_PF = 2;                  // slice elements per thread loaded ahead (a slice of 512 in one round)
+constexpr int SMP_CAND_PF = 16;            // candidates per slice the draw loads with the counts
 constexpr double SMP_FIX = 4294967296.0;   // 2^32: mass units per unit of e (e <= 1)
 static_assert(SMP_THREADS == SMP_BLOCKS, "sample_exp_kernel reduces one block maximum per thread");
 
@@ -63,16 +65,32 @@ struct SampleWs {
 };
 
 // Block-wide exclusive scan of one 64-bit value per thread (blockDim.x a multiple of 64,
-// at most 1024), with the total: shuffle scans inside each wave, then the wave totals
+// at most 1024), with the total: DPP scans inside each wave, then the wave totals
 // through LDS. wsum: LDS [16]. Every thread of the block calls it.
+// A DPP move of a 64-bit value (both halves); lanes without a source, and the rows
+// outside ROWS, read 0.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWS, 0xF, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWS, 0xF, true);
+    return ((uint64_t)hi << 32) | lo;
+}
+// Inclusive scan over the 64 lanes of a wave: shifts by 1, 2, 4 and 8 lanes inside each
+// row of 16 (row_shr), then each row's last lane broadcast to the next row (row_bcast:15
+// into rows 1 and 3) and lane 31 to the upper half (row_bcast:31 into rows 2 and 3).
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t x) {
+    x += dpp_u64<0x111>(x);
+    x += dpp_u64<0x112>(x);
+    x += dpp_u64<0x114>(x);
+    x += dpp_u64<0x118>(x);
+    x += dpp_u64<0x142, 0xA>(x);
+    x += dpp_u64<0x143, 0xC>(x);
+    return x;
+}
+
 __device__ uint64_t block_excl_scan(uint64_t v, uint64_t* wsum, uint64_t* total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    uint64_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint64_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const uint64_t x = wave_incl_scan_u64(v);
     if (lane == 63) wsum[w] = x;
     __syncthreads();
     uint64_t off = 0, tot = 0;
@@ -130,6 +148,15 @@ __global__ __launch_bounds__(SMP_THREADS) void sample_exp_kernel(const float* __
                                                                  SampleWs w) {
     __shared__ float red[SMP_THREADS];
     __shared__ unsigned long long hb[SMP_BINS];
+    // the slice's first logits are loaded with the slice maxima (they do not depend on
+    // the maximum), so both loads are in flight together
+    const int sl = smp_slice(V), i0 = blockIdx.x * sl, i1 = min(V, i0 + sl);
+    float pre[SMP_PF];
+#pragma unroll
+    for (int k = 0; k < SMP_PF; k++) {
+        const int i = i0 + (int)threadIdx.x + k * SMP_THREADS;
+        pre[k] = l[i < i1 ? i : V - 1];   // (a clamped, unused load past the slice)
+    }
     red[threadIdx.x] = w.bmax[threadIdx.x];   // SMP_THREADS == SMP_BLOCKS
     for (int b = threadIdx.x; b < SMP_BINS; b += SMP_THREADS) hb[b] = 0;
     __syncthreads();
@@ -138,14 +165,19 @@ __global__ __launch_bounds__(SMP_THREADS) void sample_exp_kernel(const float* __
         __syncthreads();
     }
     const float M = red[0];
-    const int sl = smp_slice(V), i0 = blockIdx.x * sl, i1 = min(V, i0 + sl);
-    for (int i = i0 + threadIdx.x; i < i1; i += SMP_THREADS) {
-        const float v = expf((l[i] - M) * invT);
+    auto put = [&](int i, float li) {
+        const float v = expf((li - M) * invT);
         const float ev = fminf(v, 1.0f);   // the maximum gives exactly 1
         w.e[i] = ev;
         const uint64_t ms = smp_mass(ev);
         if (ms) atomicAdd(&hb[__float_as_uint(ev) >> SMP_SHIFT], (unsigned long long)ms);
+    };
+#pragma unroll
+    for (int k = 0; k < SMP_PF; k++) {
+        const int i = i0 + (int)threadIdx.x + k * SMP_THREADS;
+        if (i < i1) put(i, pre[k]);
     }
+    for (int i = i0 + threadIdx.x + SMP_PF * SMP_THREADS; i < i1; i += SMP_THREADS) put(i, l[i]);
     __syncthreads();
     uint64_t* dst = w.hist + (size_t)(blockIdx.x % SMP_COPIES) * SMP_BINS;
     for (int b = threadIdx.x; b < SMP_BINS; b += SMP_THREADS)
@@ -161,6 +193,20 @@ __global__ __launch_bounds__(SMP_THREADS) void sample_bin_kernel(int V, double t
     // thread t holds the 4 bins [4 (255 - t), 4 (255 - t) + 4): thread 0 the highest
     constexpr int BPT = SMP_BINS / SMP_THREADS;
     const int b0 = (SMP_THREADS - 1 - t) * BPT;
+    // thread t's consecutive elements [j0, j1) of the slice (below), their first SMP_PF
+    // patterns loaded with the histogram (they do not depend on the bin)
+    const int sl = smp_slice(V), i0 = blockIdx.x * sl, i1 = min(V, i0 + sl);
+    const int per = (sl + SMP_THREADS - 1) / SMP_THREADS;
+    const int j0 = min(i1, i0 + t * per), j1 = min(i1, j0 + per);
+    uint32_t pe[SMP_PF];
+#pragma unroll
+    for (int k = 0; k < SMP_PF; k++) pe[k] = __float_as_uint(w.e[j0 + k < j1 ? j0 + k : V - 1]);
+    auto bits_at = [&](int i) {
+        uint32_t b = 0u;
+#pragma unroll
+        for (int k = 0; k < SMP_PF; k++) b = i == j0 + k ? pe[k] : b;
+        return i - j0 < SMP_PF ? b : __float_as_uint(w.e[i]);
+    };
     uint64_t hv[BPT] = {};
 #pragma unroll
     for (int c = 0; c < SMP_COPIES; c++)
@@ -193,12 +239,9 @@ __global__ __launch_bounds__(SMP_THREADS) void sample_bin_kernel(int V, double t
     }
     // this slice: mass above the bin, and its candidates in index order (thread t takes
     // the consecutive elements [i0 + t * per, i0 + (t + 1) * per) of the slice)
-    const int sl = smp_slice(V), i0 = blockIdx.x * sl, i1 = min(V, i0 + sl);
-    const int per = (sl + SMP_THREADS - 1) / SMP_THREADS;
-    const int j0 = min(i1, i0 + t * per), j1 = min(i1, j0 + per);
     uint64_t cm = 0, nmine = 0;
     for (int i = j0; i < j1; i++) {
-        const uint32_t bits = __float_as_uint(w.e[i]);
+        const uint32_t bits = bits_at(i);
         const uint32_t hbin = bits >> SMP_SHIFT;
         if (hbin > bin) cm += smp_mass_bits(bits);
         nmine += hbin == bin;
@@ -207,7 +250,7 @@ __global__ __launch_bounds__(SMP_THREADS) void sample_bin_kernel(int V, double t
     uint32_t pos = (uint32_t)block_excl_scan(nmine, tmp, &nblk);
     uint2* dst = w.cand + (size_t)blockIdx.x * sl;
     for (int i = j0; i < j1 && nmine; i++) {
-        const uint32_t bits = __float_as_uint(w.e[i]);
+        const uint32_t bits = bits_at(i);
         if ((bits >> SMP_SHIFT) == bin) dst[pos++] = make_uint2((uint32_t)i, bits);
     }
     block_excl_scan(cm, tmp, &blk);   // block sum
@@ -251,11 +294,23 @@ __global__ __launch_bounds__(SMP_DRAW_THREADS) void sample_draw_kernel(DrawArgs 
         return;
     }
     // candidate counts of the slices -> offsets of a dense candidate list. The first
-    // SMP_DRAW_THREADS / SMP_BLOCKS candidates of every slice are loaded with the counts
-    // (thread t: slice t mod 256, rank t / 256), before it is known which exist.
+    // SMP_CAND_PF * SMP_DRAW_THREADS / SMP_BLOCKS candidates of every slice are loaded
+    // with the counts (thread t: slice t mod 256, ranks t / 256 + k * NPRE), before it is
+    // known which exist.
+    constexpr uint32_t NPRE = SMP_DRAW_THREADS / SMP_BLOCKS;
     const int sl = smp_slice(a.V);
     const int pb = t % SMP_BLOCKS, pk = t / SMP_BLOCKS;
-    const uint2 pre = w.cand[(size_t)pb * sl + min(pk, sl - 1)];
+    uint2 pre[SMP_CAND_PF];
+    static_assert(NPRE == 1, "the prefetch takes a slice's first candidates with 16-byte loads");
+    {   // slice regions start at multiples of 4 entries (sl % 4 == 0): 16-byte aligned
+        const uint4* src = reinterpret_cast<const uint4*>(w.cand + (size_t)pb * sl);
+#pragma unroll
+        for (int k = 0; k < SMP_CAND_PF / 2; k++) {
+            const uint4 q = src[min(k, sl / 2 - 1)];
+            pre[2 * k] = make_uint2(q.x, q.y);
+            pre[2 * k + 1] = make_uint2(q.z, q.w);
+        }
+    }
     const uint32_t cnt = t < SMP_BLOCKS ? w.ncand[t] : 0u;
     if (t < SMP_BLOCKS) s_nm[t] = w.certain[t];
     if (t == 0) s_target = w.sel[1];
@@ -280,10 +335,11 @@ __global__ __launch_bounds__(SMP_DRAW_THREADS) void sample_draw_kernel(DrawArgs 
     };
     const bool staged = nc <= (uint32_t)SMP_CAND_LDS;
     if (staged) {
-        constexpr uint32_t NPRE = SMP_DRAW_THREADS / SMP_BLOCKS;
         const uint32_t cb = s_cnt[pb], ob = s_off[pb];
-        if ((uint32_t)pk < cb) s_cand[ob + pk] = pre;
-        for (uint32_t k = pk + NPRE; k < cb; k += NPRE)   // slices with more candidates than were prefetched
+#pragma unroll
+        for (int k = 0; k < SMP_CAND_PF; k++)
+            if ((uint32_t)pk + NPRE * k < cb) s_cand[ob + pk + NPRE * k] = pre[k];
+        for (uint32_t k = pk + NPRE * SMP_CAND_PF; k < cb; k += NPRE)   // slices with more candidates than were prefetched
             s_cand[ob + k] = w.cand[(size_t)pb * sl + k];
     }
     __syncthreads();
