@@ -24,8 +24,11 @@
 //      tau, sums the mass of its slice above that bin (certainly in the nucleus) and
 //      writes the (index, e) of its elements inside the bin, the candidates, to its own
 //      region in index order;
-//   4. sample_draw_kernel (one block): the low 20 bits of tau by radix passes of 8, 8
-//      and 4 bits over the candidates (staged in LDS); each slice's nucleus mass (its
+//   4. sample_draw_kernel (one block): the low 20 bits of tau: bits [19:12] from a
+//      histogram of the candidates that the bin kernel adds up, then the few candidates
+//      with that prefix resolved by one wave (radix passes of 8 and 4 bits over the
+//      candidates when there are many), one thread per slice holding the slice's first
+//      candidates in registers; each slice's nucleus mass (its
 //      certain mass plus its candidates at or above tau); the slice holding the target
 //      u * mass from a scan of the 256 slice masses; the token from a scan inside it.
 #include <cmath>
@@ -40,9 +43,9 @@ constexpr int SMP_BINS = 1024, SMP_SHIFT = 20;
 // The histogram is kept in one copy per XCD (block b adds to copy b mod 8, the XCD it
 // runs on), so the atomics of different XCDs never contend for one address.
 constexpr int SMP_COPIES = 8;
-constexpr int SMP_CAND_LDS = 4096;         // candidates staged in LDS by the draw (more: from memory)
 constexpr int SMP_PF = 2;                  // slice elements per thread loaded ahead (a slice of 512 in one round)
 constexpr int SMP_CAND_PF = 16;            // candidates per slice the draw loads with the counts
+constexpr int SMP_SEL_MAX = 64;            // candidates with tau's 20-bit prefix that one wave resolves
 constexpr double SMP_FIX = 4294967296.0;   // 2^32: mass units per unit of e (e <= 1)
 static_assert(SMP_THREADS == SMP_BLOCKS, "sample_exp_kernel reduces one block maximum per thread");
 
@@ -57,6 +60,7 @@ struct SampleWs {
     int* bidx;
     float* e;                  // [V]
     uint64_t* hist;            // [SMP_COPIES][SMP_BINS] masses by the top 12 bits of e's pattern
+    uint64_t* hist2;           // [SMP_COPIES][256] masses of the candidates by bits [19:12]
     uint64_t* certain;         // [SMP_BLOCKS] nucleus mass above tau's bin, per slice
     uint32_t* ncand;           // [SMP_BLOCKS] candidates of each slice
     uint2* cand;               // [SMP_BLOCKS][slice] (index, bits of e) of each slice's elements
@@ -124,6 +128,8 @@ __global__ __launch_bounds__(SMP_THREADS) void sample_max_kernel(const float* __
     if (clear) {   // the histogram starts at zero
         for (int b = blockIdx.x * SMP_THREADS + threadIdx.x; b < SMP_COPIES * SMP_BINS; b += SMP_BLOCKS * SMP_THREADS)
             w.hist[b] = 0;
+        for (int b = blockIdx.x * SMP_THREADS + threadIdx.x; b < SMP_COPIES * 256; b += SMP_BLOCKS * SMP_THREADS)
+            w.hist2[b] = 0;
     }
     __syncthreads();
     for (int o = SMP_THREADS / 2; o > 0; o >>= 1) {
@@ -249,9 +255,14 @@ __global__ __launch_bounds__(SMP_THREADS) void sample_bin_kernel(int V, double t
     uint64_t nblk, blk;
     uint32_t pos = (uint32_t)block_excl_scan(nmine, tmp, &nblk);
     uint2* dst = w.cand + (size_t)blockIdx.x * sl;
+    unsigned long long* h2 = (unsigned long long*)w.hist2 + (size_t)(blockIdx.x % SMP_COPIES) * 256;
     for (int i = j0; i < j1 && nmine; i++) {
         const uint32_t bits = bits_at(i);
-        if ((bits >> SMP_SHIFT) == bin) dst[pos++] = make_uint2((uint32_t)i, bits);
+        if ((bits >> SMP_SHIFT) == bin) {
+            dst[pos++] = make_uint2((uint32_t)i, bits);
+            // the draw's first radix pass: candidate masses by bits [19:12]
+            atomicAdd(&h2[(bits >> 12) & 0xFFu], (unsigned long long)smp_mass_bits(bits));
+        }
     }
     block_excl_scan(cm, tmp, &blk);   // block sum
     if (t == 0) {
@@ -272,12 +283,10 @@ struct DrawArgs {
 
 __global__ __launch_bounds__(SMP_DRAW_THREADS) void sample_draw_kernel(DrawArgs a) {
     __shared__ unsigned long long h[256];
-    __shared__ unsigned long long s_nm[SMP_BLOCKS];
-    __shared__ uint32_t s_off[SMP_BLOCKS], s_cnt[SMP_BLOCKS];
-    __shared__ uint2 s_cand[SMP_CAND_LDS];
     __shared__ uint64_t tmp[16];
     __shared__ uint64_t s_target, s_lo;
     __shared__ int s_bin, s_blk;
+    __shared__ uint32_t s_k, s_tau, s_sel[SMP_SEL_MAX];
     const int t = threadIdx.x;
     const SampleWs& w = a.w;
     if (a.greedy) {   // first index of the maximum over the slice partials
@@ -293,17 +302,15 @@ __global__ __launch_bounds__(SMP_DRAW_THREADS) void sample_draw_kernel(DrawArgs 
         }
         return;
     }
-    // candidate counts of the slices -> offsets of a dense candidate list. The first
-    // SMP_CAND_PF * SMP_DRAW_THREADS / SMP_BLOCKS candidates of every slice are loaded
-    // with the counts (thread t: slice t mod 256, ranks t / 256 + k * NPRE), before it is
-    // known which exist.
-    constexpr uint32_t NPRE = SMP_DRAW_THREADS / SMP_BLOCKS;
+    // Thread t owns slice t: its candidate count, certain mass and first SMP_CAND_PF
+    // candidates (loaded before it is known which exist; slice regions start at multiples
+    // of 4 entries, so they are 16-byte aligned), and bin 255 - t of the bin kernel's
+    // histogram of the candidates by bits [19:12] (thread 0 the highest).
+    static_assert(SMP_DRAW_THREADS == SMP_BLOCKS, "one thread per slice");
     const int sl = smp_slice(a.V);
-    const int pb = t % SMP_BLOCKS, pk = t / SMP_BLOCKS;
     uint2 pre[SMP_CAND_PF];
-    static_assert(NPRE == 1, "the prefetch takes a slice's first candidates with 16-byte loads");
-    {   // slice regions start at multiples of 4 entries (sl % 4 == 0): 16-byte aligned
-        const uint4* src = reinterpret_cast<const uint4*>(w.cand + (size_t)pb * sl);
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(w.cand + (size_t)t * sl);
 #pragma unroll
         for (int k = 0; k < SMP_CAND_PF / 2; k++) {
             const uint4 q = src[min(k, sl / 2 - 1)];
@@ -311,78 +318,96 @@ __global__ __launch_bounds__(SMP_DRAW_THREADS) void sample_draw_kernel(DrawArgs 
             pre[2 * k + 1] = make_uint2(q.z, q.w);
         }
     }
-    const uint32_t cnt = t < SMP_BLOCKS ? w.ncand[t] : 0u;
-    if (t < SMP_BLOCKS) s_nm[t] = w.certain[t];
-    if (t == 0) s_target = w.sel[1];
-    float u = *a.d_u;
-    uint64_t nc64;
-    const uint32_t off = (uint32_t)block_excl_scan(cnt, tmp, &nc64);
-    if (t < SMP_BLOCKS) {
-        s_off[t] = off;
-        s_cnt[t] = cnt;
+    const uint32_t cb = w.ncand[t];
+    const uint64_t cert = w.certain[t];
+    uint64_t h2own = 0;
+#pragma unroll
+    for (int c = 0; c < SMP_COPIES; c++) h2own += w.hist2[(size_t)c * 256 + 255 - t];
+    if (t == 0) {
+        s_target = w.sel[1];
+        s_k = 0u;
+        s_tau = 0u;
     }
-    __syncthreads();
-    const uint32_t nc = (uint32_t)nc64;
-    // candidate c lives in slice b with s_off[b] <= c < s_off[b + 1] (binary search)
-    auto cand_at = [&](uint32_t c) {
-        int lo = 0, hi = SMP_BLOCKS - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_off[mid] <= c) lo = mid;
-            else hi = mid - 1;
-        }
-        return w.cand[(size_t)lo * sl + (c - s_off[lo])];
-    };
-    const bool staged = nc <= (uint32_t)SMP_CAND_LDS;
-    if (staged) {
-        const uint32_t cb = s_cnt[pb], ob = s_off[pb];
+    float u = *a.d_u;
+    // f(bits) over this slice's candidates: the prefetched ones, then any further ones
+    auto each_cand = [&](auto f) {
 #pragma unroll
         for (int k = 0; k < SMP_CAND_PF; k++)
-            if ((uint32_t)pk + NPRE * k < cb) s_cand[ob + pk + NPRE * k] = pre[k];
-        for (uint32_t k = pk + NPRE * SMP_CAND_PF; k < cb; k += NPRE)   // slices with more candidates than were prefetched
-            s_cand[ob + k] = w.cand[(size_t)pb * sl + k];
-    }
-    __syncthreads();
-    auto cand_get = [&](uint32_t c) { return staged ? s_cand[c] : cand_at(c); };
-    // low 20 bits of tau: radix passes over bits [19:12], [11:4] and [3:0] of the
-    // candidates matching the prefix chosen so far
+            if ((uint32_t)k < cb) f(pre[k].y);
+        for (uint32_t k = SMP_CAND_PF; k < cb; k++) f(w.cand[(size_t)t * sl + k].y);
+    };
+    // low 20 bits of tau. Bits [19:12]: the bin (highest first) where the candidates' mass
+    // from the top reaches the remaining target.
     uint32_t prefix = (uint32_t)w.sel[0];
-    for (int pass = 0; pass < 3; pass++) {
-        const int shift = pass == 0 ? 12 : pass == 1 ? 4 : 0, width = pass == 2 ? 4 : 8;
-        if (t < 256) h[t] = 0;
-        __syncthreads();
-        for (uint32_t c = t; c < nc; c += SMP_DRAW_THREADS) {
-            const uint32_t b = cand_get(c).y;
-            if ((b >> (shift + width)) == prefix)
-                atomicAdd(&h[(b >> shift) & ((1u << width) - 1u)], (unsigned long long)smp_mass_bits(b));
-        }
-        __syncthreads();
-        // the bin (of 2^width, highest first) where the mass from the top reaches the
-        // remaining target; thread t holds bin 255 - t (bins past 2^width are empty)
-        const uint64_t own = t < 256 ? h[255 - t] : 0ull;
-        const uint64_t tg = s_target;
+    {
         uint64_t tot;
-        const uint64_t above = block_excl_scan(own, tmp, &tot);
-        if (above < tg && above + own >= tg) {   // exactly one thread (own > 0)
+        __syncthreads();   // s_target
+        const uint64_t tg = s_target;
+        const uint64_t above = block_excl_scan(h2own, tmp, &tot);
+        if (above < tg && above + h2own >= tg) {   // exactly one thread (h2own > 0)
             s_bin = 255 - t;
             s_target = tg - above;
         }
         __syncthreads();
-        prefix = (prefix << width) | (uint32_t)s_bin;
+        prefix = (prefix << 8) | (uint32_t)s_bin;
     }
-    const uint32_t tau = prefix;
-    // nucleus mass of every slice: its certain mass plus its candidates at or above tau
-    for (uint32_t c = t; c < nc; c += SMP_DRAW_THREADS) {
-        const uint2 cv = cand_get(c);
-        if (cv.y >= tau) atomicAdd(&s_nm[cv.x / (uint32_t)sl], (unsigned long long)smp_mass_bits(cv.y));
-    }
+    // The candidates with this 20-bit prefix (a handful, typically): with at most
+    // SMP_SEL_MAX of them, tau is the largest pattern b among them whose mass at or above
+    // b, C(b), reaches the remaining target (C falls as b rises), one lane per candidate.
+    each_cand([&](uint32_t b) {
+        if ((b >> 12) == prefix) {
+            const uint32_t k = atomicAdd(&s_k, 1u);
+            if (k < (uint32_t)SMP_SEL_MAX) s_sel[k] = b;
+        }
+    });
     __syncthreads();
+    const uint32_t nsel = s_k;
+    uint32_t tau;
+    if (nsel <= (uint32_t)SMP_SEL_MAX) {
+        if (t < (int)nsel) {
+            const uint32_t bj = s_sel[t];
+            uint64_t cge = 0;
+            for (uint32_t i = 0; i < nsel; i++) {
+                const uint32_t bi = s_sel[i];
+                cge += bi >= bj ? smp_mass_bits(bi) : 0ull;
+            }
+            if (cge >= s_target) atomicMax(&s_tau, bj);
+        }
+        __syncthreads();
+        tau = s_tau;
+    } else {   // many equal or close values: radix passes over bits [11:4] and [3:0]
+        for (int pass = 1; pass < 3; pass++) {
+            const int shift = pass == 1 ? 4 : 0, width = pass == 2 ? 4 : 8;
+            h[t] = 0;
+            __syncthreads();
+            each_cand([&](uint32_t b) {
+                if ((b >> (shift + width)) == prefix)
+                    atomicAdd(&h[(b >> shift) & ((1u << width) - 1u)], (unsigned long long)smp_mass_bits(b));
+            });
+            __syncthreads();
+            // thread t holds bin 255 - t (bins past 2^width are empty)
+            const uint64_t own = h[255 - t];
+            const uint64_t tg = s_target;
+            uint64_t tot;
+            const uint64_t above = block_excl_scan(own, tmp, &tot);
+            if (above < tg && above + own >= tg) {   // exactly one thread (own > 0)
+                s_bin = 255 - t;
+                s_target = tg - above;
+            }
+            __syncthreads();
+            prefix = (prefix << width) | (uint32_t)s_bin;
+        }
+        tau = prefix;
+    }
+    // nucleus mass of this slice: its certain mass plus its candidates at or above tau
+    uint64_t nm = cert;
+    each_cand([&](uint32_t b) { nm += b >= tau ? smp_mass_bits(b) : 0ull; });
     uint64_t total;
-    const uint64_t lo_b = block_excl_scan(t < SMP_BLOCKS ? s_nm[t] : 0ull, tmp, &total);
+    const uint64_t lo_b = block_excl_scan(nm, tmp, &total);
     u = u > 0.f ? u : 0.f;                      // u outside [0, 1) is clamped into it
     u = u < 1.f ? u : 0.99999994f;
     const uint64_t tgt = (uint64_t)((double)u * (double)total);   // < total
-    if (t < SMP_BLOCKS && lo_b <= tgt && tgt < lo_b + s_nm[t]) {   // exactly one slice
+    if (lo_b <= tgt && tgt < lo_b + nm) {   // exactly one slice
         s_blk = t;
         s_lo = lo_b;
     }
@@ -424,6 +449,7 @@ static size_t carve_ws(void* base, int V, SampleWs* w) {
     s.bidx = (int*)take((size_t)SMP_BLOCKS * 4);
     s.e = (float*)take((size_t)V * 4);
     s.hist = (uint64_t*)take((size_t)SMP_COPIES * SMP_BINS * 8);
+    s.hist2 = (uint64_t*)take((size_t)SMP_COPIES * 256 * 8);
     s.certain = (uint64_t*)take((size_t)SMP_BLOCKS * 8);
     s.ncand = (uint32_t*)take((size_t)SMP_BLOCKS * 4);
     s.cand = (uint2*)take((size_t)SMP_BLOCKS * smp_slice(V) * 8);
