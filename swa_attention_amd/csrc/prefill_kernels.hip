@@ -428,6 +428,239 @@ __global__ __launch_bounds__(G8_THREADS) void w4_gemm_i8_kernel(GemmArgs a) {
         }
 }
 
+// ---- the int8 GEMM with a ring of LDS stages filled by direct-to-LDS loads ------------------
+//
+// The same product as w4_gemm_i8_kernel on a 64 x 256 tile (mode 1: 128 rows of W0 and the
+// same 128 of W1) with eight waves of 32 x 64, k tiles of 128. Everything a k tile needs
+// (the three A digit planes, the raw 4-bit codes, and per row the scale word, the zero
+// word, q_s and q_sum of the tile's group) is copied from global memory straight into one
+// of GR_STAGES LDS stages by global_load_lds (16 bytes per lane for the planes and codes, 4
+// for the rest): the copies need no registers, so two k tiles stay in flight while a
+// third is multiplied. Each wave waits (vmcnt) for its own copies of the tile about to be
+// used and a block barrier publishes them. The copies are issued from inline assembly,
+// which the compiler does not count; the loop issues no other vector-memory loads, so
+// the waits written here are exact. The codes are unpacked per MFMA fragment (a mask and
+// a shift per word) after their LDS read.
+constexpr int GR_BM = 64, GR_BN = 256, GR_BK = 128, GR_THREADS = 512, GR_STAGES = 3;
+constexpr int GR_A_PLANE = GR_BM * GR_BK;                  // bytes of one digit plane per stage
+constexpr int GR_A_BYTES = 3 * GR_A_PLANE;                 // 24,576
+constexpr int GR_B_BYTES = GR_BN * GR_BK / 2;              // 16,384: 4-bit codes
+constexpr int GR_SMALL = 2 * 4 * GR_BN + 2 * 4 * GR_BM;   // scale and zero words per W row, q_s and q_sum per A row
+constexpr int GR_STAGE = GR_A_BYTES + GR_B_BYTES + GR_SMALL;  // 43,520
+constexpr size_t GR_LDS = (size_t)GR_STAGES * GR_STAGE;       // 130,560
+// copies per stage and wave: A 24 and B 16 instructions of 1 KB over the 8 waves (3 and 2
+// each); the 10 small ones of 256 B (4 scale, 4 zero, q_s, q_sum) by waves 0-4, 2 each
+constexpr int GR_COPIES_BIG = 5, GR_COPIES_SMALL = 2;
+
+// 16 bytes per lane from g into LDS at lds (wave-uniform byte address) + 16 * lane
+__device__ __forceinline__ void gr_copy16(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+// 4 bytes per lane from g into LDS at lds + 4 * lane
+__device__ __forceinline__ void gr_copy4(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+// LDS byte offset of 16-byte chunk c of row r in a plane of 128-byte rows (XOR swizzle
+// over the eight chunks of a row, so that the 16 rows of an MFMA fragment read spread
+// over the banks)
+__device__ __forceinline__ int gr_a_off(int r, int c) { return r * GR_BK + ((c ^ (r & 7)) << 4); }
+// the same for the 64-byte code rows of B (four chunks)
+__device__ __forceinline__ int gr_b_off(int r, int c) { return r * (GR_BK / 2) + ((c ^ ((r >> 1) & 3)) << 4); }
+
+template <int MODE>
+__global__ __launch_bounds__(GR_THREADS) void w4_gemm_i8r_kernel(GemmArgs a) {
+    extern __shared__ __align__(16) int8_t gr_lds[];
+    const int MT = (a.M + GR_BM - 1) / GR_BM;
+    const int NW_ = MODE ? GR_BN / 2 : GR_BN;   // output columns per tile
+    const int NT = (a.N + NW_ - 1) / NW_;
+    const int T = MT * NT, Wk = T * a.ksplit, per = (Wk + 7) / 8;
+    const int Lw = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (Lw >= Wk) return;
+    const int L = Lw % T, split = Lw / T;
+    const int k_lo = split * a.kchunk, k_hi = a.ksplit > 1 ? k_lo + a.kchunk : a.K;
+    const int m0 = (L % MT) * GR_BM, n0 = (L / MT) * NW_;
+    const int KT = (k_hi - k_lo) / GR_BK;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    const int l16 = lane & 15, l4 = lane >> 4;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int8_t*)gr_lds;
+
+    // W row of tile row r (mode 1: rows >= 128 are W1's copy of rows r - 128), clamped
+    auto second = [&](int r) { return MODE && r >= GR_BN / 2; };
+    auto wrow = [&](int r) { return min(n0 + (second(r) ? r - GR_BN / 2 : r), a.N - 1); };
+    auto bcol = [&](int nf) {
+        return MODE ? (nf < 2 ? wn * 32 + 16 * nf : GR_BN / 2 + wn * 32 + 16 * (nf - 2)) : wn * 64 + 16 * nf;
+    };
+
+    // ---- copies of k tile kt into stage st -------------------------------------------------------
+    // A: instruction i (24 per stage, wave w takes 3w..3w+2) covers plane i / 8, rows
+    // 8 (i % 8) .. + 7: lane l -> row 8 (i % 8) + l / 8, LDS chunk l % 8, which holds global
+    // chunk (l % 8) ^ (row & 7). B: instruction i (16, wave w takes 2w, 2w + 1) covers W rows
+    // 16 i .. + 15: lane l -> row 16 i + l / 4, LDS chunk l % 4 holding global chunk
+    // (l % 4) ^ ((row >> 1) & 3). Small: instruction j (waves 0-4, 2 each): j < 4 scale
+    // words of W rows 64 j + lane, 4 <= j < 8 zero words of rows 64 (j - 4) + lane, j = 8
+    // q_s and j = 9 q_sum of A row lane.
+    // N * G is even (checked by the launcher), so the dword holding scale e (of N * G) starts
+    // at e & ~1 and ends inside the table
+    auto issue = [&](int kt, int st) {
+        const int kb = k_lo + kt * GR_BK, g = kb / a.group;
+        const uint32_t sbase = lds0 + (uint32_t)(st * GR_STAGE);
+#pragma unroll
+        for (int q = 0; q < 3; q++) {
+            const int i = 3 * wave + q, p = i >> 3, rb = 8 * (i & 7);
+            const int r = rb + (lane >> 3), c = (lane & 7) ^ (r & 7);
+            const int8_t* plane = p == 0 ? a.q_hi : (p == 1 ? a.q_mid : a.q_lo);
+            const int8_t* src = plane + (size_t)min(m0 + r, a.M - 1) * a.ldq + kb + 16 * c;
+            gr_copy16(src, __builtin_amdgcn_readfirstlane(sbase + p * GR_A_PLANE + rb * GR_BK));
+        }
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            const int i = 2 * wave + q, r = 16 * i + (lane >> 2), c = (lane & 3) ^ ((r >> 1) & 3);
+            const uint32_t* qw = second(r) ? a.W1.qweight : a.W0.qweight;
+            const uint32_t* src = qw + (size_t)wrow(r) * a.W0.KW + kb / 8 + 4 * c;
+            gr_copy16(src, __builtin_amdgcn_readfirstlane(sbase + GR_A_BYTES + 16 * i * (GR_BK / 2)));
+        }
+        if (wave < 5) {
+#pragma unroll
+            for (int q = 0; q < 2; q++) {
+                const int j = 2 * wave + q;
+                const uint32_t dst = sbase + GR_A_BYTES + GR_B_BYTES + 256 * j;
+                const void* src;
+                if (j < 4) {   // the dword holding the 16-bit scale of (row, g)
+                    const int r = 64 * j + lane;
+                    const int e = wrow(r) * a.W0.G + g;
+                    src = (second(r) ? a.W1.scales : a.W0.scales) + (e & ~1);
+                } else if (j < 8) {
+                    const int r = 64 * (j - 4) + lane;
+                    src = second(r) ? a.W1.zeros + (size_t)wrow(r) * a.W1.zstride + (g >> 3)
+                                    : a.W0.zeros + (size_t)wrow(r) * a.W0.zstride + (g >> 3);
+                } else {
+                    const float* base = j == 8 ? a.q_s : a.q_sum;
+                    src = base + (size_t)min(m0 + lane, a.M - 1) * a.ldqs + g;
+                }
+                gr_copy4(src, __builtin_amdgcn_readfirstlane(dst));
+            }
+        }
+    };
+    // wait until this wave's copies of the oldest stage in flight have landed, with
+    // `newer` stages issued after it
+    auto wait_copies = [&](int newer) {
+        if (newer == 0) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        else if (wave < 5) __builtin_amdgcn_s_waitcnt(0x0F70 | (GR_COPIES_BIG + GR_COPIES_SMALL));
+        else __builtin_amdgcn_s_waitcnt(0x0F70 | GR_COPIES_BIG);
+    };
+    static_assert(GR_STAGES == 3 && GR_COPIES_BIG + GR_COPIES_SMALL < 16, "one newer stage fits vmcnt's low bits");
+
+    f32x4_t acc[2][4];
+    i32x4_t ah_acc[2][4], am_acc[2][4], al_acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            ah_acc[i][j] = i32x4_t{0, 0, 0, 0};
+            am_acc[i][j] = i32x4_t{0, 0, 0, 0};
+            al_acc[i][j] = i32x4_t{0, 0, 0, 0};
+        }
+
+    issue(0, 0);
+    if (KT > 1) issue(1, 1);
+    for (int kt = 0; kt < KT; kt++) {
+        const int st = kt % GR_STAGES, kb = k_lo + kt * GR_BK;
+        wait_copies(kt + 1 < KT ? 1 : 0);
+        __syncthreads();   // tile kt is in LDS, and every wave is done with tile kt - 1
+        if (kt + 2 < KT) issue(kt + 2, (kt + 2) % GR_STAGES);   // into the stage of tile kt - 1
+        const int8_t* sA = gr_lds + st * GR_STAGE;
+        const int8_t* sB = sA + GR_A_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < GR_BK / 64; ks++) {
+            i32x4_t ah[2], am[2], al[2], b[4];
+#pragma unroll
+            for (int mf = 0; mf < 2; mf++) {
+                const int row = wm * 32 + mf * 16 + l16, o = gr_a_off(row, 4 * ks + l4);
+                ah[mf] = *reinterpret_cast<const i32x4_t*>(sA + o);
+                am[mf] = *reinterpret_cast<const i32x4_t*>(sA + GR_A_PLANE + o);
+                al[mf] = *reinterpret_cast<const i32x4_t*>(sA + 2 * GR_A_PLANE + o);
+            }
+#pragma unroll
+            for (int nf = 0; nf < 4; nf++) {
+                // codes of columns 64 ks + 16 l4 .. + 15: 8 bytes at byte 32 ks + 8 l4 of the row
+                const int row = bcol(nf) + l16;
+                const uint2 w = *reinterpret_cast<const uint2*>(sB + gr_b_off(row, 2 * ks + (l4 >> 1)) + 8 * (l4 & 1));
+                b[nf] = i32x4_t{(int)(w.x & 0x0F0F0F0Fu), (int)((w.x >> 4) & 0x0F0F0F0Fu), (int)(w.y & 0x0F0F0F0Fu),
+                                (int)((w.y >> 4) & 0x0F0F0F0Fu)};
+            }
+#pragma unroll
+            for (int mf = 0; mf < 2; mf++)
+#pragma unroll
+                for (int nf = 0; nf < 4; nf++) {
+                    ah_acc[mf][nf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[mf], b[nf], ah_acc[mf][nf], 0, 0, 0);
+                    am_acc[mf][nf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(am[mf], b[nf], am_acc[mf][nf], 0, 0, 0);
+                    al_acc[mf][nf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al[mf], b[nf], al_acc[mf][nf], 0, 0, 0);
+                }
+        }
+        if ((kb + GR_BK) % a.group == 0) {   // group ends: combine the digit sums, scale and add
+            const int g = kb / a.group;
+            const uint32_t* sSw = reinterpret_cast<const uint32_t*>(sB + GR_B_BYTES);
+            const uint32_t* sZ = sSw + GR_BN;
+            const float* sSx = reinterpret_cast<const float*>(sZ + GR_BN);
+            const float* sSX = sSx + GR_BM;
+#pragma unroll
+            for (int nf = 0; nf < 4; nf++) {
+                const int n = bcol(nf) + l16;
+                const int e = wrow(n) * a.W0.G + g;
+                const uint32_t sw_word = sSw[n];
+                const float sw = scale_to_f32((uint16_t)((e & 1) ? sw_word >> 16 : sw_word & 0xFFFFu), a.W0.scale_dtype);
+                const int z = a.W0.zsym ? 8 : (int)((sZ[n] >> ((g & 7) * 4)) & 15u);
+#pragma unroll
+                for (int mf = 0; mf < 2; mf++) {
+#pragma unroll
+                    for (int r = 0; r < 4; r++) {
+                        const int m = wm * 32 + mf * 16 + 4 * l4 + r;
+                        const float I = fmaf(65536.f, (float)ah_acc[mf][nf][r],
+                                             fmaf(256.f, (float)am_acc[mf][nf][r], (float)al_acc[mf][nf][r])) -
+                                        (float)z * sSX[m];
+                        acc[mf][nf][r] = fmaf(I, sw * sSx[m], acc[mf][nf][r]);
+                    }
+                    ah_acc[mf][nf] = i32x4_t{0, 0, 0, 0};
+                    am_acc[mf][nf] = i32x4_t{0, 0, 0, 0};
+                    al_acc[mf][nf] = i32x4_t{0, 0, 0, 0};
+                }
+            }
+        }
+    }
+
+    // epilogue: D[row 4*l4 + r][col l16] of each fragment
+#pragma unroll
+    for (int mf = 0; mf < 2; mf++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int row = m0 + wm * 32 + mf * 16 + 4 * l4 + r;
+            if (row >= a.M) continue;
+            if (MODE == 0) {
+#pragma unroll
+                for (int nf = 0; nf < 4; nf++) {
+                    const int col = n0 + bcol(nf) + l16;
+                    if (col < a.N) a.C[split * a.c_split + (size_t)row * a.ldc + col] = acc[mf][nf][r];
+                }
+            } else {
+#pragma unroll
+                for (int f = 0; f < 2; f++) {
+                    const int col = n0 + wn * 32 + 16 * f + l16;
+                    if (col < a.N) {
+                        const float gt = acc[mf][f][r], up = acc[mf][f + 2][r];
+                        uint32_t hi, lo;
+                        pf_split(gt / (1.0f + __expf(-gt)) * up, hi, lo);
+                        a.z_hi[(size_t)row * a.ldz + col] = (uint16_t)hi;
+                        a.z_lo[(size_t)row * a.ldz + col] = (uint16_t)lo;
+                    }
+                }
+            }
+        }
+}
+
 // Group-scaled 24-bit fixed point digits of A = hi + lo (bf16 planes) for
 // w4_gemm_i8_kernel. Each lane takes 8 consecutive columns, group/8 lanes of one wave a
 // group (group <= 512): s is the power of two with max|x| / Q8_MAX <= s (so x / s is
@@ -1179,6 +1412,23 @@ int launch_w4_gemm(const GemmArgs& a, int mode, hipStream_t st, const char* labe
                               a.ldqs >= a.K / a.group && a.q_mid && a.q_lo && a.q_s && a.q_sum,
                           "int8 GEMM needs a group of 128, 256 or 512 dividing K, K ranges of whole 128-column "
                           "tiles, ldq %% 16 == 0");
+        const bool same_w = mode == 0 || (a.W1.G == a.W0.G && a.W1.KW == a.W0.KW && a.W1.zsym == a.W0.zsym &&
+                                          a.W1.zstride == a.W0.zstride && a.W1.scale_dtype == a.W0.scale_dtype);
+        if (same_w && ((size_t)a.N * a.W0.G) % 2 == 0) {   // the LDS-ring kernel
+            static bool attr_set[2] = {false, false};
+            const void* fn = mode ? (const void*)w4_gemm_i8r_kernel<1> : (const void*)w4_gemm_i8r_kernel<0>;
+            if (!attr_set[mode]) {
+                if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)GR_LDS) != hipSuccess)
+                    return fail(ATLAS_ERR_HIP, "int8 GEMM: LDS attribute");
+                attr_set[mode] = true;
+            }
+            const int NWr = mode ? GR_BN / 2 : GR_BN;
+            const int Tr = ((a.M + GR_BM - 1) / GR_BM) * ((a.N + NWr - 1) / NWr) * a.ksplit, br = 8 * ((Tr + 7) / 8);
+            if (mode == 0) ATLAS_KLAUNCH((w4_gemm_i8r_kernel<0>), dim3(br), dim3(GR_THREADS), GR_LDS, st, a);
+            else ATLAS_KLAUNCH((w4_gemm_i8r_kernel<1>), dim3(br), dim3(GR_THREADS), GR_LDS, st, a);
+            ATLAS_LAUNCH_CHECK("w4_gemm_i8r_kernel");
+            return ATLAS_OK;
+        }
         const int T8 = MT * NT * a.ksplit, b8 = 8 * ((T8 + 7) / 8);
         if (mode == 0) ATLAS_KLAUNCH((w4_gemm_i8_kernel<0>), dim3(b8), dim3(G8_THREADS), 0, st, a);
         else ATLAS_KLAUNCH((w4_gemm_i8_kernel<1>), dim3(b8), dim3(G8_THREADS), 0, st, a);
