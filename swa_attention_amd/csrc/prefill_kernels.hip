@@ -572,6 +572,7 @@ __global__ __launch_bounds__(GR_THREADS) void w4_gemm_i8r_kernel(GemmArgs a) {
         wait_copies(kt + 1 < KT ? 1 : 0);
         __syncthreads();   // tile kt is in LDS, and every wave is done with tile kt - 1
         if (kt + 2 < KT) issue(kt + 2, (kt + 2) % GR_STAGES);   // into the stage of tile kt - 1
+        const bool gstart = kb % a.group == 0;
         const int8_t* sA = gr_lds + st * GR_STAGE;
         const int8_t* sB = sA + GR_A_BYTES;
 #pragma unroll
@@ -596,37 +597,49 @@ __global__ __launch_bounds__(GR_THREADS) void w4_gemm_i8r_kernel(GemmArgs a) {
             for (int mf = 0; mf < 2; mf++)
 #pragma unroll
                 for (int nf = 0; nf < 4; nf++) {
-                    ah_acc[mf][nf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[mf], b[nf], ah_acc[mf][nf], 0, 0, 0);
-                    am_acc[mf][nf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(am[mf], b[nf], am_acc[mf][nf], 0, 0, 0);
-                    al_acc[mf][nf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al[mf], b[nf], al_acc[mf][nf], 0, 0, 0);
+                    if (ks == 0 && gstart) {   // a group's first products start from zero
+                        const i32x4_t z4 = {0, 0, 0, 0};
+                        ah_acc[mf][nf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[mf], b[nf], z4, 0, 0, 0);
+                        am_acc[mf][nf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(am[mf], b[nf], z4, 0, 0, 0);
+                        al_acc[mf][nf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al[mf], b[nf], z4, 0, 0, 0);
+                    } else {
+                        ah_acc[mf][nf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[mf], b[nf], ah_acc[mf][nf], 0, 0, 0);
+                        am_acc[mf][nf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(am[mf], b[nf], am_acc[mf][nf], 0, 0, 0);
+                        al_acc[mf][nf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al[mf], b[nf], al_acc[mf][nf], 0, 0, 0);
+                    }
                 }
         }
         if ((kb + GR_BK) % a.group == 0) {   // group ends: combine the digit sums, scale and add
+            // I = 65536 sum(c h) + 256 sum(c m) + sum(c l) - z sum(v), with the first two
+            // sums joined in int32 (|256 sum(c h) + sum(c m)| < 2^26) before one conversion
             const int g = kb / a.group;
             const uint32_t* sSw = reinterpret_cast<const uint32_t*>(sB + GR_B_BYTES);
             const uint32_t* sZ = sSw + GR_BN;
             const float* sSx = reinterpret_cast<const float*>(sZ + GR_BN);
             const float* sSX = sSx + GR_BM;
+            f32x4_t sx[2], sX[2];   // rows wm * 32 + mf * 16 + 4 l4 + r
+#pragma unroll
+            for (int mf = 0; mf < 2; mf++) {
+                const int mb = wm * 32 + mf * 16 + 4 * l4;
+                sx[mf] = *reinterpret_cast<const f32x4_t*>(sSx + mb);
+                sX[mf] = *reinterpret_cast<const f32x4_t*>(sSX + mb);
+            }
 #pragma unroll
             for (int nf = 0; nf < 4; nf++) {
                 const int n = bcol(nf) + l16;
                 const int e = wrow(n) * a.W0.G + g;
                 const uint32_t sw_word = sSw[n];
                 const float sw = scale_to_f32((uint16_t)((e & 1) ? sw_word >> 16 : sw_word & 0xFFFFu), a.W0.scale_dtype);
-                const int z = a.W0.zsym ? 8 : (int)((sZ[n] >> ((g & 7) * 4)) & 15u);
+                const float nz = -(float)(a.W0.zsym ? 8 : (int)((sZ[n] >> ((g & 7) * 4)) & 15u));
 #pragma unroll
                 for (int mf = 0; mf < 2; mf++) {
 #pragma unroll
                     for (int r = 0; r < 4; r++) {
-                        const int m = wm * 32 + mf * 16 + 4 * l4 + r;
-                        const float I = fmaf(65536.f, (float)ah_acc[mf][nf][r],
-                                             fmaf(256.f, (float)am_acc[mf][nf][r], (float)al_acc[mf][nf][r])) -
-                                        (float)z * sSX[m];
-                        acc[mf][nf][r] = fmaf(I, sw * sSx[m], acc[mf][nf][r]);
+                        const int y = ah_acc[mf][nf][r] * 256 + am_acc[mf][nf][r];
+                        float I = fmaf(256.f, (float)y, (float)al_acc[mf][nf][r]);
+                        I = fmaf(nz, sX[mf][r], I);
+                        acc[mf][nf][r] = fmaf(I * sw, sx[mf][r], acc[mf][nf][r]);
                     }
-                    ah_acc[mf][nf] = i32x4_t{0, 0, 0, 0};
-                    am_acc[mf][nf] = i32x4_t{0, 0, 0, 0};
-                    al_acc[mf][nf] = i32x4_t{0, 0, 0, 0};
                 }
             }
         }
