@@ -504,24 +504,34 @@ __global__ __launch_bounds__(GR_THREADS) void w4_gemm_i8r_kernel(GemmArgs a) {
     // q_s and j = 9 q_sum of A row lane.
     // N * G is even (checked by the launcher), so the dword holding scale e (of N * G) starts
     // at e & ~1 and ends inside the table
+    // the k-independent part of each plane and code copy's source (column k_lo)
+    const int8_t* a_src[3];
+    uint32_t a_dst[3];
+#pragma unroll
+    for (int q = 0; q < 3; q++) {
+        const int i = 3 * wave + q, p = i >> 3, rb = 8 * (i & 7);
+        const int r = rb + (lane >> 3), c = (lane & 7) ^ (r & 7);
+        const int8_t* plane = p == 0 ? a.q_hi : (p == 1 ? a.q_mid : a.q_lo);
+        a_src[q] = plane + (size_t)min(m0 + r, a.M - 1) * a.ldq + k_lo + 16 * c;
+        a_dst[q] = (uint32_t)(p * GR_A_PLANE + rb * GR_BK);
+    }
+    const int8_t* b_src[2];
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        const int i = 2 * wave + q, r = 16 * i + (lane >> 2), c = (lane & 3) ^ ((r >> 1) & 3);
+        const uint32_t* qw = second(r) ? a.W1.qweight : a.W0.qweight;
+        b_src[q] = reinterpret_cast<const int8_t*>(qw + (size_t)wrow(r) * a.W0.KW + k_lo / 8 + 4 * c);
+    }
     auto issue = [&](int kt, int st) {
         const int kb = k_lo + kt * GR_BK, g = kb / a.group;
         const uint32_t sbase = lds0 + (uint32_t)(st * GR_STAGE);
 #pragma unroll
-        for (int q = 0; q < 3; q++) {
-            const int i = 3 * wave + q, p = i >> 3, rb = 8 * (i & 7);
-            const int r = rb + (lane >> 3), c = (lane & 7) ^ (r & 7);
-            const int8_t* plane = p == 0 ? a.q_hi : (p == 1 ? a.q_mid : a.q_lo);
-            const int8_t* src = plane + (size_t)min(m0 + r, a.M - 1) * a.ldq + kb + 16 * c;
-            gr_copy16(src, __builtin_amdgcn_readfirstlane(sbase + p * GR_A_PLANE + rb * GR_BK));
-        }
+        for (int q = 0; q < 3; q++)
+            gr_copy16(a_src[q] + kt * GR_BK, __builtin_amdgcn_readfirstlane(sbase + a_dst[q]));
 #pragma unroll
-        for (int q = 0; q < 2; q++) {
-            const int i = 2 * wave + q, r = 16 * i + (lane >> 2), c = (lane & 3) ^ ((r >> 1) & 3);
-            const uint32_t* qw = second(r) ? a.W1.qweight : a.W0.qweight;
-            const uint32_t* src = qw + (size_t)wrow(r) * a.W0.KW + kb / 8 + 4 * c;
-            gr_copy16(src, __builtin_amdgcn_readfirstlane(sbase + GR_A_BYTES + 16 * i * (GR_BK / 2)));
-        }
+        for (int q = 0; q < 2; q++)
+            gr_copy16(b_src[q] + kt * (GR_BK / 2),
+                      __builtin_amdgcn_readfirstlane(sbase + GR_A_BYTES + 16 * (2 * wave + q) * (GR_BK / 2)));
         if (wave < 5) {
 #pragma unroll
             for (int q = 0; q < 2; q++) {
