@@ -320,7 +320,7 @@ def measure_prefill(args, dm, cm, m, dev, wl_name):
         ach = f / (tot / cnt * 1e-3) / 1e12
         if m.group % 128 == 0 and m.group <= 512 and m.d % m.group == 0:
             # groups of 128-512: products on the int8 matrix cores, priced at the int8 peak
-            out["roofline"] = {"bound": "mfma", "kernel": "w4_gemm_i8_kernel<1> (gate+up, SwiGLU)",
+            out["roofline"] = {"bound": "mfma", "kernel": "w4_gemm_i8r_kernel<1> (gate+up, SwiGLU)",
                                "achieved": round(ach, 1), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                                "frac": round(ach / PEAK_INT8_TOPS, 4), "avg_launch_us": round(tot / cnt * 1e3, 1),
                                "note": "algorithmic multiply-adds x 2; the three int8 digit planes of the "
