@@ -467,7 +467,9 @@ __device__ __forceinline__ int gr_a_off(int r, int c) { return r * GR_BK + ((c ^
 // the same for the 64-byte code rows of B (four chunks)
 __device__ __forceinline__ int gr_b_off(int r, int c) { return r * (GR_BK / 2) + ((c ^ ((r >> 1) & 3)) << 4); }
 
-template <int MODE>
+// G128: the group is one k tile (128 columns), so every tile starts and ends a group and the
+// epilogue is straight-line code the compiler can interleave with the MFMAs.
+template <int MODE, bool G128>
 __global__ __launch_bounds__(GR_THREADS) void w4_gemm_i8r_kernel(GemmArgs a) {
     extern __shared__ __align__(16) int8_t gr_lds[];
     const int MT = (a.M + GR_BM - 1) / GR_BM;
@@ -582,7 +584,7 @@ __global__ __launch_bounds__(GR_THREADS) void w4_gemm_i8r_kernel(GemmArgs a) {
         wait_copies(kt + 1 < KT ? 1 : 0);
         __syncthreads();   // tile kt is in LDS, and every wave is done with tile kt - 1
         if (kt + 2 < KT) issue(kt + 2, (kt + 2) % GR_STAGES);   // into the stage of tile kt - 1
-        const bool gstart = kb % a.group == 0;
+        const bool gstart = G128 || kb % a.group == 0;
         const int8_t* sA = gr_lds + st * GR_STAGE;
         const int8_t* sB = sA + GR_A_BYTES;
 #pragma unroll
@@ -619,7 +621,7 @@ __global__ __launch_bounds__(GR_THREADS) void w4_gemm_i8r_kernel(GemmArgs a) {
                     }
                 }
         }
-        if ((kb + GR_BK) % a.group == 0) {   // group ends: combine the digit sums, scale and add
+        if (G128 || (kb + GR_BK) % a.group == 0) {   // group ends: combine the digit sums, scale and add
             // I = 65536 sum(c h) + 256 sum(c m) + sum(c l) - z sum(v), with the first two
             // sums joined in int32 (|256 sum(c h) + sum(c m)| < 2^26) before one conversion
             const int g = kb / a.group;
@@ -1438,17 +1440,23 @@ int launch_w4_gemm(const GemmArgs& a, int mode, hipStream_t st, const char* labe
         const bool same_w = mode == 0 || (a.W1.G == a.W0.G && a.W1.KW == a.W0.KW && a.W1.zsym == a.W0.zsym &&
                                           a.W1.zstride == a.W0.zstride && a.W1.scale_dtype == a.W0.scale_dtype);
         if (same_w && ((size_t)a.N * a.W0.G) % 2 == 0) {   // the LDS-ring kernel
-            static bool attr_set[2] = {false, false};
-            const void* fn = mode ? (const void*)w4_gemm_i8r_kernel<1> : (const void*)w4_gemm_i8r_kernel<0>;
-            if (!attr_set[mode]) {
-                if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)GR_LDS) != hipSuccess)
+            static bool attr_set[4] = {false, false, false, false};
+            const int g128 = a.group == GR_BK ? 1 : 0, v = 2 * mode + g128;
+            const void* fns[4] = {(const void*)w4_gemm_i8r_kernel<0, false>, (const void*)w4_gemm_i8r_kernel<0, true>,
+                                  (const void*)w4_gemm_i8r_kernel<1, false>, (const void*)w4_gemm_i8r_kernel<1, true>};
+            if (!attr_set[v]) {
+                if (hipFuncSetAttribute(fns[v], hipFuncAttributeMaxDynamicSharedMemorySize, (int)GR_LDS) != hipSuccess)
                     return fail(ATLAS_ERR_HIP, "int8 GEMM: LDS attribute");
-                attr_set[mode] = true;
+                attr_set[v] = true;
             }
             const int NWr = mode ? GR_BN / 2 : GR_BN;
             const int Tr = ((a.M + GR_BM - 1) / GR_BM) * ((a.N + NWr - 1) / NWr) * a.ksplit, br = 8 * ((Tr + 7) / 8);
-            if (mode == 0) ATLAS_KLAUNCH((w4_gemm_i8r_kernel<0>), dim3(br), dim3(GR_THREADS), GR_LDS, st, a);
-            else ATLAS_KLAUNCH((w4_gemm_i8r_kernel<1>), dim3(br), dim3(GR_THREADS), GR_LDS, st, a);
+            switch (v) {
+                case 0: ATLAS_KLAUNCH((w4_gemm_i8r_kernel<0, false>), dim3(br), dim3(GR_THREADS), GR_LDS, st, a); break;
+                case 1: ATLAS_KLAUNCH((w4_gemm_i8r_kernel<0, true>), dim3(br), dim3(GR_THREADS), GR_LDS, st, a); break;
+                case 2: ATLAS_KLAUNCH((w4_gemm_i8r_kernel<1, false>), dim3(br), dim3(GR_THREADS), GR_LDS, st, a); break;
+                default: ATLAS_KLAUNCH((w4_gemm_i8r_kernel<1, true>), dim3(br), dim3(GR_THREADS), GR_LDS, st, a); break;
+            }
             ATLAS_LAUNCH_CHECK("w4_gemm_i8r_kernel");
             return ATLAS_OK;
         }
