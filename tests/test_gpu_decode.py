@@ -273,7 +273,8 @@ def test_prefill_continues_a_filled_cache():
 
 @pytest.mark.parametrize("n_tokens,n_cached,fmt", [(40, 20, "g128"), (1, 0, "g128"), (1, 30, "g128"),
                                                    (17, 5, "g128"), (40, 20, "card"), (17, 5, "card"),
-                                                   (23, 9, "g64")])
+                                                   (23, 9, "g64"), (23, 9, "g256"), (40, 20, "g512"),
+                                                   (17, 5, "g256-sym-bf16")])
 def test_prefill_split_k_shapes_match_oracle(n_tokens, n_cached, fmt):
     """A 2-layer stack with d = 1,024 (8 q / 2 KV heads) and dff = 2,048: half of the qkv,
     o and down GEMMs' K is whole 128-column groups, so the prefill splits their K in two
@@ -281,7 +282,9 @@ def test_prefill_split_k_shapes_match_oracle(n_tokens, n_cached, fmt):
     128 this runs the int8 kernel; in the card's recipe (symmetric, group 32, bf16
     scales) and with groups of 64 it runs the bf16 kernel's split path. Against the
     oracle: 40 positions after 20 cached; a one-token prompt on an empty and on a filled
-    cache (one GEMM row); 17 positions, one past a 16-row tile; 23 after 9."""
+    cache (one GEMM row); 17 positions, one past a 16-row tile; 23 after 9. Groups of 256
+    and 512 (asymmetric f16 scales, and symmetric codes with bf16 scales) run the int8
+    kernel with groups spanning several 128-column k tiles."""
     dev = device()
     m = W.Model(d=1024, hq=8, hkv=2, hd=128, dff=2048, n_layers=2, layer_types=[W.SWA, W.FULL], window=64,
                 model_id=61)
@@ -289,6 +292,12 @@ def test_prefill_split_k_shapes_match_oracle(n_tokens, n_cached, fmt):
         W.card_format(m)
     elif fmt == "g64":
         m.group = 64
+    elif fmt == "g256":
+        m.group = 256
+    elif fmt == "g512":
+        m.group = 512
+    elif fmt == "g256-sym-bf16":
+        m.group, m.scale_dtype, m.symmetric = 256, 1, True
     m.vocab = 1000
     wl = W.Workload("tiny-split-k", m, seed=0, n_cached=n_cached, t_max=96, use_tokens=True, final_head=True)
     announce(f"prefill 2-layer d=1024 stack ({fmt}), {n_tokens} tokens after {n_cached} cached (split-K GEMMs)")
