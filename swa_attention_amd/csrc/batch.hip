@@ -64,6 +64,46 @@ struct BdRopeArgs {
 // One block per sequence; the summed row stays in LDS (dynamic, ld floats) between the
 // norms and the rotation, and every global load of the partials is issued before the
 // first barrier.
+// The sum of `parts` partial rows (N columns from p, N = 4 or 8), in partial order. With
+// up to 8 partials the count is a template argument: every load is issued before the
+// first add, so their latencies overlap; more partials are summed in a loop.
+template <int P, int N>
+__device__ __forceinline__ void bd_sum_fixed(const float* p, size_t stride, float (&out)[N]) {
+    float4 a[P][N / 4];
+#pragma unroll
+    for (int q = 0; q < P; q++)
+#pragma unroll
+        for (int c = 0; c < N / 4; c++) a[q][c] = *reinterpret_cast<const float4*>(p + (size_t)q * stride + 4 * c);
+#pragma unroll
+    for (int c = 0; c < N / 4; c++) {
+        float4 s = a[0][c];
+#pragma unroll
+        for (int q = 1; q < P; q++) {
+            s.x += a[q][c].x; s.y += a[q][c].y; s.z += a[q][c].z; s.w += a[q][c].w;
+        }
+        out[4 * c] = s.x; out[4 * c + 1] = s.y; out[4 * c + 2] = s.z; out[4 * c + 3] = s.w;
+    }
+}
+template <int N>
+__device__ __forceinline__ void bd_sum(const float* p, int parts, size_t stride, float (&out)[N]) {
+    switch (parts) {
+        case 1: bd_sum_fixed<1, N>(p, stride, out); return;
+        case 2: bd_sum_fixed<2, N>(p, stride, out); return;
+        case 3: bd_sum_fixed<3, N>(p, stride, out); return;
+        case 4: bd_sum_fixed<4, N>(p, stride, out); return;
+        case 5: bd_sum_fixed<5, N>(p, stride, out); return;
+        case 6: bd_sum_fixed<6, N>(p, stride, out); return;
+        case 7: bd_sum_fixed<7, N>(p, stride, out); return;
+        case 8: bd_sum_fixed<8, N>(p, stride, out); return;
+        default: break;
+    }
+#pragma unroll
+    for (int c = 0; c < N; c++) out[c] = p[c];
+    for (int q = 1; q < parts; q++)
+#pragma unroll
+        for (int c = 0; c < N; c++) out[c] += p[(size_t)q * stride + c];
+}
+
 __global__ __launch_bounds__(1024) void bd_rope_kernel(BdRopeArgs a) {
     constexpr int D = 128;
     extern __shared__ float s_row[];   // [ld]
@@ -215,15 +255,10 @@ __global__ __launch_bounds__(256) void bd_swiglu_kernel(const float* gp, const f
 
 // Sum of `parts` partial rows at 8 consecutive columns, in split order.
 __device__ __forceinline__ void bd_sum8(const float* p, int parts, size_t stride, float out[8]) {
-    float4 s0 = *reinterpret_cast<const float4*>(p), s1 = *reinterpret_cast<const float4*>(p + 4);
-    for (int q = 1; q < parts; q++) {
-        const float4 a = *reinterpret_cast<const float4*>(p + (size_t)q * stride);
-        const float4 b = *reinterpret_cast<const float4*>(p + (size_t)q * stride + 4);
-        s0.x += a.x; s0.y += a.y; s0.z += a.z; s0.w += a.w;
-        s1.x += b.x; s1.y += b.y; s1.z += b.z; s1.w += b.w;
-    }
-    out[0] = s0.x; out[1] = s0.y; out[2] = s0.z; out[3] = s0.w;
-    out[4] = s1.x; out[5] = s1.y; out[6] = s1.z; out[7] = s1.w;
+    float v[8];
+    bd_sum(p, parts, stride, v);
+#pragma unroll
+    for (int c = 0; c < 8; c++) out[c] = v[c];
 }
 
 // X[t] += g * A[t] / rms(A[t]) (A[t] the sum of `parts` partial rows), then X[t] encoded
