@@ -452,7 +452,12 @@ constexpr size_t GR_LDS = (size_t)GR_STAGES * GR_STAGE;       // 130,560
 // each); the 10 small ones of 256 B (4 scale, 4 zero, q_s, q_sum) by waves 0-4, 2 each
 constexpr int GR_COPIES_BIG = 5, GR_COPIES_SMALL = 2;
 
-// 16 bytes per lane from g into LDS at lds (wave-uniform byte address) + 16 * lane
+// 16 bytes per lane from g into LDS at lds (wave-uniform byte address) + 16 * lane. The
+// copies take their LDS address from m0, which each statement sets itself; m0 cannot be
+// declared clobbered in inline assembly, so the kernel that uses these must not rely on m0
+// anywhere else (w4_gemm_i8r_kernel does not: its code has no other m0 access). The
+// compiler's own global_load_lds would be waited for with vmcnt(0) before every LDS read,
+// which empties the ring; it is used for that reason only through these statements.
 __device__ __forceinline__ void gr_copy16(const void* g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
 }
