@@ -628,7 +628,8 @@ __global__ __launch_bounds__(GR_THREADS) void w4_gemm_i8r_kernel(GemmArgs a) {
         }
         if (G128 || (kb + GR_BK) % a.group == 0) {   // group ends: combine the digit sums, scale and add
             // I = 65536 sum(c h) + 256 sum(c m) + sum(c l) - z sum(v), with the first two
-            // sums joined in int32 (|256 sum(c h) + sum(c m)| < 2^26) before one conversion
+            // sums joined in int32 before one conversion (|256 sum(c h) + sum(c m)| < 2^28
+            // for groups of up to 512 columns: c <= 15, |h| <= 127, |m| <= 128)
             const int g = kb / a.group;
             const uint32_t* sSw = reinterpret_cast<const uint32_t*>(sB + GR_B_BYTES);
             const uint32_t* sZ = sSw + GR_BN;

@@ -43,7 +43,7 @@ constexpr int SMP_BINS = 1024, SMP_SHIFT = 20;
 // The histogram is kept in one copy per XCD (block b adds to copy b mod 8, the XCD it
 // runs on), so the atomics of different XCDs never contend for one address.
 constexpr int SMP_COPIES = 8;
-constexpr int SMP_PF = 2;                  // slice elements per thread loaded ahead (a slice of 512 in one round)
+constexpr int SMP_PF = 2;                  // slice elements per thread loaded ahead (slices of up to 512 at once)
 constexpr int SMP_CAND_PF = 16;            // candidates per slice the draw loads with the counts
 constexpr int SMP_SEL_MAX = 64;            // candidates with tau's 20-bit prefix that one wave resolves
 constexpr double SMP_FIX = 4294967296.0;   // 2^32: mass units per unit of e (e <= 1)
