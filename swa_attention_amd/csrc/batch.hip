@@ -318,14 +318,35 @@ __global__ __launch_bounds__(256) void bd_swiglu_q_kernel(const float* gp, const
 
 // ---- lm_head over the batch: bf16 matrix cores, weights streamed once --------------------------
 
-// logits[m][n] = sum_k W[n][k] y[m][k] for m < B (<= 16), n < V. One wave per
-// BD_HEAD_TILES x 16 vocabulary rows, on v_mfma_f32_16x16x32_bf16 with y = hi + lo: lane l
-// holds the A operand y[l % 16][k0 + 8 (l / 16) ..+8] and the B operands W[n0 + 16 i +
-// l % 16][same k], each one 16-byte load, so the weights go from HBM to the matrix core
-// without LDS, and one load of y (from L2) serves BD_HEAD_TILES weight tiles. The weight
-// loads run BD_HEAD_AHEAD steps of 32 columns ahead of the products (plain loads: with
-// 16 rows x 64 bytes per wave instruction they stream faster than nontemporal ones).
-constexpr int BD_HEAD_WAVES = 4, BD_HEAD_TILES = 4, BD_HEAD_AHEAD = 4;
+// logits[m][n] = sum_k W[n][k] y[m][k] for m < B (<= 16), n < V (d % 64 == 0). One wave
+// per BD_HEAD_TILES x 16 vocabulary rows, on v_mfma_f32_16x16x32_bf16 with y = hi + lo.
+//
+// Loads. A wave instruction that reads 16 rows x 64 bytes (the MFMA operand layout: lane
+// l holds row l % 16, bytes 16 (l / 16)) streams this matrix at about 3.7 TB/s, one that
+// reads 8 whole 128-byte lines at about 5.1 (5.4 nontemporal), measured with loads alone
+// on this grid. So a step takes one 128-byte line (64 columns) of each of a tile's 16
+// rows in two nontemporal loads: X, rows 0-7, and Y, rows 8-15, lane l reading row
+// l % 8 (+8 for Y) at bytes 16 (l / 8) of the line. Rotating a 16-lane row by 8 lanes
+// (DPP row_ror:8) swaps its halves, so
+//   B0 = X with lanes 8-15 of each row taken from Y rotated: lane l holds row l % 16,
+//        16-byte chunk 2 (l / 16) of the line;
+//   B1 = Y with lanes 0-7 of each row taken from X rotated: row l % 16, chunk 2 (l / 16) + 1;
+// two bank-masked DPP moves per dword, no LDS. The A operands follow the same order:
+// y[l % 16][64 t + 16 (l / 16) ..+8] for B0, the next 8 columns for B1.
+//
+// Ring. The loads of the step BD_HEAD_AHEAD on are issued after each step's products;
+// scheduling barriers keep the compiler from hoisting them above the products (the loads
+// then reuse the slot's registers, so the loop needs no copies) or sinking them to their
+// use (which would empty the ring): a step waits only for its own loads. EVEN: the steps
+// are a multiple of BD_HEAD_AHEAD; otherwise the steps past the end multiply their
+// (clamped, in-bounds) reloads by zero activations rather than branch round them.
+constexpr int BD_HEAD_WAVES = 4, BD_HEAD_TILES = 4, BD_HEAD_AHEAD = 2;
+constexpr int BD_DPP_ROW_ROR8 = 0x128;
+__device__ __forceinline__ uint32_t bd_halves(uint32_t keep, uint32_t rot, int bank_mask_is_high) {
+    return bank_mask_is_high ? (uint32_t)__builtin_amdgcn_update_dpp((int)keep, (int)rot, BD_DPP_ROW_ROR8, 0xF, 0xC, false)
+                             : (uint32_t)__builtin_amdgcn_update_dpp((int)keep, (int)rot, BD_DPP_ROW_ROR8, 0xF, 0x3, false);
+}
+template <bool EVEN>
 __global__ __launch_bounds__(64 * BD_HEAD_WAVES) void bd_head_kernel(const uint16_t* __restrict__ y_hi,
                                                                       const uint16_t* __restrict__ y_lo, int ldy,
                                                                       int B, const uint16_t* __restrict__ W, int V,
@@ -333,20 +354,38 @@ __global__ __launch_bounds__(64 * BD_HEAD_WAVES) void bd_head_kernel(const uint1
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n0 = (blockIdx.x * BD_HEAD_WAVES + wave) * 16 * BD_HEAD_TILES;
     if (n0 >= V) return;
-    const int l16 = lane & 15, kk = 8 * (lane >> 4);
+    const int l16 = lane & 15;
     const int m = min(l16, B - 1);
-    const uint4* wrow[BD_HEAD_TILES];
+    const u32x4_t* wrow[BD_HEAD_TILES][2];
 #pragma unroll
     for (int i = 0; i < BD_HEAD_TILES; i++)
-        wrow[i] = reinterpret_cast<const uint4*>(W + (size_t)min(n0 + 16 * i + l16, V - 1) * d + kk);
-    const uint4* yh = reinterpret_cast<const uint4*>(y_hi + (size_t)m * ldy + kk);
-    const uint4* yl = reinterpret_cast<const uint4*>(y_lo + (size_t)m * ldy + kk);
-    const int steps = d / 32;   // 32 columns (4 x 16 bytes per row) per step
-    uint4 wv[BD_HEAD_AHEAD][BD_HEAD_TILES];
 #pragma unroll
-    for (int s = 0; s < BD_HEAD_AHEAD; s++)
+        for (int h = 0; h < 2; h++)
+            wrow[i][h] = reinterpret_cast<const u32x4_t*>(W + (size_t)min(n0 + 16 * i + 8 * h + (lane & 7), V - 1) * d +
+                                                          8 * (lane >> 3));
+    const uint4* yh = reinterpret_cast<const uint4*>(y_hi + (size_t)m * ldy + 16 * (lane >> 4));
+    const uint4* yl = reinterpret_cast<const uint4*>(y_lo + (size_t)m * ldy + 16 * (lane >> 4));
+    const int steps = d / 64;   // one 128-byte line of each row per step
+    // d is a positive multiple of 64 (checked before launch): with no loop guard the
+    // compiler keeps the ring's first loads in slot order rather than sinking them past it
+    __builtin_assume(steps > 0);
+    u32x4_t wv[BD_HEAD_AHEAD][BD_HEAD_TILES][2];
+    uint4 yv[BD_HEAD_AHEAD][4];   // hi B0, hi B1, lo B0, lo B1
+    auto load = [&](int s, int st) {
+        yv[s][0] = yh[8 * st];
+        yv[s][1] = yh[8 * st + 1];
+        yv[s][2] = yl[8 * st];
+        yv[s][3] = yl[8 * st + 1];
 #pragma unroll
-        for (int i = 0; i < BD_HEAD_TILES; i++) wv[s][i] = wrow[i][4 * min(s, steps - 1)];
+        for (int i = 0; i < BD_HEAD_TILES; i++)
+#pragma unroll
+            for (int h = 0; h < 2; h++) wv[s][i][h] = __builtin_nontemporal_load(wrow[i][h] + 8 * st);
+    };
+#pragma unroll
+    for (int s = 0; s < BD_HEAD_AHEAD; s++) {
+        load(s, min(s, steps - 1));
+        __builtin_amdgcn_sched_barrier(0);   // slots issue in step order, as the loop refills them
+    }
     f32x4_t acc[BD_HEAD_TILES];
 #pragma unroll
     for (int i = 0; i < BD_HEAD_TILES; i++) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -354,17 +393,28 @@ __global__ __launch_bounds__(64 * BD_HEAD_WAVES) void bd_head_kernel(const uint1
 #pragma unroll
         for (int s = 0; s < BD_HEAD_AHEAD; s++) {
             const int st = s0 + s;
-            if (st < steps) {
-                const uint4 h = yh[4 * st], lo = yl[4 * st];
-                const int nx = 4 * min(st + BD_HEAD_AHEAD, steps - 1);   // the step BD_HEAD_AHEAD on
+            const bool live = EVEN || st < steps;
+            const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+            const bd_bf16x8_t h0 = __builtin_bit_cast(bd_bf16x8_t, live ? yv[s][0] : z);
+            const bd_bf16x8_t h1 = __builtin_bit_cast(bd_bf16x8_t, live ? yv[s][1] : z);
+            const bd_bf16x8_t lo0 = __builtin_bit_cast(bd_bf16x8_t, live ? yv[s][2] : z);
+            const bd_bf16x8_t lo1 = __builtin_bit_cast(bd_bf16x8_t, live ? yv[s][3] : z);
 #pragma unroll
-                for (int i = 0; i < BD_HEAD_TILES; i++) {
-                    const bd_bf16x8_t bw = __builtin_bit_cast(bd_bf16x8_t, wv[s][i]);
-                    wv[s][i] = wrow[i][nx];
-                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bd_bf16x8_t, h), bw, acc[i], 0, 0, 0);
-                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bd_bf16x8_t, lo), bw, acc[i], 0, 0, 0);
-                }
+            for (int i = 0; i < BD_HEAD_TILES; i++) {
+                const u32x4_t x = wv[s][i][0], y = wv[s][i][1];
+                const uint4 b0 = make_uint4(bd_halves(x[0], y[0], 1), bd_halves(x[1], y[1], 1),
+                                            bd_halves(x[2], y[2], 1), bd_halves(x[3], y[3], 1));
+                const uint4 b1 = make_uint4(bd_halves(y[0], x[0], 0), bd_halves(y[1], x[1], 0),
+                                            bd_halves(y[2], x[2], 0), bd_halves(y[3], x[3], 0));
+                const bd_bf16x8_t w0 = __builtin_bit_cast(bd_bf16x8_t, b0), w1 = __builtin_bit_cast(bd_bf16x8_t, b1);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h0, w0, acc[i], 0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo0, w0, acc[i], 0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(h1, w1, acc[i], 0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo1, w1, acc[i], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            load(s, min(st + BD_HEAD_AHEAD, steps - 1));
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     // acc[i][r] = logits[row 4 (l / 16) + r][column n0 + 16 i + l % 16]
@@ -765,8 +815,12 @@ extern "C" int atlas_decode_batch(const atlas_model* m, const int32_t* d_tokens,
     float* logits = d_logits ? d_logits : w.logits;
     const int head_blocks = (m->vocab + 16 * BD_HEAD_TILES * BD_HEAD_WAVES - 1) / (16 * BD_HEAD_TILES * BD_HEAD_WAVES);
     prof_mark("bd_lm_head", st);
-    ATLAS_KLAUNCH(bd_head_kernel, dim3(head_blocks), dim3(64 * BD_HEAD_WAVES), 0, st, w.p1h, w.p1l, w.ld1, B,
-                  m->lm_head, m->vocab, d, logits);
+    if ((d / 64) % BD_HEAD_AHEAD == 0)
+        ATLAS_KLAUNCH(bd_head_kernel<true>, dim3(head_blocks), dim3(64 * BD_HEAD_WAVES), 0, st, w.p1h, w.p1l, w.ld1, B,
+                      m->lm_head, m->vocab, d, logits);
+    else
+        ATLAS_KLAUNCH(bd_head_kernel<false>, dim3(head_blocks), dim3(64 * BD_HEAD_WAVES), 0, st, w.p1h, w.p1l, w.ld1, B,
+                      m->lm_head, m->vocab, d, logits);
     ATLAS_LAUNCH_CHECK("bd_head_kernel");
     if (d_argmax) {
         prof_mark("bd_argmax", st);
