@@ -1224,13 +1224,19 @@ __device__ __forceinline__ uint4 pf_kv8_bf16(const void* cache, const void* fres
 template <int G, bool KVB>
 __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
     constexpr int D = 128, KPB = D + 8, VTP = 16 + 4, PP = 20;
-    __shared__ __align__(16) uint16_t sKh[16 * KPB];   // keys as bf16 planes: K = hi + lo
-    __shared__ __align__(16) uint16_t sKl[16 * KPB];
-    __shared__ __align__(16) uint16_t sVth[D * VTP];   // values transposed ([dim][key]) as bf16 planes
-    __shared__ __align__(16) uint16_t sVtl[D * VTP];
+    constexpr int NT = 64 * G;
+    constexpr int EPL = KVB ? 8 : 4;            // cache elements per 16-byte load
+    constexpr int NLD = 16 * D / EPL;           // 16-byte loads per tile of K (and of V)
+    constexpr int NPT = (NLD + NT - 1) / NT;    // per thread
+    // two LDS stages: the tile being multiplied and the next one being stored
+    __shared__ __align__(16) uint16_t sKh[2][16 * KPB];   // keys as bf16 planes: K = hi + lo
+    __shared__ __align__(16) uint16_t sKl[2][16 * KPB];
+    __shared__ __align__(16) uint16_t sVth[2][D * VTP];   // values transposed ([dim][key]) as bf16 planes
+    __shared__ __align__(16) uint16_t sVtl[2][D * VTP];
     __shared__ __align__(16) float sP[G][16 * PP];
-    // longest query tiles (most causal keys) first, so that they start before the short ones
-    const int t0 = (gridDim.x - 1 - blockIdx.x) * PF_QT, kv = blockIdx.y;
+    // grid (Hkv, query tiles): the longest query tiles (most causal keys) of every KV head
+    // are dispatched first, so that they start before the short ones
+    const int t0 = (gridDim.y - 1 - blockIdx.y) * PF_QT, kv = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, l4 = lane >> 4;
@@ -1274,78 +1280,97 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
     for (int gi = 0; gi < 8; gi++) o[gi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const int sp = a.ring ? a.start_pos % (int)a.slots : 0;
-    for (int kb = klo; kb <= khi; kb += 16) {
-        __syncthreads();
+    // The raw K/V words of the next key tile are loaded into registers while the current
+    // tile is multiplied; at the top of the next iteration they are split into planes and
+    // stored into the free LDS stage. Load u (< NLD) of a tile is key u / (D / EPL),
+    // 16-byte chunk u % (D / EPL); the loads are unconditional (u clamped to NLD - 1).
+    uint4 rk[NPT], rv[NPT];
+    auto issue = [&](int kb) {
         // A tile wholly inside the prompt (every tile when start_pos = 0) reads the prompt
         // buffer directly; only a tile that reaches below start_pos goes through the
         // per-key choice of buffer and the ring's slot map. kb is uniform: no divergence.
         const bool fresh_tile = kb >= a.start_pos;
         const size_t fresh0 = ((size_t)kv * a.n + (fresh_tile ? kb - a.start_pos : 0)) * D;
-        if constexpr (KVB) {   // a bf16 value is its own hi plane; its lo plane is zero and never staged
-            auto stage = [&](auto load8) {
-                for (int u = tid; u < 16 * D / 8; u += blockDim.x) {
-                    const int kr = u / (D / 8), c = u % (D / 8);
-                    const int j = min(kb + kr, khi);
-                    *reinterpret_cast<uint4*>(&sKh[kr * KPB + 8 * c]) = load8(a.k_cache, a.k_new, j, c);
-                    const uint4 vw = load8(a.v_cache, a.v_new, j, c);
-                    const uint32_t w[4] = {vw.x, vw.y, vw.z, vw.w};
 #pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        sVth[(8 * c + 2 * e) * VTP + kr] = (uint16_t)(w[e] & 0xFFFFu);
-                        sVth[(8 * c + 2 * e + 1) * VTP + kr] = (uint16_t)(w[e] >> 16);
-                    }
+        for (int r = 0; r < NPT; r++) {
+            const int u = min(tid + r * NT, NLD - 1);
+            const int kr = u / (D / EPL), c = u % (D / EPL);
+            const int j = min(kb + kr, khi);
+            if constexpr (KVB) {
+                if (fresh_tile) {
+                    const size_t e = fresh0 + (size_t)(j - kb) * D + 8 * c;
+                    rk[r] = *reinterpret_cast<const uint4*>((const uint16_t*)a.k_new + e);
+                    rv[r] = *reinterpret_cast<const uint4*>((const uint16_t*)a.v_new + e);
+                } else {
+                    rk[r] = pf_kv8_bf16(a.k_cache, a.k_new, a, kv, j, c, sp);
+                    rv[r] = pf_kv8_bf16(a.v_cache, a.v_new, a, kv, j, c, sp);
                 }
-            };
-            if (fresh_tile)
-                stage([&](const void*, const void* fresh, int j, int c) {
-                    return *reinterpret_cast<const uint4*>((const uint16_t*)fresh + fresh0 + (size_t)(j - kb) * D + 8 * c);
-                });
-            else
-                stage([&](const void* cache, const void* fresh, int j, int c) {
-                    return pf_kv8_bf16(cache, fresh, a, kv, j, c, sp);
-                });
-        } else {
-            auto stage = [&](auto load4) {
-                for (int u = tid; u < 16 * D / 4; u += blockDim.x) {
-                    const int kr = u / (D / 4), c = u % (D / 4);
-                    const int j = min(kb + kr, khi);
-                    const float4 k4 = load4(a.k_cache, a.k_new, j, c);
-                    uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-                    pf_split(k4.x, h0, l0);
-                    pf_split(k4.y, h1, l1);
-                    pf_split(k4.z, h2, l2);
-                    pf_split(k4.w, h3, l3);
-                    *reinterpret_cast<uint2*>(&sKh[kr * KPB + 4 * c]) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-                    *reinterpret_cast<uint2*>(&sKl[kr * KPB + 4 * c]) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
-                    const float4 v4 = load4(a.v_cache, a.v_new, j, c);
-                    const float ve[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        uint32_t vh, vl;
-                        pf_split(ve[e], vh, vl);
-                        sVth[(4 * c + e) * VTP + kr] = (uint16_t)vh;
-                        sVtl[(4 * c + e) * VTP + kr] = (uint16_t)vl;
-                    }
+            } else {
+                float4 k4, v4;
+                if (fresh_tile) {
+                    const size_t e = fresh0 + (size_t)(j - kb) * D + 4 * c;
+                    k4 = *reinterpret_cast<const float4*>((const float*)a.k_new + e);
+                    v4 = *reinterpret_cast<const float4*>((const float*)a.v_new + e);
+                } else {
+                    k4 = pf_kv4_f32(a.k_cache, a.k_new, a, kv, j, c, sp);
+                    v4 = pf_kv4_f32(a.v_cache, a.v_new, a, kv, j, c, sp);
                 }
-            };
-            if (fresh_tile)
-                stage([&](const void*, const void* fresh, int j, int c) {
-                    return *reinterpret_cast<const float4*>((const float*)fresh + fresh0 + (size_t)(j - kb) * D + 4 * c);
-                });
-            else
-                stage([&](const void* cache, const void* fresh, int j, int c) {
-                    return pf_kv4_f32(cache, fresh, a, kv, j, c, sp);
-                });
+                rk[r] = __builtin_bit_cast(uint4, k4);
+                rv[r] = __builtin_bit_cast(uint4, v4);
+            }
         }
-        __syncthreads();
+    };
+    auto store = [&](int st) {
+#pragma unroll
+        for (int r = 0; r < NPT; r++) {
+            const int u = tid + r * NT;
+            if (u >= NLD) continue;
+            const int kr = u / (D / EPL), c = u % (D / EPL);
+            if constexpr (KVB) {   // a bf16 value is its own hi plane; its lo plane is zero and never staged
+                *reinterpret_cast<uint4*>(&sKh[st][kr * KPB + 8 * c]) = rk[r];
+                const uint32_t w[4] = {rv[r].x, rv[r].y, rv[r].z, rv[r].w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    sVth[st][(8 * c + 2 * e) * VTP + kr] = (uint16_t)(w[e] & 0xFFFFu);
+                    sVth[st][(8 * c + 2 * e + 1) * VTP + kr] = (uint16_t)(w[e] >> 16);
+                }
+            } else {
+                const float4 k4 = __builtin_bit_cast(float4, rk[r]);
+                uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+                pf_split(k4.x, h0, l0);
+                pf_split(k4.y, h1, l1);
+                pf_split(k4.z, h2, l2);
+                pf_split(k4.w, h3, l3);
+                *reinterpret_cast<uint2*>(&sKh[st][kr * KPB + 4 * c]) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                *reinterpret_cast<uint2*>(&sKl[st][kr * KPB + 4 * c]) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+                const float4 v4 = __builtin_bit_cast(float4, rv[r]);
+                const float ve[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    uint32_t vh, vl;
+                    pf_split(ve[e], vh, vl);
+                    sVth[st][(4 * c + e) * VTP + kr] = (uint16_t)vh;
+                    sVtl[st][(4 * c + e) * VTP + kr] = (uint16_t)vl;
+                }
+            }
+        }
+    };
+    if (klo <= khi) issue(klo);
+    int st = 0;
+    for (int kb = klo; kb <= khi; kb += 16, st ^= 1) {
+        // Stage st was last read two iterations ago; every wave has passed the barrier of
+        // the previous iteration since, so none still reads it.
+        store(st);
+        __syncthreads();   // tile kb is in stage st
+        if (kb + 16 <= khi) issue(kb + 16);
         // scores Q K^T: hi*hi + hi*lo + lo*hi (the lo*lo term is below 2^-16 of the product)
         f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ks++) {
-            const bf16x8_t kh = *reinterpret_cast<const bf16x8_t*>(&sKh[l16 * KPB + 32 * ks + 8 * l4]);
+            const bf16x8_t kh = *reinterpret_cast<const bf16x8_t*>(&sKh[st][l16 * KPB + 32 * ks + 8 * l4]);
             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[ks], kh, sc, 0, 0, 0);
             if constexpr (!KVB) {
-                const bf16x8_t kl = *reinterpret_cast<const bf16x8_t*>(&sKl[l16 * KPB + 32 * ks + 8 * l4]);
+                const bf16x8_t kl = *reinterpret_cast<const bf16x8_t*>(&sKl[st][l16 * KPB + 32 * ks + 8 * l4]);
                 sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[ks], kl, sc, 0, 0, 0);
             }
             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[ks], kh, sc, 0, 0, 0);
@@ -1385,10 +1410,10 @@ __global__ __launch_bounds__(64 * G) void pf_attn_kernel(PfAttnArgs a) {
             const bf16x4_t pl = __builtin_bit_cast(bf16x4_t, make_uint2(q0 | (q1 << 16), q2 | (q3 << 16)));
 #pragma unroll
             for (int gi = 0; gi < 8; gi++) {
-                const bf16x4_t vh = *reinterpret_cast<const bf16x4_t*>(&sVth[(16 * gi + l16) * VTP + 4 * l4]);
+                const bf16x4_t vh = *reinterpret_cast<const bf16x4_t*>(&sVth[st][(16 * gi + l16) * VTP + 4 * l4]);
                 o[gi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vh, o[gi], 0, 0, 0);
                 if constexpr (!KVB) {
-                    const bf16x4_t vl = *reinterpret_cast<const bf16x4_t*>(&sVtl[(16 * gi + l16) * VTP + 4 * l4]);
+                    const bf16x4_t vl = *reinterpret_cast<const bf16x4_t*>(&sVtl[st][(16 * gi + l16) * VTP + 4 * l4]);
                     o[gi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vl, o[gi], 0, 0, 0);
                 }
                 o[gi] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vh, o[gi], 0, 0, 0);
@@ -1522,7 +1547,7 @@ int launch_pf_commit(const PfCommitArgs& a, hipStream_t st) {
 
 int launch_pf_attn(const PfAttnArgs& a, hipStream_t st) {
     const int G = a.Hq / a.Hkv;
-    dim3 grid((a.n + PF_QT - 1) / PF_QT, a.Hkv);
+    dim3 grid(a.Hkv, (a.n + PF_QT - 1) / PF_QT);
     prof_mark(a.window > 0 ? "pf_attn_window" : "pf_attn_full", st);
     switch (G) {
 #define C(G_)                                                                   \
