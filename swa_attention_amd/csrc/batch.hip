@@ -104,27 +104,76 @@ __device__ __forceinline__ void bd_sum(const float* p, int parts, size_t stride,
         for (int c = 0; c < N; c++) out[c] += p[(size_t)q * stride + c];
 }
 
-__global__ __launch_bounds__(1024) void bd_rope_kernel(BdRopeArgs a) {
-    constexpr int D = 128;
+// One block of BD_ROPE_NT threads per sequence. Every load is issued before the first
+// is used: the position, up to BD_ROPE_NV float4 of each of the first BD_ROPE_MAXP
+// partial rows per thread, and the gains of the thread's first BD_ROPE_NR rotation pairs
+// (rows, partials and pairs beyond these take the loops after them).
+constexpr int BD_ROPE_NT = 1024, BD_ROPE_NV = 2, BD_ROPE_MAXP = 4, BD_ROPE_NR = 3;
+__global__ __launch_bounds__(BD_ROPE_NT) void bd_rope_kernel(BdRopeArgs a) {
+    constexpr int D = 128, NT = BD_ROPE_NT;
     extern __shared__ float s_row[];   // [ld]
     __shared__ float red[2][16];
     __shared__ float s_cos[64], s_sin[64];
-    const int t = blockIdx.x;
+    const int t = blockIdx.x, tid = threadIdx.x;
     const int pos = a.d_pos[t];
     const int nq = a.Hq * D, nk = a.Hkv * D;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
+    const int n4 = a.ld >> 2, npairs = (a.Hq + a.Hkv) * 64;   // ld, nq, nk multiples of 4
+    const float* prow = a.part + (size_t)t * a.ld;
+    float4 pv[BD_ROPE_NV][BD_ROPE_MAXP];
+#pragma unroll
+    for (int j = 0; j < BD_ROPE_NV; j++) {
+        const int i4 = tid + NT * j, ic = i4 < n4 ? i4 : 0;
+#pragma unroll
+        for (int q = 0; q < BD_ROPE_MAXP; q++)
+            pv[j][q] = *reinterpret_cast<const float4*>(prow + (size_t)min(q, a.parts - 1) * a.part_stride + 4 * ic);
+    }
+    float g0[BD_ROPE_NR], g1[BD_ROPE_NR];
+#pragma unroll
+    for (int r = 0; r < BD_ROPE_NR; r++) {
+        const int u = tid + NT * r, uc = u < npairs ? u : 0;
+        const int h = uc >> 6, i = uc & 63;
+        const float* g = h >= a.Hq ? a.g_k + (h - a.Hq) * D : a.g_q + h * D;
+        g0[r] = g[i];
+        g1[r] = g[i + 64];
+    }
     float sq = 0.f, sk = 0.f;
-    for (int i = 4 * threadIdx.x; i < a.ld; i += 4 * blockDim.x) {   // ld, nq, nk multiples of 4
-        const float* p = a.part + (size_t)t * a.ld + i;
-        float4 v = *reinterpret_cast<const float4*>(p);
-        for (int q = 1; q < a.parts; q++) {
-            const float4 u = *reinterpret_cast<const float4*>(p + (size_t)q * a.part_stride);
-            v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
-        }
+    auto add_row = [&](int i4, float4 v) {   // v: the sum of the partials of float4 i4
+        const int i = 4 * i4;
         *reinterpret_cast<float4*>(&s_row[i]) = v;
         const float ss = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-        if (i < nq) sq += ss;
-        else if (i < nq + nk) sk += ss;
+        sq += i < nq ? ss : 0.f;
+        sk += (i >= nq && i < nq + nk) ? ss : 0.f;
+    };
+    auto more_parts = [&](int i4, float4& v) {
+        for (int q = BD_ROPE_MAXP; q < a.parts; q++) {
+            const float4 u = *reinterpret_cast<const float4*>(prow + (size_t)q * a.part_stride + 4 * i4);
+            v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < BD_ROPE_NV; j++) {
+        const int i4 = tid + NT * j;
+        if (i4 < n4) {
+            float4 v = pv[j][0];
+#pragma unroll
+            for (int q = 1; q < BD_ROPE_MAXP; q++) {
+                if (q < a.parts) {
+                    v.x += pv[j][q].x; v.y += pv[j][q].y; v.z += pv[j][q].z; v.w += pv[j][q].w;
+                }
+            }
+            more_parts(i4, v);
+            add_row(i4, v);
+        }
+    }
+    for (int i4 = tid + NT * BD_ROPE_NV; i4 < n4; i4 += NT) {
+        float4 v = *reinterpret_cast<const float4*>(prow + 4 * i4);
+        for (int q = 1; q < min(a.parts, BD_ROPE_MAXP); q++) {
+            const float4 u = *reinterpret_cast<const float4*>(prow + (size_t)q * a.part_stride + 4 * i4);
+            v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+        }
+        more_parts(i4, v);
+        add_row(i4, v);
     }
     const bool ok = pos >= 0 && pos < a.T_max;
     if (threadIdx.x < 64 && ok) {
@@ -158,14 +207,12 @@ __global__ __launch_bounds__(1024) void bd_rope_kernel(BdRopeArgs a) {
     const float rk = 1.0f / sqrtf(sk / (float)nk + a.eps);
     const int slot = a.ring ? pos % (int)a.slots : pos;
     const size_t cache0 = (size_t)t * a.seq_stride + (size_t)slot * D;
-    const int npairs = (a.Hq + a.Hkv) * 64;
-    for (int u = threadIdx.x; u < npairs; u += blockDim.x) {
+    auto rotate = [&](int u, float ga, float gb) {   // pair u: dims i and i + 64 of head u / 64
         const int h = u >> 6, i = u & 63;
         const bool isk = h >= a.Hq;
         const float rr = isk ? rk : rq;
-        const float* g = isk ? a.g_k + (h - a.Hq) * D : a.g_q + h * D;
         const int base = h * D;
-        const float x0 = g[i] * (s_row[base + i] * rr), x1 = g[i + 64] * (s_row[base + i + 64] * rr);
+        const float x0 = ga * (s_row[base + i] * rr), x1 = gb * (s_row[base + i + 64] * rr);
         const float c = s_cos[i], sn = s_sin[i];
         const float y0 = x0 * c - x1 * sn, y1 = x1 * c + x0 * sn;
         if (isk) {
@@ -181,6 +228,15 @@ __global__ __launch_bounds__(1024) void bd_rope_kernel(BdRopeArgs a) {
             row[base + i] = y0;
             row[base + i + 64] = y1;
         }
+    };
+    static_assert(BD_ROPE_NR == 3, "three preloaded pairs");
+    if (tid < npairs) rotate(tid, g0[0], g1[0]);
+    if (tid + NT < npairs) rotate(tid + NT, g0[1], g1[1]);
+    if (tid + 2 * NT < npairs) rotate(tid + 2 * NT, g0[2], g1[2]);
+    for (int u = tid + NT * BD_ROPE_NR; u < npairs; u += NT) {
+        const int h = u >> 6, i = u & 63;
+        const float* g = h >= a.Hq ? a.g_k + (h - a.Hq) * D : a.g_q + h * D;
+        rotate(u, g[i], g[i + 64]);
     }
     for (int u = threadIdx.x; u < nk; u += blockDim.x) {
         const int h = u / D, i = u % D;
