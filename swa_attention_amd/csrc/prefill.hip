@@ -245,13 +245,35 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
         ga.z_lo = w.p2l;
         ga.ldz = m->dff;
         if ((rc = attach_i8(ga, w, st))) return rc;
+        // With groups of 128 the gate/up kernel writes z as the down projection's int8
+        // digits (in the z planes' place), so no quantisation pass runs between the two
+        const bool z_digits = i8r_swiglu_digits_ok(ga, L.down.group) && gemm_i8_supported(L.down.group, m->dff);
+        if (z_digits) {
+            ga.zq_hi = reinterpret_cast<int8_t*>(w.p2h);   // [n][dff] each; p2h holds two planes
+            ga.zq_mid = ga.zq_hi + (size_t)n * m->dff;
+            ga.zq_lo = reinterpret_cast<int8_t*>(w.p2l);   // p2l the third and the per-group values
+            ga.zq_s = reinterpret_cast<float*>(ga.zq_lo + (size_t)n * m->dff);
+            ga.zq_sum = ga.zq_s + (size_t)n * (m->dff / 128);
+            ga.zq_ld = m->dff;
+            ga.zq_lds = m->dff / 128;
+        }
         if ((rc = launch_w4_gemm(ga, 1, st, "pf_gemm_gate_up"))) return rc;
         GemmArgs da = gemm(w.p2h, w.p2l, m->dff, L.down, n);
         da.C = w.A;
         da.ldc = 2 * d;
         const int sd = pf_ksplit(L.down, 2);
         set_split(da, sd, d);
-        if ((rc = attach_i8(da, w, st))) return rc;
+        if (z_digits) {
+            da.q_hi = ga.zq_hi;
+            da.q_mid = ga.zq_mid;
+            da.q_lo = ga.zq_lo;
+            da.q_s = ga.zq_s;
+            da.q_sum = ga.zq_sum;
+            da.ldq = ga.zq_ld;
+            da.ldqs = ga.zq_lds;
+        } else if ((rc = attach_i8(da, w, st))) {
+            return rc;
+        }
         if ((rc = launch_w4_gemm(da, 0, st, "pf_gemm_down"))) return rc;
         // y = h + RMSNorm_pf(m): the last layer leaves it to the head (last position only)
         if (!last || !head)

@@ -32,6 +32,15 @@ struct GemmArgs {
     const float* q_s = nullptr;
     const float* q_sum = nullptr;
     int ldq = 0, ldqs = 0;
+    // Mode 1 on the int8 ring kernel with groups of 128 (i8r_swiglu_digits_ok): when
+    // zq_hi is set, z is written as the down projection's int8 digits in the layout above
+    // (row strides zq_ld bytes and zq_lds groups of 128) instead of bf16 planes.
+    int8_t* zq_hi = nullptr;
+    int8_t* zq_mid = nullptr;
+    int8_t* zq_lo = nullptr;
+    float* zq_s = nullptr;
+    float* zq_sum = nullptr;
+    int zq_ld = 0, zq_lds = 0;
 };
 
 // KV of the prompt: keys j < start_pos come from the layer's cache ([Hkv][slots][128],
@@ -84,6 +93,9 @@ int gemm_i8_supported(int group, int K);
 int launch_pf_quant8(const uint16_t* hi, const uint16_t* lo, int lda, int M, int K, int group, int8_t* q_hi,
                      int8_t* q_mid, int8_t* q_lo, float* q_s, float* q_sum, hipStream_t st);
 int launch_w4_gemm(const GemmArgs& a, int mode, hipStream_t st, const char* label);
+// Whether a mode-1 launch of a (with its int8 digits attached) runs on the ring kernel with
+// groups of 128 and can write z as int8 digits (zq_*) for a down projection with groups of 128.
+bool i8r_swiglu_digits_ok(const GemmArgs& a, int down_group);
 int launch_pf_embed(const int32_t* tokens, int n, const uint16_t* emb, int vocab, int d, float* X, uint16_t* p_hi,
                     uint16_t* p_lo, int ldp, int* status, hipStream_t st);
 int launch_pf_rope(const PfRopeArgs& a, hipStream_t st);

@@ -428,6 +428,9 @@ __global__ __launch_bounds__(G8_THREADS) void w4_gemm_i8_kernel(GemmArgs a) {
         }
 }
 
+// Largest 24-bit activation integer of the int8 path: 127 * 65536 (see pf_quant8_kernel).
+constexpr float Q8_MAX = 8323072.f;
+
 // ---- the int8 GEMM with a ring of LDS stages filled by direct-to-LDS loads ------------------
 //
 // The same product as w4_gemm_i8_kernel on a 64 x 256 tile (mode 1: 128 rows of W0 and the
@@ -474,6 +477,107 @@ __device__ __forceinline__ int gr_b_off(int r, int c) { return r * (GR_BK / 2) +
 
 // G128: the group is one k tile (128 columns), so every tile starts and ends a group and the
 // epilogue is straight-line code the compiler can interleave with the MFMAs.
+// Mode-1 epilogue with groups of 128 (the tile's 128 z columns are one group of every row):
+// z = silu(gate) * up, split into bf16 planes and summed back (z' = hi + lo, the value
+// pf_quant8_kernel reads from the planes), then quantised to the down projection's int8
+// digits exactly as pf_quant8_kernel does: the row's group maximum gives the power of two
+// s, v = rint(z' / s) clamped to Q8_MAX, digits v = 65536 h + 256 m + l, and per row the
+// group's s and its sum of v (an exact int32 for 128 columns). A row's 32 columns of a
+// wave sit in one 16-lane row (two per lane): DPP row reductions, then the four column
+// waves meet in LDS. The digits are staged in LDS in their stored order (bytes of every
+// 8 columns as 0,2,4,6,1,3,5,7; rows padded to 144 bytes against bank conflicts) and
+// leave as 16-byte stores. The staging uses the ring stage `free_stage`, which no wave
+// reads any more, so the first barrier is the one that publishes the maxima. Every
+// thread of the block runs it (rows past M are computed and not stored).
+constexpr int GR_ZROW = 144;   // LDS bytes per staged digit row
+__device__ __forceinline__ int dpp_row16_sum_i(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true);    // quad_perm [1,0,3,2]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true);    // quad_perm [2,3,0,1]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, true);   // row_half_mirror
+    v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, true);   // row_mirror
+    return v;
+}
+__device__ __forceinline__ float dpp_row16_max(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
+    return v;
+}
+__device__ __forceinline__ void gr_swiglu_digits(const GemmArgs& a, const f32x4_t (&acc)[2][4], int8_t* lds, int m0,
+                                                 int n0, int wm, int wn, int l16, int l4, int tid) {
+    float zx[2][2][4];
+#pragma unroll
+    for (int mf = 0; mf < 2; mf++)
+#pragma unroll
+        for (int f = 0; f < 2; f++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float gt = acc[mf][f][r], up = acc[mf][f + 2][r];
+                uint32_t hi, lo;
+                pf_split(gt / (1.0f + __expf(-gt)) * up, hi, lo);
+                zx[mf][f][r] = bf16_bits_to_f32(hi) + bf16_bits_to_f32(lo);
+            }
+    float* s_max = reinterpret_cast<float*>(lds);       // [64 rows][4 column waves]
+    int* s_sum = reinterpret_cast<int*>(lds + 1024);    // [64][4]
+    int8_t* s_dig = lds + 2048;                          // [3 planes][64 rows][GR_ZROW]
+    constexpr int PL = 64 * GR_ZROW;
+#pragma unroll
+    for (int mf = 0; mf < 2; mf++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const float mx = dpp_row16_max(fmaxf(fabsf(zx[mf][0][r]), fabsf(zx[mf][1][r])));
+            if (l16 == 0) s_max[(wm * 32 + mf * 16 + 4 * l4 + r) * 4 + wn] = mx;
+        }
+    __syncthreads();
+#pragma unroll
+    for (int mf = 0; mf < 2; mf++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int rl = wm * 32 + mf * 16 + 4 * l4 + r;
+            const float mx = fmaxf(fmaxf(s_max[rl * 4], s_max[rl * 4 + 1]), fmaxf(s_max[rl * 4 + 2], s_max[rl * 4 + 3]));
+            int e;
+            (void)frexpf(mx / Q8_MAX, &e);   // s = 2^e >= max|z'| / Q8_MAX (s = 1 for a zero group)
+            const float inv = ldexpf(1.f, -e);
+            int sum = 0;
+#pragma unroll
+            for (int f = 0; f < 2; f++) {
+                const int v = (int)fminf(fmaxf(rintf(zx[mf][f][r] * inv), -Q8_MAX), Q8_MAX);
+                sum += v;
+                const int ld = ((v + 128) & 255) - 128;
+                const int v1 = (v - ld) >> 8;   // exact: v - ld is a multiple of 256
+                const int md = ((v1 + 128) & 255) - 128;
+                const int hd = (v1 - md) >> 8;
+                const int c = wn * 32 + 16 * f + l16, i = c & 7;
+                const int o = rl * GR_ZROW + (c & ~7) + ((i & 1) ? 4 + (i >> 1) : (i >> 1));
+                s_dig[o] = (int8_t)hd;
+                s_dig[PL + o] = (int8_t)md;
+                s_dig[2 * PL + o] = (int8_t)ld;
+            }
+            sum = dpp_row16_sum_i(sum);
+            if (l16 == 0) s_sum[rl * 4 + wn] = sum;
+        }
+    __syncthreads();
+    int8_t* planes[3] = {a.zq_hi, a.zq_mid, a.zq_lo};
+    for (int u = tid; u < 3 * 64 * 8; u += GR_THREADS) {
+        const int p = u >> 9, rl = (u >> 3) & 63, ch = u & 7;
+        const int row = m0 + rl;
+        if (row < a.M)
+            *reinterpret_cast<uint4*>(planes[p] + (size_t)row * a.zq_ld + n0 + 16 * ch) =
+                *reinterpret_cast<const uint4*>(s_dig + p * PL + rl * GR_ZROW + 16 * ch);
+    }
+    if (tid < 64 && m0 + tid < a.M) {
+        const float mx = fmaxf(fmaxf(s_max[tid * 4], s_max[tid * 4 + 1]), fmaxf(s_max[tid * 4 + 2], s_max[tid * 4 + 3]));
+        int e;
+        (void)frexpf(mx / Q8_MAX, &e);
+        const int sum = s_sum[tid * 4] + s_sum[tid * 4 + 1] + s_sum[tid * 4 + 2] + s_sum[tid * 4 + 3];
+        const size_t o = (size_t)(m0 + tid) * a.zq_lds + n0 / GR_BK;
+        a.zq_s[o] = ldexpf(1.f, e);
+        a.zq_sum[o] = (float)sum;
+    }
+}
+static_assert(2048 + 3 * 64 * GR_ZROW <= GR_STAGE, "the z digits fit one ring stage");
+
 template <int MODE, bool G128>
 __global__ __launch_bounds__(GR_THREADS) void w4_gemm_i8r_kernel(GemmArgs a) {
     extern __shared__ __align__(16) int8_t gr_lds[];
@@ -663,6 +767,14 @@ __global__ __launch_bounds__(GR_THREADS) void w4_gemm_i8r_kernel(GemmArgs a) {
         }
     }
 
+    if constexpr (MODE == 1 && G128) {
+        if (a.zq_hi) {   // z quantised here for the down projection's int8 kernel
+            // the stage of k tile KT - 2 (any stage but tile 0's when KT = 1): every wave has
+            // passed the barrier of the last iteration, so none still reads it
+            gr_swiglu_digits(a, acc, gr_lds + ((KT + 1) % GR_STAGES) * GR_STAGE, m0, n0, wm, wn, l16, l4, tid);
+            return;
+        }
+    }
     // epilogue: D[row 4*l4 + r][col l16] of each fragment
 #pragma unroll
     for (int mf = 0; mf < 2; mf++)
@@ -699,7 +811,6 @@ __global__ __launch_bounds__(GR_THREADS) void w4_gemm_i8r_kernel(GemmArgs a) {
 // v = rint(x / s) with |v| <= Q8_MAX = 127 * 65536, split into balanced digits
 // v = 65536 h + 256 m + l with l, m in [-128, 127] and h in [-127, 127]; bytes stored in
 // the order 0,2,4,6,1,3,5,7 of the 8 columns; q_sum = sum of v over the group (f32).
-constexpr float Q8_MAX = 8323072.f;
 __global__ __launch_bounds__(256) void pf_quant8_kernel(const uint16_t* hi, const uint16_t* lo, int lda, int M, int K,
                                                         int group, int8_t* q_hi, int8_t* q_mid, int8_t* q_lo,
                                                         float* q_s, float* q_sum) {
@@ -1453,6 +1564,17 @@ int launch_pf_quant8(const uint16_t* hi, const uint16_t* lo, int lda, int M, int
     return ATLAS_OK;
 }
 
+static bool i8r_uses_ring(const GemmArgs& a, int mode) {
+    const bool same_w = mode == 0 || (a.W1.G == a.W0.G && a.W1.KW == a.W0.KW && a.W1.zsym == a.W0.zsym &&
+                                      a.W1.zstride == a.W0.zstride && a.W1.scale_dtype == a.W0.scale_dtype);
+    return same_w && ((size_t)a.N * a.W0.G) % 2 == 0;
+}
+
+bool i8r_swiglu_digits_ok(const GemmArgs& a, int down_group) {
+    return a.q_hi && a.group == GR_BK && down_group == GR_BK && a.N % GR_BK == 0 && a.ksplit == 1 &&
+           i8r_uses_ring(a, 1);
+}
+
 int launch_w4_gemm(const GemmArgs& a, int mode, hipStream_t st, const char* label) {
     ATLAS_CHECK_SHAPE(gemm_supported(a.group), "prefill GEMM needs group 32 or a multiple of 64 (got %d)", a.group);
     ATLAS_CHECK_SHAPE(a.K % 32 == 0 && a.K >= 32 && a.lda % 8 == 0, "prefill GEMM shape K=%d lda=%d", a.K, a.lda);
@@ -1468,11 +1590,12 @@ int launch_w4_gemm(const GemmArgs& a, int mode, hipStream_t st, const char* labe
                               a.ldqs >= a.K / a.group && a.q_mid && a.q_lo && a.q_s && a.q_sum,
                           "int8 GEMM needs a group of 128, 256 or 512 dividing K, K ranges of whole 128-column "
                           "tiles, ldq %% 16 == 0");
-        const bool same_w = mode == 0 || (a.W1.G == a.W0.G && a.W1.KW == a.W0.KW && a.W1.zsym == a.W0.zsym &&
-                                          a.W1.zstride == a.W0.zstride && a.W1.scale_dtype == a.W0.scale_dtype);
-        if (same_w && ((size_t)a.N * a.W0.G) % 2 == 0) {   // the LDS-ring kernel
+        if (i8r_uses_ring(a, mode)) {   // the LDS-ring kernel
             static bool attr_set[4] = {false, false, false, false};
             const int g128 = a.group == GR_BK ? 1 : 0, v = 2 * mode + g128;
+            ATLAS_CHECK_SHAPE(!a.zq_hi || (v == 3 && a.N % GR_BK == 0 && a.zq_ld % 16 == 0 && a.zq_mid && a.zq_lo &&
+                                           a.zq_s && a.zq_sum),
+                              "int8 digits of z need mode 1 with groups of 128 on the ring kernel");
             const void* fns[4] = {(const void*)w4_gemm_i8r_kernel<0, false>, (const void*)w4_gemm_i8r_kernel<0, true>,
                                   (const void*)w4_gemm_i8r_kernel<1, false>, (const void*)w4_gemm_i8r_kernel<1, true>};
             if (!attr_set[v]) {
@@ -1491,6 +1614,7 @@ int launch_w4_gemm(const GemmArgs& a, int mode, hipStream_t st, const char* labe
             ATLAS_LAUNCH_CHECK("w4_gemm_i8r_kernel");
             return ATLAS_OK;
         }
+        ATLAS_CHECK_SHAPE(!a.zq_hi, "int8 digits of z need the ring kernel");
         const int T8 = MT * NT * a.ksplit, b8 = 8 * ((T8 + 7) / 8);
         if (mode == 0) ATLAS_KLAUNCH((w4_gemm_i8_kernel<0>), dim3(b8), dim3(G8_THREADS), 0, st, a);
         else ATLAS_KLAUNCH((w4_gemm_i8_kernel<1>), dim3(b8), dim3(G8_THREADS), 0, st, a);
