@@ -114,10 +114,7 @@ void set_split(GemmArgs& g, int S, int d) {
 
 // Int8 digit planes of the GEMM input for groups of 128, 256 or 512 (the int8 matrix-core
 // kernel); other groups keep the bf16 planes.
-int attach_i8(GemmArgs& g, const PrefillWs& w, hipStream_t st) {
-    if (!gemm_i8_supported(g.group, g.K)) return ATLAS_OK;
-    const int rc = launch_pf_quant8(g.a_hi, g.a_lo, g.lda, g.M, g.K, g.group, w.qh, w.qm, w.ql, w.qs, w.qsum, st);
-    if (rc) return rc;
+void use_i8(GemmArgs& g, const PrefillWs& w) {
     g.q_hi = w.qh;
     g.q_mid = w.qm;
     g.q_lo = w.ql;
@@ -125,7 +122,20 @@ int attach_i8(GemmArgs& g, const PrefillWs& w, hipStream_t st) {
     g.q_sum = w.qsum;
     g.ldq = g.K;
     g.ldqs = g.K / g.group;
+}
+
+int attach_i8(GemmArgs& g, const PrefillWs& w, hipStream_t st) {
+    if (!gemm_i8_supported(g.group, g.K)) return ATLAS_OK;
+    const int rc = launch_pf_quant8(g.a_hi, g.a_lo, g.lda, g.M, g.K, g.group, w.qh, w.qm, w.ql, w.qs, w.qsum, st);
+    if (rc) return rc;
+    use_i8(g, w);
     return ATLAS_OK;
+}
+
+// Whether the residual kernel writes the int8 digits of the next GEMM's input (a W4
+// matrix with K = d) in place of its bf16 planes; then no quantisation pass runs.
+bool residual_digits(const atlas_w4& next, int d) {
+    return gemm_i8_supported(next.group, d) && residual_digits_ok(next.group, d);
 }
 
 }  // namespace
@@ -162,6 +172,7 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
 
     if ((rc = launch_pf_embed(d_tokens, n, m->embedding, m->vocab, d, w.X, w.p1h, w.p1l, w.ld1, (int*)w.dec, st)))
         return rc;
+    bool qkv_digits = false;   // the previous layer's residual wrote the qkv input as int8 digits
     for (int l = 0; l < m->n_layers; l++) {
         const atlas_layer& L = m->layers[l];
         const bool last = l == m->n_layers - 1;
@@ -171,7 +182,8 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
         qa.C = w.QKV;
         qa.ldc = sq * nqkv;
         set_split(qa, sq, nqkv);
-        if ((rc = attach_i8(qa, w, st))) return rc;
+        if (qkv_digits) use_i8(qa, w);
+        else if ((rc = attach_i8(qa, w, st))) return rc;
         if ((rc = launch_w4_gemm(qa, 0, st, "pf_gemm_qkv"))) return rc;
         // QK norm and rotary; the prompt keys/values into the prompt KV buffers
         PfRopeArgs ra{};
@@ -237,14 +249,19 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
         set_split(oa, so, d);
         if ((rc = attach_i8(oa, w, st))) return rc;
         if ((rc = launch_w4_gemm(oa, 0, st, "pf_gemm_o"))) return rc;
-        if ((rc = launch_pf_residual(w.X, w.A, 2 * d, so, L.g_pa, n, d, m->eps, w.p1h, w.p1l, w.ld1, st))) return rc;
+        const bool gu_digits = residual_digits(L.gate, d);
+        const Q8Out q_gu{w.qh, w.qm, w.ql, w.qs, w.qsum, L.gate.group};
+        if ((rc = launch_pf_residual(w.X, w.A, 2 * d, so, L.g_pa, n, d, m->eps, w.p1h, w.p1l, w.ld1, st,
+                                     gu_digits ? &q_gu : nullptr)))
+            return rc;
         // gate/up with SwiGLU, then down
         GemmArgs ga = gemm(w.p1h, w.p1l, w.ld1, L.gate, n);
         ga.W1 = view(L.up);
         ga.z_hi = w.p2h;
         ga.z_lo = w.p2l;
         ga.ldz = m->dff;
-        if ((rc = attach_i8(ga, w, st))) return rc;
+        if (gu_digits) use_i8(ga, w);
+        else if ((rc = attach_i8(ga, w, st))) return rc;
         // With groups of 128 the gate/up kernel writes z as the down projection's int8
         // digits (in the z planes' place), so no quantisation pass runs between the two
         const bool z_digits = i8r_swiglu_digits_ok(ga, L.down.group) && gemm_i8_supported(L.down.group, m->dff);
@@ -276,8 +293,11 @@ extern "C" int atlas_prefill(const atlas_model* m, const int32_t* d_tokens, int3
         }
         if ((rc = launch_w4_gemm(da, 0, st, "pf_gemm_down"))) return rc;
         // y = h + RMSNorm_pf(m): the last layer leaves it to the head (last position only)
+        qkv_digits = !last && residual_digits(m->layers[l + 1].qkv, d);
+        const Q8Out q_qkv{w.qh, w.qm, w.ql, w.qs, w.qsum, last ? 128 : m->layers[l + 1].qkv.group};
         if (!last || !head)
-            if ((rc = launch_pf_residual(w.X, w.A, 2 * d, sd, L.g_pf, n, d, m->eps, w.p1h, w.p1l, w.ld1, st)))
+            if ((rc = launch_pf_residual(w.X, w.A, 2 * d, sd, L.g_pf, n, d, m->eps, w.p1h, w.p1l, w.ld1, st,
+                                         qkv_digits ? &q_qkv : nullptr)))
                 return rc;
     }
     if (!head) return ATLAS_OK;

@@ -102,7 +102,16 @@ int launch_pf_rope(const PfRopeArgs& a, hipStream_t st);
 int launch_pf_commit(const PfCommitArgs& a, hipStream_t st);
 int launch_pf_attn(const PfAttnArgs& a, hipStream_t st);
 int launch_pf_split(const float* X, int M, int K, int ldx, uint16_t* p_hi, uint16_t* p_lo, int ldp, hipStream_t st);
+// Destination of int8 digits made in place of bf16 planes (layout as in GemmArgs, row
+// strides K bytes and K / group groups).
+struct Q8Out {
+    int8_t *hi, *mid, *lo;
+    float *s, *sum;
+    int group;
+};
+// Whether the residual kernel can write the next GEMM's int8 digits for this group and d.
+bool residual_digits_ok(int group, int d);
 int launch_pf_residual(float* X, const float* A, int lda, int S, const float* g, int n, int d, float eps,
-                       uint16_t* p_hi, uint16_t* p_lo, int ldp, hipStream_t st);
+                       uint16_t* p_hi, uint16_t* p_lo, int ldp, hipStream_t st, const Q8Out* q = nullptr);
 
 }  // namespace atlas

@@ -1234,8 +1234,88 @@ __global__ __launch_bounds__(256) void pf_commit_kernel(PfCommitArgs a) {
 
 // X[t] += g * A[t] / rms(A[t]) and the bf16 planes of the new X[t].
 // A holds S (1 or 2) partial sums per row: row t's at A + t lda and A + t lda + d.
+// Digits of the int8 path for 4 consecutive columns held by one lane, quantised as
+// pf_quant8_kernel quantises its planes (x' = hi + lo, the row's group maximum, s = 2^e,
+// v = rint(x' / s), balanced digits), for groups of 128 or 256 columns: the group's lanes
+// are 32 or 64 consecutive lanes of a wave (LPG), so maxima and sums are DPP row
+// reductions plus lane swaps. Column c of an 8-column block goes to byte (c & 1) * 4 +
+// c / 2: the lane with the block's first 4 columns stores word 0 (columns 0, 2, 4, 6), its
+// neighbour word 1, each from its own two bytes and the neighbour's.
+template <int LPG>
+__device__ __forceinline__ void q8_digits4(float4 x, int8_t* q_hi, int8_t* q_mid, int8_t* q_lo, float* q_s,
+                                           float* q_sum, size_t row_q, size_t row_g, int col0, int group) {
+    float xs[4] = {x.x, x.y, x.z, x.w};
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        uint32_t hi, lo;
+        pf_split(xs[j], hi, lo);
+        xs[j] = bf16_bits_to_f32(hi) + bf16_bits_to_f32(lo);
+        mx = fmaxf(mx, fabsf(xs[j]));
+    }
+    mx = fmaxf(mx, dpp_f<0xB1>(mx));
+    mx = fmaxf(mx, dpp_f<0x4E>(mx));
+    mx = fmaxf(mx, dpp_f<0x141>(mx));
+    mx = fmaxf(mx, dpp_f<0x140>(mx));
+    mx = xor16_max(mx);
+    if (LPG == 64) mx = xor32_max(mx);
+    int e;
+    (void)frexpf(mx / Q8_MAX, &e);   // s = 2^e >= max|x'| / Q8_MAX (s = 1 for a zero group)
+    const float inv = ldexpf(1.f, -e);
+    int sum = 0;
+    uint32_t hw[2] = {0u, 0u}, mw[2] = {0u, 0u}, lw[2] = {0u, 0u};   // [even columns, odd columns]
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int v = (int)fminf(fmaxf(rintf(xs[j] * inv), -Q8_MAX), Q8_MAX);
+        sum += v;
+        const int ld = ((v + 128) & 255) - 128;
+        const int v1 = (v - ld) >> 8;   // exact: v - ld is a multiple of 256
+        const int md = ((v1 + 128) & 255) - 128;
+        const int hd = (v1 - md) >> 8;
+        const int sh = 8 * (j >> 1);
+        hw[j & 1] |= ((uint32_t)hd & 0xFFu) << sh;
+        mw[j & 1] |= ((uint32_t)md & 0xFFu) << sh;
+        lw[j & 1] |= ((uint32_t)ld & 0xFFu) << sh;
+    }
+    const bool first = ((col0 >> 2) & 1) == 0;   // the block's columns 0-3 (else 4-7)
+    auto word = [&](const uint32_t (&w)[2]) {     // this lane's word of the block
+        const uint32_t give = first ? w[1] : w[0];   // what the neighbour needs
+        const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, 0xB1, 0xF, 0xF, false);   // lane ^ 1
+        return first ? (w[0] | (got << 16)) : (got | (w[1] << 16));
+    };
+    const uint32_t H = word(hw), Mm = word(mw), Lw = word(lw);
+    const size_t o = row_q + (size_t)(col0 & ~7) + (first ? 0 : 4);
+    *reinterpret_cast<uint32_t*>(q_hi + o) = H;
+    *reinterpret_cast<uint32_t*>(q_mid + o) = Mm;
+    *reinterpret_cast<uint32_t*>(q_lo + o) = Lw;
+    // exact int32 sums: |v| <= Q8_MAX, at most 256 of them
+    sum += __builtin_amdgcn_update_dpp(0, sum, 0xB1, 0xF, 0xF, true);
+    sum += __builtin_amdgcn_update_dpp(0, sum, 0x4E, 0xF, 0xF, true);
+    sum += __builtin_amdgcn_update_dpp(0, sum, 0x141, 0xF, 0xF, true);
+    sum += __builtin_amdgcn_update_dpp(0, sum, 0x140, 0xF, 0xF, true);
+    {
+        const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)sum, (uint32_t)sum, false, false);
+        sum = (int)r[0] + (int)r[1];
+    }
+    if (LPG == 64) {
+        const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)sum, (uint32_t)sum, false, false);
+        sum = (int)r[0] + (int)r[1];
+    }
+    if (col0 % group == 0) {
+        q_s[row_g + col0 / group] = ldexpf(1.f, e);
+        q_sum[row_g + col0 / group] = (float)sum;
+    }
+}
+
+// X[t] += g * A[t] / rms(A[t]) with A[t] the sum of S partial rows (d apart); then the
+// next GEMM's input from the new X[t]: its bf16 planes, or (q_hi set; groups of 128 or
+// 256) its int8 digits, scales and group sums as pf_quant8_kernel would make them from
+// those planes. One block of 256 threads per row; d % 4 == 0, and with digits d is a
+// multiple of 1,024 so that every pass of the block covers whole groups.
 __global__ __launch_bounds__(256) void pf_residual_kernel(float* X, const float* A, int lda, int S, const float* g,
-                                                         int d, float eps, uint16_t* p_hi, uint16_t* p_lo, int ldp) {
+                                                         int d, float eps, uint16_t* p_hi, uint16_t* p_lo, int ldp,
+                                                         int8_t* q_hi, int8_t* q_mid, int8_t* q_lo, float* q_s,
+                                                         float* q_sum, int group) {
     __shared__ float red[16];
     const int t = blockIdx.x;
     const float4* a4 = reinterpret_cast<const float4*>(A + (size_t)t * lda);
@@ -1262,7 +1342,13 @@ __global__ __launch_bounds__(256) void pf_residual_kernel(float* X, const float*
         const float4 h = make_float4(x.x + gg.x * (v.x * r), x.y + gg.y * (v.y * r), x.z + gg.z * (v.z * r),
                                      x.w + gg.w * (v.w * r));
         x4[i] = h;
-        store_split4(h, p_hi + (size_t)t * ldp + 4 * i, p_lo + (size_t)t * ldp + 4 * i);
+        if (q_hi) {
+            const size_t rq = (size_t)t * d, rg = (size_t)t * (d / group);
+            if (group == 128) q8_digits4<32>(h, q_hi, q_mid, q_lo, q_s, q_sum, rq, rg, 4 * i, group);
+            else q8_digits4<64>(h, q_hi, q_mid, q_lo, q_s, q_sum, rq, rg, 4 * i, group);
+        } else {
+            store_split4(h, p_hi + (size_t)t * ldp + 4 * i, p_lo + (size_t)t * ldp + 4 * i);
+        }
     }
 }
 
@@ -1694,11 +1780,16 @@ int launch_pf_split(const float* X, int M, int K, int ldx, uint16_t* p_hi, uint1
     return ATLAS_OK;
 }
 
+bool residual_digits_ok(int group, int d) { return (group == 128 || group == 256) && d % 1024 == 0; }
+
 int launch_pf_residual(float* X, const float* A, int lda, int S, const float* g, int n, int d, float eps,
-                       uint16_t* p_hi, uint16_t* p_lo, int ldp, hipStream_t st) {
+                       uint16_t* p_hi, uint16_t* p_lo, int ldp, hipStream_t st, const Q8Out* q) {
     ATLAS_CHECK_SHAPE((S == 1 || S == 2) && lda % 4 == 0 && lda >= S * d && d % 4 == 0, "residual partials");
+    ATLAS_CHECK_SHAPE(!q || residual_digits_ok(q->group, d), "residual digits: group %d, d %d", q ? q->group : 0, d);
     prof_mark("pf_residual_norm", st);
-    ATLAS_KLAUNCH(pf_residual_kernel, dim3(n), dim3(256), 0, st, X, A, lda, S, g, d, eps, p_hi, p_lo, ldp);
+    ATLAS_KLAUNCH(pf_residual_kernel, dim3(n), dim3(256), 0, st, X, A, lda, S, g, d, eps, p_hi, p_lo, ldp,
+                  q ? q->hi : nullptr, q ? q->mid : nullptr, q ? q->lo : nullptr, q ? q->s : nullptr,
+                  q ? q->sum : nullptr, q ? q->group : 128);
     ATLAS_LAUNCH_CHECK("pf_residual_kernel");
     return ATLAS_OK;
 }
