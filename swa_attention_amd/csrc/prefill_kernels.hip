@@ -1312,6 +1312,9 @@ __device__ __forceinline__ void q8_digits4(float4 x, int8_t* q_hi, int8_t* q_mid
 // 256) its int8 digits, scales and group sums as pf_quant8_kernel would make them from
 // those planes. One block of 256 threads per row; d % 4 == 0, and with digits d is a
 // multiple of 1,024 so that every pass of the block covers whole groups.
+// NV > 0: d <= 1,024 NV, and every input of the row (partials, residual, gains) is
+// loaded into registers before the first use, one pass; NV = 0: two passes over the row.
+template <int NV>
 __global__ __launch_bounds__(256) void pf_residual_kernel(float* X, const float* A, int lda, int S, const float* g,
                                                          int d, float eps, uint16_t* p_hi, uint16_t* p_lo, int ldp,
                                                          int8_t* q_hi, int8_t* q_mid, int8_t* q_lo, float* q_s,
@@ -1328,17 +1331,9 @@ __global__ __launch_bounds__(256) void pf_residual_kernel(float* X, const float*
         }
         return v;
     };
-    float ss = 0.f;
-    for (int i = threadIdx.x; i < d / 4; i += blockDim.x) {
-        const float4 v = part(i);
-        ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
-    }
-    ss = block_sum(ss, red);
-    const float r = 1.0f / sqrtf(ss / (float)d + eps);
     float4* x4 = reinterpret_cast<float4*>(X + (size_t)t * d);
     const float4* g4 = reinterpret_cast<const float4*>(g);
-    for (int i = threadIdx.x; i < d / 4; i += blockDim.x) {
-        const float4 v = part(i), gg = g4[i], x = x4[i];
+    auto emit = [&](int i, float4 v, float4 x, float4 gg, float r) {
         const float4 h = make_float4(x.x + gg.x * (v.x * r), x.y + gg.y * (v.y * r), x.z + gg.z * (v.z * r),
                                      x.w + gg.w * (v.w * r));
         x4[i] = h;
@@ -1349,6 +1344,41 @@ __global__ __launch_bounds__(256) void pf_residual_kernel(float* X, const float*
         } else {
             store_split4(h, p_hi + (size_t)t * ldp + 4 * i, p_lo + (size_t)t * ldp + 4 * i);
         }
+    };
+    const int n4 = d / 4;
+    if constexpr (NV > 0) {
+        float4 pa[NV], pb[NV], xv[NV], gv[NV];
+#pragma unroll
+        for (int j = 0; j < NV; j++) {
+            const int i = threadIdx.x + 256 * j, ic = i < n4 ? i : 0;
+            pa[j] = a4[ic];
+            pb[j] = b4[ic];   // the first partial again when S = 1 (not added)
+            xv[j] = x4[ic];
+            gv[j] = g4[ic];
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < NV; j++) {
+            if (S > 1) pa[j] = make_float4(pa[j].x + pb[j].x, pa[j].y + pb[j].y, pa[j].z + pb[j].z, pa[j].w + pb[j].w);
+            if (threadIdx.x + 256 * j < n4)
+                ss = fmaf(pa[j].x, pa[j].x, fmaf(pa[j].y, pa[j].y, fmaf(pa[j].z, pa[j].z, fmaf(pa[j].w, pa[j].w, ss))));
+        }
+        ss = block_sum(ss, red);
+        const float r = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+        for (int j = 0; j < NV; j++) {
+            const int i = threadIdx.x + 256 * j;
+            if (i < n4) emit(i, pa[j], xv[j], gv[j], r);
+        }
+    } else {
+        float ss = 0.f;
+        for (int i = threadIdx.x; i < n4; i += blockDim.x) {
+            const float4 v = part(i);
+            ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+        }
+        ss = block_sum(ss, red);
+        const float r = 1.0f / sqrtf(ss / (float)d + eps);
+        for (int i = threadIdx.x; i < n4; i += blockDim.x) emit(i, part(i), x4[i], g4[i], r);
     }
 }
 
@@ -1787,9 +1817,15 @@ int launch_pf_residual(float* X, const float* A, int lda, int S, const float* g,
     ATLAS_CHECK_SHAPE((S == 1 || S == 2) && lda % 4 == 0 && lda >= S * d && d % 4 == 0, "residual partials");
     ATLAS_CHECK_SHAPE(!q || residual_digits_ok(q->group, d), "residual digits: group %d, d %d", q ? q->group : 0, d);
     prof_mark("pf_residual_norm", st);
-    ATLAS_KLAUNCH(pf_residual_kernel, dim3(n), dim3(256), 0, st, X, A, lda, S, g, d, eps, p_hi, p_lo, ldp,
-                  q ? q->hi : nullptr, q ? q->mid : nullptr, q ? q->lo : nullptr, q ? q->s : nullptr,
-                  q ? q->sum : nullptr, q ? q->group : 128);
+    int8_t *qh = q ? q->hi : nullptr, *qm = q ? q->mid : nullptr, *ql = q ? q->lo : nullptr;
+    float *qs = q ? q->s : nullptr, *qsum = q ? q->sum : nullptr;
+    const int qg = q ? q->group : 128;
+    if (d <= 4 * 256 * 5)
+        ATLAS_KLAUNCH((pf_residual_kernel<5>), dim3(n), dim3(256), 0, st, X, A, lda, S, g, d, eps, p_hi, p_lo, ldp, qh,
+                      qm, ql, qs, qsum, qg);
+    else
+        ATLAS_KLAUNCH((pf_residual_kernel<0>), dim3(n), dim3(256), 0, st, X, A, lda, S, g, d, eps, p_hi, p_lo, ldp, qh,
+                      qm, ql, qs, qsum, qg);
     ATLAS_LAUNCH_CHECK("pf_residual_kernel");
     return ATLAS_OK;
 }
