@@ -1232,8 +1232,6 @@ __global__ __launch_bounds__(256) void pf_commit_kernel(PfCommitArgs a) {
     }
 }
 
-// X[t] += g * A[t] / rms(A[t]) and the bf16 planes of the new X[t].
-// A holds S (1 or 2) partial sums per row: row t's at A + t lda and A + t lda + d.
 // Digits of the int8 path for 4 consecutive columns held by one lane, quantised as
 // pf_quant8_kernel quantises its planes (x' = hi + lo, the row's group maximum, s = 2^e,
 // v = rint(x' / s), balanced digits), for groups of 128 or 256 columns: the group's lanes
@@ -1307,13 +1305,14 @@ __device__ __forceinline__ void q8_digits4(float4 x, int8_t* q_hi, int8_t* q_mid
     }
 }
 
-// X[t] += g * A[t] / rms(A[t]) with A[t] the sum of S partial rows (d apart); then the
-// next GEMM's input from the new X[t]: its bf16 planes, or (q_hi set; groups of 128 or
-// 256) its int8 digits, scales and group sums as pf_quant8_kernel would make them from
-// those planes. One block of 256 threads per row; d % 4 == 0, and with digits d is a
-// multiple of 1,024 so that every pass of the block covers whole groups.
-// NV > 0: d <= 1,024 NV, and every input of the row (partials, residual, gains) is
-// loaded into registers before the first use, one pass; NV = 0: two passes over the row.
+// X[t] += g * A[t] / rms(A[t]) with A[t] the sum of S (1 or 2) partial rows (row t's at
+// A + t lda and A + t lda + d); then the next GEMM's input from the new X[t]: its bf16
+// planes, or (q_hi set; groups of 128 or 256) its int8 digits, scales and group sums as
+// pf_quant8_kernel would make them from those planes. One block of 256 threads per row;
+// d % 4 == 0, and with digits d is a multiple of 1,024 so that every pass of the block
+// covers whole groups. NV > 0: d <= 1,024 NV, and every input of the row (partials,
+// residual, gains) is loaded into registers before the first use, one pass; NV = 0: two
+// passes over the row.
 template <int NV>
 __global__ __launch_bounds__(256) void pf_residual_kernel(float* X, const float* A, int lda, int S, const float* g,
                                                          int d, float eps, uint16_t* p_hi, uint16_t* p_lo, int ldp,
