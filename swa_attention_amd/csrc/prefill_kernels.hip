@@ -1148,6 +1148,11 @@ __global__ __launch_bounds__(256) void pf_embed_kernel(const int32_t* tokens, in
 // buffers (rounded to bf16 when the cache is bf16: what is stored is what attends).
 // One block per position: the S partial projections are added into an LDS copy of the
 // row (dynamic shared memory, (Hq + 2 Hkv) * 128 floats), which every later read uses.
+// NE > 0 (S <= 2, (Hq + 2 Hkv) * 128 <= 256 NE, Hq * 128 a multiple of 256, at most 256 NR
+// rotation pairs): every load of the block (the partial rows, the gains of the thread's
+// rotation pairs) is issued before the first use, and the sums of squares come from the
+// registers in the order of the LDS loop of NE = 0.
+template <int NE, int NR>
 __global__ __launch_bounds__(256) void pf_rope_kernel(PfRopeArgs a) {
     constexpr int D = 128;
     extern __shared__ float s_row[];
@@ -1156,15 +1161,49 @@ __global__ __launch_bounds__(256) void pf_rope_kernel(PfRopeArgs a) {
     const int t = blockIdx.x, pos = a.start_pos + t;
     const int nq = a.Hq * D, nk = a.Hkv * D, nqkv = nq + 2 * nk;
     float* row = a.qkv + (size_t)t * a.ld;
-    for (int i = threadIdx.x; i < nqkv; i += blockDim.x) {
-        float v = row[i];
-        for (int s = 1; s < a.S; s++) v += row[(size_t)s * a.pstride + i];
-        s_row[i] = v;
-    }
-    __syncthreads();
     float sq = 0.f, sk = 0.f;
-    for (int i = threadIdx.x; i < nq; i += blockDim.x) sq = fmaf(s_row[i], s_row[i], sq);
-    for (int i = threadIdx.x; i < nk; i += blockDim.x) sk = fmaf(s_row[nq + i], s_row[nq + i], sk);
+    float g0[NR > 0 ? NR : 1], g1[NR > 0 ? NR : 1];
+    if constexpr (NE > 0) {
+        float v0[NE], v1[NE];
+        const size_t p1 = a.S > 1 ? (size_t)a.pstride : 0;
+#pragma unroll
+        for (int k = 0; k < NE; k++) {
+            const int i = threadIdx.x + 256 * k, ic = i < nqkv ? i : 0;
+            v0[k] = row[ic];
+            v1[k] = row[p1 + ic];
+        }
+#pragma unroll
+        for (int r = 0; r < NR; r++) {
+            const int u = threadIdx.x + 256 * r, uc = u < (a.Hq + a.Hkv) * 64 ? u : 0;
+            const int h = uc >> 6, i = uc & 63;
+            const float* g = h >= a.Hq ? a.g_k + (h - a.Hq) * D : a.g_q + h * D;
+            g0[r] = g[i];
+            g1[r] = g[i + 64];
+        }
+#pragma unroll
+        for (int k = 0; k < NE; k++) {
+            const int i = threadIdx.x + 256 * k;
+            const float v = a.S > 1 ? v0[k] + v1[k] : v0[k];
+            if (i < nqkv) s_row[i] = v;
+            if (i < nq) sq = fmaf(v, v, sq);
+        }
+#pragma unroll
+        for (int k = 0; k < NE; k++) {
+            const int i = threadIdx.x + 256 * k;
+            const float v = a.S > 1 ? v0[k] + v1[k] : v0[k];
+            if (i >= nq && i < nq + nk) sk = fmaf(v, v, sk);
+        }
+        __syncthreads();
+    } else {
+        for (int i = threadIdx.x; i < nqkv; i += blockDim.x) {
+            float v = row[i];
+            for (int s = 1; s < a.S; s++) v += row[(size_t)s * a.pstride + i];
+            s_row[i] = v;
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < nq; i += blockDim.x) sq = fmaf(s_row[i], s_row[i], sq);
+        for (int i = threadIdx.x; i < nk; i += blockDim.x) sk = fmaf(s_row[nq + i], s_row[nq + i], sk);
+    }
     sq = block_sum(sq, red);
     sk = block_sum(sk, red);
     const float rq = 1.0f / sqrtf(sq / (float)nq + a.eps);
@@ -1179,13 +1218,12 @@ __global__ __launch_bounds__(256) void pf_rope_kernel(PfRopeArgs a) {
     }
     __syncthreads();
     const int npairs = (a.Hq + a.Hkv) * 64;
-    for (int u = threadIdx.x; u < npairs; u += blockDim.x) {
+    auto rotate = [&](int u, float ga, float gb) {
         const int h = u >> 6, i = u & 63;
         const bool isk = h >= a.Hq;
         const float rr = isk ? rk : rq;
-        const float* g = isk ? a.g_k + (h - a.Hq) * D : a.g_q + h * D;
         const int base = h * D;   // q heads, then k heads, in the projection row
-        const float x0 = g[i] * (s_row[base + i] * rr), x1 = g[i + 64] * (s_row[base + i + 64] * rr);
+        const float x0 = ga * (s_row[base + i] * rr), x1 = gb * (s_row[base + i + 64] * rr);
         const float c = s_cos[i], sn = s_sin[i];
         const float y0 = x0 * c - x1 * sn, y1 = x1 * c + x0 * sn;
         if (isk) {
@@ -1200,6 +1238,17 @@ __global__ __launch_bounds__(256) void pf_rope_kernel(PfRopeArgs a) {
         } else {
             row[base + i] = y0;
             row[base + i + 64] = y1;
+        }
+    };
+    if constexpr (NR > 0) {
+#pragma unroll
+        for (int r = 0; r < NR; r++)
+            if (threadIdx.x + 256 * r < npairs) rotate(threadIdx.x + 256 * r, g0[r], g1[r]);
+    } else {
+        for (int u = threadIdx.x; u < npairs; u += blockDim.x) {
+            const int h = u >> 6, i = u & 63;
+            const float* g = h >= a.Hq ? a.g_k + (h - a.Hq) * D : a.g_q + h * D;
+            rotate(u, g[i], g[i + 64]);
         }
     }
     for (int u = threadIdx.x; u < nk; u += blockDim.x) {
@@ -1771,7 +1820,11 @@ int launch_pf_rope(const PfRopeArgs& a, hipStream_t st) {
                           nqkv * 4 <= 64 * 1024,
                       "qkv partials: S=%d pstride=%d ld=%d", a.S, a.pstride, a.ld);
     prof_mark("pf_qk_norm_rope", st);
-    ATLAS_KLAUNCH(pf_rope_kernel, dim3(a.n), dim3(256), (size_t)nqkv * 4, st, a);
+    const int nq = a.Hq * 128, npairs = (a.Hq + a.Hkv) * 64;
+    if (a.S <= 2 && nqkv <= 256 * 28 && nq % 256 == 0 && npairs <= 256 * 12)
+        ATLAS_KLAUNCH((pf_rope_kernel<28, 12>), dim3(a.n), dim3(256), (size_t)nqkv * 4, st, a);
+    else
+        ATLAS_KLAUNCH((pf_rope_kernel<0, 0>), dim3(a.n), dim3(256), (size_t)nqkv * 4, st, a);
     ATLAS_LAUNCH_CHECK("pf_rope_kernel");
     return ATLAS_OK;
 }
