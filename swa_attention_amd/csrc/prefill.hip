@@ -112,8 +112,9 @@ void set_split(GemmArgs& g, int S, int d) {
     g.c_split = S > 1 ? (size_t)d : 0;   // partial s of row t at C + t ldc + s d
 }
 
-// Int8 digit planes of the GEMM input for groups of 128, 256 or 512 (the int8 matrix-core
-// kernel); other groups keep the bf16 planes.
+// The workspace's int8 digit planes as the GEMM input (the int8 matrix-core kernel for
+// groups of 128, 256 or 512); other groups keep the bf16 planes. attach_i8() makes the
+// digits from the bf16 planes first; use_i8() takes digits a producing kernel wrote.
 void use_i8(GemmArgs& g, const PrefillWs& w) {
     g.q_hi = w.qh;
     g.q_mid = w.qm;
