@@ -330,6 +330,22 @@ def measure_prefill(args, dm, cm, m, dev, wl_name):
                                "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "avg_launch_us": round(tot / cnt * 1e3, 1),
                                "note": "algorithmic flops; the bf16 hi/lo activation planes issue twice as many"}
+    # causal attention of the prompt (positions 0 .. n-1): 4 hd flops per (query, key) pair
+    # and query head (QK^T and PV), keys limited to the window on the window layers
+    att = {k: prof[k] for k in ("pf_attn_window", "pf_attn_full") if k in prof}
+    if att:
+        def pairs(window):
+            return sum(min(t, window - 1) + 1 for t in range(n)) if window > 0 else n * (n + 1) // 2
+        fl = {"pf_attn_window": 4.0 * m.hd * m.hq * pairs(m.window), "pf_attn_full": 4.0 * m.hd * m.hq * pairs(0)}
+        cnt = sum(c for c, _ in att.values())
+        tot_ms = sum(t for _, t in att.values())
+        ach = sum(att[k][0] * fl[k] for k in att) / (tot_ms * 1e-3) / 1e12
+        out["attention"] = {"bound": "mfma", "kernel": f"pf_attn_kernel<{m.hq // m.hkv}> (causal GQA)",
+                            "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(ach / PEAK_BF16_TFLOPS, 4), "avg_launch_us": round(tot_ms / cnt * 1e3, 1),
+                            "launches": cnt,
+                            "note": "algorithmic flops; the bf16 hi/lo operand planes issue "
+                                    + ("two" if m.kv_dtype == 1 else "three") + " products per multiply-add"}
     return out
 
 
